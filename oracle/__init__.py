@@ -1,0 +1,166 @@
+"""Oracle for single-token paged-KV decode attention: TEST INFRASTRUCTURE ONLY.
+
+A plain scalar C++ implementation in fp64 (``oracle.cpp``), loaded through ctypes. Only the
+tests, the smoke check and the benchmark's CPU-baseline leg may import this package; the GPU
+library never does, and the two share no code.
+
+Every function takes and returns host NumPy arrays. Floating-point results are fp64.
+dtype codes: 0 = fp32, 1 = bf16 (raw uint16 bits), 2 = fp8 e4m3fn (raw uint8 bits).
+
+What each function follows is cited in ``oracle.cpp``. Parity against the pages is pinned by the
+``-m "not gpu"`` tests, except the RoPE convention, whose helper body the pages do not show:
+parity unpinned (only invariants pin it).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB, build
+
+F32, BF16, FP8 = 0, 1, 2
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        f32 = ctypes.c_float
+        L.oracle_decode.restype = i32
+        L.oracle_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, i32, P,
+                                    i32, i32, f32, f32, P, P, f32, P, P, i32, P, P, P, i32]
+        L.oracle_merge_state.restype = None
+        L.oracle_merge_state.argtypes = [i32, i32, i32, P, P, P, P]
+        L.oracle_append_kv.restype = i32
+        L.oracle_append_kv.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P]
+        L.oracle_validate_page_table.restype = i32
+        L.oracle_validate_page_table.argtypes = [i32, i32, i32, i32, P, P, P, i32]
+        L.oracle_fp8_e4m3fn_value.restype = ctypes.c_double
+        L.oracle_fp8_e4m3fn_value.argtypes = [ctypes.c_uint8]
+        L.oracle_fp8_e4m3fn_encode.restype = ctypes.c_uint8
+        L.oracle_fp8_e4m3fn_encode.argtypes = [f32]
+        L.oracle_bf16_value.restype = ctypes.c_double
+        L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        L.oracle_rope_rotate.restype = None
+        L.oracle_rope_rotate.argtypes = [P, i32, ctypes.c_double, f32, f32]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def decode(*, B, H_qo, H_kv, D, ps, max_num_pages, q_dtype, kv_dtype, q, pages, indptr, values,
+           length_info, sliding_window=False, rotary_mode=0, rope_scale=1.0, rope_theta=1e4,
+           q_rope_position=None, k_rope_pos_offset=None, sm_scale, k_scale=None, v_scale=None,
+           select=None, nthreads=0):
+    """Decode attention. q/pages are raw arrays in their storage dtype (fp32, uint16 bf16 bits,
+    uint8 fp8 codes). Returns (out[n, D] fp64, lse[n] fp64) for the selected (b, h_qo) pairs
+    (select = int array [n, 2]) or for all pairs in (b, h_qo) order reshaped to [B, H_qo, ...]."""
+    indptr = _c(indptr, np.int32)
+    values = _c(values, np.int32)
+    length_info = _c(length_info, np.int32)
+    if values.size == 0:
+        values = np.zeros(1, np.int32)
+    qrp = _c(q_rope_position, np.int32) if q_rope_position is not None else np.zeros(max(B, 1), np.int32)
+    kro = _c(k_rope_pos_offset, np.int32) if k_rope_pos_offset is not None else np.zeros(max(B, 1), np.int32)
+    ks = _c(k_scale, np.float32)
+    vs = _c(v_scale, np.float32)
+    sel = None if select is None else _c(select, np.int32).reshape(-1, 2)
+    n = sel.shape[0] if sel is not None else B * H_qo
+    out = np.zeros((max(n, 1), D), np.float64)
+    lse = np.zeros(max(n, 1), np.float64)
+    q = np.ascontiguousarray(q)
+    pages = np.ascontiguousarray(pages)
+    nnz = int(indptr[-1]) if indptr.size else 0
+    rc = lib().oracle_decode(B, H_qo, H_kv, D, ps, max_num_pages, q_dtype, kv_dtype, _ptr(q),
+                             _ptr(pages), _ptr(indptr), _ptr(values), max(nnz, values.size),
+                             _ptr(length_info), int(bool(sliding_window)), int(rotary_mode),
+                             float(rope_scale), float(rope_theta), _ptr(qrp), _ptr(kro),
+                             float(sm_scale), _ptr(ks), _ptr(vs), 0 if sel is None else n,
+                             _ptr(sel), _ptr(out), _ptr(lse), int(nthreads))
+    if rc != 0:
+        raise OracleError(f"oracle_decode failed with code {rc}")
+    out, lse = out[:n], lse[:n]
+    if sel is None:
+        return out.reshape(B, H_qo, D), lse.reshape(B, H_qo)
+    return out, lse
+
+
+def merge_state(v, s, v_other, s_other):
+    """Pairwise base-2 merge; returns new (v, s) arrays (fp64). v: [N, H, D], s: [N, H]."""
+    v = np.array(v, dtype=np.float64, order="C")
+    s = np.array(s, dtype=np.float64, order="C")
+    vo = _c(v_other, np.float64)
+    so = _c(s_other, np.float64)
+    N, H, D = v.shape
+    lib().oracle_merge_state(N, H, D, _ptr(v), _ptr(s), _ptr(vo), _ptr(so))
+    return v, s
+
+
+def append_kv(*, pages, new_k, new_v, slots, H_kv, D, ps, in_dtype, kv_dtype, k_scale=None,
+              v_scale=None):
+    """KV append on a host copy of the pool (modified in place and returned)."""
+    assert pages.flags["C_CONTIGUOUS"]
+    new_k = np.ascontiguousarray(new_k)
+    new_v = np.ascontiguousarray(new_v)
+    slots = _c(slots, np.int32)
+    ks = _c(k_scale, np.float32)
+    vs = _c(v_scale, np.float32)
+    max_num_pages = pages.shape[0]
+    rc = lib().oracle_append_kv(slots.size, H_kv, D, ps, max_num_pages, in_dtype, kv_dtype,
+                                _ptr(new_k), _ptr(new_v), _ptr(slots), _ptr(ks), _ptr(vs),
+                                _ptr(pages))
+    if rc != 0:
+        raise OracleError(f"oracle_append_kv failed with code {rc}")
+    return pages
+
+
+def validate_page_table(*, B, ps, max_num_pages, indptr, values, length_info, sliding_window=False):
+    indptr = _c(indptr, np.int32)
+    values = _c(values, np.int32)
+    if values.size == 0:
+        values = np.zeros(1, np.int32)
+    length_info = _c(length_info, np.int32)
+    return int(lib().oracle_validate_page_table(B, ps, max_num_pages, int(values.size),
+                                                _ptr(indptr), _ptr(values), _ptr(length_info),
+                                                int(bool(sliding_window))))
+
+
+def fp8_value(code: int) -> float:
+    return float(lib().oracle_fp8_e4m3fn_value(code))
+
+
+def fp8_encode(x: float) -> int:
+    return int(lib().oracle_fp8_e4m3fn_encode(x))
+
+
+def fp8_encode_array(x):
+    x = np.asarray(x, np.float32).ravel()
+    f = lib().oracle_fp8_e4m3fn_encode
+    return np.array([f(float(v)) for v in x], np.uint8)
+
+
+def bf16_value(bits: int) -> float:
+    return float(lib().oracle_bf16_value(bits))
+
+
+def rope_rotate(x, pos, rope_scale, rope_theta):
+    x = np.array(x, dtype=np.float64, order="C")
+    lib().oracle_rope_rotate(_ptr(x), x.size, float(pos), float(rope_scale), float(rope_theta))
+    return x

@@ -1,0 +1,464 @@
+"""Pins the oracle to what the pages and the mathematics fix (CPU only).
+
+Each test checks the oracle against something other than itself: brute force on a contiguous cache,
+closed forms, invariants, the pages' own online recurrences run in fp64, and library routines
+(torch's fp8 / bf16 conversions).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.dense_ref import LOG2E, contiguous_kv, dense_attention, to_f64
+
+
+def run_oracle(w, **over):
+    kw = w.oracle_kwargs()
+    kw.update(over)
+    return oracle.decode(**kw)
+
+
+def small(**kw):
+    base = dict(B=3, H_qo=4, H_kv=2, D=16, page_size=4, seq_lens=[7, 1, 13], q_dtype="f32",
+                kv_dtype="f32", seed=11, max_num_pages=12)
+    base.update(kw)
+    return synth.make_workload(**base)
+
+
+@pytest.mark.parametrize("kv_dtype,q_dtype", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "bf16")])
+@pytest.mark.parametrize("order", ["identity", "shuffled"])
+def test_matches_dense_bruteforce(kv_dtype, q_dtype, order):
+    """Paged oracle == textbook softmax(q K^T s) V on the flattened contiguous cache."""
+    w = small(kv_dtype=kv_dtype, q_dtype=q_dtype, page_order=order, seq_lens=[7, 1, 13])
+    out, lse = run_oracle(w)
+    G = w.H_qo // w.H_kv
+    q64 = to_f64(w.q, w.q_dtype)
+    for b in range(w.B):
+        for hq in range(w.H_qo):
+            K, V = contiguous_kv(w, b, hq // G)
+            o, l = dense_attention(q64[b, hq], K, V, w.sm_scale)
+            np.testing.assert_allclose(out[b, hq], o, rtol=0, atol=1e-12)
+            assert abs(lse[b, hq] - l) < 1e-12
+
+
+def test_single_row_closed_form():
+    """L = 1: out = v_0 exactly and lse = s_0 * log2(e)."""
+    w = small(seq_lens=[1, 1, 1])
+    out, lse = run_oracle(w)
+    q64 = to_f64(w.q, "f32")
+    for b in range(w.B):
+        page = w.page_values[w.page_indptr[b]]
+        for hq in range(w.H_qo):
+            h = hq // 2
+            k = w.pages[page, 0, h, 0].astype(np.float64)
+            v = w.pages[page, 1, h, 0].astype(np.float64)
+            assert np.array_equal(out[b, hq], v)
+            assert abs(lse[b, hq] - w.sm_scale * float(q64[b, hq] @ k) * LOG2E) < 1e-13
+
+
+def test_zero_query_is_mean():
+    """q = 0: every score is 0, so out = mean of V rows and lse = log2(L)."""
+    w = small(seq_lens=[7, 4, 13])
+    w.q[:] = 0
+    out, lse = run_oracle(w)
+    for b in range(w.B):
+        for hq in range(w.H_qo):
+            _, V = contiguous_kv(w, b, hq // 2)
+            np.testing.assert_allclose(out[b, hq], V.mean(0), rtol=0, atol=1e-14)
+            assert abs(lse[b, hq] - np.log2(w.seq_lens[b])) < 1e-13
+
+
+def test_uniform_v_gives_v():
+    """Every V row equal to u: out = u whatever the scores."""
+    w = small(seq_lens=[9, 3, 16])
+    u = np.linspace(-1, 1, w.D).astype(np.float32)
+    for p in w.used_pages:
+        w.pages[p, 1] = u
+    out, _ = run_oracle(w)
+    np.testing.assert_allclose(out, np.broadcast_to(u, out.shape), rtol=0, atol=1e-14)
+
+
+def test_empty_sequence_convention():
+    """A sequence with no pages: out = 0, lse = -5e4 (the CPU variant's initial state, no rows)."""
+    w = small(seq_lens=[5, 0, 9])
+    out, lse = run_oracle(w)
+    assert np.all(out[1] == 0.0) and np.all(lse[1] == -5e4)
+    assert np.all(np.isfinite(out[[0, 2]]))
+
+
+def test_lse_matches_natural_log_recurrence():
+    """The NKI flash kernel (vLLM nki_flash_attn page, _flash_attention_core) keeps the LSE in
+    natural log, tile by tile: first tile l = max + log(sum), later l = m + log(exp(l_prev - m) +
+    sum) with m the running max. Run that recurrence in fp64; lse_2 must equal lse_e * log2(e)."""
+    w = small(seq_lens=[13, 6, 16])
+    _, lse = run_oracle(w)
+    q64 = to_f64(w.q, "f32")
+    tile = 3
+    for b in range(w.B):
+        for hq in range(w.H_qo):
+            K, _ = contiguous_kv(w, b, hq // 2)
+            s = (K @ q64[b, hq]) * w.sm_scale
+            l = None
+            m = -np.inf
+            for t0 in range(0, s.size, tile):
+                st = s[t0:t0 + tile]
+                m = max(m, st.max())
+                ps = np.exp(st - m).sum()
+                l = m + np.log(ps) if l is None else m + np.log(np.exp(l - m) + ps)
+            assert abs(lse[b, hq] - l * LOG2E) < 1e-12
+
+
+def test_pages_online_recurrence_matches_two_pass():
+    """The TVM CPU decode's own algorithm (m = -5e4, d = 1, O = 0; scores in log2 units; per row
+    new_m = max(m, s), d = d 2^(m - new_m) + 2^(s - new_m), O rescaled then += 2^(s - m) V;
+    out = O / d, lse = m + log2 d), run in fp64, equals the oracle's two-pass definition."""
+    w = small(seq_lens=[13, 2, 16])
+    out, lse = run_oracle(w)
+    q64 = to_f64(w.q, "f32")
+    for b in range(w.B):
+        for hq in range(w.H_qo):
+            K, V = contiguous_kv(w, b, hq // 2)
+            m, d, O = -5e4, 1.0, np.zeros(w.D)
+            for r in range(K.shape[0]):
+                s = float(q64[b, hq] @ K[r]) * w.sm_scale * LOG2E
+                new_m = max(m, s)
+                d = d * 2.0 ** (m - new_m) + 2.0 ** (s - new_m)
+                O = O * 2.0 ** (m - new_m)
+                m = new_m
+                O = O + V[r] * 2.0 ** (s - m)
+            np.testing.assert_allclose(out[b, hq], O / d, rtol=0, atol=1e-12)
+            assert abs(lse[b, hq] - (m + np.log2(d))) < 1e-12
+
+
+def test_gqa_equals_mha_with_repeated_heads():
+    """GQA (q head h_qo reads kv head h_qo // G) == MHA whose kv heads are repeated G times."""
+    w = small(H_qo=8, H_kv=2, seq_lens=[7, 12, 5])
+    out_g, lse_g = run_oracle(w)
+    pages_mha = np.repeat(w.pages, 4, axis=2)
+    out_m, lse_m = run_oracle(w, H_kv=8, pages=pages_mha)
+    assert np.array_equal(out_g, out_m) and np.array_equal(lse_g, lse_m)
+
+
+def test_page_permutation_invariance():
+    """Relabel physical pages by a permutation and move the data: outputs are bit-identical."""
+    w = small(seq_lens=[7, 12, 5])
+    out0, lse0 = run_oracle(w)
+    perm = np.random.default_rng(5).permutation(w.max_num_pages).astype(np.int32)
+    pool = np.empty_like(w.pages)
+    pool[perm] = w.pages
+    out1, lse1 = run_oracle(w, pages=pool, values=perm[w.page_values])
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+
+
+def _prefix_and_suffix(w, b, k):
+    """Page tables of rows [0, k) (truncated list + last_page_len) and rows [k, L) (window with
+    sink 0 starting at k) for one sequence b of w, as separate single-sequence problems."""
+    ps = w.page_size
+    pages = w.page_values[w.page_indptr[b]:w.page_indptr[b + 1]]
+    L = int(w.seq_lens[b])
+    np_pre = (k + ps - 1) // ps
+    pre = dict(B=1, indptr=np.array([0, np_pre], np.int32), values=pages[:np_pre],
+               length_info=np.array([k - (np_pre - 1) * ps], np.int32), sliding_window=False)
+    suf = dict(B=1, indptr=np.array([0, pages.size], np.int32), values=pages,
+               length_info=np.array([[L - (pages.size - 1) * ps], [k], [0]], np.int32),
+               sliding_window=True)
+    return pre, suf
+
+
+@pytest.mark.parametrize("k", [4, 8, 5, 11])  # page boundaries (ps = 4) and mid-page
+def test_merge_of_two_halves_equals_whole(k):
+    w = small(seq_lens=[13, 13, 13], B=3)
+    out, lse = run_oracle(w)
+    b = 2
+    pre, suf = _prefix_and_suffix(w, b, k)
+    q1 = w.q[b:b + 1]
+    o1, l1 = run_oracle(w, q=q1, **pre)
+    o2, l2 = run_oracle(w, q=q1, **suf)
+    om, lm = oracle.merge_state(o1, l1, o2, l2)
+    np.testing.assert_allclose(om[0], out[b], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lm[0], lse[b], rtol=0, atol=1e-12)
+
+
+def test_nway_merge_is_order_independent_and_exact():
+    """Three partitions merged in two different orders both equal the whole (associativity)."""
+    w = small(seq_lens=[16, 16, 16])
+    out, lse = run_oracle(w)
+    b = 0
+    ps = w.page_size
+    pages = w.page_values[w.page_indptr[b]:w.page_indptr[b + 1]]
+    q1 = w.q[b:b + 1]
+    cuts = [0, 5, 11, 16]
+    states = []
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        npg = (hi + ps - 1) // ps
+        li = np.array([[hi - (npg - 1) * ps], [lo], [0]], np.int32)
+        states.append(run_oracle(w, q=q1, B=1, indptr=np.array([0, npg], np.int32),
+                                 values=pages[:npg], length_info=li, sliding_window=True))
+    a = oracle.merge_state(*oracle.merge_state(*states[0], *states[1]), *states[2])
+    c = oracle.merge_state(*states[0], *oracle.merge_state(*states[1], *states[2]))
+    for o, l in (a, c):
+        np.testing.assert_allclose(o[0], out[b], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l[0], lse[b], rtol=0, atol=1e-12)
+
+
+def test_merge_closed_forms():
+    """Merging a state with itself keeps V and adds exactly 1 to the base-2 lse; merging with a
+    state 2^-60 times lighter leaves V unchanged to fp64 rounding."""
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((2, 3, 8))
+    s = rng.standard_normal((2, 3)) * 10
+    vm, sm = oracle.merge_state(v, s, v, s)
+    np.testing.assert_allclose(vm, v, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(sm, s + 1.0, rtol=0, atol=1e-13)
+    vm, sm = oracle.merge_state(v, s, rng.standard_normal((2, 3, 8)), s - 60)
+    np.testing.assert_allclose(vm, v, rtol=0, atol=1e-17 * 1e2)
+
+
+@pytest.mark.parametrize("sink,window", [(2, 6), (0, 5), (3, 100)])
+def test_window_and_sink_bruteforce(sink, window):
+    """Window reading: attended rows are the first `sink` positions then positions
+    [win_off, total) with win_off = max(sink, total - window)."""
+    w = small(seq_lens=[13, 3, 16], window=window, sink=sink)
+    out, lse = run_oracle(w)
+    q64 = to_f64(w.q, "f32")
+    for b in range(w.B):
+        L = int(w.seq_lens[b])
+        off = max(sink, L - window)
+        rows = list(range(min(sink, L))) + list(range(off, L))
+        for hq in range(w.H_qo):
+            K, V = contiguous_kv(w, b, hq // 2)
+            o, l = dense_attention(q64[b, hq], K[rows], V[rows], w.sm_scale)
+            np.testing.assert_allclose(out[b, hq], o, rtol=0, atol=1e-12)
+            assert abs(lse[b, hq] - l) < 1e-12
+
+
+def test_window_zero_reduces_to_plain():
+    """sink = 0 and win_off = 0 is the no-window path."""
+    w = small(seq_lens=[13, 3, 16])
+    out0, lse0 = run_oracle(w)
+    li = np.stack([w.length_info, np.zeros(w.B, np.int32), np.zeros(w.B, np.int32)])
+    out1, lse1 = run_oracle(w, length_info=li, sliding_window=True)
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+
+
+# ---------------------------------------------------------------- RoPE (parity unpinned: invariants)
+def test_rope_position_zero_is_identity():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(128)
+    assert np.array_equal(oracle.rope_rotate(x, 0, 1.0, 5e5), x)
+
+
+def test_rope_decode_uses_compacted_row_positions():
+    """With rope on, the K row r sits at position k_rope_pos_offset + r: rotating the contiguous
+    K rows by their row index and q by its position reproduces the oracle through brute force."""
+    w = small(seq_lens=[13, 3, 16], rotary_mode=1, rope_theta=1e4)
+    qp = np.array([12, 2, 15], np.int32)
+    ko = np.array([0, 5, 100], np.int32)
+    out, lse = run_oracle(w, q_rope_position=qp, k_rope_pos_offset=ko)
+    q64 = to_f64(w.q, "f32")
+    for b in range(w.B):
+        for hq in range(w.H_qo):
+            K, V = contiguous_kv(w, b, hq // 2)
+            Kr = np.stack([oracle.rope_rotate(K[r], ko[b] + r, 1.0, 1e4) for r in range(K.shape[0])])
+            qr = oracle.rope_rotate(q64[b, hq], qp[b], 1.0, 1e4)
+            o, l = dense_attention(qr, Kr, V, w.sm_scale)
+            np.testing.assert_allclose(out[b, hq], o, rtol=0, atol=1e-12)
+            assert abs(lse[b, hq] - l) < 1e-12
+
+
+def test_rope_only_mode_one_applies():
+    w = small(seq_lens=[13, 3, 16])
+    out0, lse0 = run_oracle(w)
+    pos = np.array([100, 7, 3], np.int32)
+    for mode in (0, 2, -1):
+        out1, lse1 = run_oracle(w, rotary_mode=mode, q_rope_position=pos, k_rope_pos_offset=pos)
+        assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+
+
+def test_rope_relative_position_invariance():
+    """Shifting the q position and the k offset by the same amount leaves every score unchanged."""
+    w = small(seq_lens=[13, 3, 16], rotary_mode=1, rope_theta=500000.0)
+    qp = np.array([12, 2, 15], np.int32)
+    ko = np.zeros(3, np.int32)
+    out0, lse0 = run_oracle(w, q_rope_position=qp, k_rope_pos_offset=ko)
+    out1, lse1 = run_oracle(w, q_rope_position=qp + 9000, k_rope_pos_offset=ko + 9000)
+    np.testing.assert_allclose(out1, out0, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(lse1, lse0, rtol=0, atol=1e-9)
+    out2, _ = run_oracle(w, q_rope_position=qp + 5, k_rope_pos_offset=ko)
+    assert np.abs(out2 - out0).max() > 1e-3  # and a relative shift does change the result
+
+
+def test_rope_is_a_rotation():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(64)
+    for pos in (1, 37, 4099):
+        y = oracle.rope_rotate(x, pos, 1.0, 1e4)
+        assert abs(np.linalg.norm(y) - np.linalg.norm(x)) < 1e-12
+        # pairs (i, i + D/2) keep their norms
+        np.testing.assert_allclose(y[:32] ** 2 + y[32:] ** 2, x[:32] ** 2 + x[32:] ** 2, atol=1e-12)
+    a = oracle.rope_rotate(oracle.rope_rotate(x, 123, 1.0, 5e5), 456, 1.0, 5e5)
+    np.testing.assert_allclose(a, oracle.rope_rotate(x, 579, 1.0, 5e5), atol=1e-11)
+    np.testing.assert_allclose(oracle.rope_rotate(oracle.rope_rotate(x, 77, 1.0, 1e4), -77, 1.0, 1e4),
+                               x, atol=1e-12)
+    # position scaling: R_scale(p) == R_1(p * scale)
+    np.testing.assert_allclose(oracle.rope_rotate(x, 10, 0.25, 1e4), oracle.rope_rotate(x, 2.5, 1.0, 1e4),
+                               atol=1e-13)
+
+
+def test_rope_two_dims_is_plane_rotation():
+    """D = 2: a single pair at frequency theta^0 = 1, i.e. the textbook plane rotation by p."""
+    for p in (0.0, 1.0, 2.5, 100.0):
+        y = oracle.rope_rotate(np.array([1.0, 0.0]), p, 1.0, 1e4)
+        np.testing.assert_allclose(y, [np.cos(p), np.sin(p)], atol=1e-15)
+
+
+# ---------------------------------------------------------------- fp8 e4m3fn and bf16 codecs
+def test_fp8_reference_values():
+    """Values fixed by the OCP FP8 e4m3fn definition (see tests/golden/fp8_e4m3fn_values.txt)."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "fp8_e4m3fn_values.txt")
+    n = 0
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        code, val = line.split()
+        code = int(code, 16)
+        if val == "nan":
+            assert np.isnan(oracle.fp8_value(code))
+        else:
+            v = float.fromhex(val) if "p" in val else float(val)
+            got = oracle.fp8_value(code)
+            assert got == v and np.signbit(got) == np.signbit(v), (hex(code), got, v)
+        n += 1
+    assert n >= 12
+
+
+def test_fp8_table_shape():
+    """Codes 0x00..0x7E increase strictly; within each binade the step is constant; 254 finite
+    codes; the negative half mirrors the positive half."""
+    vals = np.array([oracle.fp8_value(c) for c in range(256)])
+    pos = vals[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    assert np.sum(np.isfinite(vals)) == 254
+    np.testing.assert_array_equal(vals[0x80:0xFF], -pos)
+    for e in range(1, 15):
+        binade = pos[8 * e:8 * e + 8]
+        steps = np.diff(binade)
+        assert np.all(steps == steps[0])
+
+
+def test_fp8_decode_matches_library():
+    import torch
+    codes = torch.arange(256, dtype=torch.uint8)
+    lib = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = np.array([oracle.fp8_value(c) for c in range(256)])
+    same = (lib == ours) | (np.isnan(lib) & np.isnan(ours))
+    assert same.all()
+
+
+def test_fp8_encode_roundtrip_ties_and_saturation():
+    vals = [oracle.fp8_value(c) for c in range(256)]
+    for c in range(256):
+        if np.isfinite(vals[c]):
+            assert oracle.fp8_encode(vals[c]) == c
+    # midpoints between neighbours go to the even code
+    for c in range(0, 0x7E):
+        mid = (vals[c] + vals[c + 1]) / 2
+        if np.float32(mid) == mid:
+            got = oracle.fp8_encode(mid)
+            assert got == (c if c % 2 == 0 else c + 1), hex(c)
+    assert oracle.fp8_encode(1e6) == 0x7E and oracle.fp8_encode(-1e6) == 0xFE
+    assert oracle.fp8_encode(float("inf")) == 0x7E and oracle.fp8_encode(float("-inf")) == 0xFE
+    assert oracle.fp8_encode(464.0) == 0x7E and oracle.fp8_encode(449.0) == 0x7E
+    assert oracle.fp8_encode(float("nan")) & 0x7F == 0x7F
+
+
+def test_fp8_encode_is_nearest_bruteforce_and_library():
+    import torch
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.standard_normal(3000) * 100, rng.standard_normal(1000) * 0.01,
+                        rng.uniform(-448, 448, 1000)]).astype(np.float32)
+    codes = oracle.fp8_encode_array(x)
+    table = np.array([oracle.fp8_value(c) for c in range(0x7F)])
+    for xi, c in zip(x, codes):
+        err = abs(abs(float(xi)) - table)
+        assert abs(abs(float(xi)) - table[c & 0x7F]) == err.min()
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(lib, codes)
+
+
+def test_bf16_value_matches_library():
+    import torch
+    bits = np.arange(0, 65536, 7, dtype=np.uint16)
+    lib = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ours = np.array([oracle.bf16_value(int(b)) for b in bits])
+    same = (lib == ours) | (np.isnan(lib) & np.isnan(ours))
+    assert same.all()
+
+
+# ---------------------------------------------------------------- append
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_append_bitexact_bruteforce(dtype):
+    H_kv, D, ps, P = 3, 16, 4, 10
+    pool = synth.poisoned_pool(P, H_kv, ps, D, dtype)
+    before = pool.copy()
+    k, v, slots = synth.append_inputs(T=9, H_kv=H_kv, D=D, page_size=ps, max_num_pages=P,
+                                      in_dtype=dtype, seed=4, skip_every=4)
+    oracle.append_kv(pages=pool, new_k=k, new_v=v, slots=slots, H_kv=H_kv, D=D, ps=ps,
+                     in_dtype=synth.DTYPE_CODE[dtype], kv_dtype=synth.DTYPE_CODE[dtype])
+    expect = before.copy()
+    for t, s in enumerate(slots):
+        if s >= 0:
+            expect[s // ps, 0, :, s % ps, :] = k[t]
+            expect[s // ps, 1, :, s % ps, :] = v[t]
+    assert expect.tobytes() == pool.tobytes()
+    assert (slots < 0).sum() == 3
+
+
+def test_append_fp8_matches_library_quantization():
+    import torch
+    H_kv, D, ps, P = 2, 16, 8, 6
+    pool = synth.poisoned_pool(P, H_kv, ps, D, "fp8")
+    k, v, slots = synth.append_inputs(T=7, H_kv=H_kv, D=D, page_size=ps, max_num_pages=P,
+                                      in_dtype="bf16", seed=8, skip_every=3)
+    ks = np.array([0.5 / 448, 2.0 / 448], np.float32)
+    vs = np.array([1.0 / 448, 0.75 / 448], np.float32)
+    before = pool.copy()
+    oracle.append_kv(pages=pool, new_k=k, new_v=v, slots=slots, H_kv=H_kv, D=D, ps=ps,
+                     in_dtype=1, kv_dtype=2, k_scale=ks, v_scale=vs)
+    kf = to_f64(k, "bf16").astype(np.float32)
+    vf = to_f64(v, "bf16").astype(np.float32)
+    expect = before.copy()
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        for kv, x, sc in ((0, kf, ks), (1, vf, vs)):
+            y = np.clip(x[t] / sc[:, None], -448, 448)  # fp32 divide, then satfinite
+            expect[s // ps, kv, :, s % ps, :] = (torch.from_numpy(np.ascontiguousarray(y))
+                                                 .to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert expect.tobytes() == pool.tobytes()
+
+
+# ---------------------------------------------------------------- validator
+def test_validator_codes():
+    w = small(seq_lens=[7, 0, 13], window=6, sink=2)
+    kw = dict(B=w.B, ps=w.page_size, max_num_pages=w.max_num_pages, indptr=w.page_indptr,
+              values=w.page_values, length_info=w.length_info, sliding_window=True)
+    assert oracle.validate_page_table(**kw) == 0
+    bad = dict(kw, indptr=np.array([0, 3, 2, w.page_indptr[-1]], np.int32))
+    assert oracle.validate_page_table(**bad) == 1
+    vals = w.page_values.copy(); vals[0] = w.max_num_pages
+    assert oracle.validate_page_table(**dict(kw, values=vals)) == 2
+    li = w.length_info.copy(); li[0, 0] = 0
+    assert oracle.validate_page_table(**dict(kw, length_info=li)) == 3
+    li = w.length_info.copy(); li[2, 0] = li[1, 0] + 1
+    assert oracle.validate_page_table(**dict(kw, length_info=li)) == 4
+
+
+def test_oracle_rejects_out_of_range_page():
+    w = small()
+    vals = w.page_values.copy()
+    vals[-1] = 99
+    with pytest.raises(oracle.OracleError):
+        run_oracle(w, values=vals)
