@@ -13,8 +13,9 @@
 //     That algorithm reaches exactly (up to rounding order) the plain two-pass definition
 //         out = sum_r e^{s_r - M} v_r / sum_r e^{s_r - M},   lse = log2 sum_r e^{s_r},
 //     which is what this file writes out, in fp64.
-//   * Empty sequence: the same function initialises m = -5e4, d = 1, O = 0 and loops over zero
-//     rows, so it emits out = 0 and lse = -5e4 + log2(1) = -5e4.
+//   * No attended rows (no pages, or an empty window with no sink): the same function initialises
+//     m = -5e4, d = 1, O = 0 and loops over zero rows, so it emits out = 0 and
+//     lse = -5e4 + log2(1) = -5e4.
 //   * length_info: the comment block of the same function ([B] = last_page_len, or [3, B] =
 //     last_page_len, sliding-window start offset, attention-sink length).
 //   * Merge: TVM "_decode_kernels.py", _merge_state_inplace_cpu (pairwise merge in base 2).
@@ -152,6 +153,11 @@ int decode_one(const DecodeArgs& a, int b, int h_qo, double* out, double* lse) {
   }
   const int64_t L = total - win_off + sink;
   if (last < 1 || last > a.ps || sink < 0 || win_off < sink || win_off > total) return 3;
+  if (L == 0) {  // pages but no attended row (empty window, no sink): the same initial state
+    for (int d = 0; d < D; ++d) out[d] = 0.0;
+    *lse = -5e4;
+    return 0;
+  }
 
   std::vector<double> qv(D), kv(D), vv(D), acc(D, 0.0), scores(L);
   for (int d = 0; d < D; ++d)

@@ -86,6 +86,14 @@ def test_empty_sequence_convention():
     assert np.all(np.isfinite(out[[0, 2]]))
 
 
+def test_empty_window_convention():
+    """Pages but zero attended rows (window start at the end, no sink): out = 0, lse = -5e4."""
+    w = small(seq_lens=[5, 6, 9])
+    li = np.stack([w.length_info, w.seq_lens, np.zeros(w.B, np.int32)]).astype(np.int32)
+    out, lse = run_oracle(w, length_info=li, sliding_window=True)
+    assert np.all(out == 0.0) and np.all(lse == -5e4)
+
+
 def test_lse_matches_natural_log_recurrence():
     """The NKI flash kernel (vLLM nki_flash_attn page, _flash_attention_core) keeps the LSE in
     natural log, tile by tile: first tile l = max + log(sum), later l = m + log(exp(l_prev - m) +
