@@ -16,6 +16,7 @@ Storage dtypes: fp32 -> np.float32, bf16 -> np.uint16 bits, fp8 -> np.uint8 code
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
 
@@ -133,24 +134,33 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
         length_info = np.stack([last, win_off, sinks]).astype(np.int32)
         attended = np.where(npages > 0, seq_lens - win_off + sinks, 0).astype(np.int32)
 
-    # Data for the used pages only; the rest of the pool is NaN-poisoned.
-    rng_kv = _rng(seed, 2)
+    # Data for the used pages only; the rest of the pool is NaN-poisoned. Blocks of pages draw
+    # from independent streams (seed, 1000 + block) so they can be filled in parallel threads.
     pool = poisoned_pool(max_num_pages, H_kv, ps, D, kv_dtype)
     order = np.sort(ids)
-    CH = 2048
     k_scale = v_scale = None
     if kv_dtype == "fp8":
         rng_sc = _rng(seed, 4)
         k_scale = rng_sc.uniform(*scale_range, size=H_kv).astype(np.float32)
         v_scale = rng_sc.uniform(*scale_range, size=H_kv).astype(np.float32)
-    for i in range(0, order.size, CH):
-        blk = order[i:i + CH]
-        x = rng_kv.standard_normal((blk.size, 2, H_kv, ps, D), dtype=np.float32)
+    CH = 512
+
+    def fill(i):
+        blk = order[i * CH:(i + 1) * CH]
+        x = _rng(seed, 1000 + i).standard_normal((blk.size, 2, H_kv, ps, D), dtype=np.float32)
         if kv_dtype == "fp8":
-            x = np.clip(x * np.float32(fp8_payload_sigma), -448.0, 448.0)
+            x *= np.float32(fp8_payload_sigma)
+            np.clip(x, -448.0, 448.0, out=x)
         elif kv_sigma != 1.0:
             x *= np.float32(kv_sigma)
         pool[blk] = cast_f32(x, kv_dtype)
+
+    nblk = (order.size + CH - 1) // CH
+    if nblk > 1:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, nblk)) as ex:
+            list(ex.map(fill, range(nblk)))
+    elif nblk == 1:
+        fill(0)
     rng_q = _rng(seed, 3)
     q = cast_f32(rng_q.standard_normal((B, H_qo, D), dtype=np.float32), q_dtype)
     if sm_scale is None:
