@@ -1,0 +1,156 @@
+/* libpdecode: single-token paged-KV decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (each cites the page that defines it):
+ *   pdecode_attention            TVM relax decode-kernels page, _attention_decode_cpu /
+ *                                _attention_decode (batch_decode_paged_kv): one query token per
+ *                                sequence, K/V gathered through a CSR page table, grouped-query
+ *                                heads, online softmax, output plus base-2 log-sum-exp, optional
+ *                                RoPE on Q and K, optional sliding window with attention sink.
+ *   pdecode_merge_state_inplace  Same page, _merge_state_inplace: combine two attention states
+ *                                (V, lse) in place.
+ *   pdecode_append_kv            vLLM nki_flash_attn page, reshape_and_cache: write new K/V rows
+ *                                into their cache slots. The fp8 KV cache with k_scale / v_scale
+ *                                follows the AWS Neuron attention_block_tkg page (OCP e4m3fn);
+ *                                here the scales are per KV head and a stored value is
+ *                                code * scale (read) and x / scale rounded to e4m3fn (write).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; host structs are read during the
+ *     call only. The library allocates nothing, never synchronises and keeps no state between
+ *     calls (it is reentrant). Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and runs asynchronously.
+ *   - Arguments are checked on the host before anything is launched; on error nothing is
+ *     launched and the call returns a status other than PDECODE_OK. Device-resident data
+ *     (page tables, lengths, slots) are preconditions, not checked on the device (see below).
+ *   - Layouts are row-major:
+ *       q, out        [batch, num_qo_heads, head_dim]       (dtype q_dtype)
+ *       pages         [max_num_pages, 2, num_kv_heads, page_size, head_dim]; index 1: 0 = K, 1 = V
+ *       page_indptr   int32 [batch + 1]; page_values int32 [page_indptr[batch]]
+ *       length_info   int32 [batch] = last_page_len, or, with sliding_window, int32 [3, batch] =
+ *                     (last_page_len, window start offset, sink length)
+ *       lse           fp32 [batch, num_qo_heads], base 2: lse = log2(sum_r exp(s_r))
+ *   - Sequence b owns pages page_values[page_indptr[b] .. page_indptr[b+1]); with np of them its
+ *     length is total = (np - 1) * page_size + last_page_len. Without a window it attends rows
+ *     0..total-1. With a window it attends positions [0, sink) and then [win_off, total), and the
+ *     K RoPE position of attended row r (0-based over the attended rows) is
+ *     k_rope_pos_offset[b] + r. A sequence with no pages yields out = 0 and lse = -5e4.
+ *   - Score of row r for q head h_qo: s_r = sm_scale * q[h_qo] . k_r, with k_r read from KV head
+ *     h_qo / (num_qo_heads / num_kv_heads).
+ *   - Device preconditions: page_indptr non-decreasing from 0; page ids in [0, max_num_pages);
+ *     1 <= last_page_len <= page_size for non-empty sequences; 0 <= sink <= win_off <= total.
+ */
+#ifndef PDECODE_H
+#define PDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pdecode_status {
+  PDECODE_OK = 0,
+  PDECODE_ERR_INVALID_ARG = 1,          /* null pointer, non-positive size, inconsistent heads   */
+  PDECODE_ERR_UNSUPPORTED = 2,          /* valid but outside the supported set (see below)       */
+  PDECODE_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace missing or smaller than required            */
+  PDECODE_ERR_HIP = 4                   /* a HIP launch failed                                   */
+} pdecode_status;
+
+typedef enum pdecode_dtype {
+  PDECODE_F32 = 0,
+  PDECODE_BF16 = 1,
+  PDECODE_FP8_E4M3FN = 2                /* OCP e4m3fn: bias 7, no infinities, max 448            */
+} pdecode_dtype;
+
+/* Problem description shared by pdecode_attention and pdecode_append_kv.
+ * Supported set: head_dim in {64, 128}; page_size in {16, 32}; group size
+ * num_qo_heads / num_kv_heads in 1..8; (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
+ * (BF16, FP8_E4M3FN)}. The output dtype equals q_dtype. */
+typedef struct pdecode_desc {
+  int32_t batch;          /* B >= 0                                                            */
+  int32_t num_qo_heads;   /* H_qo > 0, a multiple of num_kv_heads                              */
+  int32_t num_kv_heads;   /* H_kv > 0                                                          */
+  int32_t head_dim;       /* D                                                                 */
+  int32_t page_size;      /* rows per page                                                     */
+  int32_t max_num_pages;  /* pages in the pool (first dimension of `pages`)                    */
+  int32_t q_dtype;        /* pdecode_dtype of q and out (and of new_k / new_v for append)      */
+  int32_t kv_dtype;       /* pdecode_dtype of the pool                                         */
+  int32_t sliding_window; /* 0: length_info is [B]; 1: length_info is [3, B]                   */
+  int32_t max_kv_len;     /* host-side upper bound on attended rows per sequence, used only to
+                             plan the split-KV grid; 0 = take max_num_pages * page_size. A
+                             sequence longer than the bound is still computed exactly.           */
+  int32_t num_kv_splits;  /* 0 = automatic; 1 = never split a sequence; n > 1 = split each
+                             sequence's pages into at most n chunks merged by log-sum-exp         */
+  const float *k_scale;   /* device fp32 [H_kv]; required iff kv_dtype is FP8: K = code * scale */
+  const float *v_scale;   /* device fp32 [H_kv]; required iff kv_dtype is FP8: V = code * scale */
+} pdecode_desc;
+
+/* Rotary embedding on Q and K inside the kernel; a NULL pointer to this struct means none.
+ * Applied iff rotary_mode == 1 (any other value: none). Rotate-half over the two contiguous
+ * halves of the head dimension: for i < D/2, angle = position * rope_scale * rope_theta^(-2i/D),
+ * x'[i] = x[i] cos - x[i + D/2] sin, x'[i + D/2] = x[i + D/2] cos + x[i] sin. The rotated q and k
+ * stay in fp32. */
+typedef struct pdecode_rope {
+  int32_t rotary_mode;
+  float rope_scale;
+  float rope_theta;                   /* > 0                                                   */
+  const int32_t *q_rope_position;     /* device int32 [B]: position of the query token        */
+  const int32_t *k_rope_pos_offset;   /* device int32 [B]: position of attended row 0         */
+} pdecode_rope;
+
+/* Bytes of device workspace pdecode_attention needs for this description (0 when the planned
+ * launch does not split any sequence). Depends only on host fields of `d`. Returns 0 for an
+ * invalid description. */
+size_t pdecode_workspace_bytes(const pdecode_desc *d);
+
+/* The split plan for `d`: rows are processed in chunks of *chunk_pages pages (page slots) and a
+ * sequence uses at most *num_chunks chunks. Returns PDECODE_OK or an argument error. */
+pdecode_status pdecode_plan(const pdecode_desc *d, int32_t *chunk_pages, int32_t *num_chunks);
+
+/* Decode attention (see the header comment for the computation and layouts).
+ * q, pages, page_indptr, page_values, length_info, out, lse: device pointers as above.
+ * rope: NULL or a host struct. sm_scale: the score scale (typically 1/sqrt(head_dim)).
+ * workspace: device memory of at least pdecode_workspace_bytes(d) bytes, 256-byte aligned
+ * (may be NULL when that is 0); its contents on entry are ignored and it holds partial states
+ * afterwards. out and lse are fully written. Errors: INVALID_ARG, UNSUPPORTED,
+ * WORKSPACE_TOO_SMALL (nothing launched), HIP (launch failure). */
+pdecode_status pdecode_attention(const pdecode_desc *d, const void *q, const void *pages,
+                                 const int32_t *page_indptr, const int32_t *page_values,
+                                 const int32_t *length_info, const pdecode_rope *rope,
+                                 float sm_scale, void *out, float *lse, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* Merges the attention state (v_other, s_other) into (v, s) in place, base 2:
+ *   s_max = max(s, s'); a = 2^(s - s_max); b = 2^(s' - s_max);
+ *   v = v * a / (a + b) + v' * b / (a + b);  s = log2(a + b) + s_max.
+ * v, v_other: device [n, num_heads, head_dim] of v_dtype (F32 or BF16); s, s_other: device fp32
+ * [n, num_heads]. Arithmetic in fp32; bf16 results are rounded to nearest even. v must not
+ * alias v_other. n == 0 is a no-op. Errors: INVALID_ARG (null pointer, negative size),
+ * UNSUPPORTED (v_dtype), HIP. */
+pdecode_status pdecode_merge_state_inplace(int32_t n, int32_t num_heads, int32_t head_dim,
+                                           int32_t v_dtype, void *v, float *s,
+                                           const void *v_other, const float *s_other,
+                                           void *stream);
+
+/* Writes token t's K and V rows into slot slot_ids[t] of the pool, for every KV head:
+ *   pages[slot / page_size, 0, h, slot % page_size, :] = new_k[t, h, :]   (V at index 1).
+ * new_k, new_v: device [num_tokens, num_kv_heads, head_dim] of d->q_dtype; slot_ids: device
+ * int32 [num_tokens]. A negative slot skips its token; so does a slot at or beyond
+ * max_num_pages * page_size. Slots >= 0 must be distinct. Same dtype: bits are copied. FP8 pool:
+ * each element is divided by its head's scale in fp32 and rounded to the nearest e4m3fn value,
+ * ties to even, saturating to +-448. Uses d's head, size and dtype fields only; besides the
+ * attention pairs it also accepts fp32 rows into an FP8 pool.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+pdecode_status pdecode_append_kv(const pdecode_desc *d, const void *new_k, const void *new_v,
+                                 const int32_t *slot_ids, int32_t num_tokens, void *pages,
+                                 void *stream);
+
+/* Static string naming a status. */
+const char *pdecode_status_string(pdecode_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDECODE_H */

@@ -1,0 +1,212 @@
+// C ABI of libpdecode: host-side argument checks, split-KV planning and kernel launches.
+// Declarations and the contract of every entry point are in include/pdecode.h.
+#include "pdecode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kTargetWorkgroups = 2048;  // about 8 wavefront-workgroups per CU on 256 CUs
+constexpr int kMinChunkRows = 256;
+
+struct Plan {
+  int32_t chunk_slots = 1;
+  int32_t num_chunks = 1;
+  size_t part_o_bytes = 0;
+  size_t part_lse_bytes = 0;
+  size_t workspace_bytes() const { return part_o_bytes + part_lse_bytes; }
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool supported_pair(int q, int kv) {
+  return (q == PDECODE_F32 && kv == PDECODE_F32) || (q == PDECODE_BF16 && kv == PDECODE_BF16) ||
+         (q == PDECODE_BF16 && kv == PDECODE_FP8_E4M3FN);
+}
+
+pdecode_status check_desc(const pdecode_desc* d) {
+  if (!d) return PDECODE_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->num_qo_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
+      d->page_size <= 0 || d->max_num_pages <= 0 || d->max_kv_len < 0 || d->num_kv_splits < 0)
+    return PDECODE_ERR_INVALID_ARG;
+  if (d->num_qo_heads % d->num_kv_heads != 0) return PDECODE_ERR_INVALID_ARG;
+  if (d->sliding_window != 0 && d->sliding_window != 1) return PDECODE_ERR_INVALID_ARG;
+  if (d->q_dtype < 0 || d->q_dtype > 2 || d->kv_dtype < 0 || d->kv_dtype > 2)
+    return PDECODE_ERR_INVALID_ARG;
+  if (d->kv_dtype == PDECODE_FP8_E4M3FN && (!d->k_scale || !d->v_scale))
+    return PDECODE_ERR_INVALID_ARG;
+  if (!supported_pair(d->q_dtype, d->kv_dtype)) return PDECODE_ERR_UNSUPPORTED;
+  return PDECODE_OK;
+}
+
+pdecode_status check_attention_shape(const pdecode_desc* d) {
+  const int G = d->num_qo_heads / d->num_kv_heads;
+  if (G > 8) return PDECODE_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return PDECODE_ERR_UNSUPPORTED;
+  if (d->page_size != 16 && d->page_size != 32) return PDECODE_ERR_UNSUPPORTED;
+  return PDECODE_OK;
+}
+
+// Chunking of each sequence's page slots. A sequence with n slots uses ceil(n / chunk_slots)
+// chunks, capped at num_chunks (the last chunk then takes every remaining slot), so any length
+// is computed exactly; max_kv_len only sizes the grid.
+Plan make_plan(const pdecode_desc* d) {
+  Plan pl;
+  const int64_t ps = d->page_size;
+  const int64_t max_len = d->max_kv_len > 0 ? d->max_kv_len : int64_t(d->max_num_pages) * ps;
+  const int64_t max_slots = (max_len + ps - 1) / ps + (d->sliding_window ? 2 : 0);
+  const int64_t units = int64_t(d->batch) * d->num_kv_heads;
+  int64_t chunk;
+  if (d->num_kv_splits == 1) {
+    chunk = max_slots;
+  } else if (d->num_kv_splits > 1) {
+    chunk = (max_slots + d->num_kv_splits - 1) / d->num_kv_splits;
+  } else {
+    const int64_t min_chunk = (kMinChunkRows + ps - 1) / ps;
+    chunk = (units * max_slots + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    if (chunk < min_chunk) chunk = min_chunk;
+  }
+  if (chunk < 1) chunk = 1;
+  int64_t n = (max_slots + chunk - 1) / chunk;
+  if (n < 1) n = 1;
+  if (n > INT_MAX / 2) n = INT_MAX / 2;
+  pl.chunk_slots = static_cast<int32_t>(chunk > INT_MAX ? INT_MAX : chunk);
+  pl.num_chunks = static_cast<int32_t>(n);
+  if (pl.num_chunks > 1) {
+    const size_t rows = size_t(d->batch) * d->num_qo_heads * pl.num_chunks;
+    pl.part_o_bytes = align256(rows * d->head_dim * sizeof(float));
+    pl.part_lse_bytes = align256(rows * sizeof(float));
+  }
+  return pl;
+}
+
+pdecode_status hip_status(hipError_t e) { return e == hipSuccess ? PDECODE_OK : PDECODE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pdecode_status_string(pdecode_status s) {
+  switch (s) {
+    case PDECODE_OK: return "PDECODE_OK";
+    case PDECODE_ERR_INVALID_ARG: return "PDECODE_ERR_INVALID_ARG";
+    case PDECODE_ERR_UNSUPPORTED: return "PDECODE_ERR_UNSUPPORTED";
+    case PDECODE_ERR_WORKSPACE_TOO_SMALL: return "PDECODE_ERR_WORKSPACE_TOO_SMALL";
+    case PDECODE_ERR_HIP: return "PDECODE_ERR_HIP";
+  }
+  return "PDECODE_UNKNOWN_STATUS";
+}
+
+size_t pdecode_workspace_bytes(const pdecode_desc* d) {
+  if (check_desc(d) != PDECODE_OK || check_attention_shape(d) != PDECODE_OK) return 0;
+  return make_plan(d).workspace_bytes();
+}
+
+pdecode_status pdecode_plan(const pdecode_desc* d, int32_t* chunk_pages, int32_t* num_chunks) {
+  pdecode_status st = check_desc(d);
+  if (st != PDECODE_OK) return st;
+  if ((st = check_attention_shape(d)) != PDECODE_OK) return st;
+  if (!chunk_pages || !num_chunks) return PDECODE_ERR_INVALID_ARG;
+  const Plan pl = make_plan(d);
+  *chunk_pages = pl.chunk_slots;
+  *num_chunks = pl.num_chunks;
+  return PDECODE_OK;
+}
+
+pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const void* pages,
+                                 const int32_t* page_indptr, const int32_t* page_values,
+                                 const int32_t* length_info, const pdecode_rope* rope,
+                                 float sm_scale, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  pdecode_status st = check_desc(d);
+  if (st != PDECODE_OK) return st;
+  if ((st = check_attention_shape(d)) != PDECODE_OK) return st;
+  if (!std::isfinite(sm_scale)) return PDECODE_ERR_INVALID_ARG;
+  const bool rotary = rope && rope->rotary_mode == 1;
+  if (rotary && (!rope->q_rope_position || !rope->k_rope_pos_offset ||
+                 !(rope->rope_theta > 0.f) || !std::isfinite(rope->rope_theta) ||
+                 !std::isfinite(rope->rope_scale)))
+    return PDECODE_ERR_INVALID_ARG;
+  if (d->batch == 0) return PDECODE_OK;
+  if (!q || !pages || !page_indptr || !page_values || !length_info || !out || !lse)
+    return PDECODE_ERR_INVALID_ARG;
+  const Plan pl = make_plan(d);
+  const int64_t grid = int64_t(pl.num_chunks) * d->batch * d->num_kv_heads;
+  if (grid > INT_MAX) return PDECODE_ERR_UNSUPPORTED;
+  if (pl.workspace_bytes() > 0) {
+    if (!workspace || workspace_bytes < pl.workspace_bytes()) return PDECODE_ERR_WORKSPACE_TOO_SMALL;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PDECODE_ERR_INVALID_ARG;
+  }
+
+  pdk::DecodeParams p{};
+  p.q = q;
+  p.pages = pages;
+  p.indptr = page_indptr;
+  p.values = page_values;
+  p.length_info = length_info;
+  p.q_pos = rotary ? rope->q_rope_position : nullptr;
+  p.k_off = rotary ? rope->k_rope_pos_offset : nullptr;
+  p.k_scale = d->k_scale;
+  p.v_scale = d->v_scale;
+  p.out = out;
+  p.lse = lse;
+  p.part_o = pl.num_chunks > 1 ? static_cast<float*>(workspace) : nullptr;
+  p.part_lse = pl.num_chunks > 1
+                   ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_o_bytes)
+                   : nullptr;
+  p.B = d->batch;
+  p.H_qo = d->num_qo_heads;
+  p.H_kv = d->num_kv_heads;
+  p.G = d->num_qo_heads / d->num_kv_heads;
+  p.max_num_pages = d->max_num_pages;
+  p.sliding = d->sliding_window;
+  p.rotary = rotary ? 1 : 0;
+  p.rope_scale = rotary ? rope->rope_scale : 1.f;
+  p.rope_theta = rotary ? rope->rope_theta : 1.f;
+  p.score_scale = sm_scale * pdk::kLog2e;
+  p.chunk_slots = pl.chunk_slots;
+  p.num_chunks = pl.num_chunks;
+  const int gp = p.G <= 1 ? 1 : p.G <= 2 ? 2 : p.G <= 4 ? 4 : 8;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(pdk::launch_decode(p, d->kv_dtype, d->head_dim, d->page_size, gp,
+                                     static_cast<unsigned>(grid), s));
+  if (st != PDECODE_OK || pl.num_chunks == 1) return st;
+  return hip_status(pdk::launch_split_merge(p, d->q_dtype, d->head_dim, d->page_size, s));
+}
+
+pdecode_status pdecode_merge_state_inplace(int32_t n, int32_t num_heads, int32_t head_dim,
+                                           int32_t v_dtype, void* v, float* s,
+                                           const void* v_other, const float* s_other,
+                                           void* stream) {
+  if (n < 0 || num_heads <= 0 || head_dim <= 0) return PDECODE_ERR_INVALID_ARG;
+  if (v_dtype != PDECODE_F32 && v_dtype != PDECODE_BF16) return PDECODE_ERR_UNSUPPORTED;
+  if (n == 0) return PDECODE_OK;
+  if (!v || !s || !v_other || !s_other || v == v_other) return PDECODE_ERR_INVALID_ARG;
+  if (int64_t(n) * num_heads > INT_MAX) return PDECODE_ERR_UNSUPPORTED;
+  pdk::MergeParams p{v, s, v_other, s_other, n * num_heads, head_dim};
+  return hip_status(pdk::launch_merge_state(p, v_dtype, static_cast<hipStream_t>(stream)));
+}
+
+pdecode_status pdecode_append_kv(const pdecode_desc* d, const void* new_k, const void* new_v,
+                                 const int32_t* slot_ids, int32_t num_tokens, void* pages,
+                                 void* stream) {
+  pdecode_status st = check_desc(d);
+  // Append also quantises fp32 rows into an fp8 pool.
+  if (st == PDECODE_ERR_UNSUPPORTED && d->q_dtype == PDECODE_F32 &&
+      d->kv_dtype == PDECODE_FP8_E4M3FN)
+    st = PDECODE_OK;
+  if (st != PDECODE_OK) return st;
+  if (num_tokens < 0) return PDECODE_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PDECODE_OK;
+  if (!new_k || !new_v || !slot_ids || !pages) return PDECODE_ERR_INVALID_ARG;
+  pdk::AppendParams p{new_k, new_v, slot_ids, pages, d->k_scale, d->v_scale, num_tokens,
+                      d->num_kv_heads, d->head_dim, d->page_size, d->max_num_pages};
+  return hip_status(pdk::launch_append(p, d->q_dtype, d->kv_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,364 @@
+// Paged-KV single-token decode attention, gfx950 (wave64). One wavefront per
+// (sequence, KV head, chunk of page slots).
+//
+// Computation (TVM relax decode-kernels page, _attention_decode_cpu / _attention_decode): scores
+// s = sm_scale * q . k in log2 units, online softmax with a running max m and denominator d, output
+// O / d and lse = m + log2(d). Split-KV chunks write normalised partial states that the merge
+// kernel combines by log-sum-exp (the page's merge-state formula applied over all chunks).
+//
+// Data path per page slot: the (page, K|V, head) block of page_size rows is contiguous
+// (page_size * head_dim * elem_bytes bytes, 1-16 KiB). The wave reads it with 16-byte loads,
+// lane l taking bytes [16 l, 16 l + 16) of every 1 KiB, so each load instruction is one
+// contiguous KiB. A lane therefore holds EPV consecutive elements (column vector cv = l % VPR) of
+// rows i * RPI + l / VPR. q . k is a per-lane partial dot over its EPV elements followed by a
+// butterfly sum over the VPR lanes of the row; every lane then holds the full scores of its
+// rows, which are exactly the rows of the V elements it holds, so P.V needs no data exchange.
+// Each row group keeps partial (d, O) under a wave-uniform running max; they are summed across
+// row groups once at the end. The next slot's K/V is loaded while the current one is computed;
+// page ids come from one coalesced load per 64 slots.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace pdk {
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// cos and sin of 2*pi*frac(pos * f) with f = fhi + flo (f = rope_scale * freq / 2pi).
+__device__ __forceinline__ void rope_cs(int pos, float fhi, float flo, float& c, float& s) {
+  const float pf = static_cast<float>(pos);
+  const float prod = pf * fhi;
+  const float err = fmaf(pf, fhi, -prod);
+  const float rev = (prod - rintf(prod)) + fmaf(pf, flo, err);
+  sincospif(2.0f * rev, &s, &c);
+}
+
+template <int KVT, int QT, int D, int PS, int GP>
+__global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
+  using KV = Kv<KVT>;
+  constexpr int EPV = KV::EPV;           // elements per 16-byte vector
+  constexpr int VPR = D / EPV;           // vectors per row
+  constexpr int RPI = 64 / VPR;          // rows per load instruction
+  constexpr int NI = PS / RPI;           // load instructions per (page, K|V, head) block
+  constexpr int BLOCK_BYTES = PS * D * KV::EB;
+  static_assert(VPR >= 1 && VPR <= 64 && PS % RPI == 0, "unsupported shape");
+
+  const int lane = threadIdx.x;
+  const int cv = lane % VPR;
+  const int rg = lane / VPR;
+  const int units = p.B * p.H_kv;
+  const int c = blockIdx.x / units;
+  const int u = blockIdx.x - c * units;
+  const int b = u / p.H_kv;
+  const int h = u - b * p.H_kv;
+  const int G = p.G;
+
+  const SeqGeom sg = seq_geom(p.indptr, p.length_info, p.B, b, PS, p.sliding);
+  const int nch = chunks_used(sg.n_slots, p.chunk_slots, p.num_chunks);
+  if (nch == 0) {
+    // No attended rows: out = 0 and lse = -5e4, written by chunk 0 only.
+    if (c != 0) return;
+    for (int g = 0; g < G; ++g) {
+      const int hq = h * G + g;
+      for (int d = lane; d < D; d += 64) store_out<QT>(p.out, (size_t(b) * p.H_qo + hq) * D + d, 0.f);
+      if (lane == 0) p.lse[size_t(b) * p.H_qo + hq] = kEmptyLse;
+    }
+    return;
+  }
+  if (c >= nch) return;
+  const int s_begin = c * p.chunk_slots;
+  const int s_end = (c == nch - 1) ? sg.n_slots : s_begin + p.chunk_slots;
+
+  // ---- q (fp32, pre-scaled to log2 units; fp8 folds k_scale in), optionally rotated.
+  const float kscale = (KVT == kFP8) ? p.k_scale[h] : 1.0f;
+  const float qscale = p.score_scale * kscale;
+  const bool rotary = p.rotary != 0;
+  const int d0 = cv * EPV;                       // first dim this lane holds
+  const bool lower = d0 < D / 2;
+  float fhi[EPV], flo[EPV];                      // RoPE frequencies / 2pi of the lane's dims
+  float qo[GP][EPV];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    const bool live = g < G;
+    const size_t qb = (size_t(b) * p.H_qo + h * G + (live ? g : 0)) * D;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) qo[g][e] = live ? load_q<QT>(p.q, qb + d0 + e) : 0.f;
+  }
+  if (rotary) {
+    const double log2_theta = log2(static_cast<double>(p.rope_theta));
+    const int qpos = p.q_pos[b];
+    const int pd0 = lower ? d0 + D / 2 : d0 - D / 2;   // partner dims
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const int i = (d0 + e) % (D / 2);
+      const double f = static_cast<double>(p.rope_scale) * exp2(-(2.0 * i / D) * log2_theta) /
+                       (2.0 * 3.14159265358979323846);
+      fhi[e] = static_cast<float>(f);
+      flo[e] = static_cast<float>(f - static_cast<double>(fhi[e]));
+      float cs, sn;
+      rope_cs(qpos, fhi[e], flo[e], cs, sn);
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        const bool live = g < G;
+        const size_t qb = (size_t(b) * p.H_qo + h * G + (live ? g : 0)) * D;
+        const float partner = live ? load_q<QT>(p.q, qb + pd0 + e) : 0.f;
+        qo[g][e] = lower ? qo[g][e] * cs - partner * sn : qo[g][e] * cs + partner * sn;
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < GP; ++g)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) qo[g][e] *= qscale;
+
+  // ---- running state: m is wave-uniform per head; d and O are per row group.
+  float m[GP], dsum[GP], O[GP][EPV];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    m[g] = -INFINITY;
+    dsum[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) O[g][e] = 0.f;
+  }
+
+  const char* pool = static_cast<const char*>(p.pages);
+  const int kro = rotary ? p.k_off[b] : 0;
+  auto slot_page = [&](int s) { return s < sg.n0 ? s : sg.first1 + (s - sg.n0); };
+  int ids = 0;
+  auto load_ids = [&](int base) {
+    const int s = base + lane;
+    int id = 0;
+    if (s < s_end) id = p.values[sg.beg + min(slot_page(s), sg.np - 1)];
+    ids = min(max(id, 0), p.max_num_pages - 1);
+  };
+  auto issue = [&](uint4 (&kr)[NI], uint4 (&vr)[NI], int page) {
+    const char* kb = pool + (size_t(page) * 2 * p.H_kv + h) * BLOCK_BYTES + lane * 16;
+    const char* vb = kb + size_t(p.H_kv) * BLOCK_BYTES;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kr[i] = *reinterpret_cast<const uint4*>(kb + i * 1024);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vr[i] = *reinterpret_cast<const uint4*>(vb + i * 1024);
+  };
+
+  uint4 kc[NI], vc[NI], kn[NI], vn[NI];
+  load_ids(s_begin);
+  int pg = __builtin_amdgcn_readfirstlane(ids);
+  issue(kc, vc, pg);
+  for (int s = s_begin; s < s_end; ++s) {
+    const int sn = s + 1;
+    int pgn = pg;
+    if (sn < s_end) {
+      if (((sn - s_begin) & 63) == 0) load_ids(sn);
+      pgn = __builtin_amdgcn_readlane(ids, (sn - s_begin) & 63);
+    }
+    issue(kn, vn, pgn);  // past the end this re-reads the current block (a cache hit)
+
+    // Rows of this slot's page that are attended, and the compacted-row offset for RoPE.
+    const int j = slot_page(s);
+    int lo, hi, roff;
+    if (s < sg.n0) {
+      lo = 0;
+      hi = min(PS, sg.sink - j * PS);
+      roff = 0;
+    } else {
+      lo = max(0, sg.win_off - j * PS);
+      hi = min(PS, sg.total - j * PS);
+      roff = sg.sink - sg.win_off;
+    }
+
+    // ---- scores
+    float sc[NI][GP];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float kf[EPV];
+      KV::unpack(kc[i], kf);
+      if (rotary) {
+        const int pos = kro + j * PS + i * RPI + rg + roff;
+        float kp[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) kp[e] = shfl_xor_f(kf[e], VPR / 2);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          float cs, sn2;
+          rope_cs(pos, fhi[e], flo[e], cs, sn2);
+          kf[e] = lower ? kf[e] * cs - kp[e] * sn2 : kf[e] * cs + kp[e] * sn2;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) a = fmaf(qo[g][e], kf[e], a);
+        sc[i][g] = a;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int g = 0; g < GP; ++g)
+#pragma unroll
+        for (int msk = 1; msk < VPR; msk <<= 1) sc[i][g] += shfl_xor_f(sc[i][g], msk);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = i * RPI + rg;
+      if (row < lo || row >= hi) {
+#pragma unroll
+        for (int g = 0; g < GP; ++g) sc[i][g] = -INFINITY;
+      }
+    }
+
+    // ---- online softmax (base 2)
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      float tm = sc[0][g];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) tm = fmaxf(tm, sc[i][g]);
+#pragma unroll
+      for (int msk = VPR; msk < 64; msk <<= 1) tm = fmaxf(tm, shfl_xor_f(tm, msk));
+      const float mn = fmaxf(m[g], tm);
+      const float alpha = exp2f(m[g] - mn);
+      m[g] = mn;
+      dsum[g] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) O[g][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float pr = exp2f(sc[i][g] - mn);
+        sc[i][g] = pr;
+        dsum[g] += pr;
+      }
+    }
+
+    // ---- P.V
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float vf[EPV];
+      KV::unpack(vc[i], vf);
+#pragma unroll
+      for (int g = 0; g < GP; ++g)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) O[g][e] = fmaf(sc[i][g], vf[e], O[g][e]);
+    }
+
+#pragma unroll
+    for (int i = 0; i < NI; ++i) { kc[i] = kn[i]; vc[i] = vn[i]; }
+    pg = pgn;
+  }
+
+  // ---- sum the row groups, normalise, store
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+#pragma unroll
+    for (int msk = VPR; msk < 64; msk <<= 1) {
+      dsum[g] += shfl_xor_f(dsum[g], msk);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) O[g][e] += shfl_xor_f(O[g][e], msk);
+    }
+  }
+  if (rg != 0) return;
+  const float vscale = (KVT == kFP8) ? p.v_scale[h] : 1.0f;
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    if (g >= G) break;
+    const int hq = h * G + g;
+    const float inv = vscale / dsum[g];
+    const float l = m[g] + log2f(dsum[g]);
+    if (nch == 1) {
+      const size_t ob = (size_t(b) * p.H_qo + hq) * D + d0;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) store_out<QT>(p.out, ob + e, O[g][e] * inv);
+      if (cv == 0) p.lse[size_t(b) * p.H_qo + hq] = l;
+    } else {
+      const size_t row = (size_t(b) * p.H_qo + hq) * p.num_chunks + c;
+      float* po = p.part_o + row * D + d0;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) po[e] = O[g][e] * inv;
+      if (cv == 0) p.part_lse[row] = l;
+    }
+  }
+}
+
+// Combines the normalised partial states of every split sequence by log-sum-exp:
+// M = max_c lse_c, w_c = 2^(lse_c - M), out = sum_c w_c O_c / sum_c w_c, lse = M + log2(sum w_c).
+// Sequences that used a single chunk were finalised by the decode kernel and are skipped.
+template <int QT, int D, int PS>
+__global__ __launch_bounds__(64) void split_merge_kernel(DecodeParams p) {
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x / p.H_qo;
+  const int hq = blockIdx.x - b * p.H_qo;
+  const SeqGeom sg = seq_geom(p.indptr, p.length_info, p.B, b, PS, p.sliding);
+  const int nch = chunks_used(sg.n_slots, p.chunk_slots, p.num_chunks);
+  if (nch <= 1) return;
+  const size_t row0 = (size_t(b) * p.H_qo + hq) * p.num_chunks;
+  float M = -INFINITY;
+  for (int c = lane; c < nch; c += 64) M = fmaxf(M, p.part_lse[row0 + c]);
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, __shfl_xor(M, msk, 64));
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  float W = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const float w = exp2f(p.part_lse[row0 + c] - M);
+    W += w;
+    const float* po = p.part_o + (row0 + c) * D;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, po[lane + 64 * k], acc[k]);
+  }
+  const float inv = 1.0f / W;
+  const size_t ob = (size_t(b) * p.H_qo + hq) * D;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) store_out<QT>(p.out, ob + lane + 64 * k, acc[k] * inv);
+  if (lane == 0) p.lse[size_t(b) * p.H_qo + hq] = M + log2f(W);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host-side dispatch over the compiled shapes.
+template <int KVT, int QT, int D, int PS>
+static hipError_t launch_gp(const DecodeParams& p, int gp, unsigned grid, hipStream_t st) {
+  switch (gp) {
+    case 1: hipLaunchKernelGGL((decode_kernel<KVT, QT, D, PS, 1>), dim3(grid), dim3(64), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<KVT, QT, D, PS, 2>), dim3(grid), dim3(64), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<KVT, QT, D, PS, 4>), dim3(grid), dim3(64), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<KVT, QT, D, PS, 8>), dim3(grid), dim3(64), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int KVT, int QT>
+static hipError_t launch_shape(const DecodeParams& p, int D, int PS, int gp, unsigned grid,
+                               hipStream_t st) {
+  if (D == 64 && PS == 16) return launch_gp<KVT, QT, 64, 16>(p, gp, grid, st);
+  if (D == 64 && PS == 32) return launch_gp<KVT, QT, 64, 32>(p, gp, grid, st);
+  if (D == 128 && PS == 16) return launch_gp<KVT, QT, 128, 16>(p, gp, grid, st);
+  if (D == 128 && PS == 32) return launch_gp<KVT, QT, 128, 32>(p, gp, grid, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int D, int PS, int gp,
+                         unsigned grid, hipStream_t st) {
+  if (kv_dtype == kF32) return launch_shape<kF32, kF32>(p, D, PS, gp, grid, st);
+  if (kv_dtype == kBF16) return launch_shape<kBF16, kBF16>(p, D, PS, gp, grid, st);
+  if (kv_dtype == kFP8) return launch_shape<kFP8, kBF16>(p, D, PS, gp, grid, st);
+  return hipErrorInvalidValue;
+}
+
+template <int QT, int D>
+static hipError_t launch_merge_ps(const DecodeParams& p, int PS, unsigned grid, hipStream_t st) {
+  if (PS == 16) hipLaunchKernelGGL((split_merge_kernel<QT, D, 16>), dim3(grid), dim3(64), 0, st, p);
+  else if (PS == 32) hipLaunchKernelGGL((split_merge_kernel<QT, D, 32>), dim3(grid), dim3(64), 0, st, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_split_merge(const DecodeParams& p, int q_dtype, int D, int PS, hipStream_t st) {
+  const unsigned grid = static_cast<unsigned>(p.B) * p.H_qo;
+  if (q_dtype == kF32 && D == 64) return launch_merge_ps<kF32, 64>(p, PS, grid, st);
+  if (q_dtype == kF32 && D == 128) return launch_merge_ps<kF32, 128>(p, PS, grid, st);
+  if (q_dtype == kBF16 && D == 64) return launch_merge_ps<kBF16, 64>(p, PS, grid, st);
+  if (q_dtype == kBF16 && D == 128) return launch_merge_ps<kBF16, 128>(p, PS, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pdk

@@ -1,0 +1,162 @@
+// Device-side helpers and kernel parameter blocks shared by the libpdecode kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pdk {
+
+enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kEmptyLse = -5e4f;  // lse of a sequence with no attended rows
+
+// ---------------------------------------------------------------------------------------------
+// Parameter blocks (passed by value to the kernels).
+struct DecodeParams {
+  const void* q;
+  const void* pages;
+  const int32_t* indptr;
+  const int32_t* values;
+  const int32_t* length_info;
+  const int32_t* q_pos;      // RoPE: query positions [B]
+  const int32_t* k_off;      // RoPE: position of attended row 0 [B]
+  const float* k_scale;      // fp8 KV: per-KV-head scales
+  const float* v_scale;
+  void* out;
+  float* lse;
+  float* part_o;             // split-KV partial outputs [B, H_qo, num_chunks, D] (normalised)
+  float* part_lse;           // split-KV partial lse [B, H_qo, num_chunks]
+  int32_t B, H_qo, H_kv, G;
+  int32_t max_num_pages;     // page ids are clamped into the pool before any KV address is formed
+  int32_t sliding, rotary;
+  float rope_scale, rope_theta;
+  float score_scale;         // sm_scale * log2(e): scores are kept in log2 units
+  int32_t chunk_slots;       // page slots per chunk
+  int32_t num_chunks;        // chunks in the grid; the last one takes every remaining slot
+};
+
+struct AppendParams {
+  const void* new_k;
+  const void* new_v;
+  const int32_t* slots;
+  void* pages;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t T, H_kv, D, PS, max_num_pages;
+};
+
+struct MergeParams {
+  void* v;
+  float* s;
+  const void* v_other;
+  const float* s_other;
+  int32_t rows;              // n * num_heads
+  int32_t D;
+};
+
+// ---------------------------------------------------------------------------------------------
+// Element codecs.
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Two OCP e4m3fn codes (bytes 0,1 or 2,3 of `w`) -> two floats, with the gfx950 converter.
+template <bool HI>
+__device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
+  auto r = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI);
+  a = r[0];
+  b = r[1];
+}
+
+// fp32 -> e4m3fn code: saturate to +-448 (NaN passes through), then the hardware conversion
+// rounds to nearest even.
+__device__ __forceinline__ uint8_t f32_to_fp8(float x) {
+  x = x > 448.f ? 448.f : (x < -448.f ? -448.f : x);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false);
+  return static_cast<uint8_t>(r & 0xff);
+}
+
+// A 16-byte vector of KV elements decoded to fp32.
+template <int KVT> struct Kv;
+template <> struct Kv<kF32> {
+  static constexpr int EB = 4, EPV = 4;
+  __device__ static void unpack(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+};
+template <> struct Kv<kBF16> {
+  static constexpr int EB = 2, EPV = 8;
+  __device__ static void unpack(const uint4& v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(w[i]); f[2 * i + 1] = bf16_hi(w[i]); }
+  }
+};
+template <> struct Kv<kFP8> {
+  static constexpr int EB = 1, EPV = 16;
+  __device__ static void unpack(const uint4& v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fp8x2_to_f32<false>(w[i], f[4 * i], f[4 * i + 1]);
+      fp8x2_to_f32<true>(w[i], f[4 * i + 2], f[4 * i + 3]);
+    }
+  }
+};
+
+template <int QT> __device__ __forceinline__ float load_q(const void* base, size_t idx) {
+  if constexpr (QT == kF32) return static_cast<const float*>(base)[idx];
+  else return bf16_to_f32(static_cast<const uint16_t*>(base)[idx]);
+}
+template <int QT> __device__ __forceinline__ void store_out(void* base, size_t idx, float v) {
+  if constexpr (QT == kF32) static_cast<float*>(base)[idx] = v;
+  else static_cast<uint16_t*>(base)[idx] = f32_to_bf16(v);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Sequence geometry: which page slots a sequence attends and which rows of each page count.
+// Slots [0, n0) are the sink pages (positions [0, sink)); slots [n0, n_slots) are the pages from
+// first1 on that cover positions [win_off, total). Without a window sink = win_off = 0.
+struct SeqGeom {
+  int32_t beg, np, total, sink, win_off, n0, first1, n_slots;
+};
+
+__device__ __forceinline__ SeqGeom seq_geom(const int32_t* indptr, const int32_t* li, int B,
+                                            int b, int ps, int sliding) {
+  SeqGeom g;
+  g.beg = indptr[b];
+  g.np = indptr[b + 1] - g.beg;
+  g.total = g.sink = g.win_off = g.n0 = g.first1 = g.n_slots = 0;
+  if (g.np <= 0) return g;
+  g.total = (g.np - 1) * ps + li[b];
+  if (sliding) {
+    g.win_off = li[B + b];
+    g.sink = li[2 * B + b];
+  }
+  g.n0 = (g.sink + ps - 1) / ps;
+  g.first1 = g.win_off / ps;
+  const int n1 = g.win_off < g.total ? g.np - g.first1 : 0;
+  g.n_slots = g.n0 + n1;
+  return g;
+}
+
+// Chunks a sequence with n_slots page slots occupies.
+__device__ __forceinline__ int chunks_used(int n_slots, int chunk_slots, int num_chunks) {
+  if (n_slots <= 0) return 0;
+  int n = (n_slots + chunk_slots - 1) / chunk_slots;
+  return n < num_chunks ? n : num_chunks;
+}
+
+}  // namespace pdk

@@ -1,0 +1,139 @@
+"""CPU checks of the C ABI: the library builds, loads and exports every declared symbol, and the
+host-side argument checks return the documented status without launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_decode_08_amd as pk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pk.LIB_PATH):
+        from paged_kv_decode_08_amd import build
+        build.build()
+    return pk.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pdecode.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pdecode_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 6
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, name in pk.STATUS.items():
+        assert pk.status_string(code) == name
+
+
+def desc(**over):
+    base = dict(batch=4, num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                max_num_pages=100, q_dtype="bf16", kv_dtype="bf16", max_kv_len=4096)
+    base.update(over)
+    return pk.make_desc(**base)
+
+
+def attention_status(L, d, workspace=None, ws_bytes=0, rope=None, sm_scale=0.1, ptrs=True):
+    P = FAKE if ptrs else None
+    return L.pdecode_attention(ctypes.byref(d) if d is not None else None, P, P, P, P, P,
+                               None if rope is None else ctypes.byref(rope), sm_scale, P, P,
+                               workspace, ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(num_qo_heads=30), 1),            # not a multiple of num_kv_heads
+    (dict(batch=-1), 1),
+    (dict(head_dim=0), 1),
+    (dict(max_num_pages=0), 1),
+    (dict(num_kv_splits=-2), 1),
+    (dict(head_dim=96), 2),                # unsupported head dim
+    (dict(page_size=8), 2),
+    (dict(num_qo_heads=72), 2),            # group size 9
+    (dict(q_dtype="f32", kv_dtype="bf16"), 2),
+    (dict(q_dtype="f32", kv_dtype="fp8"), 1),  # fp8 without scales is an argument error first
+])
+def test_attention_argument_errors(L, over, code):
+    assert attention_status(L, desc(**over)) == code
+
+
+def test_attention_null_desc_and_pointers(L):
+    assert attention_status(L, None) == 1
+    assert attention_status(L, desc(), ptrs=False) == 1
+    assert attention_status(L, desc(), sm_scale=float("nan")) == 1
+
+
+def test_attention_workspace_checks(L):
+    d = desc()
+    need = pk.workspace_bytes(d)
+    assert need > 0
+    assert attention_status(L, d) == 3
+    assert attention_status(L, d, workspace=FAKE, ws_bytes=need - 1) == 3
+    unaligned = ctypes.c_void_p(0x1001)
+    assert attention_status(L, d, workspace=unaligned, ws_bytes=need) == 1
+
+
+def test_rope_checks(L):
+    d = desc(num_kv_splits=1)
+    assert pk.workspace_bytes(d) == 0
+    r = pk.Rope(1, 1.0, 5e5, None, None)
+    assert attention_status(L, d, rope=r) == 1
+    r = pk.Rope(1, 1.0, -1.0, FAKE, FAKE)
+    assert attention_status(L, d, rope=r) == 1
+
+
+def test_batch_zero_is_a_noop(L):
+    assert attention_status(L, desc(batch=0), ptrs=False) == 0
+
+
+def test_plan_and_workspace(L):
+    d = desc(num_kv_splits=1)
+    assert pk.plan(d)[1] == 1 and pk.workspace_bytes(d) == 0
+    d = desc(num_kv_splits=5)
+    cp, nc = pk.plan(d)
+    assert nc == 5 and cp * 5 >= 4096 // 16
+    ws = pk.workspace_bytes(d)
+    assert ws >= 4 * 32 * 5 * (128 + 1) * 4 and ws % 256 == 0
+    # automatic plan: chunks of at least 256 rows; long contexts split, tiny ones do not
+    cp, nc = pk.plan(desc(batch=2, max_kv_len=131072))
+    assert nc > 1 and cp * 16 >= 256
+    assert pk.plan(desc(batch=4, num_qo_heads=4, num_kv_heads=4, head_dim=64, max_kv_len=50))[1] == 1
+    assert pk.workspace_bytes(desc(head_dim=96)) == 0
+
+
+def test_merge_argument_errors(L):
+    f = L.pdecode_merge_state_inplace
+    assert f(-1, 4, 128, 1, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert f(3, 0, 128, 1, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert f(3, 4, 128, 2, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert f(3, 4, 128, 1, FAKE, FAKE, FAKE, FAKE, None) == 1  # v aliases v_other
+    assert f(3, 4, 128, 1, None, FAKE, ctypes.c_void_p(0x2000), FAKE, None) == 1
+    assert f(0, 4, 128, 1, None, None, None, None, None) == 0
+
+
+def test_append_argument_errors(L):
+    f = L.pdecode_append_kv
+    d = desc()
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, -1, FAKE, None) == 1
+    assert f(ctypes.byref(d), None, FAKE, FAKE, 4, FAKE, None) == 1
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, None) == 0
+    assert f(ctypes.byref(desc(q_dtype="f32")), FAKE, FAKE, FAKE, 4, FAKE, None) == 2
+    assert f(ctypes.byref(desc(kv_dtype="fp8")), FAKE, FAKE, FAKE, 4, FAKE, None) == 1
+    assert f(None, FAKE, FAKE, FAKE, 4, FAKE, None) == 1
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        pk._ptr(torch.zeros(3))

@@ -1,0 +1,376 @@
+"""GPU parity: libpdecode (HIP, through the C ABI) against the oracle on the same seeded inputs.
+
+Tolerances (stated for this path): fp32 KV |d out| <= 1e-5 and |d lse| <= 1e-5; bf16 KV and fp8
+KV after dequantisation |d out| <= 2e-2 absolute and |d lse| <= 1e-3. Page gathers and append
+placement are bit-exact. Unused pool pages are NaN-poisoned, so a stray gather shows as NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_decode_08_amd as pk
+    pk.lib()
+    yield
+
+
+def check(w, out, lse, select=None, label=""):
+    """Compares GPU out/lse with the oracle (all pairs, or the selected (b, h_qo) pairs)."""
+    tol_o, tol_l = gu.tolerance(w)
+    o_gpu = gu.to_np64(out)
+    l_gpu = gu.to_np64(lse)
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(l_gpu)), f"{label}: non-finite output"
+    if select is None:
+        o_ref, l_ref = oracle.decode(**w.oracle_kwargs())
+        do = np.abs(o_gpu - o_ref).max(initial=0)
+        dl = np.abs(l_gpu - l_ref).max(initial=0)
+    else:
+        o_ref, l_ref = oracle.decode(**w.oracle_kwargs(), select=select)
+        og = o_gpu[select[:, 0], select[:, 1]]
+        lg = l_gpu[select[:, 0], select[:, 1]]
+        do = np.abs(og - o_ref).max(initial=0)
+        dl = np.abs(lg - l_ref).max(initial=0)
+    print(f"{label}: max|dout|={do:.3g} max|dlse|={dl:.3g}", flush=True)
+    assert do <= tol_o, f"{label}: |dout| {do} > {tol_o}"
+    assert dl <= tol_l, f"{label}: |dlse| {dl} > {tol_l}"
+
+
+def run_and_check(w, **kw):
+    dev = gu.upload(w)
+    out, lse = gu.run_attention(w, dev, **kw)
+    torch.cuda.synchronize()
+    check(w, out, lse, label=w.name)
+    return dev, out, lse
+
+
+# ------------------------------------------------------------------ small cases, all outputs
+def test_tiny_fp32_config():
+    """The tiny fp32 workload: B=4, 4/4 heads, D=64, page 16, lengths {1,17,33,50}, pool 16."""
+    run_and_check(synth.tiny_fp32())
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+def test_group_sizes_and_dtypes(G, kv):
+    qd = "f32" if kv == "f32" else "bf16"
+    lens = [1, 15, 16, 17, 100, 257, 0, 33]
+    w = synth.make_workload(name=f"G{G}_{kv}", B=len(lens), H_qo=2 * G, H_kv=2, D=128,
+                            page_size=16 if kv != "fp8" else 32, seq_lens=lens, q_dtype=qd,
+                            kv_dtype=kv, seed=100 + G, max_num_pages=64)
+    run_and_check(w)
+
+
+@pytest.mark.parametrize("D,ps", [(64, 16), (64, 32), (128, 16), (128, 32)])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+def test_head_dims_and_page_sizes(D, ps, kv):
+    qd = "f32" if kv == "f32" else "bf16"
+    lens = [3, 64, 130, 31, 1]
+    w = synth.make_workload(name=f"D{D}_ps{ps}_{kv}", B=5, H_qo=8, H_kv=2, D=D, page_size=ps,
+                            seq_lens=lens, q_dtype=qd, kv_dtype=kv, seed=7 + D + ps,
+                            max_num_pages=32)
+    run_and_check(w)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7, 64])
+def test_forced_splits(splits):
+    """Split-KV chunking (any chunk count, ragged last chunk, more chunks than pages)."""
+    lens = [1000, 17, 0, 513, 2048, 1]
+    w = synth.make_workload(name=f"splits{splits}", B=6, H_qo=16, H_kv=4, D=128, page_size=16,
+                            seq_lens=lens, seed=31, max_num_pages=400)
+    run_and_check(w, num_kv_splits=splits)
+
+
+def test_max_len_hint_too_small_is_still_exact():
+    """max_kv_len only sizes the grid: a hint far below the real lengths still gives exact
+    results (the last chunk takes the rest)."""
+    lens = [700, 1200, 64]
+    w = synth.make_workload(name="hint_small", B=3, H_qo=8, H_kv=2, D=128, page_size=16,
+                            seq_lens=lens, seed=32, max_num_pages=200)
+    run_and_check(w, max_kv_len=100)
+    run_and_check(w, max_kv_len=1)
+
+
+@pytest.mark.parametrize("sink,window", [(4, 64), (0, 50), (3, 1000), (16, 40), (5, 5)])
+def test_sliding_window_and_sink(sink, window):
+    lens = [300, 70, 16, 5, 0, 129]
+    w = synth.make_workload(name=f"swa_s{sink}_w{window}", B=6, H_qo=8, H_kv=2, D=128,
+                            page_size=16, seq_lens=lens, seed=41, max_num_pages=64,
+                            window=window, sink=sink)
+    run_and_check(w)
+    run_and_check(w, num_kv_splits=3)
+
+
+def test_rope_small():
+    lens = [300, 70, 16, 1, 129]
+    w = synth.make_workload(name="rope", B=5, H_qo=8, H_kv=2, D=128, page_size=16,
+                            seq_lens=lens, seed=51, max_num_pages=64, rotary_mode=1,
+                            rope_theta=500000.0)
+    run_and_check(w)
+
+
+def test_rope_window_large_positions():
+    """RoPE with sink + window at positions up to ~16k (the angle must be computed accurately)."""
+    lens = [16384, 9000, 4200]
+    w = synth.make_workload(name="rope_swa_pos", B=3, H_qo=8, H_kv=2, D=128, page_size=16,
+                            seq_lens=lens, seed=52, max_num_pages=2048, rotary_mode=1,
+                            rope_theta=500000.0, window=4096, sink=4)
+    run_and_check(w)
+    w2 = synth.make_workload(name="rope_scale", B=3, H_qo=4, H_kv=1, D=64, page_size=32,
+                             seq_lens=lens, seed=53, max_num_pages=2048, rotary_mode=1,
+                             rope_theta=10000.0, rope_scale=0.25, window=2048, sink=0)
+    run_and_check(w2)
+
+
+def test_empty_window():
+    """Pages but an empty window and no sink: out = 0, lse = -5e4."""
+    w = synth.make_workload(name="empty_win", B=3, H_qo=4, H_kv=2, D=64, page_size=16,
+                            seq_lens=[5, 40, 0], seed=3, max_num_pages=16, window=4, sink=0)
+    w.length_info[1] = w.seq_lens  # window starts at the end
+    w.attended[:] = 0
+    dev, out, lse = run_and_check(w)
+    assert np.all(gu.to_np64(out) == 0) and np.all(gu.to_np64(lse) == -5e4)
+
+
+def test_all_empty_batch():
+    w = synth.make_workload(name="all_empty", B=4, H_qo=4, H_kv=4, D=64, page_size=16,
+                            seq_lens=[0, 0, 0, 0], seed=3, max_num_pages=4, q_dtype="f32",
+                            kv_dtype="f32")
+    dev, out, lse = run_and_check(w)
+    assert np.all(gu.to_np64(lse) == -5e4)
+
+
+# ------------------------------------------------------------------ properties on the GPU
+def test_deterministic_and_permutation_invariant():
+    """Two runs are bit-identical; relabelling the physical pages (moving the data) leaves the
+    GPU output bit-identical (the gather follows the table exactly)."""
+    w = synth.llama3_8b_bf16(B=4, lens=[600, 1000, 37, 2100])
+    dev = gu.upload(w)
+    o1, l1 = gu.run_attention(w, dev)
+    o2, l2 = gu.run_attention(w, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    perm = np.random.default_rng(9).permutation(w.max_num_pages).astype(np.int32)
+    pool = np.empty_like(w.pages)
+    pool[perm] = w.pages
+    w2 = synth.Workload(**{**w.__dict__, "pages": pool, "page_values": perm[w.page_values]})
+    dev2 = gu.upload(w2)
+    o3, l3 = gu.run_attention(w2, dev2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16)) and torch.equal(l1, l3)
+
+
+def test_split_equals_unsplit_long():
+    """Long context (a scaled-down long-context split case): auto split vs. no split agree
+    within the bf16 tolerance, and both match the oracle."""
+    w = synth.make_workload(name="long_small", B=2, H_qo=32, H_kv=8, D=128, page_size=16,
+                            seq_lens=[8192, 20000], seed=1003, max_num_pages=2048)
+    dev = gu.upload(w)
+    oa, la = gu.run_attention(w, dev, num_kv_splits=0)
+    o1, l1 = gu.run_attention(w, dev, num_kv_splits=1)
+    torch.cuda.synchronize()
+    check(w, oa, la, label="auto split")
+    check(w, o1, l1, label="no split")
+    assert np.abs(gu.to_np64(oa) - gu.to_np64(o1)).max() <= 2e-2
+    assert np.abs(gu.to_np64(la) - gu.to_np64(l1)).max() <= 1e-3
+
+
+# ------------------------------------------------------------------ merge and append
+@pytest.mark.parametrize("vd", ["f32", "bf16"])
+def test_merge_state_inplace(vd):
+    import paged_kv_decode_08_amd as pk
+    rng = np.random.default_rng(4)
+    n, H, D = 7, 5, 96
+    v = rng.standard_normal((n, H, D)).astype(np.float32)
+    vo = rng.standard_normal((n, H, D)).astype(np.float32)
+    s = (rng.standard_normal((n, H)) * 8).astype(np.float32)
+    so = (rng.standard_normal((n, H)) * 8).astype(np.float32)
+    s[0, 0] = so[0, 0] = -5e4  # two empty states
+    if vd == "bf16":
+        v = synth.cast_f32(v, "bf16")
+        vo = synth.cast_f32(vo, "bf16")
+    tv = gu.to_device_storage(v, vd)
+    tvo = gu.to_device_storage(vo, vd)
+    ts = torch.from_numpy(s).cuda()
+    tso = torch.from_numpy(so).cuda()
+    pk.merge_state_inplace(tv, ts, tvo, tso)
+    torch.cuda.synchronize()
+    from tests.dense_ref import to_f64
+    ref_v, ref_s = oracle.merge_state(to_f64(v, vd), s, to_f64(vo, vd), so)
+    tol = 1e-5 if vd == "f32" else 2e-2
+    assert np.abs(gu.to_np64(tv) - ref_v).max() <= tol
+    assert np.abs(gu.to_np64(ts) - ref_s).max() <= 1e-5 * max(1, np.abs(ref_s).max())
+
+
+def test_merge_two_halves_equals_whole_on_gpu():
+    """Attention over rows [0, k) and over [k, L) (a window with sink 0 starting at k), merged by
+    pdecode_merge_state_inplace, equals attention over [0, L)."""
+    import paged_kv_decode_08_amd as pk
+    L, k = 1000, 421
+    w = synth.make_workload(name="whole", B=1, H_qo=8, H_kv=2, D=128, page_size=16,
+                            seq_lens=[L], seed=61, max_num_pages=128)
+    dev = gu.upload(w)
+    ow, lw = gu.run_attention(w, dev)
+    np_pre = (k + 15) // 16
+    pre = synth.Workload(**{**w.__dict__, "page_indptr": np.array([0, np_pre], np.int32),
+                            "length_info": np.array([k - (np_pre - 1) * 16], np.int32),
+                            "attended": np.array([k], np.int32)})
+    suf = synth.Workload(**{**w.__dict__, "sliding_window": True,
+                            "length_info": np.array([[w.length_info[0]], [k], [0]], np.int32),
+                            "attended": np.array([L - k], np.int32)})
+    o1, l1 = gu.run_attention(pre, gu.upload(pre))
+    o2, l2 = gu.run_attention(suf, gu.upload(suf))
+    pk.merge_state_inplace(o1, l1, o2, l2)
+    torch.cuda.synchronize()
+    assert np.abs(gu.to_np64(o1) - gu.to_np64(ow)).max() <= 2e-2
+    assert np.abs(gu.to_np64(l1) - gu.to_np64(lw)).max() <= 1e-3
+    check(w, o1, l1, label="merged halves")
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+def test_append_bitexact(kv):
+    import paged_kv_decode_08_amd as pk
+    ind = "f32" if kv == "f32" else "bf16"
+    H_kv, D, ps, P = 8, 128, 16 if kv != "fp8" else 32, 64
+    pool = synth.poisoned_pool(P, H_kv, ps, D, kv)
+    k, v, slots = synth.append_inputs(T=40, H_kv=H_kv, D=D, page_size=ps, max_num_pages=P,
+                                      in_dtype=ind, seed=12, skip_every=5)
+    slots[1] = P * ps + 3  # past the pool: skipped
+    ks = vs = None
+    if kv == "fp8":
+        ks = np.random.default_rng(1).uniform(0.5 / 448, 2 / 448, H_kv).astype(np.float32)
+        vs = np.random.default_rng(2).uniform(0.5 / 448, 2 / 448, H_kv).astype(np.float32)
+        k = synth.cast_f32(np.random.default_rng(3).standard_normal(k.shape).astype(np.float32) * 0.6, "bf16")
+    tks = None if ks is None else torch.from_numpy(ks).cuda()
+    tvs = None if vs is None else torch.from_numpy(vs).cuda()
+    desc = pk.make_desc(batch=1, num_qo_heads=H_kv, num_kv_heads=H_kv, head_dim=D, page_size=ps,
+                        max_num_pages=P, q_dtype=ind, kv_dtype=kv, k_scale=tks, v_scale=tvs)
+    tpool = gu.to_device_storage(pool, kv)
+    pk.append_kv(desc, gu.to_device_storage(k, ind), gu.to_device_storage(v, ind),
+                 torch.from_numpy(slots).cuda(), tpool)
+    torch.cuda.synchronize()
+    slots_o = slots.copy()
+    slots_o[1] = -1
+    ref = oracle.append_kv(pages=pool.copy(), new_k=k, new_v=v, slots=slots_o, H_kv=H_kv, D=D,
+                           ps=ps, in_dtype=synth.DTYPE_CODE[ind], kv_dtype=synth.DTYPE_CODE[kv],
+                           k_scale=ks, v_scale=vs)
+    got = tpool.cpu()
+    got = got.view(torch.int16).numpy().view(np.uint16) if kv == "bf16" else got.numpy()
+    assert got.tobytes() == ref.tobytes()
+
+
+def test_append_fp8_rounding_exhaustive():
+    """Every e4m3fn code's value, the midpoints between neighbours (ties to even), values beyond
+    448 (saturation) and tiny values, quantised by the GPU append, match the oracle's encoder."""
+    import paged_kv_decode_08_amd as pk
+    table = np.array([oracle.fp8_value(c) for c in range(0x7F)])
+    mids = (table[:-1] + table[1:]) / 2
+    xs = np.concatenate([table, mids, -table, -mids, [500.0, 1e4, -1e4, 448.5, 463.9, 464.0,
+                                                      1e-4, 2e-3, -3e-3]]).astype(np.float32)
+    D, H_kv, ps = 64, 1, 16
+    T = (xs.size + D - 1) // D
+    x = np.zeros(T * D, np.float32)
+    x[:xs.size] = xs
+    x = x.reshape(T, 1, D)
+    ks = np.array([1.0], np.float32)
+    P = (T + ps - 1) // ps
+    pool = synth.poisoned_pool(P, H_kv, ps, D, "fp8")
+    slots = np.arange(T, dtype=np.int32)
+    desc = pk.make_desc(batch=1, num_qo_heads=1, num_kv_heads=1, head_dim=D, page_size=ps,
+                        max_num_pages=P, q_dtype="f32", kv_dtype="fp8",
+                        k_scale=torch.from_numpy(ks).cuda(), v_scale=torch.from_numpy(ks).cuda())
+    # The public supported set pairs fp8 KV with bf16 q; fp32 input is used here only to feed
+    # exact fp32 values to the quantiser.
+    tpool = torch.from_numpy(pool).cuda()
+    st = pk.lib().pdecode_append_kv(
+        __import__("ctypes").byref(desc), pk._ptr(torch.from_numpy(x).cuda()),
+        pk._ptr(torch.from_numpy(x).cuda()), pk._ptr(torch.from_numpy(slots).cuda()), T,
+        pk._ptr(tpool), pk._stream(None))
+    if st == 2:
+        pytest.skip("fp32 -> fp8 append outside the supported set")
+    assert st == 0
+    torch.cuda.synchronize()
+    got = tpool.cpu().numpy()[:, 0, 0].reshape(-1)[:T * D].reshape(T, D)
+    ref = oracle.append_kv(pages=pool.copy(), new_k=x, new_v=x, slots=slots, H_kv=1, D=D, ps=ps,
+                           in_dtype=0, kv_dtype=2, k_scale=ks, v_scale=ks)
+    assert got.tobytes() == ref[:, 0, 0].reshape(-1)[:T * D].reshape(T, D).tobytes()
+
+
+def test_append_then_decode():
+    """Append one token per sequence into its next slot, then decode: matches the oracle run on
+    the oracle's own appended pool."""
+    import paged_kv_decode_08_amd as pk
+    w = synth.make_workload(name="append_decode", B=4, H_qo=8, H_kv=2, D=128, page_size=16,
+                            seq_lens=[31, 32, 1, 100], seed=71, max_num_pages=64)
+    # slot of the next token of each sequence: its last page when not full, else a fresh page
+    free = sorted(set(range(w.max_num_pages)) - set(w.page_values.tolist()))
+    slots, new_vals, new_indptr, new_last = [], [], [0], []
+    for b in range(w.B):
+        pages = list(w.page_values[w.page_indptr[b]:w.page_indptr[b + 1]])
+        last = int(w.length_info[b])
+        if last == 16:
+            pages.append(free.pop(0))
+            last = 0
+        slots.append(pages[-1] * 16 + last)
+        new_vals += pages
+        new_indptr.append(len(new_vals))
+        new_last.append(last + 1)
+    slots = np.array(slots, np.int32)
+    k, v, _ = synth.append_inputs(T=w.B, H_kv=w.H_kv, D=w.D, page_size=16,
+                                  max_num_pages=w.max_num_pages, in_dtype="bf16", seed=72,
+                                  slots=slots)
+    dev = gu.upload(w)
+    desc = gu.desc_for(w, dev)
+    pk.append_kv(desc, gu.to_device_storage(k, "bf16"), gu.to_device_storage(v, "bf16"),
+                 torch.from_numpy(slots).cuda(), dev["pages"])
+    pool_ref = oracle.append_kv(pages=w.pages.copy(), new_k=k, new_v=v, slots=slots,
+                                H_kv=w.H_kv, D=w.D, ps=16, in_dtype=1, kv_dtype=1)
+    w2 = synth.Workload(**{**w.__dict__, "pages": pool_ref,
+                           "page_values": np.array(new_vals, np.int32),
+                           "page_indptr": np.array(new_indptr, np.int32),
+                           "length_info": np.array(new_last, np.int32),
+                           "seq_lens": w.seq_lens + 1, "attended": w.attended + 1})
+    dev["values"] = torch.from_numpy(w2.page_values).cuda()
+    dev["indptr"] = torch.from_numpy(w2.page_indptr).cuda()
+    dev["length_info"] = torch.from_numpy(w2.length_info).cuda()
+    out, lse = gu.run_attention(w2, dev)
+    torch.cuda.synchronize()
+    check(w2, out, lse, label="append+decode")
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled
+def _sample_pairs(w, n, seed):
+    rng = np.random.default_rng(seed)
+    b = rng.integers(0, w.B, n)
+    h = rng.integers(0, w.H_qo, n)
+    # always include the longest sequence and first / last heads
+    b[0], h[0] = int(np.argmax(w.attended)), 0
+    b[1], h[1] = int(np.argmax(w.attended)), w.H_qo - 1
+    return np.stack([b, h], 1).astype(np.int32)
+
+
+@pytest.mark.parametrize("name,n", [("llama3_8b_bf16", 48), ("long_ctx_bf16", 12),
+                                    ("rope_swa_bf16", 32), ("fp8_gqa8", 48)])
+def test_full_size_config_sampled(name, n):
+    """Full-size workloads in the benchmark's launch configuration (automatic split plan),
+    checked on sampled (sequence, head) outputs against the oracle; every output finite."""
+    w = synth.CONFIGS[name]()
+    print(f"{name}: B={w.B} kv_bytes={w.kv_bytes}", flush=True)
+    dev = gu.upload(w)
+    out, lse = gu.run_attention(w, dev)
+    torch.cuda.synchronize()
+    check(w, out, lse, select=_sample_pairs(w, n, 5), label=name)
+    if name == "long_ctx_bf16":
+        o1, l1 = gu.run_attention(w, dev, num_kv_splits=1)
+        torch.cuda.synchronize()
+        assert np.abs(gu.to_np64(out) - gu.to_np64(o1)).max() <= 2e-2
+        assert np.abs(gu.to_np64(lse) - gu.to_np64(l1)).max() <= 1e-3
