@@ -11,7 +11,8 @@ LIB = os.path.join(HERE, "libpdecode.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["decode.hip", "merge.hip", "append.hip", "api.cpp"]
+SOURCES = ["decode_mfma.hip", "decode_valu.hip", "split_merge.hip", "merge.hip", "append.hip",
+           "api.cpp"]
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

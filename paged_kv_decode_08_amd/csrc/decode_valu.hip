@@ -33,7 +33,7 @@ __device__ __forceinline__ void rope_cs(int pos, float fhi, float flo, float& c,
 }
 
 template <int KVT, int QT, int D, int PS, int GP>
-__global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   using KV = Kv<KVT>;
   constexpr int EPV = KV::EPV;           // elements per 16-byte vector
   constexpr int VPR = D / EPV;           // vectors per row
@@ -277,50 +277,15 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   }
 }
 
-// Combines the normalised partial states of every split sequence by log-sum-exp:
-// M = max_c lse_c, w_c = 2^(lse_c - M), out = sum_c w_c O_c / sum_c w_c, lse = M + log2(sum w_c).
-// Sequences that used a single chunk were finalised by the decode kernel and are skipped.
-template <int QT, int D, int PS>
-__global__ __launch_bounds__(64) void split_merge_kernel(DecodeParams p) {
-  const int lane = threadIdx.x;
-  const int b = blockIdx.x / p.H_qo;
-  const int hq = blockIdx.x - b * p.H_qo;
-  const SeqGeom sg = seq_geom(p.indptr, p.length_info, p.B, b, PS, p.sliding);
-  const int nch = chunks_used(sg.n_slots, p.chunk_slots, p.num_chunks);
-  if (nch <= 1) return;
-  const size_t row0 = (size_t(b) * p.H_qo + hq) * p.num_chunks;
-  float M = -INFINITY;
-  for (int c = lane; c < nch; c += 64) M = fmaxf(M, p.part_lse[row0 + c]);
-#pragma unroll
-  for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, __shfl_xor(M, msk, 64));
-  constexpr int PER = D / 64;
-  float acc[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  float W = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const float w = exp2f(p.part_lse[row0 + c] - M);
-    W += w;
-    const float* po = p.part_o + (row0 + c) * D;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, po[lane + 64 * k], acc[k]);
-  }
-  const float inv = 1.0f / W;
-  const size_t ob = (size_t(b) * p.H_qo + hq) * D;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) store_out<QT>(p.out, ob + lane + 64 * k, acc[k] * inv);
-  if (lane == 0) p.lse[size_t(b) * p.H_qo + hq] = M + log2f(W);
-}
-
 // ---------------------------------------------------------------------------------------------
 // Host-side dispatch over the compiled shapes.
 template <int KVT, int QT, int D, int PS>
 static hipError_t launch_gp(const DecodeParams& p, int gp, unsigned grid, hipStream_t st) {
   switch (gp) {
-    case 1: hipLaunchKernelGGL((decode_kernel<KVT, QT, D, PS, 1>), dim3(grid), dim3(64), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<KVT, QT, D, PS, 2>), dim3(grid), dim3(64), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<KVT, QT, D, PS, 4>), dim3(grid), dim3(64), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<KVT, QT, D, PS, 8>), dim3(grid), dim3(64), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((decode_valu_kernel<KVT, QT, D, PS, 1>), dim3(grid), dim3(64), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_valu_kernel<KVT, QT, D, PS, 2>), dim3(grid), dim3(64), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_valu_kernel<KVT, QT, D, PS, 4>), dim3(grid), dim3(64), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_valu_kernel<KVT, QT, D, PS, 8>), dim3(grid), dim3(64), 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -336,28 +301,11 @@ static hipError_t launch_shape(const DecodeParams& p, int D, int PS, int gp, uns
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int D, int PS, int gp,
+hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, int D, int PS, int gp,
                          unsigned grid, hipStream_t st) {
   if (kv_dtype == kF32) return launch_shape<kF32, kF32>(p, D, PS, gp, grid, st);
   if (kv_dtype == kBF16) return launch_shape<kBF16, kBF16>(p, D, PS, gp, grid, st);
   if (kv_dtype == kFP8) return launch_shape<kFP8, kBF16>(p, D, PS, gp, grid, st);
-  return hipErrorInvalidValue;
-}
-
-template <int QT, int D>
-static hipError_t launch_merge_ps(const DecodeParams& p, int PS, unsigned grid, hipStream_t st) {
-  if (PS == 16) hipLaunchKernelGGL((split_merge_kernel<QT, D, 16>), dim3(grid), dim3(64), 0, st, p);
-  else if (PS == 32) hipLaunchKernelGGL((split_merge_kernel<QT, D, 32>), dim3(grid), dim3(64), 0, st, p);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_split_merge(const DecodeParams& p, int q_dtype, int D, int PS, hipStream_t st) {
-  const unsigned grid = static_cast<unsigned>(p.B) * p.H_qo;
-  if (q_dtype == kF32 && D == 64) return launch_merge_ps<kF32, 64>(p, PS, grid, st);
-  if (q_dtype == kF32 && D == 128) return launch_merge_ps<kF32, 128>(p, PS, grid, st);
-  if (q_dtype == kBF16 && D == 64) return launch_merge_ps<kBF16, 64>(p, PS, grid, st);
-  if (q_dtype == kBF16 && D == 128) return launch_merge_ps<kBF16, 128>(p, PS, grid, st);
   return hipErrorInvalidValue;
 }
 

@@ -105,7 +105,8 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
                   k_rope_pos_offset=None, page_order="shuffled", kv_sigma=1.0,
                   fp8_payload_sigma=112.0, scale_range=(0.5 / 448, 2.0 / 448)) -> Workload:
     """Draws a workload. seq_lens: total tokens per sequence (0 = empty sequence).
-    window: None (length_info [B]) or W (length_info [3, B]: last_page_len, max(sink, L - W), sink).
+    window: None (length_info [B]) or W (length_info [3, B]: last_page_len, max(sink', L - W),
+    sink') with sink' = min(sink, L).
     page_order: 'shuffled' (a seeded permutation of the pool, consecutive slices per sequence) or
     'identity' (pages 0, 1, 2, ... in order). fp8 KV: payload codes are fp8(clip(N(0,1) *
     fp8_payload_sigma, +-448)); per-KV-head scales ~ U[scale_range]."""
@@ -129,8 +130,8 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
         length_info = last
         attended = seq_lens.astype(np.int32)
     else:
-        win_off = np.where(npages > 0, np.maximum(sink, seq_lens - window), 0).astype(np.int32)
-        sinks = np.where(npages > 0, sink, 0).astype(np.int32)
+        sinks = np.where(npages > 0, np.minimum(sink, seq_lens), 0).astype(np.int32)
+        win_off = np.where(npages > 0, np.maximum(sinks, seq_lens - window), 0).astype(np.int32)
         length_info = np.stack([last, win_off, sinks]).astype(np.int32)
         attended = np.where(npages > 0, seq_lens - win_off + sinks, 0).astype(np.int32)
 
