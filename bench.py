@@ -1,11 +1,12 @@
 """Benchmark: single-token paged-KV decode attention on one MI355X.
 
 One step = one pdecode_attention call (every kernel of the path, split-KV merge included) over one
-batch of the Llama-3-8B-shaped bf16 decode workload: B=32, 32 q / 8 kv heads, D=128, page size 16,
-context lengths uniform in [512, 4096], page ids a shuffled subset of a 16384-page pool. Inputs
-are synthetic and resident in HBM before timing starts. Steps cycle through several independent
-input sets (disjoint pools, same lengths) so that no step finds its KV in the 256 MB last-level
-cache left warm by the previous one.
+batch of a decode workload; by default the Llama-3-8B-shaped bf16 one: B=32, 32 q / 8 kv heads,
+D=128, page size 16, context lengths uniform in [512, 4096], page ids a shuffled subset of a
+16384-page pool (--workload selects the other synthetic workloads of the parity tests). Inputs are
+synthetic and resident in HBM before timing starts. When a step reads less than 512 MB, steps cycle
+through several independent input sets (disjoint pools, same lengths) so that no step finds its KV
+in the 256 MB last-level cache left warm by the previous one.
 
 Prints one JSON line. value = KV-read GB/s (bytes of attended K/V rows per step / step time);
 ms_per_step is the wall time per step between synchronisations; `roofline` uses the average
@@ -22,6 +23,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+CTX_DESC = {"llama3_8b_bf16": "uniform[512,4096]", "long_ctx_bf16": "{32768,131072}",
+            "rope_swa_bf16": "uniform[1024,16384], window 4096 + sink 4, RoPE theta 5e5",
+            "fp8_gqa8": "lognormal(median 2048, sigma 0.5) capped at 8192",
+            "tiny_fp32": "{1,17,33,50}"}
 
 
 def parse():
@@ -33,6 +38,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="num_kv_splits (0 = automatic plan)")
+    ap.add_argument("--workload", default="llama3_8b_bf16",
+                    choices=["llama3_8b_bf16", "long_ctx_bf16", "rope_swa_bf16", "fp8_gqa8",
+                             "tiny_fp32"])
     return ap.parse_args()
 
 
@@ -51,22 +59,29 @@ def main():
     from tests import gpu_util as gu
 
     torch.cuda.set_device(0)
-    base = synth.llama3_8b_bf16()
+    make = synth.CONFIGS[args.workload]
+    base = make()
+    nsets = args.sets if base.kv_bytes < 512e6 else 1
     lens = base.seq_lens.astype(np.int64)
-    sets = [base] + [synth.llama3_8b_bf16(seed=1002 + 100 * i, lens=lens)
-                     for i in range(1, args.sets)]
+    sets = [base] + [make(seed=1002 + 100 * i, lens=lens) for i in range(1, nsets)]
     devs = [gu.upload(w) for w in sets]
     kv_bytes = base.kv_bytes
     desc = gu.desc_for(base, devs[0], num_kv_splits=args.splits)
     ws = pk.alloc_workspace(desc)
-    out = torch.empty((base.B, base.H_qo, base.D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((base.B, base.H_qo, base.D), dtype=gu.TORCH_STORAGE[base.q_dtype],
+                      device="cuda")
     lse = torch.empty((base.B, base.H_qo), dtype=torch.float32, device="cuda")
+    ropes = [None] * len(devs)
+    if base.rotary_mode:
+        ropes = [pk.make_rope(rotary_mode=base.rotary_mode, rope_scale=base.rope_scale,
+                              rope_theta=base.rope_theta, q_rope_position=d["q_pos"],
+                              k_rope_pos_offset=d["k_off"]) for d in devs]
     stream = torch.cuda.current_stream()
 
     def step(i):
         d = devs[i % len(devs)]
         pk.attention(desc, d["q"], d["pages"], d["indptr"], d["values"], d["length_info"], out,
-                     lse, base.sm_scale, workspace=ws, stream=stream)
+                     lse, base.sm_scale, rope=ropes[i % len(devs)], workspace=ws, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -108,11 +123,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": base.kv_dtype if base.kv_dtype != "fp8" else "fp8-e4m3fn KV, bf16 q/out",
         "data": "synthetic",
-        "config": {"workload": "llama3_8b_decode_bf16", "batch": base.B,
+        "config": {"workload": base.name, "batch": base.B,
                    "num_qo_heads": base.H_qo, "num_kv_heads": base.H_kv, "head_dim": base.D,
-                   "page_size": base.page_size, "ctx_len": "uniform[512,4096]",
+                   "page_size": base.page_size, "kv_dtype": base.kv_dtype,
+                   "ctx_len": CTX_DESC.get(args.workload, ""),
                    "kv_bytes_per_step": kv_bytes, "input_sets": len(sets),
                    "chunk_pages": cp, "num_chunks": nc},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

@@ -104,17 +104,20 @@ typedef struct pdecode_rope {
  * invalid description. */
 size_t pdecode_workspace_bytes(const pdecode_desc *d);
 
-/* The split plan for `d`: rows are processed in chunks of *chunk_pages pages (page slots) and a
- * sequence uses at most *num_chunks chunks. Returns PDECODE_OK or an argument error. */
+/* The split plan for `d`: rows are processed in chunks of *chunk_pages page slots and a sequence
+ * uses at most *num_chunks chunks. Returns PDECODE_OK or an argument error. */
 pdecode_status pdecode_plan(const pdecode_desc *d, int32_t *chunk_pages, int32_t *num_chunks);
 
 /* Decode attention (see the header comment for the computation and layouts).
  * q, pages, page_indptr, page_values, length_info, out, lse: device pointers as above.
  * rope: NULL or a host struct. sm_scale: the score scale (typically 1/sqrt(head_dim)).
  * workspace: device memory of at least pdecode_workspace_bytes(d) bytes, 256-byte aligned
- * (may be NULL when that is 0); its contents on entry are ignored and it holds partial states
- * afterwards. out and lse are fully written. Errors: INVALID_ARG, UNSUPPORTED,
- * WORKSPACE_TOO_SMALL (nothing launched), HIP (launch failure). */
+ * (may be NULL when that is 0). It holds the split partial states and, at its end, arrival
+ * counters of the split (sequence, KV head) pairs: zero-fill it once before its first use; every
+ * call leaves the counters zero again, so it can be reused by later calls (also with other
+ * descriptions that fit). Calls that may run at the same time need separate workspaces.
+ * out and lse are fully written. Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL (nothing
+ * launched), HIP (launch failure). */
 pdecode_status pdecode_attention(const pdecode_desc *d, const void *q, const void *pages,
                                  const int32_t *page_indptr, const int32_t *page_values,
                                  const int32_t *length_info, const pdecode_rope *rope,

@@ -134,8 +134,10 @@ def plan(desc: Desc):
 
 
 def alloc_workspace(desc: Desc, device="cuda") -> torch.Tensor | None:
+    """A zero-filled workspace of pdecode_workspace_bytes(desc) bytes (the library keeps its
+    split counters zero between calls), or None when none is needed."""
     n = workspace_bytes(desc)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 
 def attention(desc: Desc, q, pages, page_indptr, page_values, length_info, out, lse, sm_scale,

@@ -19,7 +19,8 @@ struct Plan {
   int32_t num_chunks = 1;
   size_t part_o_bytes = 0;
   size_t part_lse_bytes = 0;
-  size_t workspace_bytes() const { return part_o_bytes + part_lse_bytes; }
+  size_t counter_bytes = 0;
+  size_t workspace_bytes() const { return part_o_bytes + part_lse_bytes + counter_bytes; }
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -61,6 +62,7 @@ Plan make_plan(const pdecode_desc* d) {
   const int64_t max_len = d->max_kv_len > 0 ? d->max_kv_len : int64_t(d->max_num_pages) * ps;
   const int64_t max_slots = (max_len + ps - 1) / ps + (d->sliding_window ? 2 : 0);
   const int64_t units = int64_t(d->batch) * d->num_kv_heads;
+
   int64_t chunk;
   if (d->num_kv_splits == 1) {
     chunk = max_slots;
@@ -81,6 +83,7 @@ Plan make_plan(const pdecode_desc* d) {
     const size_t rows = size_t(d->batch) * d->num_qo_heads * pl.num_chunks;
     pl.part_o_bytes = align256(rows * d->head_dim * sizeof(float));
     pl.part_lse_bytes = align256(rows * sizeof(float));
+    pl.counter_bytes = align256(size_t(d->batch) * d->num_kv_heads * sizeof(int32_t));
   }
   return pl;
 }
@@ -155,10 +158,13 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
   p.v_scale = d->v_scale;
   p.out = out;
   p.lse = lse;
-  p.part_o = pl.num_chunks > 1 ? static_cast<float*>(workspace) : nullptr;
-  p.part_lse = pl.num_chunks > 1
-                   ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_o_bytes)
-                   : nullptr;
+  const bool ws = pl.workspace_bytes() > 0;
+  p.part_o = ws ? static_cast<float*>(workspace) : nullptr;
+  p.part_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_o_bytes)
+                  : nullptr;
+  p.counters = ws ? reinterpret_cast<int*>(static_cast<char*>(workspace) + pl.part_o_bytes +
+                                           pl.part_lse_bytes)
+                  : nullptr;
   p.B = d->batch;
   p.H_qo = d->num_qo_heads;
   p.H_kv = d->num_kv_heads;
@@ -173,16 +179,15 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
   p.num_chunks = pl.num_chunks;
   const int gp = p.G <= 1 ? 1 : p.G <= 2 ? 2 : p.G <= 4 ? 4 : 8;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // bf16 KV without RoPE: q.K on the matrix cores (one 4-wave workgroup per work unit);
-  // otherwise the vector-ALU kernel (one wave per work unit; RoPE rotates K in fp32).
+  // bf16 KV without RoPE: q.K on the matrix cores (one 4-wave workgroup per chunk); otherwise
+  // the vector-ALU kernel (one wave per chunk; RoPE rotates K in fp32).
   if (d->kv_dtype == PDECODE_BF16 && !rotary)
     st = hip_status(pdk::launch_decode_mfma_bf16(p, d->head_dim, d->page_size, gp,
                                                  static_cast<unsigned>(grid), s));
   else
     st = hip_status(pdk::launch_decode_valu(p, d->kv_dtype, d->head_dim, d->page_size, gp,
                                             static_cast<unsigned>(grid), s));
-  if (st != PDECODE_OK || pl.num_chunks == 1) return st;
-  return hip_status(pdk::launch_split_merge(p, d->q_dtype, d->head_dim, d->page_size, s));
+  return st;
 }
 
 pdecode_status pdecode_merge_state_inplace(int32_t n, int32_t num_heads, int32_t head_dim,

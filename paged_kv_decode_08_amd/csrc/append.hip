@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     } else {
       const float x = load_q<IT>(in, src);
       const float sc = kv ? p.v_scale[h] : p.k_scale[h];
-      static_cast<uint8_t*>(p.pages)[dst] = f32_to_fp8(x / sc);
+      static_cast<uint8_t*>(p.pages)[dst] = f32_to_fp8(__fdiv_rn(x, sc));
     }
   }
 }

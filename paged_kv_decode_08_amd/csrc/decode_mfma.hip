@@ -17,9 +17,18 @@
 //  * P.V: P goes through LDS (transposed, [head][row]) to the V layout, where lane l holds 8
 //    consecutive dims of NI consecutive rows (each V load instruction reads whole 256-byte rows);
 //    O[g][dims] accumulates in fp32 FMAs.
-// The next slot's K and V are in flight while the current one is computed.
+// The next DEPTH slots' K and V are in flight while the current one is computed. A split sequence
+// is finished by the last of its workgroups to arrive (split.hpp).
 #include "device.hpp"
 #include "launch.hpp"
+#include "split.hpp"
+
+#ifndef PDK_MFMA_WAVES
+#define PDK_MFMA_WAVES 4  // wavefronts per workgroup (each takes every WAVES-th slot of the chunk)
+#endif
+#ifndef PDK_MFMA_DEPTH
+#define PDK_MFMA_DEPTH 1  // slots in flight per wave besides the one being computed
+#endif
 
 namespace pdk {
 
@@ -43,7 +52,7 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int PS, int GP, int WAVES>
+template <int D, int PS, int GP, int WAVES, int DEPTH>
 __global__ __launch_bounds__(64 * WAVES) void decode_mfma_bf16_kernel(DecodeParams p) {
   constexpr int RB = PS / 16;          // 16-row blocks per page
   constexpr int KS = D / 32;           // MFMA k-steps over the head dim
@@ -172,14 +181,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_bf16_kernel(DecodePara
       }
     tmax = xmax(xmax(tmax, 16), 32);
     const float mn = fmaxf(m, tmax);
-    const float alpha = exp2f(m - mn);
+    const float alpha = fast_exp2(m - mn);
     m = mn;
     float psum = 0.f;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        sv[rb][v] = exp2f(sv[rb][v] - mn);
+        sv[rb][v] = fast_exp2(sv[rb][v] - mn);
         psum += sv[rb][v];
       }
     dl = dl * alpha + psum;
@@ -214,10 +223,16 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_bf16_kernel(DecodePara
       }
     }
     wave_lds_fence();
+    const bool partial = lo > 0 || hi < PS;  // rows outside [lo, hi) may hold anything, even NaN
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float vf[8];
       Kv<kBF16>::unpack(vr[i], vf);
+      if (partial) {
+        const bool ok = NI * rg + i >= lo && NI * rg + i < hi;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[e] = ok ? vf[e] : 0.f;
+      }
 #pragma unroll
       for (int g = 0; g < GP; ++g)
 #pragma unroll
@@ -226,19 +241,25 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_bf16_kernel(DecodePara
   };
 
   if (nw > 0) {
-    uint4 ka[NK], va[NI], kb[NK], vb[NI];
-    issue(ka, va, page_of(0));
-    for (int k = 0; k < nw; k += 2) {
-      if (k - id_base >= 64) {  // keep the ids of slots k .. k + 2 at hand
+    // Ring of DEPTH + 1 register buffers: slot k is computed while slots k+1 .. k+DEPTH load.
+    uint4 kbuf[DEPTH + 1][NK], vbuf[DEPTH + 1][NI];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(kbuf[d], vbuf[d], page_of(min(d, nw - 1)));
+    for (int k = 0; k < nw; k += DEPTH + 1) {
+      if (k - id_base >= 64) {  // keep the ids of slots k .. k + 2 DEPTH at hand
         id_base += 64;
         ids0 = ids1;
         ids1 = fetch_id(id_base + 64 + l);
       }
-      issue(kb, vb, page_of(min(k + 1, nw - 1)));  // past the end: re-reads a cached block
-      process(ka, va, k);
-      if (k + 1 >= nw) break;
-      issue(ka, va, page_of(min(k + 2, nw - 1)));
-      process(kb, vb, k + 1);
+#pragma unroll
+      for (int r = 0; r <= DEPTH; ++r) {
+        if (k + r >= nw) break;
+        // unconditional, so the compiler's wait counts are static; past the end it re-reads the
+        // last slot's blocks (cache hits)
+        issue(kbuf[(r + DEPTH) % (DEPTH + 1)], vbuf[(r + DEPTH) % (DEPTH + 1)],
+              page_of(min(k + r + DEPTH, nw - 1)));
+        process(kbuf[r], vbuf[r], k + r);
+      }
     }
   }
 
@@ -273,7 +294,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_bf16_kernel(DecodePara
     float wsum = 0.f, o = 0.f;
 #pragma unroll
     for (int ww = 0; ww < WAVES; ++ww) {
-      const float f = exp2f(s_m[ww][g] - M);  // 0 for a wave without slots (m = -inf)
+      const float f = fast_exp2(s_m[ww][g] - M);  // 0 for a wave without slots (m = -inf)
       wsum = fmaf(f, s_d[ww][g], wsum);
       o = fmaf(f, s_o[ww][g][d], o);
     }
@@ -285,17 +306,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_mfma_bf16_kernel(DecodePara
       if (d == 0) p.lse[size_t(b) * p.H_qo + hq] = l2;
     } else {
       const size_t row = (size_t(b) * p.H_qo + hq) * p.num_chunks + c;
-      p.part_o[row * D + d] = val;
-      if (d == 0) p.part_lse[row] = l2;
+      store_agent(&p.part_o[row * D + d], val);
+      if (d == 0) store_agent(&p.part_lse[row], l2);
     }
   }
+  if (nch > 1) split_finish<kBF16, D, GP, 64 * WAVES>(p, b, h, nch);
 }
 
 template <int D, int PS, int GP>
 static hipError_t launch_w(const DecodeParams& p, unsigned grid, hipStream_t st) {
-  constexpr int WAVES = 4;
-  hipLaunchKernelGGL((decode_mfma_bf16_kernel<D, PS, GP, WAVES>), dim3(grid), dim3(64 * WAVES), 0,
-                     st, p);
+  constexpr int WAVES = PDK_MFMA_WAVES;
+  constexpr int DEPTH = PDK_MFMA_DEPTH;
+  hipLaunchKernelGGL((decode_mfma_bf16_kernel<D, PS, GP, WAVES, DEPTH>), dim3(grid),
+                     dim3(64 * WAVES), 0, st, p);
   return hipGetLastError();
 }
 

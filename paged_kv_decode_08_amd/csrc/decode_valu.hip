@@ -3,8 +3,8 @@
 //
 // Computation (TVM relax decode-kernels page, _attention_decode_cpu / _attention_decode): scores
 // s = sm_scale * q . k in log2 units, online softmax with a running max m and denominator d, output
-// O / d and lse = m + log2(d). Split-KV chunks write normalised partial states that the merge
-// kernel combines by log-sum-exp (the page's merge-state formula applied over all chunks).
+// O / d and lse = m + log2(d). Split-KV chunks write normalised partial states that are combined
+// by log-sum-exp (the page's merge-state formula applied over all chunks).
 //
 // Data path per page slot: the (page, K|V, head) block of page_size rows is contiguous
 // (page_size * head_dim * elem_bytes bytes, 1-16 KiB). The wave reads it with 16-byte loads,
@@ -15,9 +15,11 @@
 // rows, which are exactly the rows of the V elements it holds, so P.V needs no data exchange.
 // Each row group keeps partial (d, O) under a wave-uniform running max; they are summed across
 // row groups once at the end. The next slot's K/V is loaded while the current one is computed;
-// page ids come from one coalesced load per 64 slots.
+// page ids come from one coalesced load per 64 slots. A split sequence is finished by the last of
+// its workgroups to arrive (split.hpp).
 #include "device.hpp"
 #include "launch.hpp"
+#include "split.hpp"
 
 namespace pdk {
 
@@ -229,10 +231,16 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     }
 
     // ---- P.V
+    const bool partial = lo > 0 || hi < PS;  // rows outside [lo, hi) may hold anything, even NaN
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float vf[EPV];
       KV::unpack(vc[i], vf);
+      if (partial) {
+        const bool ok = i * RPI + rg >= lo && i * RPI + rg < hi;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) vf[e] = ok ? vf[e] : 0.f;
+      }
 #pragma unroll
       for (int g = 0; g < GP; ++g)
 #pragma unroll
@@ -254,27 +262,29 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
       for (int e = 0; e < EPV; ++e) O[g][e] += shfl_xor_f(O[g][e], msk);
     }
   }
-  if (rg != 0) return;
   const float vscale = (KVT == kFP8) ? p.v_scale[h] : 1.0f;
+  if (rg == 0) {
 #pragma unroll
-  for (int g = 0; g < GP; ++g) {
-    if (g >= G) break;
-    const int hq = h * G + g;
-    const float inv = vscale / dsum[g];
-    const float l = m[g] + log2f(dsum[g]);
-    if (nch == 1) {
-      const size_t ob = (size_t(b) * p.H_qo + hq) * D + d0;
+    for (int g = 0; g < GP; ++g) {
+      if (g >= G) break;
+      const int hq = h * G + g;
+      const float inv = vscale / dsum[g];
+      const float l = m[g] + log2f(dsum[g]);
+      if (nch == 1) {
+        const size_t ob = (size_t(b) * p.H_qo + hq) * D + d0;
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) store_out<QT>(p.out, ob + e, O[g][e] * inv);
-      if (cv == 0) p.lse[size_t(b) * p.H_qo + hq] = l;
-    } else {
-      const size_t row = (size_t(b) * p.H_qo + hq) * p.num_chunks + c;
-      float* po = p.part_o + row * D + d0;
+        for (int e = 0; e < EPV; ++e) store_out<QT>(p.out, ob + e, O[g][e] * inv);
+        if (cv == 0) p.lse[size_t(b) * p.H_qo + hq] = l;
+      } else {
+        const size_t row = (size_t(b) * p.H_qo + hq) * p.num_chunks + c;
+        float* po = p.part_o + row * D + d0;
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) po[e] = O[g][e] * inv;
-      if (cv == 0) p.part_lse[row] = l;
+        for (int e = 0; e < EPV; ++e) store_agent(&po[e], O[g][e] * inv);
+        if (cv == 0) store_agent(&p.part_lse[row], l);
+      }
     }
   }
+  if (nch > 1) split_finish<QT, D, GP, 64>(p, b, h, nch);
 }
 
 // ---------------------------------------------------------------------------------------------

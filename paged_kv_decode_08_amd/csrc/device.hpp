@@ -27,6 +27,7 @@ struct DecodeParams {
   float* lse;
   float* part_o;             // split-KV partial outputs [B, H_qo, num_chunks, D] (normalised)
   float* part_lse;           // split-KV partial lse [B, H_qo, num_chunks]
+  int* counters;             // split-KV arrival counters [B, H_kv]; zero between calls
   int32_t B, H_qo, H_kv, G;
   int32_t max_num_pages;     // page ids are clamped into the pool before any KV address is formed
   int32_t sliding, rotary;
@@ -79,12 +80,22 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
   b = r[1];
 }
 
-// fp32 -> e4m3fn code: saturate to +-448 (NaN passes through), then the hardware conversion
-// rounds to nearest even.
+// fp32 -> OCP e4m3fn code, round to nearest even, saturating to +-448 (NaN -> 0x7F). Bit-level,
+// so fp8 subnormals (down to 2^-9) are produced exactly.
 __device__ __forceinline__ uint8_t f32_to_fp8(float x) {
-  x = x > 448.f ? 448.f : (x < -448.f ? -448.f : x);
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false);
-  return static_cast<uint8_t>(r & 0xff);
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t u = bits & 0x7fffffffu;
+  if (u > 0x7f800000u) return 0x7f;                   // NaN
+  if (u >= 0x43e00000u) return sign | 0x7eu;          // |x| >= 448 (and inf): saturate
+  if (u >= 0x3c800000u) {                             // |x| >= 2^-6: normal fp8
+    const uint32_t r = (u + 0x7ffffu + ((u >> 20) & 1u)) >> 20;  // 3 mantissa bits, RNE
+    return static_cast<uint8_t>(sign | (r - (120u << 3)));      // rebias exponent 127 -> 7
+  }
+  // subnormal: value = m * 2^-9; |x| * 512 is exact, rintf rounds to nearest even (m = 8 is the
+  // smallest normal, code 0x08)
+  const uint32_t m = static_cast<uint32_t>(rintf(__uint_as_float(u) * 512.0f));
+  return static_cast<uint8_t>(sign | m);
 }
 
 // A 16-byte vector of KV elements decoded to fp32.

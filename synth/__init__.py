@@ -11,7 +11,8 @@ Layouts (row-major), as in the TVM decode page (batch_decode_paged_kv buffers):
   page_indptr  int32 [B + 1],  page_values int32 [nnz]
   length_info  int32 [B] (last_page_len) or [3, B] (last_page_len, window start, sink length)
 
-Unused pool pages are poisoned with NaN (fp32 NaN, bf16 0x7FC0, fp8 0x7F) so a stray gather shows.
+Unused pool pages, and the unused slots past the end of each sequence's last page, are poisoned
+with NaN (fp32 NaN, bf16 0x7FC0, fp8 0x7F) so a stray gather or an unmasked row shows.
 Storage dtypes: fp32 -> np.float32, bf16 -> np.uint16 bits, fp8 -> np.uint8 codes.
 """
 from __future__ import annotations
@@ -162,6 +163,10 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
             list(ex.map(fill, range(nblk)))
     elif nblk == 1:
         fill(0)
+    # Slots past the end of each sequence's last page are unused: poison them too.
+    for b in range(B):
+        if npages[b] > 0 and last[b] < ps:
+            pool[ids[indptr[b + 1] - 1], :, :, last[b]:, :] = poisoned_pool(1, 1, 1, 1, kv_dtype)[0, 0, 0, 0, 0]
     rng_q = _rng(seed, 3)
     q = cast_f32(rng_q.standard_normal((B, H_qo, D), dtype=np.float32), q_dtype)
     if sm_scale is None:
@@ -184,9 +189,10 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
 # The five benchmark workloads. Their sizes follow the decode settings the pages describe
 # (Llama-3-8B-shaped GQA heads, page size 16, long-context split, RoPE + sliding window + sink,
 # fp8 KV with per-KV-head scales); every value is synthetic.
-def tiny_fp32(seed=1001):
+def tiny_fp32(seed=1001, lens=None):
     return make_workload(name="tiny_fp32", B=4, H_qo=4, H_kv=4, D=64, page_size=16,
-                         seq_lens=[1, 17, 33, 50], max_num_pages=16, q_dtype="f32",
+                         seq_lens=[1, 17, 33, 50] if lens is None else lens, max_num_pages=16,
+                         q_dtype="f32",
                          kv_dtype="f32", seed=seed, sm_scale=1.0 / 8.0)
 
 
@@ -197,9 +203,10 @@ def llama3_8b_bf16(seed=1002, B=32, lens=None):
                          page_size=16, seq_lens=lens, max_num_pages=16384, seed=seed)
 
 
-def long_ctx_bf16(seed=1003):
+def long_ctx_bf16(seed=1003, lens=None):
     return make_workload(name="long_ctx_split_bf16", B=2, H_qo=32, H_kv=8, D=128, page_size=16,
-                         seq_lens=[32768, 131072], max_num_pages=16384, seed=seed)
+                         seq_lens=[32768, 131072] if lens is None else lens,
+                         max_num_pages=16384, seed=seed)
 
 
 def rope_swa_bf16(seed=1004, B=64, lens=None):

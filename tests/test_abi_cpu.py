@@ -105,10 +105,19 @@ def test_plan_and_workspace(L):
     assert nc == 5 and cp * 5 >= 4096 // 16
     ws = pk.workspace_bytes(d)
     assert ws >= 4 * 32 * 5 * (128 + 1) * 4 and ws % 256 == 0
-    # automatic plan: chunks of at least 256 rows; long contexts split, tiny ones do not
+    # automatic plan: chunks of at least 256 rows, sized so the grid has about 2048 workgroups
     cp, nc = pk.plan(desc(batch=2, max_kv_len=131072))
+    assert nc > 1 and cp * 16 >= 256 and cp * nc * 16 >= 131072
+    cp, nc = pk.plan(desc(batch=1, num_qo_heads=4, num_kv_heads=1, max_kv_len=64))
+    assert nc == 1
+    cp, nc = pk.plan(desc())
+    ws = pk.workspace_bytes(desc())
+    assert ws >= 4 * 32 * nc * (128 + 1) * 4 + 4 * 8 * 4 and ws % 256 == 0
+    # fp32 / fp8 KV: chunks of at least 256 rows; long contexts split, tiny ones do not
+    cp, nc = pk.plan(desc(q_dtype="f32", kv_dtype="f32", batch=2, max_kv_len=131072))
     assert nc > 1 and cp * 16 >= 256
-    assert pk.plan(desc(batch=4, num_qo_heads=4, num_kv_heads=4, head_dim=64, max_kv_len=50))[1] == 1
+    assert pk.plan(desc(q_dtype="f32", kv_dtype="f32", batch=4, num_qo_heads=4, num_kv_heads=4,
+                        head_dim=64, max_kv_len=50))[1] == 1
     assert pk.workspace_bytes(desc(head_dim=96)) == 0
 
 

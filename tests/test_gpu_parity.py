@@ -291,9 +291,11 @@ def test_append_fp8_rounding_exhaustive():
     # The public supported set pairs fp8 KV with bf16 q; fp32 input is used here only to feed
     # exact fp32 values to the quantiser.
     tpool = torch.from_numpy(pool).cuda()
+    # keep every device tensor referenced until the asynchronous kernel has run
+    tx = torch.from_numpy(x).cuda()
+    tslots = torch.from_numpy(slots).cuda()
     st = pk.lib().pdecode_append_kv(
-        __import__("ctypes").byref(desc), pk._ptr(torch.from_numpy(x).cuda()),
-        pk._ptr(torch.from_numpy(x).cuda()), pk._ptr(torch.from_numpy(slots).cuda()), T,
+        __import__("ctypes").byref(desc), pk._ptr(tx), pk._ptr(tx), pk._ptr(tslots), T,
         pk._ptr(tpool), pk._stream(None))
     if st == 2:
         pytest.skip("fp32 -> fp8 append outside the supported set")
@@ -374,3 +376,51 @@ def test_full_size_config_sampled(name, n):
         torch.cuda.synchronize()
         assert np.abs(gu.to_np64(out) - gu.to_np64(o1)).max() <= 2e-2
         assert np.abs(gu.to_np64(lse) - gu.to_np64(l1)).max() <= 1e-3
+
+
+def test_fp8_decode_all_codes():
+    """Every finite e4m3fn code, read through decode with one attended row and v_scale = 1: the
+    bf16 output equals the code's value exactly (all e4m3fn values are bf16 values)."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    D, ps = 128, 32
+    B = (codes.size + D - 1) // D
+    w = synth.make_workload(name="fp8_codes", B=B, H_qo=1, H_kv=1, D=D, page_size=ps,
+                            seq_lens=[1] * B, q_dtype="bf16", kv_dtype="fp8", seed=5,
+                            max_num_pages=B)
+    vals = np.zeros(B * D, np.uint8)
+    vals[:codes.size] = codes
+    w.k_scale[:] = 1.0
+    w.v_scale[:] = 1.0
+    for b in range(B):
+        page = w.page_values[w.page_indptr[b]]
+        w.pages[page, 1, 0, 0, :] = vals[b * D:(b + 1) * D]
+    dev = gu.upload(w)
+    out, lse = gu.run_attention(w, dev)
+    torch.cuda.synchronize()
+    got = gu.to_np64(out).reshape(-1)[:codes.size]
+    expect = np.array([oracle.fp8_value(int(c)) for c in codes])
+    assert np.array_equal(got, expect)
+
+
+def test_many_short_sequences():
+    """Many short (and empty) sequences in one call."""
+    lens = np.random.default_rng(17).integers(0, 60, size=300)
+    w = synth.make_workload(name="many_short", B=300, H_qo=16, H_kv=4, D=128, page_size=16,
+                            seq_lens=lens, seed=18, max_num_pages=1400)
+    run_and_check(w)
+
+
+def test_single_long_sequence():
+    """One long sequence: each (sequence, KV head) is split into many chunks."""
+    w = synth.make_workload(name="one_long", B=1, H_qo=8, H_kv=2, D=128, page_size=16,
+                            seq_lens=[50000], seed=19, max_num_pages=3200)
+    run_and_check(w)
+
+
+@pytest.mark.parametrize("D,ps", [(64, 16), (64, 32), (128, 32)])
+def test_shapes_with_small_hint(D, ps):
+    lens = [1, 2, 600, 33, 0, 1000, 17]
+    w = synth.make_workload(name=f"bal_D{D}_ps{ps}", B=7, H_qo=16, H_kv=2, D=D, page_size=ps,
+                            seq_lens=lens, seed=20 + D + ps, max_num_pages=128)
+    run_and_check(w)
+    run_and_check(w, max_kv_len=50)
