@@ -179,11 +179,11 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
   p.num_chunks = pl.num_chunks;
   const int gp = p.G <= 1 ? 1 : p.G <= 2 ? 2 : p.G <= 4 ? 4 : 8;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // bf16 KV without RoPE: q.K on the matrix cores (one 4-wave workgroup per chunk); otherwise
-  // the vector-ALU kernel (one wave per chunk; RoPE rotates K in fp32).
-  if (d->kv_dtype == PDECODE_BF16 && !rotary)
-    st = hip_status(pdk::launch_decode_mfma_bf16(p, d->head_dim, d->page_size, gp,
-                                                 static_cast<unsigned>(grid), s));
+  // bf16 / fp8 KV without RoPE: q.K on the matrix cores (one 4-wave workgroup per chunk);
+  // otherwise the vector-ALU kernel (one wave per chunk; RoPE rotates K in fp32).
+  if ((d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN) && !rotary)
+    st = hip_status(pdk::launch_decode_mfma(p, d->kv_dtype, d->head_dim, d->page_size, gp,
+                                            static_cast<unsigned>(grid), s));
   else
     st = hip_status(pdk::launch_decode_valu(p, d->kv_dtype, d->head_dim, d->page_size, gp,
                                             static_cast<unsigned>(grid), s));
