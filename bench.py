@@ -14,8 +14,10 @@ pdecode_attention duration from HIP events on the launch stream; `cpu_baseline` 
 on the host on a bounded sample of the same workload.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -41,7 +43,57 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_bf16",
                     choices=["llama3_8b_bf16", "long_ctx_bf16", "rope_swa_bf16", "fp8_gqa8",
                              "tiny_fp32"])
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the decode, run a plain 512 MiB device-to-device copy "
+                         "(the reference point for the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+# Sources of the decode kernels: the HBM-traffic figure recorded under profiles/ is used only while
+# their hash matches the one it was measured with.
+KERNEL_SOURCES = ["paged_kv_decode_08_amd/csrc/decode_mfma.hip",
+                  "paged_kv_decode_08_amd/csrc/decode_valu.hip",
+                  "paged_kv_decode_08_amd/csrc/device.hpp",
+                  "paged_kv_decode_08_amd/csrc/split.hpp",
+                  "paged_kv_decode_08_amd/csrc/api.cpp"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE summary under profiles/ for this
+    workload, or None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not sha or not val or sha.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def copy_calibration(steps):
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": steps,
+                      "GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
 def main():
@@ -51,6 +103,9 @@ def main():
               "the multi-GPU sharding of this path is a design note, not an implementation.",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(max(args.steps, 1))
+        return
     import numpy as np
     import torch
 
@@ -133,7 +188,10 @@ def main():
                    "chunk_pages": cp, "num_chunks": nc},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "pdecode_attention (decode + split merge)",
+                     "traffic": recorded_traffic(args.workload),
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                     "algorithmic_bytes": kv_bytes,
+                     "kernel": "pdecode_attention (decode + split merge)",
                      "avg_launch_us": round(avg_call_s * 1e6, 3),
                      "p10_us": round(float(np.percentile(call_ms, 10)) * 1e3, 3),
                      "p90_us": round(float(np.percentile(call_ms, 90)) * 1e3, 3)},
