@@ -14,8 +14,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["decode_mfma.hip", "decode_valu.hip", "merge.hip", "append.hip",
            "api.cpp"]
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
+# atomic optimizer off: the job-queue ticket is fetched by one lane and consumed a whole job later;
+# the wave-aggregated form would wait for its result at once.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 

@@ -13,6 +13,7 @@ namespace {
 
 constexpr int kTargetWorkgroups = 2048;  // about 8 wavefront-workgroups per CU on 256 CUs
 constexpr int kMinChunkRows = 256;
+constexpr int kPersistMaxBatch = 1024;  // the persistent schedule keeps a per-sequence table in LDS
 
 struct Plan {
   int32_t chunk_slots = 1;
@@ -20,6 +21,7 @@ struct Plan {
   size_t part_o_bytes = 0;
   size_t part_lse_bytes = 0;
   size_t counter_bytes = 0;
+  bool persistent = false;  // matrix-core kernel on the persistent schedule (when no RoPE)
   size_t workspace_bytes() const { return part_o_bytes + part_lse_bytes + counter_bytes; }
 };
 
@@ -79,12 +81,16 @@ Plan make_plan(const pdecode_desc* d) {
   if (n > INT_MAX / 2) n = INT_MAX / 2;
   pl.chunk_slots = static_cast<int32_t>(chunk > INT_MAX ? INT_MAX : chunk);
   pl.num_chunks = static_cast<int32_t>(n);
+  pl.persistent = (d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN) &&
+                  d->batch <= kPersistMaxBatch;
   if (pl.num_chunks > 1) {
     const size_t rows = size_t(d->batch) * d->num_qo_heads * pl.num_chunks;
     pl.part_o_bytes = align256(rows * d->head_dim * sizeof(float));
     pl.part_lse_bytes = align256(rows * sizeof(float));
-    pl.counter_bytes = align256(size_t(d->batch) * d->num_kv_heads * sizeof(int32_t));
   }
+  // split arrival counters [B * H_kv], then the two job-queue counters of the persistent schedule
+  if (pl.num_chunks > 1 || pl.persistent)
+    pl.counter_bytes = align256((size_t(d->batch) * d->num_kv_heads + 2) * sizeof(int32_t));
   return pl;
 }
 
@@ -165,6 +171,7 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
   p.counters = ws ? reinterpret_cast<int*>(static_cast<char*>(workspace) + pl.part_o_bytes +
                                            pl.part_lse_bytes)
                   : nullptr;
+  p.queue = ws ? p.counters + size_t(d->batch) * d->num_kv_heads : nullptr;
   p.B = d->batch;
   p.H_qo = d->num_qo_heads;
   p.H_kv = d->num_kv_heads;
@@ -179,11 +186,12 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
   p.num_chunks = pl.num_chunks;
   const int gp = p.G <= 1 ? 1 : p.G <= 2 ? 2 : p.G <= 4 ? 4 : 8;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // bf16 / fp8 KV without RoPE: q.K on the matrix cores (one 4-wave workgroup per chunk);
-  // otherwise the vector-ALU kernel (one wave per chunk; RoPE rotates K in fp32).
+  // bf16 / fp8 KV without RoPE: q.K on the matrix cores (4-wave workgroups, persistent over a job
+  // queue up to kPersistMaxBatch sequences, else one per chunk); otherwise the vector-ALU kernel
+  // (one wave per chunk; RoPE rotates K in fp32).
   if ((d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN) && !rotary)
     st = hip_status(pdk::launch_decode_mfma(p, d->kv_dtype, d->head_dim, d->page_size, gp,
-                                            static_cast<unsigned>(grid), s));
+                                            pl.persistent, grid, s));
   else
     st = hip_status(pdk::launch_decode_valu(p, d->kv_dtype, d->head_dim, d->page_size, gp,
                                             static_cast<unsigned>(grid), s));

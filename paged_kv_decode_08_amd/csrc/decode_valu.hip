@@ -67,8 +67,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     return;
   }
   if (c >= nch) return;
-  const int s_begin = c * p.chunk_slots;
-  const int s_end = (c == nch - 1) ? sg.n_slots : s_begin + p.chunk_slots;
+  int s_begin, s_end;
+  chunk_bounds(sg.n_slots, nch, c, s_begin, s_end);
 
   // ---- q (fp32, pre-scaled to log2 units; fp8 folds k_scale in), optionally rotated.
   const float kscale = (KVT == kFP8) ? p.k_scale[h] : 1.0f;

@@ -28,6 +28,8 @@ struct DecodeParams {
   float* part_o;             // split-KV partial outputs [B, H_qo, num_chunks, D] (normalised)
   float* part_lse;           // split-KV partial lse [B, H_qo, num_chunks]
   int* counters;             // split-KV arrival counters [B, H_kv]; zero between calls
+  int* queue;                // persistent schedule: [0] next job ticket, [1] workgroups done;
+                             // zero between calls
   int32_t B, H_qo, H_kv, G;
   int32_t max_num_pages;     // page ids are clamped into the pool before any KV address is formed
   int32_t sliding, rotary;
@@ -168,6 +170,14 @@ __device__ __forceinline__ int chunks_used(int n_slots, int chunk_slots, int num
   if (n_slots <= 0) return 0;
   int n = (n_slots + chunk_slots - 1) / chunk_slots;
   return n < num_chunks ? n : num_chunks;
+}
+
+// Slots [begin, end) of chunk c when a sequence's n_slots are split evenly over nch chunks
+// (sizes differ by at most one slot; none exceeds chunk_slots unless the sequence is longer than
+// chunk_slots * num_chunks).
+__device__ __forceinline__ void chunk_bounds(int n_slots, int nch, int c, int& begin, int& end) {
+  begin = static_cast<int>((int64_t(c) * n_slots) / nch);
+  end = static_cast<int>((int64_t(c + 1) * n_slots) / nch);
 }
 
 }  // namespace pdk

@@ -9,8 +9,10 @@ namespace pdk {
 
 hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, int D, int PS, int gp,
                               unsigned grid, hipStream_t st);
+// persistent: grid = the jobs upper bound (units x num_chunks), capped at the workgroups that fit
+// on the device; otherwise one workgroup per (chunk, unit) and grid is that count.
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int D, int PS, int gp,
-                              unsigned grid, hipStream_t st);
+                              bool persistent, long long grid, hipStream_t st);
 hipError_t launch_merge_state(const MergeParams& p, int v_dtype, hipStream_t st);
 hipError_t launch_append(const AppendParams& p, int in_dtype, int kv_dtype, hipStream_t st);
 

@@ -85,7 +85,7 @@ def test_attention_workspace_checks(L):
 
 
 def test_rope_checks(L):
-    d = desc(num_kv_splits=1)
+    d = desc(num_kv_splits=1, q_dtype="f32", kv_dtype="f32")
     assert pk.workspace_bytes(d) == 0
     r = pk.Rope(1, 1.0, 5e5, None, None)
     assert attention_status(L, d, rope=r) == 1
@@ -98,8 +98,12 @@ def test_batch_zero_is_a_noop(L):
 
 
 def test_plan_and_workspace(L):
-    d = desc(num_kv_splits=1)
+    # unsplit fp32: no workspace; unsplit bf16 / fp8: the persistent schedule's job-queue counters
+    d = desc(num_kv_splits=1, q_dtype="f32", kv_dtype="f32")
     assert pk.plan(d)[1] == 1 and pk.workspace_bytes(d) == 0
+    d = desc(num_kv_splits=1)
+    assert pk.plan(d)[1] == 1 and pk.workspace_bytes(d) == 256
+    assert pk.workspace_bytes(desc(num_kv_splits=1, batch=2000)) == 0  # above the persistent limit
     d = desc(num_kv_splits=5)
     cp, nc = pk.plan(d)
     assert nc == 5 and cp * 5 >= 4096 // 16
