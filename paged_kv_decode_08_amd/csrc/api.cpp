@@ -11,7 +11,8 @@
 
 namespace {
 
-constexpr int kTargetWorkgroups = 2048;  // about 8 wavefront-workgroups per CU on 256 CUs
+constexpr int kTargetWorkgroups = 2048;  // one-wave workgroups of the vector-ALU kernel
+constexpr int kTargetJobs = 1024;         // jobs of the persistent matrix-core schedule
 constexpr int kMinChunkRows = 256;
 constexpr int kPersistMaxBatch = 1024;  // the persistent schedule keeps a per-sequence table in LDS
 
@@ -65,6 +66,8 @@ Plan make_plan(const pdecode_desc* d) {
   const int64_t max_slots = (max_len + ps - 1) / ps + (d->sliding_window ? 2 : 0);
   const int64_t units = int64_t(d->batch) * d->num_kv_heads;
 
+  const bool persistent = (d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN) &&
+                          d->batch <= kPersistMaxBatch;
   int64_t chunk;
   if (d->num_kv_splits == 1) {
     chunk = max_slots;
@@ -72,7 +75,10 @@ Plan make_plan(const pdecode_desc* d) {
     chunk = (max_slots + d->num_kv_splits - 1) / d->num_kv_splits;
   } else {
     const int64_t min_chunk = (kMinChunkRows + ps - 1) / ps;
-    chunk = (units * max_slots + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    // about two jobs per resident workgroup of the persistent schedule (long jobs amortise the
+    // job switch and need fewer split merges; the queue hands out the longest first)
+    const int64_t target = persistent ? kTargetJobs : kTargetWorkgroups;
+    chunk = (units * max_slots + target - 1) / target;
     if (chunk < min_chunk) chunk = min_chunk;
   }
   if (chunk < 1) chunk = 1;
@@ -81,8 +87,7 @@ Plan make_plan(const pdecode_desc* d) {
   if (n > INT_MAX / 2) n = INT_MAX / 2;
   pl.chunk_slots = static_cast<int32_t>(chunk > INT_MAX ? INT_MAX : chunk);
   pl.num_chunks = static_cast<int32_t>(n);
-  pl.persistent = (d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN) &&
-                  d->batch <= kPersistMaxBatch;
+  pl.persistent = persistent;
   if (pl.num_chunks > 1) {
     const size_t rows = size_t(d->batch) * d->num_qo_heads * pl.num_chunks;
     pl.part_o_bytes = align256(rows * d->head_dim * sizeof(float));

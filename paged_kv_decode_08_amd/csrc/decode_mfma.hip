@@ -154,22 +154,32 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeParams p
 // ------------------------------------------------------------------------------------------------
 // Persistent workgroups over a job queue.
 
-// Per-sequence table in LDS: first job of each sequence (exclusive prefix over sequences of
-// chunks x KV heads; jobs of one sequence are ordered chunk-major, KV head minor) and geometry.
+// Per-sequence table in LDS. Sequences are ranked by the size of their chunks, largest first (four
+// size classes, stable within a class), and jobs are numbered in that order: the queue hands out
+// long jobs first and ends with short ones, which shortens the tail of the call. Jobs of one
+// sequence are ordered chunk-major, KV head minor.
 struct SeqTable {
-  int* pre;    // [B + 1]
-  int4* geo;   // [B]: beg, np, total, win_off
-  int* sink;   // [B]
+  int* pre;     // [B + 1]: first job of the sequence of each rank (exclusive prefix)
+  int* seq;     // [B]: sequence of each rank
+  int* njobs;   // [B]: jobs of each sequence
+  int4* geo;    // [B]: beg, np, total, win_off
+  int* sink;    // [B]
 };
 
 __host__ __device__ inline size_t seq_table_bytes(int B) {
-  return size_t((B + 4) & ~3) * 4 + size_t(B) * 16 + size_t(B) * 4;
+  const size_t pre = size_t((B + 4) & ~3);
+  const size_t rest = size_t((B + 3) & ~3);
+  return (pre + 2 * rest) * 4 + size_t(B) * 16 + rest * 4;
 }
 
 __device__ inline SeqTable seq_table(int* base, int B) {
+  const int pre = (B + 4) & ~3;
+  const int rest = (B + 3) & ~3;
   SeqTable t;
   t.pre = base;
-  t.geo = reinterpret_cast<int4*>(base + ((B + 4) & ~3));
+  t.seq = base + pre;
+  t.njobs = t.seq + rest;
+  t.geo = reinterpret_cast<int4*>(t.njobs + rest);
   t.sink = reinterpret_cast<int*>(t.geo + B);
   return t;
 }
@@ -209,7 +219,8 @@ __device__ __forceinline__ Job decode_job(const DecodeParams& p, const SeqTable&
     const int c = lo + s;
     if (c < p.B && t.pre[c] <= j) lo = c;
   }
-  const int b = uni(lo);
+  const int rank = uni(lo);
+  const int b = uni(t.seq[rank]);
   const int4 gg = t.geo[b];
   SeqGeom g;
   g.beg = uni(gg.x);
@@ -220,9 +231,9 @@ __device__ __forceinline__ Job decode_job(const DecodeParams& p, const SeqTable&
   g.n0 = (g.sink + PS - 1) / PS;
   g.first1 = g.win_off / PS;
   g.n_slots = g.n0 + (g.win_off < g.total ? g.np - g.first1 : 0);
-  const int p0 = uni(t.pre[b]);
+  const int p0 = uni(t.pre[rank]);
   const int r = j - p0;
-  J.nch = (uni(t.pre[b + 1]) - p0) / p.H_kv;
+  J.nch = (uni(t.pre[rank + 1]) - p0) / p.H_kv;
   J.c = r / p.H_kv;
   J.h = r - J.c * p.H_kv;
   J.b = b;
@@ -266,6 +277,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_persist_kernel(Decode
   __shared__ __attribute__((aligned(16))) uint32_t s_q[2][QW * NT];
   __shared__ int s_ids[2][kWaves][64];  // page-table entries of each wave's first 64 items
   __shared__ int s_scan[kWaves];
+  __shared__ unsigned long long s_scan64[kWaves];
   __shared__ int s_ticket;
 
   const int tid = threadIdx.x;
@@ -276,30 +288,79 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_persist_kernel(Decode
   C core;
   core.init_lane(l);
 
-  // ---- job table: jobs of sequence b = chunks(b) x H_kv, exclusive prefix over b
+  // ---- job table: sequences ranked by chunk size (largest first), exclusive prefix of their
+  // jobs (chunks x H_kv) in rank order
   const SeqTable tab = seq_table(s_dyn, B);
   {
     const int per = (B + NT - 1) / NT;
     const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
-    int run = 0;
+    // size class of a sequence: 0 for chunks above 7/8 of chunk_slots, .. 3 for 5/8 and below
+    auto size_class = [&](int n_slots, int nch) {
+      const int sz = nch > 0 ? (n_slots + nch - 1) / nch : 0;
+      return 8 * sz > 7 * p.chunk_slots ? 0 : 8 * sz > 6 * p.chunk_slots ? 1
+             : 8 * sz > 5 * p.chunk_slots ? 2 : 3;
+    };
+    unsigned long long cnt = 0;  // this thread's sequences per class, 16 bits each
     for (int b = b0; b < b1; ++b) {
       const SeqGeom g = seq_geom(p.indptr, p.length_info, B, b, PS, p.sliding);
       tab.geo[b] = make_int4(g.beg, g.np, g.total, g.win_off);
       tab.sink[b] = g.sink;
-      run += chunks_used(g.n_slots, p.chunk_slots, p.num_chunks) * p.H_kv;
-      tab.pre[b + 1] = run;
+      const int nch = chunks_used(g.n_slots, p.chunk_slots, p.num_chunks);
+      tab.njobs[b] = nch * p.H_kv;
+      cnt += 1ull << (16 * size_class(g.n_slots, nch));
     }
-    int x = run;  // inclusive scan over the wave
+    // exclusive scan of the packed class counts over the workgroup
+    unsigned long long x = cnt;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o, 64);
+      const unsigned long long y = __shfl_up(x, o, 64);
       if (l >= o) x += y;
     }
-    if (l == 63) s_scan[w] = x;
+    if (l == 63) s_scan64[w] = x;
     __syncthreads();
-    int off = x - run;
-    for (int ww = 0; ww < w; ++ww) off += s_scan[ww];
-    for (int b = b0; b < b1; ++b) tab.pre[b + 1] += off;
+    unsigned long long off = x - cnt, total = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      if (ww < w) off += s_scan64[ww];
+      total += s_scan64[ww];
+    }
+    int cls_start[4];
+    int acc = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      cls_start[c] = acc + int((off >> (16 * c)) & 0xffff);
+      acc += int((total >> (16 * c)) & 0xffff);
+    }
+    for (int b = b0; b < b1; ++b) {
+      const int4 gg = tab.geo[b];
+      SeqGeom g;
+      g.np = gg.y;
+      g.total = gg.z;
+      g.win_off = gg.w;
+      g.sink = tab.sink[b];
+      const int n0 = (g.sink + PS - 1) / PS;
+      const int n_slots = g.np > 0 ? n0 + (g.win_off < g.total ? g.np - g.win_off / PS : 0) : 0;
+      const int c = size_class(n_slots, tab.njobs[b] / p.H_kv);
+      tab.seq[cls_start[c]++] = b;
+    }
+    __syncthreads();
+    // prefix of the jobs in rank order
+    int run = 0;
+    for (int r = b0; r < b1; ++r) {
+      run += tab.njobs[tab.seq[r]];
+      tab.pre[r + 1] = run;
+    }
+    int y = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int z = __shfl_up(y, o, 64);
+      if (l >= o) y += z;
+    }
+    if (l == 63) s_scan[w] = y;
+    __syncthreads();
+    int off2 = y - run;
+    for (int ww = 0; ww < w; ++ww) off2 += s_scan[ww];
+    for (int r = b0; r < b1; ++r) tab.pre[r + 1] += off2;
     if (tid == 0) tab.pre[0] = 0;
     __syncthreads();
   }
@@ -307,7 +368,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_persist_kernel(Decode
 
   // ---- sequences without attended rows: out = 0, lse = -5e4
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
-    if (tab.pre[b + 1] != tab.pre[b]) continue;
+    if (tab.njobs[b] != 0) continue;
     for (int idx = tid; idx < p.H_qo * D; idx += NT)
       store_out<kBF16>(p.out, size_t(b) * p.H_qo * D + idx, 0.f);
     for (int hq = tid; hq < p.H_qo; hq += NT) p.lse[size_t(b) * p.H_qo + hq] = kEmptyLse;

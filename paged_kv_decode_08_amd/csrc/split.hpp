@@ -21,26 +21,14 @@ __device__ __forceinline__ float load_agent(const float* ptr) {
   return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Merges the nch chunk states of (sequence b, KV head h), all stored and complete, into out and lse.
+// Every thread of the workgroup takes part.
 template <int QT, int D, int GP, int NT>
-__device__ void split_finish(const DecodeParams& p, int b, int h, int nch) {
-  __shared__ int s_last;
+__device__ void merge_chunks(const DecodeParams& p, int b, int h, int nch) {
   __shared__ float s_mx[GP];
   __shared__ float s_w[GP][64];
   const int tid = threadIdx.x;
   const int G = p.G;
-  // The partial states were stored as agent-scope atomics (coherent across the XCDs' L2s without
-  // cache write-back). Drain them, then take the ticket.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0) {
-    int* cnt = &p.counters[b * p.H_kv + h];
-    const int ticket = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = ticket == nch - 1;
-    if (ticket == nch - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (!s_last) return;
-
   const size_t row0 = (size_t(b) * p.H_qo + h * G) * p.num_chunks;  // head g: row0 + g * num_chunks
   // per-head maximum of the chunk lse values
   for (int g = tid / 64; g < G; g += NT / 64) {
@@ -90,6 +78,25 @@ __device__ void split_finish(const DecodeParams& p, int b, int h, int nch) {
     store_out<QT>(p.out, (size_t(b) * p.H_qo + hq) * D + d, acc[k] / wsum[k]);
     if (d == 0) p.lse[size_t(b) * p.H_qo + hq] = s_mx[g] + log2f(wsum[k]);
   }
+}
+
+template <int QT, int D, int GP, int NT>
+__device__ void split_finish(const DecodeParams& p, int b, int h, int nch) {
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  // The partial states were stored as agent-scope atomics (coherent across the XCDs' L2s without
+  // cache write-back). Drain them, then take the ticket.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    int* cnt = &p.counters[b * p.H_kv + h];
+    const int ticket = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = ticket == nch - 1;
+    if (ticket == nch - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  merge_chunks<QT, D, GP, NT>(p, b, h, nch);
 }
 
 }  // namespace pdk
