@@ -59,7 +59,8 @@ pdecode_status check_attention_shape(const pdecode_desc* d) {
 // Chunking of each sequence's page slots. A sequence with n slots uses ceil(n / chunk_slots)
 // chunks, capped at num_chunks (the last chunk then takes every remaining slot), so any length
 // is computed exactly; max_kv_len only sizes the grid.
-Plan make_plan(const pdecode_desc* d) {
+// rope: the call applies RoPE (vector-ALU kernel; smaller chunks, one wave each).
+Plan make_plan(const pdecode_desc* d, bool rope) {
   Plan pl;
   const int64_t ps = d->page_size;
   const int64_t max_len = d->max_kv_len > 0 ? d->max_kv_len : int64_t(d->max_num_pages) * ps;
@@ -67,7 +68,7 @@ Plan make_plan(const pdecode_desc* d) {
   const int64_t units = int64_t(d->batch) * d->num_kv_heads;
 
   const bool persistent = (d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN) &&
-                          d->batch <= kPersistMaxBatch;
+                          d->batch <= kPersistMaxBatch && !rope;
   int64_t chunk;
   if (d->num_kv_splits == 1) {
     chunk = max_slots;
@@ -118,7 +119,9 @@ const char* pdecode_status_string(pdecode_status s) {
 
 size_t pdecode_workspace_bytes(const pdecode_desc* d) {
   if (check_desc(d) != PDECODE_OK || check_attention_shape(d) != PDECODE_OK) return 0;
-  return make_plan(d).workspace_bytes();
+  // enough for calls with and without RoPE
+  const size_t a = make_plan(d, false).workspace_bytes(), b = make_plan(d, true).workspace_bytes();
+  return a > b ? a : b;
 }
 
 pdecode_status pdecode_plan(const pdecode_desc* d, int32_t* chunk_pages, int32_t* num_chunks) {
@@ -126,7 +129,7 @@ pdecode_status pdecode_plan(const pdecode_desc* d, int32_t* chunk_pages, int32_t
   if (st != PDECODE_OK) return st;
   if ((st = check_attention_shape(d)) != PDECODE_OK) return st;
   if (!chunk_pages || !num_chunks) return PDECODE_ERR_INVALID_ARG;
-  const Plan pl = make_plan(d);
+  const Plan pl = make_plan(d, false);
   *chunk_pages = pl.chunk_slots;
   *num_chunks = pl.num_chunks;
   return PDECODE_OK;
@@ -149,7 +152,7 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
   if (d->batch == 0) return PDECODE_OK;
   if (!q || !pages || !page_indptr || !page_values || !length_info || !out || !lse)
     return PDECODE_ERR_INVALID_ARG;
-  const Plan pl = make_plan(d);
+  const Plan pl = make_plan(d, rotary);
   const int64_t grid = int64_t(pl.num_chunks) * d->batch * d->num_kv_heads;
   if (grid > INT_MAX) return PDECODE_ERR_UNSUPPORTED;
   if (pl.workspace_bytes() > 0) {

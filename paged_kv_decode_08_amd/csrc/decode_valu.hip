@@ -25,6 +25,8 @@ namespace pdk {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+constexpr int kRopeAnchor = 8;  // page slots between exact RoPE angles (the rest by recurrence)
+
 // cos and sin of 2*pi*frac(pos * f) with f = fhi + flo (f = rope_scale * freq / 2pi).
 __device__ __forceinline__ void rope_cs(int pos, float fhi, float flo, float& c, float& s) {
   const float pf = static_cast<float>(pos);
@@ -77,6 +79,10 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   const int d0 = cv * EPV;                       // first dim this lane holds
   const bool lower = d0 < D / 2;
   float fhi[EPV], flo[EPV];                      // RoPE frequencies / 2pi of the lane's dims
+  // RoPE angle of the lane's current K row (cos, sin per dim), advanced row by row by the
+  // rotation of RPI positions (stc, sts); re-anchored exactly every kRopeAnchor slots and where
+  // the compacted positions jump (first window slot after the sink pages)
+  float rc[EPV] = {}, rsn[EPV] = {}, stc[EPV] = {}, sts[EPV] = {};
   float qo[GP][EPV];
 #pragma unroll
   for (int g = 0; g < GP; ++g) {
@@ -96,6 +102,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
                        (2.0 * 3.14159265358979323846);
       fhi[e] = static_cast<float>(f);
       flo[e] = static_cast<float>(f - static_cast<double>(fhi[e]));
+      rope_cs(RPI, fhi[e], flo[e], stc[e], sts[e]);
       float cs, sn;
       rope_cs(qpos, fhi[e], flo[e], cs, sn);
 #pragma unroll
@@ -168,21 +175,26 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     }
 
     // ---- scores
+    if (rotary && (s == s_begin || s == sg.n0 || (s - s_begin) % kRopeAnchor == 0)) {
+      const int pos0 = kro + j * PS + rg + roff;  // the lane's first row in this page
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) rope_cs(pos0, fhi[e], flo[e], rc[e], rsn[e]);
+    }
     float sc[NI][GP];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float kf[EPV];
       KV::unpack(kc[i], kf);
       if (rotary) {
-        const int pos = kro + j * PS + i * RPI + rg + roff;
         float kp[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) kp[e] = shfl_xor_f(kf[e], VPR / 2);
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          float cs, sn2;
-          rope_cs(pos, fhi[e], flo[e], cs, sn2);
-          kf[e] = lower ? kf[e] * cs - kp[e] * sn2 : kf[e] * cs + kp[e] * sn2;
+          kf[e] = lower ? kf[e] * rc[e] - kp[e] * rsn[e] : kf[e] * rc[e] + kp[e] * rsn[e];
+          const float c2 = rc[e] * stc[e] - rsn[e] * sts[e];  // next row: RPI positions on
+          rsn[e] = rsn[e] * stc[e] + rc[e] * sts[e];
+          rc[e] = c2;
         }
       }
 #pragma unroll
