@@ -52,6 +52,7 @@ def parse():
 # Sources of the decode kernels: the HBM-traffic figure recorded under profiles/ is used only while
 # their hash matches the one it was measured with.
 KERNEL_SOURCES = ["paged_kv_decode_08_amd/csrc/decode_mfma.hip",
+                  "paged_kv_decode_08_amd/csrc/mfma_core.hpp",
                   "paged_kv_decode_08_amd/csrc/decode_valu.hip",
                   "paged_kv_decode_08_amd/csrc/device.hpp",
                   "paged_kv_decode_08_amd/csrc/split.hpp",
