@@ -76,9 +76,11 @@ Plan make_plan(const pdecode_desc* d, bool rope) {
     chunk = (max_slots + d->num_kv_splits - 1) / d->num_kv_splits;
   } else {
     const int64_t min_chunk = (kMinChunkRows + ps - 1) / ps;
-    // about two jobs per resident workgroup of the persistent schedule (long jobs amortise the
-    // job switch and need fewer split merges; the queue hands out the longest first)
-    const int64_t target = persistent ? kTargetJobs : kTargetWorkgroups;
+    // about two jobs per resident workgroup of the persistent schedule, and at least two per
+    // (sequence, KV head) (long jobs amortise the job switch and need fewer split merges; the
+    // queue hands out the longest first)
+    const int64_t target =
+        persistent ? (kTargetJobs > 2 * units ? kTargetJobs : 2 * units) : kTargetWorkgroups;
     chunk = (units * max_slots + target - 1) / target;
     if (chunk < min_chunk) chunk = min_chunk;
   }

@@ -191,7 +191,7 @@ struct Job {
   SeqGeom g;
   int s_w;      // this wave's first slot
   int nw;       // slots of this wave (may be 0)
-  int nitems;   // nw rounded up to even, at least 2: items past nw are unused (cache re-reads)
+  int nitems;   // nw * SUB rounded up to even, at least 2: items past that are unused (re-reads)
   int s_first;  // first slot of the chunk (its page serves the item of a wave without slots)
 };
 
@@ -201,7 +201,8 @@ __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlan
 // outstanding, and not for the export or LDS/scalar counters.
 constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) & 3) << 14 | 0x7 << 4 | 0xf << 8; }
 
-template <int PS>
+// SUB: items per page slot (a 32-row page is walked as two 16-row items).
+template <int PS, int SUB>
 __device__ __forceinline__ Job decode_job(const DecodeParams& p, const SeqTable& t, int total_jobs,
                                           int j, int w) {
   Job J;
@@ -243,7 +244,7 @@ __device__ __forceinline__ Job decode_job(const DecodeParams& p, const SeqTable&
   J.s_first = sb;
   J.s_w = sb + w;
   J.nw = J.s_w < se ? (se - J.s_w + kWaves - 1) / kWaves : 0;
-  J.nitems = max(2, (J.nw + 1) & ~1);
+  J.nitems = max(2, (J.nw * SUB + 1) & ~1);
   return J;
 }
 
@@ -262,7 +263,10 @@ __device__ __forceinline__ int clamp_page(const DecodeParams& p, int id) {
 
 template <int KVT, int D, int PS, int GP>
 __global__ __launch_bounds__(64 * kWaves) void decode_mfma_persist_kernel(DecodeParams p) {
-  using C = MfmaCore<KVT, D, PS, GP>;
+  // items of 16 rows: a 32-row page is two items (half the registers per item in flight)
+  using C = MfmaCore<KVT, D, 16, GP>;
+  constexpr int SUB = PS / 16;
+  constexpr int BLOCK = PS * C::ROW;  // bytes of one (page, K|V, head) block
   using Buf = typename C::Buf;
   constexpr int NT = 64 * kWaves;
   // q of the next job, staged in LDS by all threads: QW 32-bit words per thread
@@ -375,9 +379,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_persist_kernel(Decode
   }
 
   const char* pool = static_cast<const char*>(p.pages);
-  const size_t kv_stride = size_t(p.H_kv) * C::BLOCK;
+  const size_t kv_stride = size_t(p.H_kv) * BLOCK;
   auto block_of = [&](int page, int h) {
-    return pool + (size_t(page) * 2 * p.H_kv + h) * C::BLOCK;
+    return pool + (size_t(page) * 2 * p.H_kv + h) * BLOCK;
   };
   const uint32_t* qsrc = static_cast<const uint32_t*>(p.q);
   // This thread's share of J's q rows (words past the G rows repeat the last one; an invalid job
@@ -394,8 +398,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_persist_kernel(Decode
   // wait for the item covers them); nothing loaded lives across items in registers, which keeps
   // the compiler's memory-wait counts exact in the item loop.
   int* queue = p.queue;
-  Job J = decode_job<PS>(p, tab, total_jobs, blockIdx.x, w);
-  Job J1 = decode_job<PS>(p, tab, total_jobs, blockIdx.x + gridDim.x, w);
+  Job J = decode_job<PS, SUB>(p, tab, total_jobs, blockIdx.x, w);
+  Job J1 = decode_job<PS, SUB>(p, tab, total_jobs, blockIdx.x + gridDim.x, w);
   int par = 0;  // s_q[par] / s_ids[par] hold J's data, [par ^ 1] receive J1's
   {
     uint32_t q0[QW];
@@ -414,28 +418,36 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_persist_kernel(Decode
     Buf buf0, buf1;
     core.issue(buf0, block_of(clamp_page(p, uni(s_ids[0][w][0])), J.h), kv_stride);
 
-    // Page id of item k of the current job (k < nitems; refilled per 64 items from the page table).
+    // Page id of item k of the current job (slot k / SUB of the wave; refilled per 64 slots from
+    // the page table).
     auto item_id = [&](int k) __attribute__((always_inline)) {
-      if ((k & 63) == 0 && k > 0) {  // chunks of more than 64 slots per wave only
-        const int id = load_id(p, J, k + l);
+      const int si = k / SUB;
+      if ((si & 63) == 0 && si > 0 && k % SUB == 0) {  // chunks of more than 64 slots per wave only
+        const int id = load_id(p, J, si + l);
         wave_lds_fence();
         s_ids[par][w][l] = id;
         wave_lds_fence();
       }
-      return s_ids[par][w][k & 63];
+      return s_ids[par][w][si & 63];
     };
-    // Computes item k from `cur` (items past nw are unused), then retires `cur`: only the loads
-    // just issued stay in flight.
+    // Computes item k from `cur` (rows 16 (k % SUB) .. + 16 of slot k / SUB; items past the
+    // wave's slots are unused), then retires `cur`: only the loads just issued stay in flight.
     auto compute = [&](const Buf& cur, int k) __attribute__((always_inline)) {
-      if (k < J.nw) {
+      const int si = k / SUB;
+      if (si < J.nw) {
         int j, lo, hi;
-        slot_rows(J.g, J.s_w + kWaves * k, PS, j, lo, hi);
-        core.process(cur, lo, hi, scale, s_pt[w], s_alpha[w]);
+        slot_rows(J.g, J.s_w + kWaves * si, PS, j, lo, hi);
+        const int r0 = 16 * (k % SUB);
+        lo = max(lo - r0, 0);
+        hi = min(hi - r0, 16);
+        if (lo < hi) core.process(cur, lo, hi, scale, s_pt[w], s_alpha[w]);
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NLOADS));
     };
-    auto issue_id = [&](Buf& nxt, int raw, int hh) __attribute__((always_inline)) {
-      core.issue(nxt, block_of(clamp_page(p, uni(raw)), uni(hh)), kv_stride);
+    // Issues the loads of item `k`'s 16 rows (k % SUB selects the rows in the page).
+    auto issue_id = [&](Buf& nxt, int raw, int hh, int k) __attribute__((always_inline)) {
+      core.issue(nxt, block_of(clamp_page(p, uni(raw)), uni(hh)) + (k % SUB) * 16 * C::ROW,
+                 kv_stride);
     };
 
     // Every job has an even number of items per wave, item k in buf0 for even k, so the next
@@ -452,11 +464,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_persist_kernel(Decode
         q_words(J1, qs);
         int ticket_raw = 0;
         if (last && J1.valid && tid == 0) ticket_raw = atomicAdd(queue, 1);
-        issue_id(buf1, item_id(1), J.h);
+        issue_id(buf1, item_id(1), J.h, 1);
         compute(buf0, 0);
-        if (!last) issue_id(buf0, item_id(2), J.h);
-        else if (J1.valid) issue_id(buf0, __builtin_amdgcn_readlane(ids_n, 0), J1.h);
-        else issue_id(buf0, item_id(1), J.h);
+        if (!last) issue_id(buf0, item_id(2), J.h, 2);
+        else if (J1.valid) issue_id(buf0, __builtin_amdgcn_readlane(ids_n, 0), J1.h, 0);
+        else issue_id(buf0, item_id(1), J.h, 1);
         compute(buf1, 1);
 #pragma unroll
         for (int i = 0; i < QW; ++i) s_q[par ^ 1][tid + i * NT] = qs[i];
@@ -465,9 +477,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_persist_kernel(Decode
       }
       // ---- items 2 .. nitems - 3
       for (int k = 2; k + 2 < J.nitems; k += 2) {
-        issue_id(buf1, item_id(k + 1), J.h);
+        issue_id(buf1, item_id(k + 1), J.h, k + 1);
         compute(buf0, k);
-        issue_id(buf0, item_id(k + 2), J.h);
+        issue_id(buf0, item_id(k + 2), J.h, k + 2);
         compute(buf1, k + 1);
       }
       // ---- the last pair takes the ticket and issues the next job's first item
@@ -475,10 +487,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_persist_kernel(Decode
         const int k = J.nitems - 2;
         int ticket_raw = 0;
         if (J1.valid && tid == 0) ticket_raw = atomicAdd(queue, 1);
-        issue_id(buf1, item_id(k + 1), J.h);
+        issue_id(buf1, item_id(k + 1), J.h, k + 1);
         compute(buf0, k);
-        if (J1.valid) issue_id(buf0, s_ids[par ^ 1][w][0], J1.h);
-        else issue_id(buf0, item_id(k + 1), J.h);
+        if (J1.valid) issue_id(buf0, s_ids[par ^ 1][w][0], J1.h, 0);
+        else issue_id(buf0, item_id(k + 1), J.h, k + 1);
         compute(buf1, k + 1);
         if (tid == 0) s_ticket = 2 * int(gridDim.x) + ticket_raw;
       }
@@ -527,7 +539,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_persist_kernel(Decode
         vscale = p.v_scale[J.h];
       }
       core.reset();
-      J1 = decode_job<PS>(p, tab, total_jobs, next_ticket, w);
+      J1 = decode_job<PS, SUB>(p, tab, total_jobs, next_ticket, w);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
