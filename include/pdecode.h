@@ -99,8 +99,9 @@ typedef struct pdecode_rope {
   const int32_t *k_rope_pos_offset;   /* device int32 [B]: position of attended row 0         */
 } pdecode_rope;
 
-/* Bytes of device workspace pdecode_attention needs for this description (0 when the planned
- * launch does not split any sequence). Depends only on host fields of `d`. Returns 0 for an
+/* Bytes of device workspace pdecode_attention needs for this description: the split partial
+ * states and counters (for the persistent bf16 / fp8 schedule also its job-queue counters), 0 when
+ * the planned launch needs none of them. Depends only on host fields of `d`. Returns 0 for an
  * invalid description. */
 size_t pdecode_workspace_bytes(const pdecode_desc *d);
 
@@ -114,7 +115,8 @@ pdecode_status pdecode_plan(const pdecode_desc *d, int32_t *chunk_pages, int32_t
  * rope: NULL or a host struct. sm_scale: the score scale (typically 1/sqrt(head_dim)).
  * workspace: device memory of at least pdecode_workspace_bytes(d) bytes, 256-byte aligned
  * (may be NULL when that is 0). It holds the split partial states and, at its end, arrival
- * counters of the split (sequence, KV head) pairs: zero-fill it once before its first use; every
+ * counters of the split (sequence, KV head) pairs and the job-queue counters of the persistent
+ * schedule: zero-fill it once before its first use; every
  * call leaves the counters zero again, so it can be reused by later calls (also with other
  * descriptions that fit). Calls that may run at the same time need separate workspaces.
  * out and lse are fully written. Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL (nothing

@@ -148,20 +148,23 @@ struct SeqGeom {
 
 __device__ __forceinline__ SeqGeom seq_geom(const int32_t* indptr, const int32_t* li, int B,
                                             int b, int ps, int sliding) {
+  // every load is issued before any is used (one memory round trip); all are in bounds whatever
+  // the page count
+  const int32_t i0 = indptr[b], i1 = indptr[b + 1];
+  const int32_t last = li[b];
+  const int32_t woff = sliding ? li[B + b] : 0;
+  const int32_t snk = sliding ? li[2 * B + b] : 0;
   SeqGeom g;
-  g.beg = indptr[b];
-  g.np = indptr[b + 1] - g.beg;
-  g.total = g.sink = g.win_off = g.n0 = g.first1 = g.n_slots = 0;
-  if (g.np <= 0) return g;
-  g.total = (g.np - 1) * ps + li[b];
-  if (sliding) {
-    g.win_off = li[B + b];
-    g.sink = li[2 * B + b];
-  }
+  g.beg = i0;
+  g.np = i1 - i0;
+  const bool any = g.np > 0;
+  g.total = any ? (g.np - 1) * ps + last : 0;
+  g.win_off = any ? woff : 0;
+  g.sink = any ? snk : 0;
   g.n0 = (g.sink + ps - 1) / ps;
   g.first1 = g.win_off / ps;
   const int n1 = g.win_off < g.total ? g.np - g.first1 : 0;
-  g.n_slots = g.n0 + n1;
+  g.n_slots = any ? g.n0 + n1 : 0;
   return g;
 }
 
@@ -172,12 +175,16 @@ __device__ __forceinline__ int chunks_used(int n_slots, int chunk_slots, int num
   return n < num_chunks ? n : num_chunks;
 }
 
-// Slots [begin, end) of chunk c when a sequence's n_slots are split evenly over nch chunks
-// (sizes differ by at most one slot; none exceeds chunk_slots unless the sequence is longer than
-// chunk_slots * num_chunks).
+// Slots [begin, end) of chunk c when a sequence's n_slots are split evenly over nch chunks: with
+// q = n_slots / nch and rem = n_slots % nch, the first rem chunks take q + 1 slots, the others q
+// (none exceeds chunk_slots unless the sequence is longer than chunk_slots * num_chunks).
+__device__ __forceinline__ void chunk_bounds_q(int q, int rem, int c, int& begin, int& end) {
+  begin = c * q + (c < rem ? c : rem);
+  end = begin + q + (c < rem ? 1 : 0);
+}
 __device__ __forceinline__ void chunk_bounds(int n_slots, int nch, int c, int& begin, int& end) {
-  begin = static_cast<int>((int64_t(c) * n_slots) / nch);
-  end = static_cast<int>((int64_t(c + 1) * n_slots) / nch);
+  const int q = n_slots / nch;
+  chunk_bounds_q(q, n_slots - q * nch, c, begin, end);
 }
 
 }  // namespace pdk

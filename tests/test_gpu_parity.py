@@ -424,3 +424,18 @@ def test_shapes_with_small_hint(D, ps):
                             seq_lens=lens, seed=20 + D + ps, max_num_pages=128)
     run_and_check(w)
     run_and_check(w, max_kv_len=50)
+
+
+@pytest.mark.parametrize("B", [63, 64, 65, 257, 1024, 1025])
+def test_batch_sizes_around_schedule_limits(B):
+    """Batches at the limits of the persistent schedule's job-table build (one wave up to 64
+    sequences, the whole workgroup above; 1024 is the largest batch the table holds, 1025 takes
+    the one-workgroup-per-chunk grid), with empty, short and split sequences mixed."""
+    rng = np.random.default_rng(300 + B)
+    lens = rng.integers(0, 200, size=B)
+    lens[rng.integers(0, B, size=max(1, B // 16))] = 0
+    lens[rng.integers(0, B, size=max(1, B // 20))] = 1500
+    pages = int(np.sum((lens + 15) // 16)) + 8
+    w = synth.make_workload(name=f"batch{B}", B=B, H_qo=8, H_kv=2, D=128, page_size=16,
+                            seq_lens=lens, seed=400 + B, max_num_pages=pages)
+    run_and_check(w)
