@@ -513,15 +513,21 @@ __global__ __launch_bounds__(64 * kPWaves) void decode_mfma_persist_kernel(Decod
   // the compiler's memory-wait counts exact in the item loop.
   int* queue = p.queue;
   Job J = decode_job<PS, SUB>(p, tab, total_jobs, hinv, blockIdx.x, w, l);
-  Job J1 = decode_job<PS, SUB>(p, tab, total_jobs, hinv, blockIdx.x + gridDim.x, w, l);
   int par = 0;  // s_q[par] / s_ids[par] hold J's data, [par ^ 1] receive J1's
-  {
-    uint32_t q0[QW];
-    q_words(J, q0);
+  // J's page ids and q words are loaded first; J1 is decoded while they are in flight, and each
+  // wave issues J's first item from its own ids before the workgroup meets to stage q.
+  const int ids0 = load_id(p, J, l);
+  uint32_t q0[QW];
+  q_words(J, q0);
+  Job J1 = decode_job<PS, SUB>(p, tab, total_jobs, hinv, blockIdx.x + gridDim.x, w, l);
+  // (unconditional, so both paths reach the barrier with the same loads outstanding: an invalid
+  // job's id is a clamped page-table entry and its head 0, a harmless read)
+  Buf buf0, buf1;
+  core.issue(buf0, block_of(clamp_page(p, uni(__builtin_amdgcn_readlane(ids0, 0))), J.h),
+             kv_stride);
 #pragma unroll
-    for (int i = 0; i < QW; ++i) s_q[0][tid + i * NT] = q0[i];
-    s_ids[0][w][l] = load_id(p, J, l);
-  }
+  for (int i = 0; i < QW; ++i) s_q[0][tid + i * NT] = q0[i];
+  s_ids[0][w][l] = ids0;
   __syncthreads();
 
   if (J.valid) {
@@ -529,8 +535,6 @@ __global__ __launch_bounds__(64 * kPWaves) void decode_mfma_persist_kernel(Decod
     float scale = p.score_scale * (C::FP8 ? p.k_scale[J.h] : 1.0f);
     float vscale = C::FP8 ? p.v_scale[J.h] : 1.0f;
     core.reset();
-    Buf buf0, buf1;
-    core.issue(buf0, block_of(clamp_page(p, uni(s_ids[0][w][0])), J.h), kv_stride);
 
     // Page id of item k of the current job (slot k / SUB of the wave; refilled per 64 slots from
     // the page table).
