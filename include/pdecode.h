@@ -114,11 +114,13 @@ pdecode_status pdecode_plan(const pdecode_desc *d, int32_t *chunk_pages, int32_t
  * q, pages, page_indptr, page_values, length_info, out, lse: device pointers as above.
  * rope: NULL or a host struct. sm_scale: the score scale (typically 1/sqrt(head_dim)).
  * workspace: device memory of at least pdecode_workspace_bytes(d) bytes, 256-byte aligned
- * (may be NULL when that is 0). It holds the split partial states and, at its end, arrival
- * counters of the split (sequence, KV head) pairs and the job-queue counters of the persistent
- * schedule: zero-fill it once before its first use; every
- * call leaves the counters zero again, so it can be reused by later calls (also with other
- * descriptions that fit). Calls that may run at the same time need separate workspaces.
+ * (may be NULL when that is 0). It starts with the arrival counters of the split (sequence, KV
+ * head) pairs and the job-queue counters of the persistent schedule, followed by the split partial
+ * states. Zero-fill it once before its first use; every call leaves the counters zero again, so
+ * a later call whose batch x KV-head count is no larger than the previous call's can reuse it as
+ * it is (with or without RoPE, any hint or split count that fits). Before a call with a larger
+ * count, zero its first pdecode_workspace_bytes(new description) bytes again. Calls that may run
+ * at the same time need separate workspaces.
  * out and lse are fully written. Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL (nothing
  * launched), HIP (launch failure). */
 pdecode_status pdecode_attention(const pdecode_desc *d, const void *q, const void *pages,

@@ -96,7 +96,10 @@ Plan make_plan(const pdecode_desc* d, bool rope) {
     pl.part_o_bytes = align256(rows * d->head_dim * sizeof(float));
     pl.part_lse_bytes = align256(rows * sizeof(float));
   }
-  // split arrival counters [B * H_kv], then the two job-queue counters of the persistent schedule
+  // split arrival counters [B * H_kv], then the two job-queue counters of the persistent schedule.
+  // They lead the workspace, at the same offset and size in every plan of a description (with or
+  // without RoPE), so a workspace alternating between those plans keeps its counters apart from
+  // the partial states.
   if (pl.num_chunks > 1 || pl.persistent)
     pl.counter_bytes = align256((size_t(d->batch) * d->num_kv_heads + 2) * sizeof(int32_t));
   return pl;
@@ -175,12 +178,10 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
   p.out = out;
   p.lse = lse;
   const bool ws = pl.workspace_bytes() > 0;
-  p.part_o = ws ? static_cast<float*>(workspace) : nullptr;
-  p.part_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_o_bytes)
-                  : nullptr;
-  p.counters = ws ? reinterpret_cast<int*>(static_cast<char*>(workspace) + pl.part_o_bytes +
-                                           pl.part_lse_bytes)
-                  : nullptr;
+  char* wsb = static_cast<char*>(workspace);
+  p.counters = ws ? reinterpret_cast<int*>(wsb) : nullptr;
+  p.part_o = ws ? reinterpret_cast<float*>(wsb + pl.counter_bytes) : nullptr;
+  p.part_lse = ws ? reinterpret_cast<float*>(wsb + pl.counter_bytes + pl.part_o_bytes) : nullptr;
   p.queue = ws ? p.counters + size_t(d->batch) * d->num_kv_heads : nullptr;
   p.B = d->batch;
   p.H_qo = d->num_qo_heads;

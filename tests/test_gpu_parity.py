@@ -81,7 +81,7 @@ def test_head_dims_and_page_sizes(D, ps, kv):
     run_and_check(w)
 
 
-@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7, 64])
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7, 8, 9, 64])
 def test_forced_splits(splits):
     """Split-KV chunking (any chunk count, ragged last chunk, more chunks than pages)."""
     lens = [1000, 17, 0, 513, 2048, 1]
@@ -439,3 +439,71 @@ def test_batch_sizes_around_schedule_limits(B):
     w = synth.make_workload(name=f"batch{B}", B=B, H_qo=8, H_kv=2, D=128, page_size=16,
                             seq_lens=lens, seed=400 + B, max_num_pages=pages)
     run_and_check(w)
+
+
+@pytest.mark.parametrize("splits", [4, 8, 9])
+def test_split_counters_reset_across_calls(splits):
+    """Split sequences merged inside the persistent kernel (up to 8 chunks) or by the merge
+    kernel (more): the arrival counters and the job queue are back at zero after every call, so
+    repeated calls on one workspace give identical results, and a smaller batch reusing the
+    workspace is exact too."""
+    lens = np.random.default_rng(500 + splits).integers(300, 3000, size=12)
+    w = synth.make_workload(name=f"reuse{splits}", B=12, H_qo=16, H_kv=4, D=128, page_size=16,
+                            seq_lens=lens, seed=501 + splits, max_num_pages=2400)
+    dev = gu.upload(w)
+    desc = gu.desc_for(w, dev, num_kv_splits=splits)
+    ws = pk_alloc(desc)
+    outs = []
+    for _ in range(3):
+        out = torch.empty((w.B, w.H_qo, w.D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.B, w.H_qo), dtype=torch.float32, device="cuda")
+        gu.pk.attention(desc, dev["q"], dev["pages"], dev["indptr"], dev["values"],
+                        dev["length_info"], out, lse, w.sm_scale, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((out.clone(), lse.clone()))
+    check(w, *outs[0], label=w.name)
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l, outs[0][1])
+    # a smaller batch on the same workspace
+    w2 = synth.make_workload(name=f"reuse{splits}_small", B=5, H_qo=16, H_kv=4, D=128,
+                             page_size=16, seq_lens=lens[:5], seed=502 + splits,
+                             max_num_pages=2400)
+    dev2 = gu.upload(w2)
+    desc2 = gu.desc_for(w2, dev2, num_kv_splits=splits)
+    assert gu.pk.workspace_bytes(desc2) <= ws.numel()
+    out = torch.empty((w2.B, w2.H_qo, w2.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w2.B, w2.H_qo), dtype=torch.float32, device="cuda")
+    gu.pk.attention(desc2, dev2["q"], dev2["pages"], dev2["indptr"], dev2["values"],
+                    dev2["length_info"], out, lse, w2.sm_scale, workspace=ws)
+    torch.cuda.synchronize()
+    check(w2, out, lse, label=w2.name)
+
+
+def pk_alloc(desc):
+    return gu.pk.alloc_workspace(desc)
+
+
+def test_workspace_shared_by_rope_and_plain_calls():
+    """One description and one workspace used by calls with RoPE (vector-ALU kernel, its own
+    chunking) and without (persistent matrix-core kernel): each call finds its counters zero and
+    its results exact, in any order."""
+    lens = np.random.default_rng(600).integers(200, 4000, size=16)
+    common = dict(B=16, H_qo=32, H_kv=8, D=128, page_size=16, seq_lens=lens, seed=601,
+                  max_num_pages=4200)
+    w_rope = synth.make_workload(name="ws_rope", rotary_mode=1, rope_theta=500000.0, **common)
+    w_plain = synth.make_workload(name="ws_plain", **common)
+    dev_r, dev_p = gu.upload(w_rope), gu.upload(w_plain)
+    desc = gu.desc_for(w_plain, dev_p)
+    ws = gu.pk.alloc_workspace(desc)
+    rope = gu.pk.make_rope(rotary_mode=1, rope_scale=w_rope.rope_scale,
+                           rope_theta=w_rope.rope_theta, q_rope_position=dev_r["q_pos"],
+                           k_rope_pos_offset=dev_r["k_off"])
+    for w, dev, r in [(w_plain, dev_p, None), (w_rope, dev_r, rope), (w_plain, dev_p, None),
+                      (w_rope, dev_r, rope), (w_plain, dev_p, None)]:
+        out = torch.empty((w.B, w.H_qo, w.D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.B, w.H_qo), dtype=torch.float32, device="cuda")
+        gu.pk.attention(desc, dev["q"], dev["pages"], dev["indptr"], dev["values"],
+                        dev["length_info"], out, lse, w.sm_scale, rope=r, workspace=ws)
+        torch.cuda.synchronize()
+        check(w, out, lse, label=w.name)
