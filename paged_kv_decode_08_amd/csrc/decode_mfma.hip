@@ -170,12 +170,13 @@ struct SeqTable {
   int* njobs;   // [B] by sequence: chunks x H_kv
   int* rnj;     // [B] by rank: the same
   int* sink;    // [B] by sequence (multi-wave build only)
+  int2* rpos;   // [B] by rank, RoPE only: q position, position of attended row 0
 };
 
 __host__ __device__ inline size_t seq_table_bytes(int B) {
   const size_t pre = size_t((B + 4) & ~3);
   const size_t rest = size_t((B + 3) & ~3);
-  return size_t(B) * (16 + 16 + 16) + (pre + 3 * rest) * 4;
+  return size_t(B) * (16 + 16 + 16) + (pre + 3 * rest) * 4 + size_t(B) * 8;
 }
 
 __device__ inline SeqTable seq_table(int* base, int B) {
@@ -189,6 +190,7 @@ __device__ inline SeqTable seq_table(int* base, int B) {
   t.njobs = t.pre + pre;
   t.rnj = t.njobs + rest;
   t.sink = t.rnj + rest;
+  t.rpos = reinterpret_cast<int2*>(t.sink + rest);
   return t;
 }
 
@@ -201,6 +203,7 @@ struct Job {
   int nw;       // slots of this wave (may be 0)
   int nitems;   // nw * SUB rounded up to even, at least 2: items past that are unused (re-reads)
   int s_first;  // first slot of the chunk (its page serves the item of a wave without slots)
+  int qpos, kro;  // RoPE: position of q and of the sequence's attended row 0
 };
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -213,12 +216,12 @@ constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) & 3) << 14 | 0x7 <
 __device__ __forceinline__ uint32_t div_reciprocal(uint32_t d) { return 0xffffffffu / d + 1u; }
 
 // SUB: items per page slot (a 32-row page is walked as two 16-row items).
-template <int PS, int SUB>
+template <int PS, int SUB, bool ROPE>
 __device__ __forceinline__ Job decode_job(const DecodeParams& p, const SeqTable& t, int total_jobs,
                                           uint32_t hinv, int j, int w, int l) {
   Job J;
   J.valid = j < total_jobs;
-  J.b = J.h = J.c = J.nch = J.s_w = J.nw = J.s_first = 0;
+  J.b = J.h = J.c = J.nch = J.s_w = J.nw = J.s_first = J.qpos = J.kro = 0;
   J.nitems = 2;
   J.g = SeqGeom{0, 0, 0, 0, 0, 0, 0, 0};
   if (!J.valid) return J;
@@ -256,6 +259,11 @@ __device__ __forceinline__ Job decode_job(const DecodeParams& p, const SeqTable&
   J.h = int(r - c * uint32_t(p.H_kv));
   J.b = b;
   J.g = g;
+  if constexpr (ROPE) {
+    const int2 rp = t.rpos[rank];
+    J.qpos = uni(rp.x);
+    J.kro = uni(rp.y);
+  }
   int sb, se;
   const int q = uni(sk_b.w);
   chunk_bounds_q(q, g.n_slots - q * J.nch, J.c, sb, se);
@@ -336,10 +344,10 @@ __device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
   __syncthreads();  // s_l is free again
 }
 
-template <int KVT, int D, int PS, int GP>
+template <int KVT, int D, int PS, int GP, bool ROPE>
 __global__ __launch_bounds__(64 * kPWaves) void decode_mfma_persist_kernel(DecodeParams p) {
   // items of 16 rows: a 32-row page is two items (half the registers per item in flight)
-  using C = MfmaCore<KVT, D, 16, GP>;
+  using C = MfmaCore<KVT, D, 16, GP, ROPE>;
   constexpr int SUB = PS / 16;
   constexpr int BLOCK = PS * C::ROW;  // bytes of one (page, K|V, head) block
   using Buf = typename C::Buf;
@@ -359,6 +367,7 @@ __global__ __launch_bounds__(64 * kPWaves) void decode_mfma_persist_kernel(Decod
   __shared__ unsigned long long s_scan64[kPWaves];
   __shared__ int s_ticket;
   __shared__ int s_mrg[kPWaves];  // wave w's arrival completed the previous job's split sequence
+  __shared__ float2 s_freq[ROPE ? D / 2 : 1];  // RoPE: frequencies (rope_freq) of dims i, i + D/2
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (wave-uniform)
@@ -367,6 +376,13 @@ __global__ __launch_bounds__(64 * kPWaves) void decode_mfma_persist_kernel(Decod
   const int G = p.G;
   C core;
   core.init_lane(l);
+  if constexpr (ROPE) {
+    if (tid < D / 2) {
+      float fhi, flo;
+      rope_freq(tid, D, p.rope_scale, p.rope_theta, fhi, flo);
+      s_freq[tid] = make_float2(fhi, flo);
+    }
+  }
 
   // ---- job table: sequences ranked by chunk size (largest first), exclusive prefix of their
   // jobs (chunks x H_kv) in rank order
@@ -402,6 +418,7 @@ __global__ __launch_bounds__(64 * kPWaves) void decode_mfma_persist_kernel(Decod
           tab.rgeo[rank] = make_int4(g.beg, g.np, g.total, g.win_off);
           tab.rsb[rank] = make_int4(g.sink, l, nch, nch > 0 ? g.n_slots / nch : 0);
           tab.rnj[rank] = nj;
+          if constexpr (ROPE) tab.rpos[rank] = make_int2(p.q_pos[l], p.k_off[l]);
         }
         wave_lds_fence();
         int x = ok ? tab.rnj[l] : 0;  // jobs of rank l, then the inclusive prefix
@@ -459,6 +476,7 @@ __global__ __launch_bounds__(64 * kPWaves) void decode_mfma_persist_kernel(Decod
         tab.rgeo[rank] = gg;
         tab.rsb[rank] = make_int4(sk, b, nch, nch > 0 ? n_slots / nch : 0);
         tab.rnj[rank] = tab.njobs[b];
+        if constexpr (ROPE) tab.rpos[rank] = make_int2(p.q_pos[b], p.k_off[b]);
       }
       __syncthreads();
       int run = 0;
@@ -512,19 +530,15 @@ __global__ __launch_bounds__(64 * kPWaves) void decode_mfma_persist_kernel(Decod
   // wait for the item covers them); nothing loaded lives across items in registers, which keeps
   // the compiler's memory-wait counts exact in the item loop.
   int* queue = p.queue;
-  Job J = decode_job<PS, SUB>(p, tab, total_jobs, hinv, blockIdx.x, w, l);
+  Job J = decode_job<PS, SUB, ROPE>(p, tab, total_jobs, hinv, blockIdx.x, w, l);
   int par = 0;  // s_q[par] / s_ids[par] hold J's data, [par ^ 1] receive J1's
-  // J's page ids and q words are loaded first; J1 is decoded while they are in flight, and each
-  // wave issues J's first item from its own ids before the workgroup meets to stage q.
+  // J's page ids and q words are loaded first; J1 is decoded while they are in flight. (Issuing
+  // J's first item before the barrier, from each wave's own ids, keeps its registers live across
+  // the prologue and costs 12 VGPRs at the peak.)
   const int ids0 = load_id(p, J, l);
   uint32_t q0[QW];
   q_words(J, q0);
-  Job J1 = decode_job<PS, SUB>(p, tab, total_jobs, hinv, blockIdx.x + gridDim.x, w, l);
-  // (unconditional, so both paths reach the barrier with the same loads outstanding: an invalid
-  // job's id is a clamped page-table entry and its head 0, a harmless read)
-  Buf buf0, buf1;
-  core.issue(buf0, block_of(clamp_page(p, uni(__builtin_amdgcn_readlane(ids0, 0))), J.h),
-             kv_stride);
+  Job J1 = decode_job<PS, SUB, ROPE>(p, tab, total_jobs, hinv, blockIdx.x + gridDim.x, w, l);
 #pragma unroll
   for (int i = 0; i < QW; ++i) s_q[0][tid + i * NT] = q0[i];
   s_ids[0][w][l] = ids0;
@@ -532,9 +546,12 @@ __global__ __launch_bounds__(64 * kPWaves) void decode_mfma_persist_kernel(Decod
 
   if (J.valid) {
     core.load_q(reinterpret_cast<const uint16_t*>(s_q[0]), G);
+    core.rope_q(J.qpos, s_freq);
     float scale = p.score_scale * (C::FP8 ? p.k_scale[J.h] : 1.0f);
     float vscale = C::FP8 ? p.v_scale[J.h] : 1.0f;
     core.reset();
+    Buf buf0, buf1;
+    core.issue(buf0, block_of(clamp_page(p, uni(s_ids[0][w][0])), J.h), kv_stride);
 
     // Page id of item k of the current job (slot k / SUB of the wave; refilled per 64 slots from
     // the page table).
@@ -558,7 +575,11 @@ __global__ __launch_bounds__(64 * kPWaves) void decode_mfma_persist_kernel(Decod
         const int r0 = 16 * (k % SUB);
         lo = max(lo - r0, 0);
         hi = min(hi - r0, 16);
-        if (lo < hi) core.process(cur, lo, hi, scale, s_pt[w], s_alpha[w]);
+        // RoPE position of the item's row 0: attended rows are numbered from the sequence's
+        // first one, so window pages shift by the rows the window skips (sink - win_off)
+        const int pos0 = J.kro + j * PS + r0 +
+                         (J.s_w + kPWaves * si < J.g.n0 ? 0 : J.g.sink - J.g.win_off);
+        if (lo < hi) core.process(cur, lo, hi, scale, s_pt[w], s_alpha[w], pos0, s_freq);
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NLOADS));
     };
@@ -700,12 +721,13 @@ __global__ __launch_bounds__(64 * kPWaves) void decode_mfma_persist_kernel(Decod
       J = J1;
       par ^= 1;
       core.load_q(reinterpret_cast<const uint16_t*>(s_q[par]), G);
+      core.rope_q(J.qpos, s_freq);
       if (C::FP8) {
         scale = p.score_scale * p.k_scale[J.h];
         vscale = p.v_scale[J.h];
       }
       core.reset();
-      J1 = decode_job<PS, SUB>(p, tab, total_jobs, hinv, next_ticket, w, l);
+      J1 = decode_job<PS, SUB, ROPE>(p, tab, total_jobs, hinv, next_ticket, w, l);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
@@ -836,15 +858,15 @@ static int resident_workgroups(const void* kernel, size_t lds) {
   return n;
 }
 
-template <int KVT, int D, int PS, int GP>
+template <int KVT, int D, int PS, int GP, bool ROPE>
 static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipStream_t st) {
-  const void* k = reinterpret_cast<const void*>(&decode_mfma_persist_kernel<KVT, D, PS, GP>);
+  const void* k = reinterpret_cast<const void*>(&decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE>);
   const size_t lds = seq_table_bytes(p.B);
   const int resident = resident_workgroups(k, lds);
   if (resident <= 0) return hipErrorInvalidConfiguration;
   const unsigned grid = static_cast<unsigned>((max_jobs < resident ? (max_jobs > 0 ? max_jobs : 1) : resident));
-  hipLaunchKernelGGL((decode_mfma_persist_kernel<KVT, D, PS, GP>), dim3(grid), dim3(64 * kPWaves),
-                     lds, st, p);
+  hipLaunchKernelGGL((decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE>), dim3(grid),
+                     dim3(64 * kPWaves), lds, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.num_chunks <= 1 || p.num_chunks <= kInMergeChunks) return e;
   const unsigned rows = static_cast<unsigned>(p.B) * p.H_qo;
@@ -853,39 +875,46 @@ static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipS
   return hipGetLastError();
 }
 
+// RoPE on the matrix cores: bf16 KV, persistent schedule only.
 template <int KVT, int D, int PS, int GP>
-static hipError_t launch_sched(const DecodeParams& p, bool persistent, long long grid,
+static hipError_t launch_sched(const DecodeParams& p, bool persistent, bool rope, long long grid,
                                hipStream_t st) {
-  return persistent ? launch_persist<KVT, D, PS, GP>(p, grid, st)
+  if (rope) {
+    if constexpr (KVT == kBF16) {
+      if (persistent) return launch_persist<KVT, D, PS, GP, true>(p, grid, st);
+    }
+    return hipErrorInvalidValue;
+  }
+  return persistent ? launch_persist<KVT, D, PS, GP, false>(p, grid, st)
                     : launch_chunked<KVT, D, PS, GP>(p, static_cast<unsigned>(grid), st);
 }
 
 template <int KVT, int D, int PS>
-static hipError_t launch_g(const DecodeParams& p, int gp, bool persistent, long long grid,
-                           hipStream_t st) {
+static hipError_t launch_g(const DecodeParams& p, int gp, bool persistent, bool rope,
+                           long long grid, hipStream_t st) {
   switch (gp) {
-    case 1: return launch_sched<KVT, D, PS, 1>(p, persistent, grid, st);
-    case 2: return launch_sched<KVT, D, PS, 2>(p, persistent, grid, st);
-    case 4: return launch_sched<KVT, D, PS, 4>(p, persistent, grid, st);
-    case 8: return launch_sched<KVT, D, PS, 8>(p, persistent, grid, st);
+    case 1: return launch_sched<KVT, D, PS, 1>(p, persistent, rope, grid, st);
+    case 2: return launch_sched<KVT, D, PS, 2>(p, persistent, rope, grid, st);
+    case 4: return launch_sched<KVT, D, PS, 4>(p, persistent, rope, grid, st);
+    case 8: return launch_sched<KVT, D, PS, 8>(p, persistent, rope, grid, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <int KVT>
 static hipError_t launch_kv(const DecodeParams& p, int D, int PS, int gp, bool persistent,
-                            long long grid, hipStream_t st) {
-  if (D == 64 && PS == 16) return launch_g<KVT, 64, 16>(p, gp, persistent, grid, st);
-  if (D == 64 && PS == 32) return launch_g<KVT, 64, 32>(p, gp, persistent, grid, st);
-  if (D == 128 && PS == 16) return launch_g<KVT, 128, 16>(p, gp, persistent, grid, st);
-  if (D == 128 && PS == 32) return launch_g<KVT, 128, 32>(p, gp, persistent, grid, st);
+                            bool rope, long long grid, hipStream_t st) {
+  if (D == 64 && PS == 16) return launch_g<KVT, 64, 16>(p, gp, persistent, rope, grid, st);
+  if (D == 64 && PS == 32) return launch_g<KVT, 64, 32>(p, gp, persistent, rope, grid, st);
+  if (D == 128 && PS == 16) return launch_g<KVT, 128, 16>(p, gp, persistent, rope, grid, st);
+  if (D == 128 && PS == 32) return launch_g<KVT, 128, 32>(p, gp, persistent, rope, grid, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int D, int PS, int gp,
-                              bool persistent, long long grid, hipStream_t st) {
-  if (kv_dtype == kBF16) return launch_kv<kBF16>(p, D, PS, gp, persistent, grid, st);
-  if (kv_dtype == kFP8) return launch_kv<kFP8>(p, D, PS, gp, persistent, grid, st);
+                              bool persistent, bool rope, long long grid, hipStream_t st) {
+  if (kv_dtype == kBF16) return launch_kv<kBF16>(p, D, PS, gp, persistent, rope, grid, st);
+  if (kv_dtype == kFP8) return launch_kv<kFP8>(p, D, PS, gp, persistent, rope, grid, st);
   return hipErrorInvalidValue;
 }
 

@@ -27,15 +27,6 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_x
 
 constexpr int kRopeAnchor = 8;  // page slots between exact RoPE angles (the rest by recurrence)
 
-// cos and sin of 2*pi*frac(pos * f) with f = fhi + flo (f = rope_scale * freq / 2pi).
-__device__ __forceinline__ void rope_cs(int pos, float fhi, float flo, float& c, float& s) {
-  const float pf = static_cast<float>(pos);
-  const float prod = pf * fhi;
-  const float err = fmaf(pf, fhi, -prod);
-  const float rev = (prod - rintf(prod)) + fmaf(pf, flo, err);
-  sincospif(2.0f * rev, &s, &c);
-}
-
 template <int KVT, int QT, int D, int PS, int GP>
 __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   using KV = Kv<KVT>;
@@ -92,16 +83,11 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     for (int e = 0; e < EPV; ++e) qo[g][e] = live ? load_q<QT>(p.q, qb + d0 + e) : 0.f;
   }
   if (rotary) {
-    const double log2_theta = log2(static_cast<double>(p.rope_theta));
     const int qpos = p.q_pos[b];
     const int pd0 = lower ? d0 + D / 2 : d0 - D / 2;   // partner dims
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
-      const int i = (d0 + e) % (D / 2);
-      const double f = static_cast<double>(p.rope_scale) * exp2(-(2.0 * i / D) * log2_theta) /
-                       (2.0 * 3.14159265358979323846);
-      fhi[e] = static_cast<float>(f);
-      flo[e] = static_cast<float>(f - static_cast<double>(fhi[e]));
+      rope_freq((d0 + e) % (D / 2), D, p.rope_scale, p.rope_theta, fhi[e], flo[e]);
       rope_cs(RPI, fhi[e], flo[e], stc[e], sts[e]);
       float cs, sn;
       rope_cs(qpos, fhi[e], flo[e], cs, sn);

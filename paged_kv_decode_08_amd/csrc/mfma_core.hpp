@@ -16,6 +16,12 @@
 //    O[g][dims] accumulates in fp32 FMAs (bf16 V) or in v_dot2_f32_bf16 over row pairs (fp8 V:
 //    two rows' bytes interleaved with v_perm, converted exactly to bf16, P rounded to bf16).
 //  * fp8: k_scale multiplies the scores, v_scale the output.
+//  * RoPE (bf16 KV, ROPE = true): rotate-half pairs dims i and i + D/2, and the MFMA layout puts
+//    both in the same lane (k-steps j and j + KS/2), so q (once per job) and each K row (per item)
+//    are rotated in registers in fp32 (angles: rope_cs_hw). The rotated values no longer
+//    fit bf16, so each is split into a bf16 high part and a bf16 remainder, and the scores take
+//    three products: q_hi.k_hi + q_hi.k_lo + q_lo.k_hi (the dropped q_lo.k_lo is below 2^-16 of
+//    the score).
 //  * rows outside the attended range [lo, hi) of a page are masked out of the scores and their V
 //    entries zeroed before use (an unused slot may hold anything, NaN included).
 #pragma once
@@ -68,7 +74,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-template <int KVT, int D, int PS, int GP>
+// Splits x into a bf16 high part and a bf16 remainder (x - hi), both rounded to nearest even.
+__device__ __forceinline__ void split_bf16(float x, float y, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(x, y);
+  lo = pack_bf16x2(x - bf16_lo(hi), y - bf16_hi(hi));
+}
+
+template <int KVT, int D, int PS, int GP, bool ROPE = false>
 struct MfmaCore {
   static constexpr bool FP8 = KVT == kFP8;
   static constexpr int EB = FP8 ? 1 : 2;        // bytes per element
@@ -85,6 +97,8 @@ struct MfmaCore {
   static constexpr int PT_STRIDE = PS + 4;      // P^T row stride in floats (bank-conflict-free)
   using VT = typename VVec<KVT>::type;
   static_assert(GP <= 16 && (NI == 2 || NI % 4 == 0), "unsupported shape");
+  static_assert(!ROPE || (!FP8 && RB == 1), "RoPE on the matrix cores: bf16 KV, 16-row items");
+  static constexpr int KH = KS / 2;             // k-steps of the lower half of the head dim
 
   struct Buf {
     uint4 k[NK];
@@ -92,7 +106,8 @@ struct MfmaCore {
   };
 
   int l, n, qg, cv, rg;  // lane coordinates: MFMA layout (n, qg), V layout (cv, rg)
-  uint4 qop[KS];         // q as the MFMA B operand
+  uint4 qop[KS];         // q as the MFMA B operand (with RoPE: the bf16 high part)
+  uint4 qlo[ROPE ? KS : 1];  // with RoPE: the bf16 remainder of the rotated q
   float m;               // running max of head n (MFMA layout, identical across qg)
   float dl;              // partial denominator over this lane's rows
   float O[GP][8];
@@ -129,6 +144,38 @@ struct MfmaCore {
       qop[j] = n < G ? *reinterpret_cast<const uint4*>(qr + q_dim0(j)) : make_uint4(0, 0, 0, 0);
   }
 
+  // Rotates the q operand to position qpos (RoPE) and splits it into qop (high) and qlo.
+  // s_freq[i] = (fhi, flo) of frequency i (rope_freq).
+  __device__ __forceinline__ void rope_q(int qpos, const float2* s_freq) {
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int j = 0; j < KH; ++j) {
+        float x1[8], x2[8];
+        Kv<kBF16>::unpack(qop[j], x1);
+        Kv<kBF16>::unpack(qop[j + KH], x2);
+        float y1[8], y2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 f = s_freq[32 * j + 8 * qg + e];
+          float c, sn;
+          rope_cs_hw(qpos, f.x, f.y, c, sn);
+          y1[e] = x1[e] * c - x2[e] * sn;
+          y2[e] = x2[e] * c + x1[e] * sn;
+        }
+        uint32_t h1[4], l1[4], h2[4], l2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          split_bf16(y1[2 * e], y1[2 * e + 1], h1[e], l1[e]);
+          split_bf16(y2[2 * e], y2[2 * e + 1], h2[e], l2[e]);
+        }
+        qop[j] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
+        qlo[j] = make_uint4(l1[0], l1[1], l1[2], l1[3]);
+        qop[j + KH] = make_uint4(h2[0], h2[1], h2[2], h2[3]);
+        qlo[j + KH] = make_uint4(l2[0], l2[1], l2[2], l2[3]);
+      }
+    }
+  }
+
   // Issues the K and V loads of one (page, head) block pair.
   __device__ __forceinline__ void issue(Buf& bf, const char* kb, size_t kv_stride) const {
     const char* vb = kb + kv_stride;
@@ -147,25 +194,64 @@ struct MfmaCore {
 
   // Online-softmax update with one page whose attended rows are [lo, hi) (lo < hi).
   // s_pt: this wave's [16][PT_STRIDE] P^T tile; s_alpha: this wave's 16 rescale factors.
+  // RoPE: row r of the item is at position pos0 + r; s_freq as in rope_q.
   __device__ __forceinline__ void process(const Buf& bf, int lo, int hi, float scale,
-                                          float (*s_pt)[PT_STRIDE], float* s_alpha) {
+                                          float (*s_pt)[PT_STRIDE], float* s_alpha, int pos0 = 0,
+                                          const float2* s_freq = nullptr) {
     // scores S^T[row][head] on the matrix cores
     f32x4_t acc[RB];
+    if constexpr (ROPE) {
+      // this lane's K row (n) rotated to its position, split into high parts and remainders
+      uint4 khi[KS], klo[KS];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      acc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < KH; ++j) {
+        float x1[8], x2[8];
+        Kv<kBF16>::unpack(bf.k[j], x1);
+        Kv<kBF16>::unpack(bf.k[j + KH], x2);
+        float y1[8], y2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 f = s_freq[32 * j + 8 * qg + e];
+          float c, sn;
+          rope_cs_hw(pos0 + n, f.x, f.y, c, sn);
+          y1[e] = x1[e] * c - x2[e] * sn;
+          y2[e] = x2[e] * c + x1[e] * sn;
+        }
+        uint32_t h1[4], l1[4], h2[4], l2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          split_bf16(y1[2 * e], y1[2 * e + 1], h1[e], l1[e]);
+          split_bf16(y2[2 * e], y2[2 * e + 1], h2[e], l2[e]);
+        }
+        khi[j] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
+        klo[j] = make_uint4(l1[0], l1[1], l1[2], l1[3]);
+        khi[j + KH] = make_uint4(h2[0], h2[1], h2[2], h2[3]);
+        klo[j + KH] = make_uint4(l2[0], l2[1], l2[2], l2[3]);
+      }
+      acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jj = 0; jj < KS; ++jj) {
-        uint4 a;
-        if constexpr (FP8) {
-          const uint4 raw = bf.k[rb * KL + jj / 2];
-          const uint32_t w0 = (jj % 2) ? raw.z : raw.x, w1 = (jj % 2) ? raw.w : raw.y;
-          a = make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
-                         fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
-        } else {
-          a = bf.k[rb * KS + jj];
+        acc[0] = mfma_16x16x32_bf16(khi[jj], qop[jj], acc[0]);
+        acc[0] = mfma_16x16x32_bf16(klo[jj], qop[jj], acc[0]);
+        acc[0] = mfma_16x16x32_bf16(khi[jj], qlo[jj], acc[0]);
+      }
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        acc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < KS; ++jj) {
+          uint4 a;
+          if constexpr (FP8) {
+            const uint4 raw = bf.k[rb * KL + jj / 2];
+            const uint32_t w0 = (jj % 2) ? raw.z : raw.x, w1 = (jj % 2) ? raw.w : raw.y;
+            a = make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                           fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
+          } else {
+            a = bf.k[rb * KS + jj];
+          }
+          acc[rb] = mfma_16x16x32_bf16(a, qop[jj], acc[rb]);
         }
-        acc[rb] = mfma_16x16x32_bf16(a, qop[jj], acc[rb]);
       }
     }
     float sv[RB][4];
