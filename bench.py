@@ -28,6 +28,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 CTX_DESC = {"llama3_8b_bf16": "uniform[512,4096]", "long_ctx_bf16": "{32768,131072}",
             "rope_swa_bf16": "uniform[1024,16384], window 4096 + sink 4, RoPE theta 5e5",
             "fp8_gqa8": "lognormal(median 2048, sigma 0.5) capped at 8192",
+            "gqa8_bf16": "uniform[512,4096]",
             "tiny_fp32": "{1,17,33,50}"}
 
 
@@ -42,7 +43,7 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="num_kv_splits (0 = automatic plan)")
     ap.add_argument("--workload", default="llama3_8b_bf16",
                     choices=["llama3_8b_bf16", "long_ctx_bf16", "rope_swa_bf16", "fp8_gqa8",
-                             "tiny_fp32"])
+                             "tiny_fp32", "gqa8_bf16"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the decode, run a plain 512 MiB device-to-device copy "
                          "(the reference point for the HBM byte counters) and exit")

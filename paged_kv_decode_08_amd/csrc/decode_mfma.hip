@@ -345,7 +345,8 @@ __device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
 }
 
 template <int KVT, int D, int PS, int GP, bool ROPE>
-__global__ __launch_bounds__(64 * kPWaves) void decode_mfma_persist_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_mfma_persist_kernel(DecodeParams p) {
   // items of 16 rows: a 32-row page is two items (half the registers per item in flight)
   using C = MfmaCore<KVT, D, 16, GP, ROPE>;
   constexpr int SUB = PS / 16;

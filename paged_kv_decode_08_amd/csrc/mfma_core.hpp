@@ -13,8 +13,9 @@
 //  * softmax: the tile max per head needs two cross-row exchanges; one exp2 per score.
 //  * P.V: P goes through LDS (transposed, [head][row]) to the V layout, where lane l holds 8
 //    consecutive dims of NI consecutive rows (each V load instruction reads whole rows);
-//    O[g][dims] accumulates in fp32 FMAs (bf16 V) or in v_dot2_f32_bf16 over row pairs (fp8 V:
-//    two rows' bytes interleaved with v_perm, converted exactly to bf16, P rounded to bf16).
+//    O[g][dims] accumulates in fp32 FMAs (bf16 V, up to 4 heads) or in v_dot2_f32_bf16 over row
+//    pairs with P rounded to bf16 (fp8 V: two rows' bytes interleaved with v_perm, converted
+//    exactly to bf16; bf16 V with 8 heads: two rows' elements regrouped with v_perm).
 //  * fp8: k_scale multiplies the scores, v_scale the output.
 //  * RoPE (bf16 KV, ROPE = true): rotate-half pairs dims i and i + D/2, and the MFMA layout puts
 //    both in the same lane (k-steps j and j + KS/2), so q (once per job) and each K row (per item)
@@ -99,6 +100,9 @@ struct MfmaCore {
   static_assert(GP <= 16 && (NI == 2 || NI % 4 == 0), "unsupported shape");
   static_assert(!ROPE || (!FP8 && RB == 1), "RoPE on the matrix cores: bf16 KV, 16-row items");
   static constexpr int KH = KS / 2;             // k-steps of the lower half of the head dim
+  // P.V with P rounded to bf16 and row pairs through v_dot2_f32_bf16: fp8 V always, bf16 V with 8
+  // heads (fp32 P for 8 heads would take the kernel past 256 VGPRs, one wave per SIMD)
+  static constexpr bool PBF16 = FP8 || GP >= 8;
 
   struct Buf {
     uint4 k[NK];
@@ -295,8 +299,8 @@ struct MfmaCore {
       }
     }
     // this lane's rows of P, per head: fp32 (bf16 V) or bf16 row pairs (fp8 V)
-    float pv[FP8 ? 1 : GP][NI];
-    uint32_t pp[FP8 ? GP : 1][NI / 2];
+    float pv[PBF16 ? 1 : GP][NI];
+    uint32_t pp[PBF16 ? GP : 1][NI / 2];
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
       const float* src = &s_pt[g][NI * rg];
@@ -317,7 +321,7 @@ struct MfmaCore {
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        if constexpr (FP8) {
+        if constexpr (PBF16) {
           if (i % 2) pp[g][i / 2] = pack_bf16x2(t[i - 1], t[i]);
         } else {
           pv[g][i] = t[i];
@@ -349,6 +353,31 @@ struct MfmaCore {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               O[g][4 * wi + e] = dot2_bf16(pp[g][ip], vp[e], O[g][4 * wi + e]);
+        }
+      }
+    } else if constexpr (PBF16) {
+      VT vv[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        vv[i] = bf.v[i];
+        if (partial && !(NI * rg + i >= lo && NI * rg + i < hi)) vv[i] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ip = 0; ip < NI / 2; ++ip) {
+        // rows (2 ip, 2 ip + 1): P as a bf16 pair per head; V dims (2w, 2w + 1) of both rows
+        // regrouped into one bf16 pair per dim
+        const uint32_t a[4] = {vv[2 * ip].x, vv[2 * ip].y, vv[2 * ip].z, vv[2 * ip].w};
+        const uint32_t bb[4] = {vv[2 * ip + 1].x, vv[2 * ip + 1].y, vv[2 * ip + 1].z,
+                                vv[2 * ip + 1].w};
+#pragma unroll
+        for (int wi = 0; wi < 4; ++wi) {
+          const uint32_t d0 = __builtin_amdgcn_perm(bb[wi], a[wi], 0x05040100u);  // a.lo b.lo
+          const uint32_t d1 = __builtin_amdgcn_perm(bb[wi], a[wi], 0x07060302u);  // a.hi b.hi
+#pragma unroll
+          for (int g = 0; g < GP; ++g) {
+            O[g][2 * wi] = dot2_bf16(pp[g][ip], d0, O[g][2 * wi]);
+            O[g][2 * wi + 1] = dot2_bf16(pp[g][ip], d1, O[g][2 * wi + 1]);
+          }
         }
       }
     } else {

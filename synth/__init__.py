@@ -226,12 +226,21 @@ def fp8_gqa8(seed=1005, B=256, lens=None, sigma=0.5):
                          seed=seed)
 
 
+def gqa8_bf16(seed=1006, B=32, lens=None):
+    """Llama-3-70B-shaped attention layer (64 q / 8 KV heads, GQA 8) at the Llama-3-8B lengths."""
+    if lens is None:
+        lens = _rng(seed, 0).integers(512, 4096, size=B, endpoint=True)
+    return make_workload(name="gqa8_decode_bf16", B=B, H_qo=64, H_kv=8, D=128, page_size=16,
+                         seq_lens=lens, max_num_pages=16384, seed=seed)
+
+
 CONFIGS = {
     "tiny_fp32": tiny_fp32,
     "llama3_8b_bf16": llama3_8b_bf16,
     "long_ctx_bf16": long_ctx_bf16,
     "rope_swa_bf16": rope_swa_bf16,
     "fp8_gqa8": fp8_gqa8,
+    "gqa8_bf16": gqa8_bf16,
 }
 
 
