@@ -507,3 +507,16 @@ def test_workspace_shared_by_rope_and_plain_calls():
                         dev["length_info"], out, lse, w.sm_scale, rope=r, workspace=ws)
         torch.cuda.synchronize()
         check(w, out, lse, label=w.name)
+
+
+@pytest.mark.parametrize("G,D,ps", [(1, 128, 16), (2, 64, 32), (8, 128, 16), (8, 64, 32), (5, 128, 32)])
+def test_rope_group_sizes_and_shapes(G, D, ps):
+    """RoPE on the matrix-core path across q-head groups (8 heads take P.V through bf16 row
+    pairs), head dims and page sizes, with a window and sink, and split sequences."""
+    lens = [3000, 17, 0, 1100, 64, 5000]
+    w = synth.make_workload(name=f"rope_G{G}_D{D}_ps{ps}", B=len(lens), H_qo=2 * G, H_kv=2, D=D,
+                            page_size=ps, seq_lens=lens, seed=700 + G + D + ps,
+                            max_num_pages=900, rotary_mode=1, rope_theta=500000.0,
+                            rope_scale=0.5, window=2048, sink=4)
+    run_and_check(w)
+    run_and_check(w, num_kv_splits=5)
