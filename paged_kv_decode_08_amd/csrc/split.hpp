@@ -60,10 +60,19 @@ __device__ void merge_chunks(const DecodeParams& p, int b, int h, int nch) {
       const int g = idx / D, d = idx % D;
       const float* po = p.part_o + (row0 + size_t(g) * p.num_chunks + c0) * D + d;
       float a = acc[k], ws = wsum[k];
-      for (int cc = 0; cc < cnt; ++cc) {
-        const float wc = s_w[g][cc];
-        a = fmaf(wc, load_agent(&po[size_t(cc) * D]), a);
-        ws += wc;
+      // 8 chunks' loads issued together (one round trip per 8 chunks, not one per chunk)
+      for (int cc = 0; cc < cnt; cc += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = cc + u < cnt ? load_agent(&po[size_t(cc + u) * D]) : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (cc + u < cnt) {
+            const float wc = s_w[g][cc + u];
+            a = fmaf(wc, x[u], a);
+            ws += wc;
+          }
+        }
       }
       acc[k] = a;
       wsum[k] = ws;
