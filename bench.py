@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_bf16",
                     choices=["llama3_8b_bf16", "long_ctx_bf16", "rope_swa_bf16", "fp8_gqa8",
                              "tiny_fp32", "gqa8_bf16"])
+    ap.add_argument("--op", choices=["merge_state", "append_kv"], default=None,
+                    help="instead of the decode, time pdecode_merge_state_inplace or "
+                         "pdecode_append_kv at a decode-step size and a bulk size")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the decode, run a plain 512 MiB device-to-device copy "
                          "(the reference point for the HBM byte counters) and exit")
@@ -98,6 +101,67 @@ def copy_calibration(steps):
                       "GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
+def op_bench(op, steps, warmup):
+    """Times the two small calls of the path: one launch per step, HIP events around the K steps.
+    merge_state: bf16 v [n, 32, 128] and fp32 s merged in place with (v', s'); bytes = both states
+    read + one written. append_kv: T new bf16 K and V rows of 8 KV heads x 128 into a bf16 pool;
+    bytes = rows read + written (+ slot ids)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_08_amd as pk
+    import synth
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    results = []
+    for label, size in (("decode_step", 32), ("bulk", 4096)):
+        if op == "merge_state":
+            n, H, D = size, 32, 128
+            rng = np.random.default_rng(7)
+            mk = lambda: torch.from_numpy(synth.cast_f32(
+                rng.standard_normal((n, H, D), dtype=np.float32), "bf16")).view(torch.int16).view(
+                    torch.bfloat16).cuda()
+            v, vo = mk(), mk()
+            s = torch.from_numpy(rng.standard_normal((n, H)).astype(np.float32)).cuda()
+            so = torch.from_numpy(rng.standard_normal((n, H)).astype(np.float32)).cuda()
+            nbytes = 3 * (n * H * D * 2 + n * H * 4)
+            call = lambda: pk.merge_state_inplace(v, s, vo, so, stream=stream)
+            shape = {"n": n, "num_heads": H, "head_dim": D, "v_dtype": "bf16"}
+        else:
+            T, H_kv, D, ps, pool = size, 8, 128, 16, 16384
+            k, vv, slots = synth.append_inputs(T=T, H_kv=H_kv, D=D, page_size=ps,
+                                               max_num_pages=pool, in_dtype="bf16", seed=8)
+            desc = pk.make_desc(batch=1, num_qo_heads=H_kv, num_kv_heads=H_kv, head_dim=D,
+                                page_size=ps, max_num_pages=pool, q_dtype="bf16", kv_dtype="bf16")
+            tk = torch.from_numpy(k).view(torch.int16).view(torch.bfloat16).cuda()
+            tv = torch.from_numpy(vv).view(torch.int16).view(torch.bfloat16).cuda()
+            ts = torch.from_numpy(slots).cuda()
+            pages = torch.zeros((pool, 2, H_kv, ps, D), dtype=torch.bfloat16, device="cuda")
+            nbytes = 2 * 2 * T * H_kv * D * 2 + T * 4
+            call = lambda: pk.append_kv(desc, tk, tv, ts, pages, stream=stream)
+            shape = {"tokens": T, "num_kv_heads": H_kv, "head_dim": D, "page_size": ps,
+                     "kv_dtype": "bf16"}
+        for _ in range(warmup):
+            call()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(steps):
+            call()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall_us = (time.perf_counter() - t0) * 1e6 / steps
+        ev_us = ev0.elapsed_time(ev1) * 1e3 / steps
+        results.append({"size": label, **shape, "bytes": nbytes, "us_per_call_events": round(ev_us, 3),
+                        "us_per_call_wall": round(wall_us, 3),
+                        "GBps_events": round(nbytes / (ev_us * 1e-6) / 1e9, 1)})
+    print(json.dumps({"op": op, "n_gpus": 1, "steps": steps, "warmup": warmup,
+                      "data": "synthetic", "results": results}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -107,6 +171,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(max(args.steps, 1))
+        return
+    if args.op:
+        op_bench(args.op, max(args.steps, 1), args.warmup)
         return
     import numpy as np
     import torch

@@ -236,11 +236,14 @@ def test_merge_two_halves_equals_whole_on_gpu():
     check(w, o1, l1, label="merged halves")
 
 
+@pytest.mark.parametrize("D", [128, 36])
 @pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
-def test_append_bitexact(kv):
+def test_append_bitexact(kv, D):
+    """Placement and encoding are bit-exact. D = 128 takes the 16-byte vector form for every
+    dtype; D = 36 (rows of 72 bf16 bytes, 36 fp8 bytes) the element form, fp32 still vectors."""
     import paged_kv_decode_08_amd as pk
     ind = "f32" if kv == "f32" else "bf16"
-    H_kv, D, ps, P = 8, 128, 16 if kv != "fp8" else 32, 64
+    H_kv, ps, P = 8, 16 if kv != "fp8" else 32, 64
     pool = synth.poisoned_pool(P, H_kv, ps, D, kv)
     k, v, slots = synth.append_inputs(T=40, H_kv=H_kv, D=D, page_size=ps, max_num_pages=P,
                                       in_dtype=ind, seed=12, skip_every=5)
