@@ -36,8 +36,12 @@ constexpr int kPersistMaxBatch = 1024;  // sequences the persistent schedule's L
 // ------------------------------------------------------------------------------------------------
 // One workgroup per job.
 template <int KVT, int D, int PS, int GP>
-__global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeParams p) {
-  using C = MfmaCore<KVT, D, PS, GP>;
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_mfma_kernel(DecodeParams p) {
+  // items of 16 rows: a 32-row page is two items (half the registers per item in flight)
+  using C = MfmaCore<KVT, D, 16, GP>;
+  constexpr int SUB = PS / 16;
+  constexpr int BLOCK = PS * C::ROW;  // bytes of one (page, K|V, head) block
   using Buf = typename C::Buf;
   constexpr int NT = 64 * kWaves;
   __shared__ __attribute__((aligned(16))) float s_pt[kWaves][16][C::PT_STRIDE];
@@ -97,28 +101,35 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeParams p
     return r < 64 ? __builtin_amdgcn_readlane(ids0, r) : __builtin_amdgcn_readlane(ids1, r - 64);
   };
   const char* pool = static_cast<const char*>(p.pages);
-  const size_t kv_stride = size_t(p.H_kv) * C::BLOCK;
-  auto block_of = [&](int page) { return pool + (size_t(page) * 2 * p.H_kv + h) * C::BLOCK; };
+  const size_t kv_stride = size_t(p.H_kv) * BLOCK;
+  // item i: rows 16 (i % SUB) .. + 16 of the wave's slot i / SUB
+  auto item_block = [&](int i) {
+    return pool + (size_t(page_of(i / SUB)) * 2 * p.H_kv + h) * BLOCK + (i % SUB) * 16 * C::ROW;
+  };
+  const int nitems = nw * SUB;
 
   if (nw > 0) {
-    // two register buffers: slot k is computed while slot k + 1 loads
+    // two register buffers: item k is computed while item k + 1 loads
     Buf buf[2];
-    core.issue(buf[0], block_of(page_of(0)), kv_stride);
-    for (int k = 0; k < nw; k += 2) {
-      if (k - id_base >= 64) {  // keep the ids of slots k .. k + 2 at hand
+    core.issue(buf[0], item_block(0), kv_stride);
+    for (int k = 0; k < nitems; k += 2) {
+      if (k / SUB - id_base >= 64) {  // keep the ids of the slots of items k .. k + 2 at hand
         id_base += 64;
         ids0 = ids1;
         ids1 = fetch_id(id_base + 64 + l);
       }
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        if (k + r >= nw) break;
+        if (k + r >= nitems) break;
         // unconditional, so the compiler's wait counts are static; past the end it re-reads the
-        // last slot's blocks (cache hits)
-        core.issue(buf[r ^ 1], block_of(page_of(min(k + r + 1, nw - 1))), kv_stride);
+        // last item's rows (cache hits)
+        core.issue(buf[r ^ 1], item_block(min(k + r + 1, nitems - 1)), kv_stride);
         int j, lo, hi;
-        slot_rows(sg, slot_of(k + r), PS, j, lo, hi);
-        core.process(buf[r], lo, hi, scale, s_pt[w], s_alpha[w]);
+        slot_rows(sg, slot_of((k + r) / SUB), PS, j, lo, hi);
+        const int r0 = 16 * ((k + r) % SUB);
+        lo = max(lo - r0, 0);
+        hi = min(hi - r0, 16);
+        if (lo < hi) core.process(buf[r], lo, hi, scale, s_pt[w], s_alpha[w]);
       }
     }
   }

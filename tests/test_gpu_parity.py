@@ -523,3 +523,18 @@ def test_rope_group_sizes_and_shapes(G, D, ps):
                             rope_scale=0.5, window=2048, sink=4)
     run_and_check(w)
     run_and_check(w, num_kv_splits=5)
+
+
+@pytest.mark.parametrize("kv,G,ps", [("fp8", 8, 32), ("bf16", 2, 32), ("bf16", 8, 16)])
+def test_large_batch_one_workgroup_per_chunk(kv, G, ps):
+    """More sequences than the persistent job table holds: the one-workgroup-per-chunk kernel,
+    on 16-row items of 16- and 32-row pages, with short, empty and split sequences."""
+    B = 1100
+    rng = np.random.default_rng(800 + G + ps)
+    lens = rng.integers(0, 160, size=B)
+    lens[rng.integers(0, B, size=40)] = 1200
+    pages = int(np.sum((lens + ps - 1) // ps)) + 8
+    w = synth.make_workload(name=f"bigB_{kv}_G{G}_ps{ps}", B=B, H_qo=2 * G, H_kv=2, D=128,
+                            page_size=ps, seq_lens=lens, seed=810 + G + ps, max_num_pages=pages,
+                            kv_dtype=kv)
+    run_and_check(w)
