@@ -59,8 +59,9 @@ pdecode_status check_attention_shape(const pdecode_desc* d) {
 // Chunking of each sequence's page slots. A sequence with n slots uses ceil(n / chunk_slots)
 // chunks, capped at num_chunks (the last chunk then takes every remaining slot), so any length
 // is computed exactly; max_kv_len only sizes the grid.
-// rope: the call applies RoPE (bf16 KV up to kPersistMaxBatch sequences: the persistent matrix-core
-// kernel, planned as without RoPE; otherwise the vector-ALU kernel: smaller chunks, one wave each).
+// rope: the call applies RoPE (bf16 KV, or fp8 KV at head_dim 128, up to kPersistMaxBatch
+// sequences: the persistent matrix-core kernel, planned as without RoPE; otherwise the vector-ALU
+// kernel: smaller chunks, one wave each).
 Plan make_plan(const pdecode_desc* d, bool rope) {
   Plan pl;
   const int64_t ps = d->page_size;
@@ -69,7 +70,8 @@ Plan make_plan(const pdecode_desc* d, bool rope) {
   const int64_t units = int64_t(d->batch) * d->num_kv_heads;
 
   const bool persistent = (d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN) &&
-                          d->batch <= kPersistMaxBatch && (!rope || d->kv_dtype == PDECODE_BF16);
+                          d->batch <= kPersistMaxBatch &&
+                          (!rope || d->kv_dtype == PDECODE_BF16 || d->head_dim == 128);
   int64_t chunk;
   if (d->num_kv_splits == 1) {
     chunk = max_slots;
@@ -199,8 +201,9 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
   const int gp = p.G <= 1 ? 1 : p.G <= 2 ? 2 : p.G <= 4 ? 4 : 8;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // bf16 / fp8 KV: q.K on the matrix cores (4-wave workgroups, persistent over a job queue up to
-  // kPersistMaxBatch sequences, else one per chunk), RoPE included for bf16 KV on the persistent
-  // schedule; otherwise the vector-ALU kernel (one wave per chunk; RoPE rotates K in fp32).
+  // kPersistMaxBatch sequences, else one per chunk), RoPE included on the persistent schedule for
+  // bf16 KV and for fp8 KV at head_dim 128; otherwise the vector-ALU kernel (one wave per chunk;
+  // RoPE rotates K in fp32).
   const bool mfma = (d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN) &&
                     (!rotary || pl.persistent);
   if (mfma)

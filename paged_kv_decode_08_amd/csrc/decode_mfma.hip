@@ -887,12 +887,12 @@ static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipS
   return hipGetLastError();
 }
 
-// RoPE on the matrix cores: bf16 KV, persistent schedule only.
+// RoPE on the matrix cores: bf16 KV, or fp8 KV at D = 128; persistent schedule only.
 template <int KVT, int D, int PS, int GP>
 static hipError_t launch_sched(const DecodeParams& p, bool persistent, bool rope, long long grid,
                                hipStream_t st) {
   if (rope) {
-    if constexpr (KVT == kBF16) {
+    if constexpr (KVT == kBF16 || D == 128) {
       if (persistent) return launch_persist<KVT, D, PS, GP, true>(p, grid, st);
     }
     return hipErrorInvalidValue;

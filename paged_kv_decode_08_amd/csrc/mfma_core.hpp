@@ -17,8 +17,9 @@
 //    pairs with P rounded to bf16 (fp8 V: two rows' bytes interleaved with v_perm, converted
 //    exactly to bf16; bf16 V with 8 heads: two rows' elements regrouped with v_perm).
 //  * fp8: k_scale multiplies the scores, v_scale the output.
-//  * RoPE (bf16 KV, ROPE = true): rotate-half pairs dims i and i + D/2, and the MFMA layout puts
-//    both in the same lane (k-steps j and j + KS/2), so q (once per job) and each K row (per item)
+//  * RoPE (ROPE = true; bf16 KV, or fp8 KV at D = 128): rotate-half pairs dims i and i + D/2, and
+//    the MFMA layout puts both in the same lane (k-steps j and j + KS/2; fp8 codes are converted
+//    exactly to fp32 first), so q (once per job) and each K row (per item)
 //    are rotated in registers in fp32 (angles: rope_cs_hw). The rotated values no longer
 //    fit bf16, so each is split into a bf16 high part and a bf16 remainder, and the scores take
 //    three products: q_hi.k_hi + q_hi.k_lo + q_lo.k_hi (the dropped q_lo.k_lo is below 2^-16 of
@@ -98,7 +99,8 @@ struct MfmaCore {
   static constexpr int PT_STRIDE = PS + 4;      // P^T row stride in floats (bank-conflict-free)
   using VT = typename VVec<KVT>::type;
   static_assert(GP <= 16 && (NI == 2 || NI % 4 == 0), "unsupported shape");
-  static_assert(!ROPE || (!FP8 && RB == 1), "RoPE on the matrix cores: bf16 KV, 16-row items");
+  // RoPE needs dims i and i + D/2 in one lane: true for bf16, and for fp8 at D = 128
+  static_assert(!ROPE || (RB == 1 && (!FP8 || D == 128)), "RoPE on the matrix cores: 16-row items, bf16 or fp8 at D = 128");
   static constexpr int KH = KS / 2;             // k-steps of the lower half of the head dim
   // P.V with P rounded to bf16 and row pairs through v_dot2_f32_bf16: fp8 V always, bf16 V with 8
   // heads (fp32 P for 8 heads would take the kernel past 256 VGPRs, one wave per SIMD)
@@ -148,6 +150,20 @@ struct MfmaCore {
       qop[j] = n < G ? *reinterpret_cast<const uint4*>(qr + q_dim0(j)) : make_uint4(0, 0, 0, 0);
   }
 
+  // The 8 K elements of k-step jj of this lane's row, in fp32 (fp8 codes convert exactly).
+  __device__ __forceinline__ void kstep_f32(const Buf& bf, int jj, float (&x)[8]) const {
+    if constexpr (FP8) {
+      const uint4 raw = bf.k[jj / 2];
+      const uint32_t w0 = (jj % 2) ? raw.z : raw.x, w1 = (jj % 2) ? raw.w : raw.y;
+      fp8x2_to_f32<false>(w0, x[0], x[1]);
+      fp8x2_to_f32<true>(w0, x[2], x[3]);
+      fp8x2_to_f32<false>(w1, x[4], x[5]);
+      fp8x2_to_f32<true>(w1, x[6], x[7]);
+    } else {
+      Kv<kBF16>::unpack(bf.k[jj], x);
+    }
+  }
+
   // Rotates the q operand to position qpos (RoPE) and splits it into qop (high) and qlo.
   // s_freq[i] = (fhi, flo) of frequency i (rope_freq).
   __device__ __forceinline__ void rope_q(int qpos, const float2* s_freq) {
@@ -160,7 +176,7 @@ struct MfmaCore {
         float y1[8], y2[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float2 f = s_freq[32 * j + 8 * qg + e];
+          const float2 f = s_freq[q_dim0(j) + e];
           float c, sn;
           rope_cs_hw(qpos, f.x, f.y, c, sn);
           y1[e] = x1[e] * c - x2[e] * sn;
@@ -210,12 +226,12 @@ struct MfmaCore {
 #pragma unroll
       for (int j = 0; j < KH; ++j) {
         float x1[8], x2[8];
-        Kv<kBF16>::unpack(bf.k[j], x1);
-        Kv<kBF16>::unpack(bf.k[j + KH], x2);
+        kstep_f32(bf, j, x1);
+        kstep_f32(bf, j + KH, x2);
         float y1[8], y2[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float2 f = s_freq[32 * j + 8 * qg + e];
+          const float2 f = s_freq[q_dim0(j) + e];
           float c, sn;
           rope_cs_hw(pos0 + n, f.x, f.y, c, sn);
           y1[e] = x1[e] * c - x2[e] * sn;

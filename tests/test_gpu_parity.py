@@ -538,3 +538,16 @@ def test_large_batch_one_workgroup_per_chunk(kv, G, ps):
                             page_size=ps, seq_lens=lens, seed=810 + G + ps, max_num_pages=pages,
                             kv_dtype=kv)
     run_and_check(w)
+
+
+@pytest.mark.parametrize("G,D,ps", [(8, 128, 32), (4, 128, 16), (1, 128, 32), (4, 64, 16)])
+def test_rope_fp8_kv(G, D, ps):
+    """RoPE with fp8 KV: on the matrix cores at D = 128 (codes converted exactly to fp32 before
+    the rotation), on the vector-ALU kernel at D = 64 (rotation partners in different lanes)."""
+    lens = [2500, 33, 0, 700, 4100]
+    w = synth.make_workload(name=f"rope_fp8_G{G}_D{D}_ps{ps}", B=len(lens), H_qo=2 * G, H_kv=2,
+                            D=D, page_size=ps, seq_lens=lens, seed=900 + G + D + ps,
+                            max_num_pages=800, kv_dtype="fp8", rotary_mode=1,
+                            rope_theta=500000.0, window=3000, sink=4)
+    run_and_check(w)
+    run_and_check(w, num_kv_splits=4)
