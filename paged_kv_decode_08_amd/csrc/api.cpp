@@ -59,9 +59,8 @@ pdecode_status check_attention_shape(const pdecode_desc* d) {
 // Chunking of each sequence's page slots. A sequence with n slots uses ceil(n / chunk_slots)
 // chunks, capped at num_chunks (the last chunk then takes every remaining slot), so any length
 // is computed exactly; max_kv_len only sizes the grid.
-// rope: the call applies RoPE (bf16 KV, or fp8 KV at head_dim 128, up to kPersistMaxBatch
-// sequences: the persistent matrix-core kernel, planned as without RoPE; otherwise the vector-ALU
-// kernel: smaller chunks, one wave each).
+// rope: the call applies RoPE (bf16 KV, or fp8 KV at head_dim 128: the matrix-core kernels, planned
+// as without RoPE; otherwise the vector-ALU kernel).
 Plan make_plan(const pdecode_desc* d, bool rope) {
   Plan pl;
   const int64_t ps = d->page_size;
@@ -201,11 +200,10 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
   const int gp = p.G <= 1 ? 1 : p.G <= 2 ? 2 : p.G <= 4 ? 4 : 8;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // bf16 / fp8 KV: q.K on the matrix cores (4-wave workgroups, persistent over a job queue up to
-  // kPersistMaxBatch sequences, else one per chunk), RoPE included on the persistent schedule for
-  // bf16 KV and for fp8 KV at head_dim 128; otherwise the vector-ALU kernel (one wave per chunk;
-  // RoPE rotates K in fp32).
+  // kPersistMaxBatch sequences, else one per chunk), RoPE included for bf16 KV and for fp8 KV at
+  // head_dim 128; otherwise the vector-ALU kernel (one wave per chunk; RoPE rotates K in fp32).
   const bool mfma = (d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN) &&
-                    (!rotary || pl.persistent);
+                    (!rotary || d->kv_dtype == PDECODE_BF16 || d->head_dim == 128);
   if (mfma)
     st = hip_status(pdk::launch_decode_mfma(p, d->kv_dtype, d->head_dim, d->page_size, gp,
                                             pl.persistent, rotary, grid, s));

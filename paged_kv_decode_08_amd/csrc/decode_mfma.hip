@@ -35,11 +35,11 @@ constexpr int kPersistMaxBatch = 1024;  // sequences the persistent schedule's L
 
 // ------------------------------------------------------------------------------------------------
 // One workgroup per job.
-template <int KVT, int D, int PS, int GP>
+template <int KVT, int D, int PS, int GP, bool ROPE>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mfma_kernel(DecodeParams p) {
   // items of 16 rows: a 32-row page is two items (half the registers per item in flight)
-  using C = MfmaCore<KVT, D, 16, GP>;
+  using C = MfmaCore<KVT, D, 16, GP, ROPE>;
   constexpr int SUB = PS / 16;
   constexpr int BLOCK = PS * C::ROW;  // bytes of one (page, K|V, head) block
   using Buf = typename C::Buf;
@@ -49,12 +49,21 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ float s_m[kWaves][GP];
   __shared__ float s_d[kWaves][GP];
   __shared__ __attribute__((aligned(16))) float s_o[kWaves][GP][D];
+  __shared__ float2 s_freq[ROPE ? D / 2 : 1];  // RoPE: frequencies (rope_freq) of dims i, i + D/2
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (wave-uniform)
   C core;
   core.init_lane(tid & 63);
   const int l = core.l;
+  if constexpr (ROPE) {
+    if (tid < D / 2) {
+      float fhi, flo;
+      rope_freq(tid, D, p.rope_scale, p.rope_theta, fhi, flo);
+      s_freq[tid] = make_float2(fhi, flo);
+    }
+    __syncthreads();
+  }
 
   const int units = p.B * p.H_kv;
   const int c = blockIdx.x / units;
@@ -79,6 +88,8 @@ void decode_mfma_kernel(DecodeParams p) {
   const int nw = s_w < s_end ? (s_end - s_w + kWaves - 1) / kWaves : 0;  // slots of this wave
 
   core.load_q(static_cast<const uint16_t*>(p.q) + (size_t(b) * p.H_qo + h * G) * D, G);
+  const int kro = ROPE ? p.k_off[b] : 0;
+  if constexpr (ROPE) core.rope_q(p.q_pos[b], s_freq);
   const float scale = p.score_scale * (C::FP8 ? p.k_scale[h] : 1.0f);
   const float vscale = C::FP8 ? p.v_scale[h] : 1.0f;
   core.reset();
@@ -129,7 +140,10 @@ void decode_mfma_kernel(DecodeParams p) {
         const int r0 = 16 * ((k + r) % SUB);
         lo = max(lo - r0, 0);
         hi = min(hi - r0, 16);
-        if (lo < hi) core.process(buf[r], lo, hi, scale, s_pt[w], s_alpha[w]);
+        // RoPE position of the item's row 0 (attended rows numbered from the sequence's first)
+        const int pos0 = kro + j * PS + r0 +
+                         (slot_of((k + r) / SUB) < sg.n0 ? 0 : sg.sink - sg.win_off);
+        if (lo < hi) core.process(buf[r], lo, hi, scale, s_pt[w], s_alpha[w], pos0, s_freq);
       }
     }
   }
@@ -835,9 +849,10 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
 // ------------------------------------------------------------------------------------------------
 // Launchers.
 
-template <int KVT, int D, int PS, int GP>
+template <int KVT, int D, int PS, int GP, bool ROPE>
 static hipError_t launch_chunked(const DecodeParams& p, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_mfma_kernel<KVT, D, PS, GP>), dim3(grid), dim3(64 * kWaves), 0, st, p);
+  hipLaunchKernelGGL((decode_mfma_kernel<KVT, D, PS, GP, ROPE>), dim3(grid), dim3(64 * kWaves), 0,
+                     st, p);
   return hipGetLastError();
 }
 
@@ -887,18 +902,19 @@ static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipS
   return hipGetLastError();
 }
 
-// RoPE on the matrix cores: bf16 KV, or fp8 KV at D = 128; persistent schedule only.
+// RoPE on the matrix cores: bf16 KV, or fp8 KV at D = 128.
 template <int KVT, int D, int PS, int GP>
 static hipError_t launch_sched(const DecodeParams& p, bool persistent, bool rope, long long grid,
                                hipStream_t st) {
   if (rope) {
     if constexpr (KVT == kBF16 || D == 128) {
-      if (persistent) return launch_persist<KVT, D, PS, GP, true>(p, grid, st);
+      return persistent ? launch_persist<KVT, D, PS, GP, true>(p, grid, st)
+                        : launch_chunked<KVT, D, PS, GP, true>(p, static_cast<unsigned>(grid), st);
     }
     return hipErrorInvalidValue;
   }
   return persistent ? launch_persist<KVT, D, PS, GP, false>(p, grid, st)
-                    : launch_chunked<KVT, D, PS, GP>(p, static_cast<unsigned>(grid), st);
+                    : launch_chunked<KVT, D, PS, GP, false>(p, static_cast<unsigned>(grid), st);
 }
 
 template <int KVT, int D, int PS>
