@@ -1,5 +1,6 @@
 // Paged-KV decode attention for bf16 or fp8-e4m3fn KV (bf16 q) on gfx950: q.K on the matrix cores,
-// softmax and P.V on the vector ALUs (per-page steps: mfma_core.hpp).
+// softmax and P.V on the vector ALUs, optional RoPE on q and K in registers (per-item steps:
+// mfma_core.hpp).
 //
 // Work unit ("job"): one chunk of page slots of one (sequence, KV head), done by one workgroup of
 // 4 wavefronts (kWaves, kPWaves); wave w takes slots w, w + 4, ... of the chunk and the waves' states are
