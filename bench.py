@@ -44,9 +44,11 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_bf16",
                     choices=["llama3_8b_bf16", "long_ctx_bf16", "rope_swa_bf16", "fp8_gqa8",
                              "tiny_fp32", "gqa8_bf16"])
-    ap.add_argument("--op", choices=["merge_state", "append_kv"], default=None,
+    ap.add_argument("--op", choices=["merge_state", "append_kv", "append_attention"], default=None,
                     help="instead of the decode, time pdecode_merge_state_inplace or "
-                         "pdecode_append_kv at a decode-step size and a bulk size")
+                         "pdecode_append_kv at a decode-step size and a bulk size, or a whole "
+                         "decode step of --workload: pdecode_append_attention against "
+                         "pdecode_append_kv followed by pdecode_attention")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the decode, run a plain 512 MiB device-to-device copy "
                          "(the reference point for the HBM byte counters) and exit")
@@ -56,6 +58,7 @@ def parse():
 # Sources of the decode kernels: the HBM-traffic figure recorded under profiles/ is used only while
 # their hash matches the one it was measured with.
 KERNEL_SOURCES = ["paged_kv_decode_08_amd/csrc/decode_mfma.hip",
+                  "paged_kv_decode_08_amd/csrc/decode_persist.hpp",
                   "paged_kv_decode_08_amd/csrc/mfma_core.hpp",
                   "paged_kv_decode_08_amd/csrc/decode_valu.hip",
                   "paged_kv_decode_08_amd/csrc/device.hpp",
@@ -162,6 +165,78 @@ def op_bench(op, steps, warmup):
                       "data": "synthetic", "results": results}), flush=True)
 
 
+def step_bench(workload, steps, warmup, nsets):
+    """A whole decode step: the step's new K/V row of every (sequence, KV head) goes to the
+    sequence's last position, then attention. Fused (one pdecode_append_attention launch) against
+    separate (pdecode_append_kv, then pdecode_attention), K steps each between synchronisations,
+    input sets cycled as in the decode bench."""
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_08_amd as pk
+    import synth
+    from tests import gpu_util as gu
+
+    torch.cuda.set_device(0)
+    make = synth.CONFIGS[workload]
+    base = make()
+    nsets = nsets if base.kv_bytes < 512e6 else 1
+    lens = base.seq_lens.astype(np.int64)
+    sets = [base] + [make(seed=1002 + 100 * i, lens=lens) for i in range(1, nsets)]
+    devs = [gu.upload(w) for w in sets]
+    desc = gu.desc_for(base, devs[0])
+    ws = pk.alloc_workspace(desc)
+    out = torch.empty((base.B, base.H_qo, base.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((base.B, base.H_qo), dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(9)
+    new = [torch.from_numpy(synth.cast_f32(rng.standard_normal((base.B, base.H_kv, base.D),
+                                                               dtype=np.float32), "bf16"))
+           .view(torch.int16).view(torch.bfloat16).cuda() for _ in range(2)]
+    slots = []
+    for w in sets:  # each sequence's position total - 1 (its last page, row last_page_len - 1)
+        last = np.asarray(w.length_info).reshape(-1, w.B)[0].astype(np.int64)
+        ids = w.page_values[w.page_indptr[1:] - 1].astype(np.int64)
+        slots.append(torch.from_numpy((ids * w.page_size + last - 1).astype(np.int32)).cuda())
+    ropes = [None] * len(devs)
+    if base.rotary_mode:
+        ropes = [pk.make_rope(rotary_mode=base.rotary_mode, rope_scale=base.rope_scale,
+                              rope_theta=base.rope_theta, q_rope_position=d["q_pos"],
+                              k_rope_pos_offset=d["k_off"]) for d in devs]
+    stream = torch.cuda.current_stream()
+
+    def fused(i):
+        d = devs[i % len(devs)]
+        pk.append_attention(desc, new[0], new[1], d["q"], d["pages"], d["indptr"], d["values"],
+                            d["length_info"], out, lse, base.sm_scale, rope=ropes[i % len(devs)],
+                            workspace=ws, stream=stream)
+
+    def separate(i):
+        d = devs[i % len(devs)]
+        pk.append_kv(desc, new[0], new[1], slots[i % len(devs)], d["pages"], stream=stream)
+        pk.attention(desc, d["q"], d["pages"], d["indptr"], d["values"], d["length_info"], out,
+                     lse, base.sm_scale, rope=ropes[i % len(devs)], workspace=ws, stream=stream)
+
+    res = {}
+    for name, fn in (("separate", separate), ("fused", fused), ("separate_again", separate),
+                     ("fused_again", fused)):
+        for i in range(warmup):
+            fn(i)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = {"us_per_step_wall": round((time.perf_counter() - t0) * 1e6 / steps, 2),
+                     "us_per_step_events": round(ev0.elapsed_time(ev1) * 1e3 / steps, 2)}
+    print(json.dumps({"op": "append_attention", "workload": base.name, "n_gpus": 1,
+                      "steps": steps, "warmup": warmup, "input_sets": len(sets),
+                      "kv_bytes_per_step": base.kv_bytes, "data": "synthetic", **res}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -171,6 +246,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(max(args.steps, 1))
+        return
+    if args.op == "append_attention":
+        step_bench(args.workload, max(args.steps, 1), args.warmup, args.sets)
         return
     if args.op:
         op_bench(args.op, max(args.steps, 1), args.warmup)

@@ -8,6 +8,8 @@
  *                                RoPE on Q and K, optional sliding window with attention sink.
  *   pdecode_merge_state_inplace  Same page, _merge_state_inplace: combine two attention states
  *                                (V, lse) in place.
+ *   pdecode_append_attention     pdecode_append_kv of each sequence's newest token fused into
+ *                                pdecode_attention (one launch).
  *   pdecode_append_kv            vLLM nki_flash_attn page, reshape_and_cache: write new K/V rows
  *                                into their cache slots. The fp8 KV cache with k_scale / v_scale
  *                                follows the AWS Neuron attention_block_tkg page (OCP e4m3fn);
@@ -128,6 +130,26 @@ pdecode_status pdecode_attention(const pdecode_desc *d, const void *q, const voi
                                  const int32_t *length_info, const pdecode_rope *rope,
                                  float sm_scale, void *out, float *lse, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/* One decode step with its KV append fused into the attention launch: for every sequence b with
+ * pages and every KV head h, new_k[b, h, :] and new_v[b, h, :] are written to the sequence's row
+ * of position total_b - 1 (page page_values[page_indptr[b+1] - 1], row last_page_len[b] - 1)
+ * exactly as pdecode_append_kv writes a token to that slot (vLLM nki_flash_attn page,
+ * reshape_and_cache), and out / lse are those of pdecode_attention over the updated pool (TVM
+ * relax decode-kernels page, _attention_decode). The AWS Neuron attention_block_tkg page fuses
+ * its cache update with the attention in the same way. The row is read from the staged new
+ * values, never from the pool, so the result does not depend on what the row held before.
+ * new_k, new_v: device [batch, num_kv_heads, head_dim] of q_dtype (BF16); pages is written; the
+ * other arguments, the workspace rules and the results are those of pdecode_attention.
+ * Supported: the calls pdecode_attention runs on its persistent matrix-core schedule (BF16 or
+ * FP8_E4M3FN pool, batch <= 1024; with RoPE, an FP8 pool needs head_dim 128); otherwise
+ * UNSUPPORTED. Errors: as pdecode_attention, and INVALID_ARG for a null new_k / new_v. */
+pdecode_status pdecode_append_attention(const pdecode_desc *d, const void *new_k,
+                                        const void *new_v, const void *q, void *pages,
+                                        const int32_t *page_indptr, const int32_t *page_values,
+                                        const int32_t *length_info, const pdecode_rope *rope,
+                                        float sm_scale, void *out, float *lse, void *workspace,
+                                        size_t workspace_bytes, void *stream);
 
 /* Merges the attention state (v_other, s_other) into (v, s) in place, base 2:
  *   s_max = max(s, s'); a = 2^(s - s_max); b = 2^(s' - s_max);

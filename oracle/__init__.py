@@ -131,6 +131,35 @@ def append_kv(*, pages, new_k, new_v, slots, H_kv, D, ps, in_dtype, kv_dtype, k_
     return pages
 
 
+def last_position_slots(*, B, ps, indptr, values, length_info):
+    """Pool slot (page * ps + row) of each sequence's position total - 1, the row a decode step's
+    new token occupies: its last page page_values[indptr[b+1] - 1], row last_page_len[b] - 1 (the
+    TVM relax decode-kernels page's length of a paged sequence). -1 for a sequence without pages,
+    which has no such row. length_info: [B] or [3, B] (row 0 is last_page_len)."""
+    indptr = np.asarray(indptr, np.int64)
+    values = np.asarray(values, np.int64)
+    last = np.asarray(length_info, np.int64).reshape(-1, B)[0] if B else np.zeros(0, np.int64)
+    slots = np.full(B, -1, np.int64)
+    for b in range(B):
+        if indptr[b + 1] > indptr[b]:
+            slots[b] = values[indptr[b + 1] - 1] * ps + last[b] - 1
+    return slots.astype(np.int32)
+
+
+def append_then_decode(*, new_k, new_v, **kw):
+    """The fused decode step: append_kv of token b's new K/V rows (new_k/new_v [B, H_kv, D]) to
+    sequence b's last position (last_position_slots; skipped without pages), on a copy of the
+    pool, then decode over the updated pool. Returns (out, lse, updated pool)."""
+    pages = np.array(kw.pop("pages"), copy=True, order="C")
+    slots = last_position_slots(B=kw["B"], ps=kw["ps"], indptr=kw["indptr"], values=kw["values"],
+                                length_info=kw["length_info"])
+    append_kv(pages=pages, new_k=new_k, new_v=new_v, slots=slots, H_kv=kw["H_kv"], D=kw["D"],
+              ps=kw["ps"], in_dtype=kw["q_dtype"], kv_dtype=kw["kv_dtype"],
+              k_scale=kw.get("k_scale"), v_scale=kw.get("v_scale"))
+    out, lse = decode(pages=pages, **kw)
+    return out, lse, pages
+
+
 def validate_page_table(*, B, ps, max_num_pages, indptr, values, length_info, sliding_window=False):
     indptr = _c(indptr, np.int32)
     values = _c(values, np.int32)

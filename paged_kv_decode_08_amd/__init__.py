@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.pdecode_attention.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P,
                                         ctypes.POINTER(Rope), ctypes.c_float, P, P, P,
                                         ctypes.c_size_t, P]
+        L.pdecode_append_attention.restype = _c_i32
+        L.pdecode_append_attention.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P, P, P,
+                                               ctypes.POINTER(Rope), ctypes.c_float, P, P, P,
+                                               ctypes.c_size_t, P]
         L.pdecode_merge_state_inplace.restype = _c_i32
         L.pdecode_merge_state_inplace.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, P, P, P, P, P]
         L.pdecode_append_kv.restype = _c_i32
@@ -151,6 +155,22 @@ def attention(desc: Desc, q, pages, page_indptr, page_values, length_info, out, 
                                  ws_bytes, _stream(stream))
     if st:
         raise PdecodeError(st, "pdecode_attention")
+
+
+def append_attention(desc: Desc, new_k, new_v, q, pages, page_indptr, page_values, length_info,
+                     out, lse, sm_scale, rope: Rope | None = None, workspace=None,
+                     stream=None) -> None:
+    """pdecode_append_attention: writes new_k/new_v [B, H_kv, D] (bf16) to each sequence's row of
+    position total - 1 in `pages`, then writes out [B, H_qo, D] and lse [B, H_qo] as attention()."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().pdecode_append_attention(ctypes.byref(desc), _ptr(new_k), _ptr(new_v), _ptr(q),
+                                        _ptr(pages), _ptr(page_indptr), _ptr(page_values),
+                                        _ptr(length_info),
+                                        None if rope is None else ctypes.byref(rope),
+                                        float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                        ws_bytes, _stream(stream))
+    if st:
+        raise PdecodeError(st, "pdecode_append_attention")
 
 
 def merge_state_inplace(v, s, v_other, s_other, stream=None) -> None:

@@ -142,11 +142,18 @@ pdecode_status pdecode_plan(const pdecode_desc* d, int32_t* chunk_pages, int32_t
   return PDECODE_OK;
 }
 
-pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const void* pages,
-                                 const int32_t* page_indptr, const int32_t* page_values,
-                                 const int32_t* length_info, const pdecode_rope* rope,
-                                 float sm_scale, void* out, float* lse, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pdecode_attention, and with new_k / new_v set the fused append of pdecode_append_attention
+// (the persistent matrix-core schedule only).
+pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const void* new_v,
+                              const void* q, const void* pages, const int32_t* page_indptr,
+                              const int32_t* page_values, const int32_t* length_info,
+                              const pdecode_rope* rope, float sm_scale, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  const bool fused = new_k != nullptr;
   pdecode_status st = check_desc(d);
   if (st != PDECODE_OK) return st;
   if ((st = check_attention_shape(d)) != PDECODE_OK) return st;
@@ -160,6 +167,7 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
   if (!q || !pages || !page_indptr || !page_values || !length_info || !out || !lse)
     return PDECODE_ERR_INVALID_ARG;
   const Plan pl = make_plan(d, rotary);
+  if (fused && !pl.persistent) return PDECODE_ERR_UNSUPPORTED;
   const int64_t grid = int64_t(pl.num_chunks) * d->batch * d->num_kv_heads;
   if (grid > INT_MAX) return PDECODE_ERR_UNSUPPORTED;
   if (pl.workspace_bytes() > 0) {
@@ -177,6 +185,9 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
   p.k_off = rotary ? rope->k_rope_pos_offset : nullptr;
   p.k_scale = d->k_scale;
   p.v_scale = d->v_scale;
+  p.new_k = new_k;
+  p.new_v = new_v;
+  p.pages_w = fused ? const_cast<void*>(pages) : nullptr;
   p.out = out;
   p.lse = lse;
   const bool ws = pl.workspace_bytes() > 0;
@@ -211,6 +222,33 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
     st = hip_status(pdk::launch_decode_valu(p, d->kv_dtype, d->head_dim, d->page_size, gp,
                                             static_cast<unsigned>(grid), s));
   return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const void* pages,
+                                 const int32_t* page_indptr, const int32_t* page_values,
+                                 const int32_t* length_info, const pdecode_rope* rope,
+                                 float sm_scale, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
+                        rope, sm_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+pdecode_status pdecode_append_attention(const pdecode_desc* d, const void* new_k,
+                                        const void* new_v, const void* q, void* pages,
+                                        const int32_t* page_indptr, const int32_t* page_values,
+                                        const int32_t* length_info, const pdecode_rope* rope,
+                                        float sm_scale, void* out, float* lse, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (d && d->batch > 0 && (!new_k || !new_v)) return PDECODE_ERR_INVALID_ARG;
+  if (d && d->batch > 0 &&
+      !(d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN))
+    return check_desc(d) != PDECODE_OK ? check_desc(d) : PDECODE_ERR_UNSUPPORTED;
+  return attention_impl(d, new_k, new_v, q, pages, page_indptr, page_values, length_info, rope,
+                        sm_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
 pdecode_status pdecode_merge_state_inplace(int32_t n, int32_t num_heads, int32_t head_dim,

@@ -1,0 +1,743 @@
+// Persistent matrix-core decode (bf16 or fp8-e4m3fn KV, bf16 q): workgroups resident for the
+// whole call take (sequence, KV head, chunk) jobs from an atomic queue (TVM relax decode-kernels
+// page, _attention_decode, for the computation; the schedule is this library's). Included by
+// decode_mfma.hip (attention) and decode_fused.hip (attention with the fused KV append), which
+// instantiate it separately so the two compile in parallel.
+#pragma once
+
+#include <mutex>
+
+#include "device.hpp"
+#include "mfma_core.hpp"
+#include "split.hpp"
+
+namespace pdk {
+
+constexpr int kPWaves = 4;              // wavefronts per workgroup of the persistent schedule
+constexpr int kPersistMaxBatch = 1024;  // sequences the persistent schedule's LDS table holds
+
+// ------------------------------------------------------------------------------------------------
+// Persistent workgroups over a job queue.
+
+// Per-sequence table in LDS. Sequences are ranked by the size of their chunks, largest first (four
+// size classes, stable within a class), and jobs are numbered in that order: the queue hands out
+// long jobs first and ends with short ones, which shortens the tail of the call. Jobs of one
+// sequence are ordered chunk-major, KV head minor. What a job needs is stored by rank, so decoding
+// a job number takes two ballots and one round of LDS reads.
+struct SeqTable {
+  int4* geo;    // [B] by sequence: beg, np, total, win_off (multi-wave build only)
+  int4* rgeo;   // [B] by rank: the same
+  int4* rsb;    // [B] by rank: sink, sequence, chunks, slots per chunk (rounded down)
+  int* pre;     // [B + 1] by rank: first job of each rank (exclusive prefix); pre[B] = all jobs
+  int* njobs;   // [B] by sequence: chunks x H_kv
+  int* rnj;     // [B] by rank: the same
+  int* sink;    // [B] by sequence (multi-wave build only)
+  int2* rpos;   // [B] by rank, RoPE only: q position, position of attended row 0
+};
+
+__host__ __device__ inline size_t seq_table_bytes(int B) {
+  const size_t pre = size_t((B + 4) & ~3);
+  const size_t rest = size_t((B + 3) & ~3);
+  return size_t(B) * (16 + 16 + 16) + (pre + 3 * rest) * 4 + size_t(B) * 8;
+}
+
+__device__ inline SeqTable seq_table(int* base, int B) {
+  const int pre = (B + 4) & ~3;
+  const int rest = (B + 3) & ~3;
+  SeqTable t;
+  t.geo = reinterpret_cast<int4*>(base);
+  t.rgeo = t.geo + B;
+  t.rsb = t.rgeo + B;
+  t.pre = reinterpret_cast<int*>(t.rsb + B);
+  t.njobs = t.pre + pre;
+  t.rnj = t.njobs + rest;
+  t.sink = t.rnj + rest;
+  t.rpos = reinterpret_cast<int2*>(t.sink + rest);
+  return t;
+}
+
+// A job as one wave sees it (wave-uniform values).
+struct Job {
+  int valid;
+  int b, h, c, nch;
+  SeqGeom g;
+  int s_w;      // this wave's first slot
+  int nw;       // slots of this wave (may be 0)
+  int nitems;   // nw * SUB rounded up to even, at least 2: items past that are unused (re-reads)
+  int s_first;  // first slot of the chunk (its page serves the item of a wave without slots)
+  int qpos, kro;  // RoPE: position of q and of the sequence's attended row 0
+};
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory operations are
+// outstanding, and not for the export or LDS/scalar counters.
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) & 3) << 14 | 0x7 << 4 | 0xf << 8; }
+
+// ceil(2^32 / d) for d >= 2: __umulhi(r, it) is r / d or r / d + 1 for every 32-bit r.
+__device__ __forceinline__ uint32_t div_reciprocal(uint32_t d) { return 0xffffffffu / d + 1u; }
+
+// SUB: items per page slot (a 32-row page is walked as two 16-row items).
+template <int PS, int SUB, bool ROPE>
+__device__ __forceinline__ Job decode_job(const DecodeParams& p, const SeqTable& t, int total_jobs,
+                                          uint32_t hinv, int j, int w, int l) {
+  Job J;
+  J.valid = j < total_jobs;
+  J.b = J.h = J.c = J.nch = J.s_w = J.nw = J.s_first = J.qpos = J.kro = 0;
+  J.nitems = 2;
+  J.g = SeqGeom{0, 0, 0, 0, 0, 0, 0, 0};
+  if (!J.valid) return J;
+  // rank = the largest r with pre[r] <= j (pre is non-decreasing from pre[0] = 0; sequences
+  // without jobs repeat a value): a ballot over every S-th entry, then one over the S - 1 entries
+  // after the last one found
+  static_assert(kPersistMaxBatch <= 64 * 16, "two ballots cover the table");
+  const int S = (p.B + 63) >> 6;
+  int idx = l * S;
+  int rank = (__popcll(__ballot(idx < p.B && t.pre[idx] <= j)) - 1) * S;
+  if (S > 1) {
+    idx = rank + l;
+    rank += __popcll(__ballot(l >= 1 && l < S && idx < p.B && t.pre[idx] <= j));
+  }
+  rank = uni(rank);
+  const int4 gg = t.rgeo[rank];
+  const int4 sk_b = t.rsb[rank];
+  const int p0 = uni(t.pre[rank]);
+  const int b = uni(sk_b.y);
+  SeqGeom g;
+  g.beg = uni(gg.x);
+  g.np = uni(gg.y);
+  g.total = uni(gg.z);
+  g.win_off = uni(gg.w);
+  g.sink = uni(sk_b.x);
+  g.n0 = (g.sink + PS - 1) / PS;
+  g.first1 = g.win_off / PS;
+  g.n_slots = g.n0 + (g.win_off < g.total ? g.np - g.first1 : 0);
+  // job r of the sequence is chunk r / H_kv, KV head r % H_kv (hinv = div_reciprocal(H_kv))
+  const uint32_t r = uint32_t(j - p0);
+  uint32_t c = p.H_kv == 1 ? r : __umulhi(r, hinv);
+  c -= c * uint32_t(p.H_kv) > r ? 1u : 0u;
+  J.nch = uni(sk_b.z);
+  J.c = int(c);
+  J.h = int(r - c * uint32_t(p.H_kv));
+  J.b = b;
+  J.g = g;
+  if constexpr (ROPE) {
+    const int2 rp = t.rpos[rank];
+    J.qpos = uni(rp.x);
+    J.kro = uni(rp.y);
+  }
+  int sb, se;
+  const int q = uni(sk_b.w);
+  chunk_bounds_q(q, g.n_slots - q * J.nch, J.c, sb, se);
+  J.s_first = sb;
+  J.s_w = sb + w;
+  J.nw = J.s_w < se ? (se - J.s_w + kPWaves - 1) / kPWaves : 0;
+  J.nitems = max(2, (J.nw * SUB + 1) & ~1);
+  return J;
+}
+
+// Raw page-table entry of item k of a job for this wave. The load is unconditional (an invalid job
+// reads indptr[0] instead) and nothing consumes the value here, so the wait for it falls where the
+// id is used; clamp_page() clamps it into the pool there.
+__device__ __forceinline__ int load_id(const DecodeParams& p, const Job& J, int k) {
+  const int s = J.nw > 0 ? J.s_w + kPWaves * min(k, J.nw - 1) : J.s_first;
+  const int j = s < J.g.n0 ? s : J.g.first1 + (s - J.g.n0);
+  const int32_t* src = J.valid ? p.values + J.g.beg + min(j, J.g.np - 1) : p.indptr;
+  return *src;
+}
+__device__ __forceinline__ int clamp_page(const DecodeParams& p, int id) {
+  return min(max(id, 0), p.max_num_pages - 1);
+}
+
+// Fused append for a sequence that no job covers (no attended rows): every KV head's new K and V
+// rows go to the row of position total - 1 when the sequence has pages (the append kernel's
+// element arithmetic). All threads take part; one element per thread and step.
+template <int KVT, int D, int PS, int NT>
+__device__ void append_last_row(const DecodeParams& p, int b) {
+  const SeqGeom g = seq_geom(p.indptr, p.length_info, p.B, b, PS, p.sliding);
+  if (g.np == 0) return;
+  const size_t page = size_t(clamp_page(p, p.values[g.beg + g.np - 1]));
+  const int row = g.total - (g.np - 1) * PS - 1;
+  for (int idx = threadIdx.x; idx < 2 * p.H_kv * D; idx += NT) {
+    const int kv = idx / (p.H_kv * D);
+    const int h = (idx - kv * p.H_kv * D) / D;
+    const int d = idx % D;
+    const uint16_t x = static_cast<const uint16_t*>(kv ? p.new_v : p.new_k)[(size_t(b) * p.H_kv + h) * D + d];
+    const size_t dst = (((page * 2 + kv) * p.H_kv + h) * PS + row) * D + d;
+    if constexpr (KVT == kFP8) {
+      const float sc = (kv ? p.v_scale : p.k_scale)[h];
+      static_cast<uint8_t*>(p.pages_w)[dst] = f32_to_fp8(__fdiv_rn(bf16_to_f32(x), sc));
+    } else {
+      static_cast<uint16_t*>(p.pages_w)[dst] = x;
+    }
+  }
+}
+
+// Split sequences of calls with at most this many chunks are merged inside the persistent kernel.
+constexpr int kInMergeChunks = 8;
+
+// Merges the nch (2 .. kInMergeChunks) chunk states of (sequence b, KV head h), stored with
+// store_agent() and complete, into out and lse: M = max_c lse_c, w_c = 2^(lse_c - M),
+// out = sum_c w_c O_c / sum_c w_c, lse = M + log2(sum_c w_c). Thread t produces 4 dims of one q
+// head; every load is issued before any is used (one memory round trip). All threads take part.
+template <int D, int GP, int NT>
+__device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
+  constexpr int V = D / 4;
+  static_assert(GP * V <= NT, "one float4 of output per thread");
+  __shared__ float s_l[GP][kInMergeChunks];
+  const int tid = threadIdx.x;
+  const int G = p.G;
+  const size_t row0 = (size_t(b) * p.H_qo + size_t(h) * G) * p.num_chunks;
+  if (tid < G * nch) {
+    const int g = tid / nch;
+    s_l[g][tid - g * nch] = load_agent(&p.part_lse[row0 + size_t(g) * p.num_chunks + (tid - g * nch)]);
+  }
+  const int g = min(tid / V, G - 1);
+  const int v = tid % V;
+  const float* src = p.part_o + (row0 + size_t(g) * p.num_chunks) * D + 4 * v;
+  float o[kInMergeChunks][4];
+#pragma unroll
+  for (int c = 0; c < kInMergeChunks; ++c) {
+    if (c < nch) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[c][k] = load_agent(src + size_t(c) * D + k);
+    }
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kInMergeChunks; ++c)
+    if (c < nch) M = fmaxf(M, s_l[g][c]);
+  float ws = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kInMergeChunks; ++c) {
+    if (c < nch) {
+      const float wc = exp2_fast(s_l[g][c] - M);
+      ws += wc;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[k] = fmaf(wc, o[c][k], a[k]);
+    }
+  }
+  if (tid < G * V) {
+    const float inv = 1.f / ws;
+    const size_t orow = size_t(b) * p.H_qo + size_t(h) * G + g;
+    uint16_t* dst = static_cast<uint16_t*>(p.out) + orow * D + 4 * v;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(
+        uint32_t(f32_to_bf16(a[0] * inv)) | uint32_t(f32_to_bf16(a[1] * inv)) << 16,
+        uint32_t(f32_to_bf16(a[2] * inv)) | uint32_t(f32_to_bf16(a[3] * inv)) << 16);
+    if (v == 0) p.lse[orow] = M + log2f(ws);
+  }
+  __syncthreads();  // s_l is free again
+}
+
+// FUSED: the call also appends each sequence's new K/V row (p.new_k, p.new_v).
+template <int KVT, int D, int PS, int GP, bool ROPE, bool FUSED>
+__global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_mfma_persist_kernel(DecodeParams p) {
+  // items of 16 rows: a 32-row page is two items (half the registers per item in flight)
+  using C = MfmaCore<KVT, D, 16, GP, ROPE>;
+  constexpr int SUB = PS / 16;
+  constexpr int BLOCK = PS * C::ROW;  // bytes of one (page, K|V, head) block
+  using Buf = typename C::Buf;
+  constexpr int NT = 64 * kPWaves;
+  // q of the next job, staged in LDS by all threads: QW 32-bit words per thread
+  constexpr int QWORDS = GP * D / 2;
+  constexpr int QW = (QWORDS + NT - 1) / NT;
+  extern __shared__ __attribute__((aligned(16))) int s_dyn[];
+  __shared__ __attribute__((aligned(16))) float s_pt[kPWaves][16][C::PT_STRIDE];
+  __shared__ float s_alpha[kPWaves][16];
+  __shared__ float s_m[kPWaves][GP];
+  __shared__ float s_d[kPWaves][GP];
+  __shared__ __attribute__((aligned(16))) float s_o[kPWaves][GP][D];
+  __shared__ __attribute__((aligned(16))) uint32_t s_q[2][QW * NT];
+  // fused append: the new K and V rows of the current and the next job, in the pool's element type
+  __shared__ __attribute__((aligned(16))) uint32_t s_new[FUSED ? 2 : 1][FUSED ? 2 * C::ROW / 4 : 1];
+  __shared__ int s_ids[2][kPWaves][64];  // page-table entries of each wave's first 64 items
+  __shared__ int s_scan[kPWaves];
+  __shared__ unsigned long long s_scan64[kPWaves];
+  __shared__ int s_ticket;
+  __shared__ int s_mrg[kPWaves];  // wave w's arrival completed the previous job's split sequence
+  __shared__ float2 s_freq[ROPE ? D / 2 : 1];  // RoPE: frequencies (rope_freq) of dims i, i + D/2
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (wave-uniform)
+  const int l = tid & 63;
+  const int B = p.B;
+  const int G = p.G;
+  C core;
+  core.init_lane(l);
+  if constexpr (ROPE) {
+    if (tid < D / 2) {
+      float fhi, flo;
+      rope_freq(tid, D, p.rope_scale, p.rope_theta, fhi, flo);
+      s_freq[tid] = make_float2(fhi, flo);
+    }
+  }
+
+  // ---- job table: sequences ranked by chunk size (largest first), exclusive prefix of their
+  // jobs (chunks x H_kv) in rank order
+  const SeqTable tab = seq_table(s_dyn, B);
+  {
+    // size class of a sequence: 0 for chunks above 7/8 of chunk_slots, .. 3 for 5/8 and below
+    auto size_class = [&](int n_slots, int nch) {
+      const int sz = nch > 0 ? (n_slots + nch - 1) / nch : 0;
+      return 8 * sz > 7 * p.chunk_slots ? 0 : 8 * sz > 6 * p.chunk_slots ? 1
+             : 8 * sz > 5 * p.chunk_slots ? 2 : 3;
+    };
+    if (B <= 64) {
+      // One wave, lane b for sequence b: the rank counts the sequences of lower classes (ballots)
+      // and those of the same class before b (mbcnt); the job prefix is a wave scan.
+      if (w == 0) {
+        const bool ok = l < B;
+        const SeqGeom g = seq_geom(p.indptr, p.length_info, B, ok ? l : B - 1, PS, p.sliding);
+        const int nch = chunks_used(g.n_slots, p.chunk_slots, p.num_chunks);
+        const int nj = nch * p.H_kv;
+        const int c = ok ? size_class(g.n_slots, nch) : 4;
+        int rank = 0;
+        unsigned long long same = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const unsigned long long m = __ballot(c == k);
+          if (k < c) rank += __popcll(m);
+          if (k == c) same = m;
+        }
+        rank += __builtin_amdgcn_mbcnt_hi(uint32_t(same >> 32),
+                                          __builtin_amdgcn_mbcnt_lo(uint32_t(same), 0u));
+        if (ok) {
+          tab.njobs[l] = nj;
+          tab.rgeo[rank] = make_int4(g.beg, g.np, g.total, g.win_off);
+          tab.rsb[rank] = make_int4(g.sink, l, nch, nch > 0 ? g.n_slots / nch : 0);
+          tab.rnj[rank] = nj;
+          if constexpr (ROPE) tab.rpos[rank] = make_int2(p.q_pos[l], p.k_off[l]);
+        }
+        wave_lds_fence();
+        int x = ok ? tab.rnj[l] : 0;  // jobs of rank l, then the inclusive prefix
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(x, o, 64);
+          if (l >= o) x += y;
+        }
+        if (ok) tab.pre[l + 1] = x;
+        if (l == 0) tab.pre[0] = 0;
+      }
+      __syncthreads();
+    } else {
+      // Every thread takes `per` consecutive sequences; class counts and the job prefix are
+      // scanned over the workgroup.
+      const int per = (B + NT - 1) / NT;
+      const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+      unsigned long long cnt = 0;  // this thread's sequences per class, 16 bits each
+      for (int b = b0; b < b1; ++b) {
+        const SeqGeom g = seq_geom(p.indptr, p.length_info, B, b, PS, p.sliding);
+        tab.geo[b] = make_int4(g.beg, g.np, g.total, g.win_off);
+        tab.sink[b] = g.sink;
+        const int nch = chunks_used(g.n_slots, p.chunk_slots, p.num_chunks);
+        tab.njobs[b] = nch * p.H_kv;
+        cnt += 1ull << (16 * size_class(g.n_slots, nch));
+      }
+      unsigned long long x = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long y = __shfl_up(x, o, 64);
+        if (l >= o) x += y;
+      }
+      if (l == 63) s_scan64[w] = x;
+      __syncthreads();
+      unsigned long long off = x - cnt, total = 0;
+#pragma unroll
+      for (int ww = 0; ww < kPWaves; ++ww) {
+        if (ww < w) off += s_scan64[ww];
+        total += s_scan64[ww];
+      }
+      int cls_start[4];
+      int acc = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        cls_start[c] = acc + int((off >> (16 * c)) & 0xffff);
+        acc += int((total >> (16 * c)) & 0xffff);
+      }
+      for (int b = b0; b < b1; ++b) {
+        const int4 gg = tab.geo[b];
+        const int sk = tab.sink[b];
+        const int n0 = (sk + PS - 1) / PS;
+        const int n_slots = gg.y > 0 ? n0 + (gg.w < gg.z ? gg.y - gg.w / PS : 0) : 0;
+        const int nch = tab.njobs[b] / p.H_kv;
+        const int rank = cls_start[size_class(n_slots, nch)]++;
+        tab.rgeo[rank] = gg;
+        tab.rsb[rank] = make_int4(sk, b, nch, nch > 0 ? n_slots / nch : 0);
+        tab.rnj[rank] = tab.njobs[b];
+        if constexpr (ROPE) tab.rpos[rank] = make_int2(p.q_pos[b], p.k_off[b]);
+      }
+      __syncthreads();
+      int run = 0;
+      for (int r = b0; r < b1; ++r) {
+        run += tab.rnj[r];
+        tab.pre[r + 1] = run;
+      }
+      int y = run;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int z = __shfl_up(y, o, 64);
+        if (l >= o) y += z;
+      }
+      if (l == 63) s_scan[w] = y;
+      __syncthreads();
+      int off2 = y - run;
+      for (int ww = 0; ww < w; ++ww) off2 += s_scan[ww];
+      for (int r = b0; r < b1; ++r) tab.pre[r + 1] += off2;
+      if (tid == 0) tab.pre[0] = 0;
+      __syncthreads();
+    }
+  }
+  const int total_jobs = tab.pre[B];
+  const uint32_t hinv = div_reciprocal(uint32_t(max(p.H_kv, 2)));
+
+  // ---- sequences without attended rows: out = 0, lse = -5e4 (fused append: a sequence with pages
+  // still gets its new row, written by append_last_row)
+  for (int b = blockIdx.x; b < B; b += gridDim.x) {
+    if (tab.njobs[b] != 0) continue;
+    for (int idx = tid; idx < p.H_qo * D; idx += NT)
+      store_out<kBF16>(p.out, size_t(b) * p.H_qo * D + idx, 0.f);
+    for (int hq = tid; hq < p.H_qo; hq += NT) p.lse[size_t(b) * p.H_qo + hq] = kEmptyLse;
+    if constexpr (FUSED) append_last_row<KVT, D, PS, NT>(p, b);
+  }
+
+  const char* pool = static_cast<const char*>(p.pages);
+  const size_t kv_stride = size_t(p.H_kv) * BLOCK;
+  auto block_of = [&](int page, int h) {
+    return pool + (size_t(page) * 2 * p.H_kv + h) * BLOCK;
+  };
+  const uint32_t* qsrc = static_cast<const uint32_t*>(p.q);
+  // This thread's share of J's q rows (words past the G rows repeat the last one; an invalid job
+  // reads sequence 0's). Unconditional loads, consumed only when staged into LDS.
+  auto q_words = [&](const Job& J, uint32_t (&qs)[QW]) {
+    const size_t base = (size_t(J.b) * p.H_qo + size_t(J.h) * G) * (D / 2);
+#pragma unroll
+    for (int i = 0; i < QW; ++i) qs[i] = qsrc[base + min(tid + i * NT, G * D / 2 - 1)];
+  };
+
+  // ---- fused append (p.new_k set): thread t < 2 * D / 8 takes 8 elements of J's new K (t < D / 8)
+  // or V row: loads them with J's q words (new_words), then, once the loads are waited for,
+  // encodes them into the pool's element type (fp8: x / scale rounded to e4m3fn, as the append
+  // kernel), stages them in LDS for the item holding the row, and, in the sequence's last chunk,
+  // stores them to the row of position total - 1 (stage_new). Every thread of an invalid job reads
+  // sequence 0's rows and page-table entry 0, and nothing is staged or stored.
+  constexpr bool fused = FUSED;
+  constexpr int NV = D / 8;
+  struct NewWords {
+    uint4 x;    // 8 bf16 elements
+    int pid;    // page id of the sequence's last page
+    float sc;   // fp8: the row's scale
+  };
+  auto new_words = [&](const Job& J, NewWords& nw) __attribute__((always_inline)) {
+    const int t = min(tid, 2 * NV - 1);
+    const int kv = t >= NV;
+    const uint16_t* src = static_cast<const uint16_t*>(kv ? p.new_v : p.new_k) +
+                          (size_t(J.b) * p.H_kv + J.h) * D + 8 * (t - kv * NV);
+    nw.x = *reinterpret_cast<const uint4*>(src);
+    nw.pid = *(J.valid ? p.values + J.g.beg + J.g.np - 1 : p.indptr);
+    nw.sc = C::FP8 ? (kv ? p.v_scale : p.k_scale)[J.h] : 1.f;
+  };
+  auto stage_new = [&](const Job& J, const NewWords& nw, uint32_t* dst) __attribute__((always_inline)) {
+    if (!J.valid || tid >= 2 * NV) return;
+    const int kv = tid >= NV;
+    const int v = tid - kv * NV;
+    const int row = J.g.total - (J.g.np - 1) * PS - 1;  // last_page_len - 1
+    char* prow = static_cast<char*>(p.pages_w) +
+                 (size_t(clamp_page(p, nw.pid)) * 2 * p.H_kv + kv * p.H_kv + J.h) * BLOCK +
+                 row * C::ROW;
+    const bool store = J.c == J.nch - 1;
+    if constexpr (C::FP8) {
+      float f[8];
+      Kv<kBF16>::unpack(nw.x, f);
+      uint32_t w2[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        w2[q] = uint32_t(f32_to_fp8(__fdiv_rn(f[4 * q], nw.sc))) |
+                uint32_t(f32_to_fp8(__fdiv_rn(f[4 * q + 1], nw.sc))) << 8 |
+                uint32_t(f32_to_fp8(__fdiv_rn(f[4 * q + 2], nw.sc))) << 16 |
+                uint32_t(f32_to_fp8(__fdiv_rn(f[4 * q + 3], nw.sc))) << 24;
+      const uint2 o = make_uint2(w2[0], w2[1]);
+      *reinterpret_cast<uint2*>(dst + kv * (C::ROW / 4) + 2 * v) = o;
+      if (store) *reinterpret_cast<uint2*>(prow + 8 * v) = o;
+    } else {
+      *reinterpret_cast<uint4*>(dst + kv * (C::ROW / 4) + 4 * v) = nw.x;
+      if (store) *reinterpret_cast<uint4*>(prow + 16 * v) = nw.x;
+    }
+  };
+
+  // ---- the first two jobs are static, later ones come from the queue.
+  // The next job's page ids and q words, and the ticket of the job after it, are loaded at the top
+  // of the current job's first item and staged into LDS right after that item is computed (the
+  // wait for the item covers them); nothing loaded lives across items in registers, which keeps
+  // the compiler's memory-wait counts exact in the item loop.
+  int* queue = p.queue;
+  Job J = decode_job<PS, SUB, ROPE>(p, tab, total_jobs, hinv, blockIdx.x, w, l);
+  int par = 0;  // s_q[par] / s_ids[par] hold J's data, [par ^ 1] receive J1's
+  // J's page ids and q words are loaded first; J1 is decoded while they are in flight. (Issuing
+  // J's first item before the barrier, from each wave's own ids, keeps its registers live across
+  // the prologue and costs 12 VGPRs at the peak.)
+  const int ids0 = load_id(p, J, l);
+  uint32_t q0[QW];
+  q_words(J, q0);
+  NewWords nw0;
+  if constexpr (FUSED) new_words(J, nw0);
+  Job J1 = decode_job<PS, SUB, ROPE>(p, tab, total_jobs, hinv, blockIdx.x + gridDim.x, w, l);
+#pragma unroll
+  for (int i = 0; i < QW; ++i) s_q[0][tid + i * NT] = q0[i];
+  s_ids[0][w][l] = ids0;
+  if constexpr (FUSED) stage_new(J, nw0, s_new[0]);
+  __syncthreads();
+
+  if (J.valid) {
+    core.load_q(reinterpret_cast<const uint16_t*>(s_q[0]), G);
+    core.rope_q(J.qpos, s_freq);
+    float scale = p.score_scale * (C::FP8 ? p.k_scale[J.h] : 1.0f);
+    float vscale = C::FP8 ? p.v_scale[J.h] : 1.0f;
+    core.reset();
+    Buf buf0, buf1;
+    core.issue(buf0, block_of(clamp_page(p, uni(s_ids[0][w][0])), J.h), kv_stride);
+
+    // Page id of item k of the current job (slot k / SUB of the wave; refilled per 64 slots from
+    // the page table).
+    auto item_id = [&](int k) __attribute__((always_inline)) {
+      const int si = k / SUB;
+      if ((si & 63) == 0 && si > 0 && k % SUB == 0) {  // chunks of more than 64 slots per wave only
+        const int id = load_id(p, J, si + l);
+        wave_lds_fence();
+        s_ids[par][w][l] = id;
+        wave_lds_fence();
+      }
+      return s_ids[par][w][si & 63];
+    };
+    // Computes item k from `cur` (rows 16 (k % SUB) .. + 16 of slot k / SUB; items past the
+    // wave's slots are unused), then retires `cur`: only the loads just issued stay in flight.
+    auto compute = [&](Buf& cur, int k) __attribute__((always_inline)) {
+      const int si = k / SUB;
+      if (si < J.nw) {
+        int j, lo, hi;
+        slot_rows(J.g, J.s_w + kPWaves * si, PS, j, lo, hi);
+        const int r0 = 16 * (k % SUB);
+        if constexpr (FUSED) {
+          if (j == J.g.np - 1) {
+            // the sequence's last page: its row at position total - 1 is the appended one
+            const int rn = J.g.total - (J.g.np - 1) * PS - 1 - r0;
+            if (rn >= 0 && rn < 16) core.substitute(cur, rn, s_new[par]);
+          }
+        }
+        lo = max(lo - r0, 0);
+        hi = min(hi - r0, 16);
+        // RoPE position of the item's row 0: attended rows are numbered from the sequence's
+        // first one, so window pages shift by the rows the window skips (sink - win_off)
+        const int pos0 = J.kro + j * PS + r0 +
+                         (J.s_w + kPWaves * si < J.g.n0 ? 0 : J.g.sink - J.g.win_off);
+        if (lo < hi) core.process(cur, lo, hi, scale, s_pt[w], s_alpha[w], pos0, s_freq);
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NLOADS));
+    };
+    // Issues the loads of item `k`'s 16 rows (k % SUB selects the rows in the page).
+    auto issue_id = [&](Buf& nxt, int raw, int hh, int k) __attribute__((always_inline)) {
+      core.issue(nxt, block_of(clamp_page(p, uni(raw)), uni(hh)) + (k % SUB) * 16 * C::ROW,
+                 kv_stride);
+    };
+
+    // Split sequences are merged here when the call has few chunks. Each wave arrives at its
+    // sequence's counter once its own partial stores are known complete (in the next job's first
+    // pair, where they are older than the loads waited for); the workgroup whose wave brings the
+    // count to chunks x waves merges the sequence at the end of that next job. pb < 0: no
+    // arrival pending.
+    const bool in_merge = p.num_chunks <= kInMergeChunks;
+    int pb = -1, ph = 0, pnch = 0;
+
+    // Every job has an even number of items per wave, item k in buf0 for even k, so the next
+    // job's first item is always in flight in buf0 when a job ends: every path into the loops has
+    // the same loads in flight and the compiler's wait counts stay exact.
+    for (;;) {
+      // ---- items 0 and 1, with the loads for the next job (its page ids and q words, staged into
+      // LDS once item 1 is computed). The ticket of the job after the next one is taken in the
+      // last pair of items, so a workgroup holds at most one job beyond the current one.
+      {
+        const bool last = J.nitems == 2;
+        const int ids_n = load_id(p, J1, l);
+        uint32_t qs[QW];
+        q_words(J1, qs);
+        NewWords nw1;
+        if constexpr (FUSED) new_words(J1, nw1);
+        int ticket_raw = 0;
+        if (last && J1.valid && tid == 0) ticket_raw = atomicAdd(queue, 1);
+        issue_id(buf1, item_id(1), J.h, 1);
+        compute(buf0, 0);
+        // the previous job's partial stores are older than the loads just waited for
+        int arrival = 0;
+        if (pb >= 0 && l == 0)
+          arrival = __hip_atomic_fetch_add(&p.counters[pb * p.H_kv + ph], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+        if (!last) issue_id(buf0, item_id(2), J.h, 2);
+        else if (J1.valid) issue_id(buf0, __builtin_amdgcn_readlane(ids_n, 0), J1.h, 0);
+        else issue_id(buf0, item_id(1), J.h, 1);
+        compute(buf1, 1);
+#pragma unroll
+        for (int i = 0; i < QW; ++i) s_q[par ^ 1][tid + i * NT] = qs[i];
+        s_ids[par ^ 1][w][l] = ids_n;
+        if constexpr (FUSED) stage_new(J1, nw1, s_new[par ^ 1]);
+        if (last && tid == 0) s_ticket = 2 * int(gridDim.x) + ticket_raw;
+        if (l == 0) s_mrg[w] = pb >= 0 && arrival == pnch * kPWaves - 1;
+      }
+      // ---- items 2 .. nitems - 3
+      for (int k = 2; k + 2 < J.nitems; k += 2) {
+        issue_id(buf1, item_id(k + 1), J.h, k + 1);
+        compute(buf0, k);
+        issue_id(buf0, item_id(k + 2), J.h, k + 2);
+        compute(buf1, k + 1);
+      }
+      // ---- the last pair takes the ticket and issues the next job's first item
+      if (J.nitems > 2) {
+        const int k = J.nitems - 2;
+        int ticket_raw = 0;
+        if (J1.valid && tid == 0) ticket_raw = atomicAdd(queue, 1);
+        issue_id(buf1, item_id(k + 1), J.h, k + 1);
+        compute(buf0, k);
+        if (J1.valid) issue_id(buf0, s_ids[par ^ 1][w][0], J1.h, 0);
+        else issue_id(buf0, item_id(k + 1), J.h, k + 1);
+        compute(buf1, k + 1);
+        if (tid == 0) s_ticket = 2 * int(gridDim.x) + ticket_raw;
+      }
+
+      // ---- end of job J: merge the waves, store
+      core.to_lds(s_m[w], s_d[w], s_o[w]);
+      __syncthreads();
+      const int next_ticket = s_ticket;
+      int merge_prev = 0;  // s_mrg: written in this job's first pair, rewritten after the next barrier
+#pragma unroll
+      for (int ww = 0; ww < kPWaves; ++ww) merge_prev |= s_mrg[ww];
+#pragma unroll
+      for (int it = 0; it < (GP * D + NT - 1) / NT; ++it) {
+        const int idx = tid + it * NT;
+        if (idx < G * D) {
+          const int g = idx / D;
+          const int d = idx - g * D;
+          float M = -INFINITY;
+#pragma unroll
+          for (int ww = 0; ww < kPWaves; ++ww) M = fmaxf(M, s_m[ww][g]);
+          float wsum = 0.f, o = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < kPWaves; ++ww) {
+            const float f = exp2_fast(s_m[ww][g] - M);  // 0 for a wave without slots
+            wsum = fmaf(f, s_d[ww][g], wsum);
+            o = fmaf(f, s_o[ww][g][d], o);
+          }
+          const int hq = J.h * G + g;
+          const float val = o / wsum * vscale;
+          const float l2 = M + log2f(wsum);
+          if (J.nch == 1) {
+            store_out<kBF16>(p.out, (size_t(J.b) * p.H_qo + hq) * D + d, val);
+            if (d == 0) p.lse[size_t(J.b) * p.H_qo + hq] = l2;
+          } else {
+            const size_t row = (size_t(J.b) * p.H_qo + hq) * p.num_chunks + J.c;
+            if (in_merge) {
+              store_agent(&p.part_o[row * D + d], val);
+              if (d == 0) store_agent(&p.part_lse[row], l2);
+            } else {
+              p.part_o[row * D + d] = val;
+              if (d == 0) p.part_lse[row] = l2;
+            }
+          }
+        }
+      }
+      __syncthreads();  // s_m / s_d / s_o / s_ticket are free again
+      if (merge_prev) {
+        merge_split<D, GP, NT>(p, pb, ph, pnch);
+        if (tid == 0)
+          __hip_atomic_store(&p.counters[pb * p.H_kv + ph], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      pb = in_merge && J.nch > 1 ? J.b : -1;
+      ph = J.h;
+      pnch = J.nch;
+      if (!J1.valid) {
+        // no next job to hide the arrival behind: drain the stores, arrive, merge if last
+        if (pb >= 0) {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+          __syncthreads();  // every wave's partial stores are complete
+          if (tid == 0) {
+            const int t = __hip_atomic_fetch_add(&p.counters[pb * p.H_kv + ph], kPWaves,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_ticket = t == (pnch - 1) * kPWaves;
+          }
+          __syncthreads();
+          if (s_ticket) {
+            merge_split<D, GP, NT>(p, pb, ph, pnch);
+            if (tid == 0)
+              __hip_atomic_store(&p.counters[pb * p.H_kv + ph], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        break;
+      }
+      // ---- move on: J1 becomes current; decode the job after it
+      J = J1;
+      par ^= 1;
+      core.load_q(reinterpret_cast<const uint16_t*>(s_q[par]), G);
+      core.rope_q(J.qpos, s_freq);
+      if (C::FP8) {
+        scale = p.score_scale * p.k_scale[J.h];
+        vscale = p.v_scale[J.h];
+      }
+      core.reset();
+      J1 = decode_job<PS, SUB, ROPE>(p, tab, total_jobs, hinv, next_ticket, w, l);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+
+  // ---- the last workgroup out puts the queue back to zero for the next call
+  if (tid == 0 && atomicAdd(queue + 1, 1) == int(gridDim.x) - 1) {
+    __hip_atomic_store(queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(queue + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Workgroups of a kernel that fit on the current device at once (cached per kernel, device and
+// dynamic LDS size).
+inline int resident_workgroups(const void* kernel, size_t lds) {
+  struct Entry {
+    const void* k;
+    int dev;
+    size_t lds;
+    int n;
+  };
+  static std::mutex mu;
+  static Entry cache[64];
+  static int ncache = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < ncache; ++i)
+      if (cache[i].k == kernel && cache[i].dev == dev && cache[i].lds == lds) return cache[i].n;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kPWaves, lds) != hipSuccess)
+    return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const int n = per_cu * cus;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ncache < 64) cache[ncache++] = Entry{kernel, dev, lds, n};
+  return n;
+}
+
+template <int KVT, int D, int PS, int GP, bool ROPE, bool FUSED>
+hipError_t launch_persist_k(const DecodeParams& p, long long max_jobs, hipStream_t st) {
+  const void* k =
+      reinterpret_cast<const void*>(&decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE, FUSED>);
+  const size_t lds = seq_table_bytes(p.B);
+  const int resident = resident_workgroups(k, lds);
+  if (resident <= 0) return hipErrorInvalidConfiguration;
+  const unsigned grid = static_cast<unsigned>((max_jobs < resident ? (max_jobs > 0 ? max_jobs : 1) : resident));
+  hipLaunchKernelGGL((decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE, FUSED>), dim3(grid),
+                     dim3(64 * kPWaves), lds, st, p);
+  return hipGetLastError();
+}
+
+// The fused-append instantiations of launch_persist_k (decode_fused.hip).
+template <int KVT, int D, int PS, int GP, bool ROPE>
+hipError_t launch_persist_fused(const DecodeParams& p, long long max_jobs, hipStream_t st);
+
+}  // namespace pdk

@@ -30,6 +30,9 @@ struct DecodeParams {
   int* counters;             // split-KV arrival counters [B, H_kv]; zero between calls
   int* queue;                // persistent schedule: [0] next job ticket, [1] workgroups done;
                              // zero between calls
+  const void* new_k;         // fused append: the step's K and V rows [B, H_kv, D] (bf16), written
+  const void* new_v;         // to each sequence's last position; null: attention only
+  void* pages_w;             // fused append: the pool (the same memory as pages)
   int32_t B, H_qo, H_kv, G;
   int32_t max_num_pages;     // page ids are clamped into the pool before any KV address is formed
   int32_t sliding, rotary;

@@ -212,6 +212,22 @@ struct MfmaCore {
       bf.v[i] = *reinterpret_cast<const VT*>(vb + (NI * rg + i) * ROW + cv * 8 * EB);
   }
 
+  // Fused append: row rn of the item (loaded from the pool, whatever it held) is replaced by the
+  // staged new row `row` (K then V, ROW bytes each, in the pool's element type), in the registers
+  // that issue() loads it into.
+  __device__ __forceinline__ void substitute(Buf& bf, int rn, const uint32_t* row) const {
+    static_assert(RB == 1, "16-row items");
+    const uint4* nk = reinterpret_cast<const uint4*>(row);
+    const char* nv = reinterpret_cast<const char*>(row) + ROW;
+    if (n == rn) {
+#pragma unroll
+      for (int j = 0; j < KL; ++j) bf.k[j] = nk[4 * j + qg];  // bytes 16 (4 j + qg), as issue()
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (NI * rg + i == rn) bf.v[i] = *reinterpret_cast<const VT*>(nv + cv * 8 * EB);
+  }
+
   // Online-softmax update with one page whose attended rows are [lo, hi) (lo < hi).
   // s_pt: this wave's [16][PT_STRIDE] P^T tile; s_alpha: this wave's 16 rescale factors.
   // RoPE: row r of the item is at position pos0 + r; s_freq as in rope_q.

@@ -150,3 +150,21 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         pk._ptr(torch.zeros(3))
+
+
+def test_append_attention_argument_errors(L):
+    """pdecode_append_attention: null new rows, an fp32 pool and a batch beyond the persistent
+    schedule are refused before anything is launched; batch 0 is a no-op."""
+    f = L.pdecode_append_attention
+
+    def call(d, nk=FAKE, nv=FAKE):
+        return f(ctypes.byref(d), nk, nv, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.1, FAKE, FAKE,
+                 FAKE, 1 << 30, None)
+    assert call(desc(), nk=None) == 1
+    assert call(desc(), nv=None) == 1
+    assert call(desc(q_dtype="f32", kv_dtype="f32")) == 2
+    assert call(desc(batch=2000)) == 2
+    assert call(desc(kv_dtype="fp8")) == 1  # fp8 pool without scales
+    assert call(desc(batch=0), nk=None, nv=None) == 0
+    assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.1, FAKE, FAKE, FAKE, 0,
+             None) == 1

@@ -566,3 +566,100 @@ def test_large_batch_rope(kv, G, ps):
                             page_size=ps, seq_lens=lens, seed=860 + G + ps, max_num_pages=pages,
                             kv_dtype=kv, rotary_mode=1, rope_theta=500000.0, window=1500, sink=4)
     run_and_check(w)
+
+
+# ---- fused decode step: pdecode_append_attention
+
+def _poison_last_rows(w):
+    """NaN in every sequence's row of position total - 1 (all heads, K and V): the fused call must
+    take that row from the new values, never from the pool."""
+    slots = oracle.last_position_slots(B=w.B, ps=w.page_size, indptr=w.page_indptr,
+                                       values=w.page_values, length_info=w.length_info)
+    nan = {"bf16": 0x7FC0, "fp8": 0x7F}[w.kv_dtype]
+    for s in slots[slots >= 0]:
+        w.pages[s // w.page_size, :, :, s % w.page_size, :] = nan
+
+
+def _fused_case(w, seed, num_kv_splits=0):
+    _poison_last_rows(w)
+    nk, nv, _ = synth.append_inputs(T=w.B, H_kv=w.H_kv, D=w.D, page_size=w.page_size,
+                                    max_num_pages=w.max_num_pages, in_dtype="bf16", seed=seed,
+                                    slots=np.zeros(w.B, np.int32))
+    o_ref, l_ref, pool_ref = oracle.append_then_decode(new_k=nk, new_v=nv, **w.oracle_kwargs())
+    dev = gu.upload(w)
+    desc = gu.desc_for(w, dev, num_kv_splits)
+    out = torch.empty((w.B, w.H_qo, w.D), dtype=torch.bfloat16, device="cuda")
+    out.view(torch.int16).fill_(0x7FC0)
+    lse = torch.full((w.B, w.H_qo), float("nan"), dtype=torch.float32, device="cuda")
+    rope = None
+    if w.rotary_mode:
+        rope = pk.make_rope(rotary_mode=w.rotary_mode, rope_scale=w.rope_scale,
+                            rope_theta=w.rope_theta, q_rope_position=dev["q_pos"],
+                            k_rope_pos_offset=dev["k_off"])
+    ws = pk.alloc_workspace(desc)
+    nk_d = gu.to_device_storage(nk, "bf16")
+    nv_d = gu.to_device_storage(nv, "bf16")
+    pk.append_attention(desc, nk_d, nv_d, dev["q"], dev["pages"], dev["indptr"], dev["values"],
+                        dev["length_info"], out, lse, w.sm_scale, rope=rope, workspace=ws)
+    torch.cuda.synchronize()
+    # the pool: bit-exact against the oracle's append, every byte of it
+    pool_gpu = dev["pages"].view(torch.uint8).cpu().numpy().reshape(-1)
+    assert np.array_equal(pool_gpu, np.ascontiguousarray(pool_ref).view(np.uint8).reshape(-1)), \
+        f"{w.name}: pool differs from the oracle's append"
+    tol_o, tol_l = gu.tolerance(w)
+    o_gpu, l_gpu = gu.to_np64(out), gu.to_np64(lse)
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(l_gpu)), w.name
+    do = np.abs(o_gpu - o_ref).max(initial=0)
+    dl = np.abs(l_gpu - l_ref).max(initial=0)
+    print(f"{w.name}: fused max|dout|={do:.3g} max|dlse|={dl:.3g}", flush=True)
+    assert do <= tol_o and dl <= tol_l, (w.name, do, dl)
+    # the same as the two separate calls on the updated pool, bit for bit
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    pk.attention(desc, dev["q"], dev["pages"], dev["indptr"], dev["values"], dev["length_info"],
+                 out2, lse2, w.sm_scale, rope=rope, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), w.name
+    assert torch.equal(lse, lse2), w.name
+
+
+import paged_kv_decode_08_amd as pk  # noqa: E402  (the fixture above loads the library)
+
+
+@pytest.mark.parametrize("kv,G,D,ps", [("bf16", 4, 128, 16), ("bf16", 1, 64, 32),
+                                       ("bf16", 8, 128, 16), ("fp8", 8, 128, 32),
+                                       ("fp8", 2, 64, 16)])
+def test_append_attention(kv, G, D, ps):
+    """Fused append + decode against the oracle (append_kv at each sequence's last position, then
+    decode): lengths at and around page boundaries, a one-row sequence and one without pages."""
+    lens = [1, ps, ps + 1, 3 * ps - 1, 700, 0, 2 * ps]
+    w = synth.make_workload(name=f"fused_{kv}_G{G}_D{D}_ps{ps}", B=len(lens), H_qo=2 * G,
+                            H_kv=2, D=D, page_size=ps, seq_lens=lens, q_dtype="bf16",
+                            kv_dtype=kv, seed=700 + G + D + ps, max_num_pages=256)
+    _fused_case(w, seed=71 + G)
+
+
+@pytest.mark.parametrize("splits", [3, 12])
+def test_append_attention_split(splits):
+    """Forced splits: merged in the kernel (3 chunks) and by the split merge kernel (12)."""
+    w = synth.make_workload(name=f"fused_split{splits}", B=4, H_qo=16, H_kv=4, D=128,
+                            page_size=16, seq_lens=[3000, 17, 1200, 640], seed=720 + splits,
+                            max_num_pages=512)
+    _fused_case(w, seed=73, num_kv_splits=splits)
+
+
+def test_append_attention_rope_window():
+    """RoPE and a sliding window with a sink: the new row is the window's last (RoPE rotates it
+    like any K row); one sequence shorter than the window."""
+    w = synth.make_workload(name="fused_rope_swa", B=4, H_qo=32, H_kv=8, D=128, page_size=16,
+                            seq_lens=[5000, 300, 4100, 2049], seed=730, max_num_pages=1024,
+                            window=1024, sink=4, rotary_mode=1, rope_theta=500000.0)
+    _fused_case(w, seed=74)
+
+
+def test_append_attention_no_attended_rows():
+    """An empty window without a sink: no row is attended (out = 0, lse = -5e4), yet every
+    sequence with pages still gets its new row."""
+    w = synth.make_workload(name="fused_empty_win", B=3, H_qo=8, H_kv=2, D=128, page_size=16,
+                            seq_lens=[40, 0, 16], seed=740, max_num_pages=64, window=0, sink=0)
+    _fused_case(w, seed=75)

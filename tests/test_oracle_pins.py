@@ -470,3 +470,58 @@ def test_oracle_rejects_out_of_range_page():
     vals[-1] = 99
     with pytest.raises(oracle.OracleError):
         run_oracle(w, values=vals)
+
+
+# ---- fused decode step (append at each sequence's last position, then decode)
+
+def test_last_position_slots_brute_force():
+    """The slot of position total - 1, found by walking every position of every sequence through
+    the page table (position p -> page values[beg + p // ps], row p % ps), for lengths at and
+    around page boundaries, an empty sequence and shuffled page ids."""
+    ps = 4
+    lens = [0, 1, 3, 4, 5, 8, 9, 13]
+    B = len(lens)
+    npages = [(L + ps - 1) // ps for L in lens]
+    indptr = np.concatenate([[0], np.cumsum(npages)]).astype(np.int32)
+    values = np.random.default_rng(3).permutation(64)[: indptr[-1]].astype(np.int32)
+    last = np.array([L - (n - 1) * ps if n else 0 for L, n in zip(lens, npages)], np.int32)
+    got = oracle.last_position_slots(B=B, ps=ps, indptr=indptr, values=values, length_info=last)
+    for b, L in enumerate(lens):
+        want = -1
+        for pos in range(L):
+            want = int(values[indptr[b] + pos // ps]) * ps + pos % ps
+        assert got[b] == want, (b, L)
+    # with a window the row is the same: length_info row 0 is still last_page_len
+    li3 = np.stack([last, np.zeros(B, np.int32), np.zeros(B, np.int32)])
+    got3 = oracle.last_position_slots(B=B, ps=ps, indptr=indptr, values=values, length_info=li3)
+    assert np.array_equal(got3, got)
+
+
+def test_append_then_decode_single_row_is_the_new_row():
+    """Sequences of one row: after the step that row is the new token, so out = new_v of the KV
+    head and lse = sm_scale * (q . new_k) * log2 e (the L = 1 closed form), whatever the pool held
+    there before (here NaN); a sequence without pages gets no row and the empty convention."""
+    B, H_kv, G, D, ps = 3, 2, 2, 8, 4
+    H_qo = H_kv * G
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((B, H_qo, D)).astype(np.float32)
+    pages = np.full((6, 2, H_kv, ps, D), np.nan, np.float32)
+    indptr = np.array([0, 1, 1, 2], np.int32)
+    values = np.array([4, 1], np.int32)
+    last = np.array([1, 0, 1], np.int32)
+    nk = rng.standard_normal((B, H_kv, D)).astype(np.float32)
+    nv = rng.standard_normal((B, H_kv, D)).astype(np.float32)
+    sm = float(np.float32(0.3))  # the oracle takes sm_scale as the fp32 value the ABI receives
+    out, lse, pool = oracle.append_then_decode(
+        new_k=nk, new_v=nv, B=B, H_qo=H_qo, H_kv=H_kv, D=D, ps=ps, max_num_pages=6, q_dtype=0,
+        kv_dtype=0, q=q, pages=pages, indptr=indptr, values=values, length_info=last,
+        sm_scale=sm)
+    for b in (0, 2):
+        for h in range(H_qo):
+            hk = h // G
+            assert np.array_equal(out[b, h], nv[b, hk].astype(np.float64))
+            s = sm * float(np.dot(q[b, h].astype(np.float64), nk[b, hk].astype(np.float64)))
+            assert abs(lse[b, h] - s * LOG2E) < 1e-12
+    assert np.all(out[1] == 0) and np.all(lse[1] == -5e4)
+    assert np.array_equal(pool[4, 0, :, 0], nk[0]) and np.array_equal(pool[1, 1, :, 0], nv[2])
+    assert np.isnan(pool[4, 0, :, 1:]).all()  # nothing else written
