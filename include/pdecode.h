@@ -8,6 +8,8 @@
  *                                RoPE on Q and K, optional sliding window with attention sink.
  *   pdecode_merge_state_inplace  Same page, _merge_state_inplace: combine two attention states
  *                                (V, lse) in place.
+ *   pdecode_attention_multi      Several query tokens per sequence, causal over the new tokens
+ *                                (the same page's decode per token, over its visible prefix).
  *   pdecode_append_attention     pdecode_append_kv of each sequence's newest token fused into
  *                                pdecode_attention (one launch).
  *   pdecode_append_kv            vLLM nki_flash_attn page, reshape_and_cache: write new K/V rows
@@ -130,6 +132,26 @@ pdecode_status pdecode_attention(const pdecode_desc *d, const void *q, const voi
                                  const int32_t *length_info, const pdecode_rope *rope,
                                  float sm_scale, void *out, float *lse, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/* Decode with qo_len query tokens per sequence, causal over the new tokens (speculative
+ * verification, chunked decode): the sequence's last qo_len positions hold the new tokens, already
+ * in the pool, and token t (0-based) attends the positions 0 .. total_b - qo_len + t. Each token's
+ * result is that of pdecode_attention over that prefix of the sequence (TVM relax decode-kernels
+ * page, _attention_decode); a token whose prefix is empty (total_b < qo_len - t) gets out = 0 and
+ * lse = -5e4, as a sequence without pages does.
+ * q, out: device [batch, qo_len, num_qo_heads, head_dim] (q_dtype); lse: fp32 [batch, qo_len,
+ * num_qo_heads]. The other arguments are those of pdecode_attention, without RoPE; the workspace
+ * is sized by pdecode_workspace_bytes_multi(d, qo_len), with the same reuse rules.
+ * qo_len == 1 is pdecode_attention. Supported for qo_len > 1: no sliding window,
+ * (num_qo_heads / num_kv_heads) * qo_len <= 8, and the persistent matrix-core schedule (BF16 or
+ * FP8_E4M3FN pool, batch <= 1024); otherwise UNSUPPORTED. Errors: as pdecode_attention, and
+ * INVALID_ARG for qo_len < 1. */
+size_t pdecode_workspace_bytes_multi(const pdecode_desc *d, int32_t qo_len);
+pdecode_status pdecode_attention_multi(const pdecode_desc *d, int32_t qo_len, const void *q,
+                                       const void *pages, const int32_t *page_indptr,
+                                       const int32_t *page_values, const int32_t *length_info,
+                                       float sm_scale, void *out, float *lse, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /* One decode step with its KV append fused into the attention launch: for every sequence b with
  * pages and every KV head h, new_k[b, h, :] and new_v[b, h, :] are written to the sequence's row

@@ -131,6 +131,43 @@ def append_kv(*, pages, new_k, new_v, slots, H_kv, D, ps, in_dtype, kv_dtype, k_
     return pages
 
 
+def decode_multi(*, qo_len, q, **kw):
+    """Decode with qo_len query tokens per sequence (q [B, qo_len, H_qo, D]), causal over the new
+    tokens: the last qo_len positions of each sequence are the new tokens, and token t attends
+    positions 0 .. total - qo_len + t, i.e. it is the TVM page's single-token decode over that
+    prefix of the sequence (its first ceil(len / ps) pages, the last one holding len - (np - 1) ps
+    rows). An empty prefix gives the empty convention. No window. Returns (out [B, T, H_qo, D],
+    lse [B, T, H_qo])."""
+    B, T, ps = kw["B"], int(qo_len), kw["ps"]
+    assert not kw.get("sliding_window"), "several query tokens: no sliding window"
+    indptr = np.asarray(kw["indptr"], np.int64)
+    values = np.asarray(kw["values"], np.int64)
+    last = np.asarray(kw["length_info"], np.int64).reshape(-1)[:B]
+    ip2, val2, last2 = [0], [], []
+    for b in range(B):
+        npg = int(indptr[b + 1] - indptr[b])
+        total = (npg - 1) * ps + int(last[b]) if npg else 0
+        for t in range(T):
+            n = total - T + t + 1  # rows token t sees
+            if n <= 0:
+                ip2.append(ip2[-1])
+                last2.append(0)
+                continue
+            k = (n + ps - 1) // ps
+            val2.extend(values[indptr[b]:indptr[b] + k].tolist())
+            ip2.append(ip2[-1] + k)
+            last2.append(n - (k - 1) * ps)
+    kw = dict(kw)
+    kw.update(B=B * T, indptr=np.array(ip2, np.int32), values=np.array(val2, np.int32),
+              length_info=np.array(last2, np.int32), q=np.ascontiguousarray(q).reshape(
+                  B * T, kw["H_qo"], kw["D"]))
+    for key in ("q_rope_position", "k_rope_pos_offset"):
+        kw.pop(key, None)
+    kw.pop("rotary_mode", None)
+    out, lse = decode(**kw)
+    return out.reshape(B, T, kw["H_qo"], kw["D"]), lse.reshape(B, T, kw["H_qo"])
+
+
 def last_position_slots(*, B, ps, indptr, values, length_info):
     """Pool slot (page * ps + row) of each sequence's position total - 1, the row a decode step's
     new token occupies: its last page page_values[indptr[b+1] - 1], row last_page_len[b] - 1 (the

@@ -64,6 +64,11 @@ def lib() -> ctypes.CDLL:
         L.pdecode_attention.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P,
                                         ctypes.POINTER(Rope), ctypes.c_float, P, P, P,
                                         ctypes.c_size_t, P]
+        L.pdecode_workspace_bytes_multi.restype = ctypes.c_size_t
+        L.pdecode_workspace_bytes_multi.argtypes = [ctypes.POINTER(Desc), _c_i32]
+        L.pdecode_attention_multi.restype = _c_i32
+        L.pdecode_attention_multi.argtypes = [ctypes.POINTER(Desc), _c_i32, P, P, P, P, P,
+                                              ctypes.c_float, P, P, P, ctypes.c_size_t, P]
         L.pdecode_append_attention.restype = _c_i32
         L.pdecode_append_attention.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P, P, P,
                                                ctypes.POINTER(Rope), ctypes.c_float, P, P, P,
@@ -155,6 +160,25 @@ def attention(desc: Desc, q, pages, page_indptr, page_values, length_info, out, 
                                  ws_bytes, _stream(stream))
     if st:
         raise PdecodeError(st, "pdecode_attention")
+
+
+def alloc_workspace_multi(desc: Desc, qo_len: int, device="cuda") -> torch.Tensor | None:
+    """A zero-filled workspace of pdecode_workspace_bytes_multi(desc, qo_len) bytes, or None."""
+    n = int(lib().pdecode_workspace_bytes_multi(ctypes.byref(desc), int(qo_len)))
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def attention_multi(desc: Desc, qo_len: int, q, pages, page_indptr, page_values, length_info,
+                    out, lse, sm_scale, workspace=None, stream=None) -> None:
+    """pdecode_attention_multi: q/out [B, qo_len, H_qo, D], lse [B, qo_len, H_qo]; token t of a
+    sequence attends its positions up to total - qo_len + t."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().pdecode_attention_multi(ctypes.byref(desc), int(qo_len), _ptr(q), _ptr(pages),
+                                       _ptr(page_indptr), _ptr(page_values), _ptr(length_info),
+                                       float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                       ws_bytes, _stream(stream))
+    if st:
+        raise PdecodeError(st, "pdecode_attention_multi")
 
 
 def append_attention(desc: Desc, new_k, new_v, q, pages, page_indptr, page_values, length_info,

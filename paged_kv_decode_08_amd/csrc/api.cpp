@@ -61,7 +61,7 @@ pdecode_status check_attention_shape(const pdecode_desc* d) {
 // is computed exactly; max_kv_len only sizes the grid.
 // rope: the call applies RoPE (bf16 KV, or fp8 KV at head_dim 128: the matrix-core kernels, planned
 // as without RoPE; otherwise the vector-ALU kernel).
-Plan make_plan(const pdecode_desc* d, bool rope) {
+Plan make_plan(const pdecode_desc* d, bool rope, int qo_len = 1) {
   Plan pl;
   const int64_t ps = d->page_size;
   const int64_t max_len = d->max_kv_len > 0 ? d->max_kv_len : int64_t(d->max_num_pages) * ps;
@@ -94,7 +94,7 @@ Plan make_plan(const pdecode_desc* d, bool rope) {
   pl.num_chunks = static_cast<int32_t>(n);
   pl.persistent = persistent;
   if (pl.num_chunks > 1) {
-    const size_t rows = size_t(d->batch) * d->num_qo_heads * pl.num_chunks;
+    const size_t rows = size_t(d->batch) * qo_len * d->num_qo_heads * pl.num_chunks;
     pl.part_o_bytes = align256(rows * d->head_dim * sizeof(float));
     pl.part_lse_bytes = align256(rows * sizeof(float));
   }
@@ -148,11 +148,13 @@ namespace {
 
 // pdecode_attention, and with new_k / new_v set the fused append of pdecode_append_attention
 // (the persistent matrix-core schedule only).
+// qo_len > 1: several query tokens per sequence (pdecode_attention_multi; no RoPE, no window).
 pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const void* new_v,
                               const void* q, const void* pages, const int32_t* page_indptr,
                               const int32_t* page_values, const int32_t* length_info,
                               const pdecode_rope* rope, float sm_scale, void* out, float* lse,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              int qo_len = 1) {
   const bool fused = new_k != nullptr;
   pdecode_status st = check_desc(d);
   if (st != PDECODE_OK) return st;
@@ -166,8 +168,8 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   if (d->batch == 0) return PDECODE_OK;
   if (!q || !pages || !page_indptr || !page_values || !length_info || !out || !lse)
     return PDECODE_ERR_INVALID_ARG;
-  const Plan pl = make_plan(d, rotary);
-  if (fused && !pl.persistent) return PDECODE_ERR_UNSUPPORTED;
+  const Plan pl = make_plan(d, rotary, qo_len);
+  if ((fused || qo_len > 1) && !pl.persistent) return PDECODE_ERR_UNSUPPORTED;
   const int64_t grid = int64_t(pl.num_chunks) * d->batch * d->num_kv_heads;
   if (grid > INT_MAX) return PDECODE_ERR_UNSUPPORTED;
   if (pl.workspace_bytes() > 0) {
@@ -200,6 +202,7 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   p.H_qo = d->num_qo_heads;
   p.H_kv = d->num_kv_heads;
   p.G = d->num_qo_heads / d->num_kv_heads;
+  p.T = qo_len;
   p.max_num_pages = d->max_num_pages;
   p.sliding = d->sliding_window;
   p.rotary = rotary ? 1 : 0;
@@ -208,7 +211,8 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   p.score_scale = sm_scale * pdk::kLog2e;
   p.chunk_slots = pl.chunk_slots;
   p.num_chunks = pl.num_chunks;
-  const int gp = p.G <= 1 ? 1 : p.G <= 2 ? 2 : p.G <= 4 ? 4 : 8;
+  const int cols = p.G * qo_len;  // q columns of the matrix-core B operand
+  const int gp = cols <= 1 ? 1 : cols <= 2 ? 2 : cols <= 4 ? 4 : 8;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // bf16 / fp8 KV: q.K on the matrix cores (4-wave workgroups, persistent over a job queue up to
   // kPersistMaxBatch sequences, else one per chunk), RoPE included for bf16 KV and for fp8 KV at
@@ -235,6 +239,29 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
                                  size_t workspace_bytes, void* stream) {
   return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
                         rope, sm_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t pdecode_workspace_bytes_multi(const pdecode_desc* d, int32_t qo_len) {
+  if (qo_len < 1) return 0;
+  if (check_desc(d) != PDECODE_OK || check_attention_shape(d) != PDECODE_OK) return 0;
+  return make_plan(d, false, qo_len).workspace_bytes();
+}
+
+pdecode_status pdecode_attention_multi(const pdecode_desc* d, int32_t qo_len, const void* q,
+                                       const void* pages, const int32_t* page_indptr,
+                                       const int32_t* page_values, const int32_t* length_info,
+                                       float sm_scale, void* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  pdecode_status st = check_desc(d);
+  if (st != PDECODE_OK) return st;
+  if (qo_len < 1) return PDECODE_ERR_INVALID_ARG;
+  if (qo_len == 1)
+    return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
+                          nullptr, sm_scale, out, lse, workspace, workspace_bytes, stream);
+  if (d->sliding_window) return PDECODE_ERR_UNSUPPORTED;
+  if (int64_t(qo_len) * (d->num_qo_heads / d->num_kv_heads) > 8) return PDECODE_ERR_UNSUPPORTED;
+  return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
+                        nullptr, sm_scale, out, lse, workspace, workspace_bytes, stream, qo_len);
 }
 
 pdecode_status pdecode_append_attention(const pdecode_desc* d, const void* new_k,

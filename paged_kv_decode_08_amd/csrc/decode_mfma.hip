@@ -192,8 +192,8 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
   static_assert(64 % CB == 0 || CB % 64 == 0, "batches and lse words line up");
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kMergeRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (row >= p.B * p.H_qo) return;
-  const int b = row / p.H_qo;
+  if (row >= p.B * p.T * p.H_qo) return;  // rows [B, T, H_qo]
+  const int b = row / (p.T * p.H_qo);
   const int nc = p.num_chunks;
   const float* lse_c = p.part_lse + size_t(row) * nc;
   const float* o_c = p.part_o + size_t(row) * nc * D;
@@ -213,7 +213,9 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
   for (int c = 64 + lane; c < nch; c += 64) mx = fmaxf(mx, lse_c[c]);
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  const float M = mx;
+  // several query tokens: a token that sees no row of the sequence has every chunk lse -inf
+  const bool none = mx == -INFINITY;
+  const float M = none ? 0.f : mx;
   const float w_l = lane < nch ? exp2_fast(lse_l - M) : 0.f;  // weight of chunk `lane`
   float ws = w_l;
   for (int c = 64 + lane; c < nch; c += 64) ws += exp2_fast(lse_c[c] - M);
@@ -245,14 +247,14 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
   }
   if (nch <= 1) return;  // unsplit (or empty) sequence: the decode kernel wrote its row
   if (lane < V) {
-    const float inv = 1.f / ws;
+    const float inv = none ? 0.f : 1.f / ws;
     uint16_t* dst = static_cast<uint16_t*>(p.out) + size_t(row) * D + 4 * lane;
     const uint2 packed = make_uint2(
         uint32_t(f32_to_bf16(acc.x * inv)) | uint32_t(f32_to_bf16(acc.y * inv)) << 16,
         uint32_t(f32_to_bf16(acc.z * inv)) | uint32_t(f32_to_bf16(acc.w * inv)) << 16);
     *reinterpret_cast<uint2*>(dst) = packed;
   }
-  if (lane == 0) p.lse[row] = M + log2f(ws);
+  if (lane == 0) p.lse[row] = none ? kEmptyLse : M + log2f(ws);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -267,10 +269,16 @@ static hipError_t launch_chunked(const DecodeParams& p, unsigned grid, hipStream
 
 template <int KVT, int D, int PS, int GP, bool ROPE>
 static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipStream_t st) {
-  hipError_t e = p.new_k != nullptr ? launch_persist_fused<KVT, D, PS, GP, ROPE>(p, max_jobs, st)
-                                    : launch_persist_k<KVT, D, PS, GP, ROPE, false>(p, max_jobs, st);
+  hipError_t e;
+  if (p.T > 1) {
+    if constexpr (ROPE) return hipErrorInvalidValue;  // several query tokens: no RoPE
+    else e = launch_persist_multi<KVT, D, PS, GP>(p, max_jobs, st);
+  } else {
+    e = p.new_k != nullptr ? launch_persist_fused<KVT, D, PS, GP, ROPE>(p, max_jobs, st)
+                           : launch_persist_k<KVT, D, PS, GP, ROPE, false>(p, max_jobs, st);
+  }
   if (e != hipSuccess || p.num_chunks <= 1 || p.num_chunks <= kInMergeChunks) return e;
-  const unsigned rows = static_cast<unsigned>(p.B) * p.H_qo;
+  const unsigned rows = static_cast<unsigned>(p.B) * p.T * p.H_qo;
   hipLaunchKernelGGL((split_merge_kernel<D, PS>), dim3((rows + kMergeRows - 1) / kMergeRows),
                      dim3(64 * kMergeRows), 0, st, p);
   return hipGetLastError();

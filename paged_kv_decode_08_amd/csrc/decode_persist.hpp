@@ -180,21 +180,33 @@ constexpr int kInMergeChunks = 8;
 // store_agent() and complete, into out and lse: M = max_c lse_c, w_c = 2^(lse_c - M),
 // out = sum_c w_c O_c / sum_c w_c, lse = M + log2(sum_c w_c). Thread t produces 4 dims of one q
 // head; every load is issued before any is used (one memory round trip). All threads take part.
-template <int D, int GP, int NT>
+// Output row of q column c of (sequence b, KV head h): columns are token-major (token c / G, q
+// head h G + c % G); with one token, c is the q head's index in the group.
+template <bool MT>
+__device__ __forceinline__ size_t out_row(const DecodeParams& p, int b, int h, int c) {
+  if constexpr (MT)
+    return (size_t(b) * p.T + c / p.G) * p.H_qo + size_t(h) * p.G + c % p.G;
+  else
+    return size_t(b) * p.H_qo + size_t(h) * p.G + c;
+}
+
+// MT: several query tokens (p.T): G T columns, and a column whose token sees no row of the
+// sequence (all chunk lse -inf) gives out = 0, lse = -5e4.
+template <int D, int GP, int NT, bool MT = false>
 __device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
   constexpr int V = D / 4;
   static_assert(GP * V <= NT, "one float4 of output per thread");
   __shared__ float s_l[GP][kInMergeChunks];
   const int tid = threadIdx.x;
-  const int G = p.G;
-  const size_t row0 = (size_t(b) * p.H_qo + size_t(h) * G) * p.num_chunks;
+  const int G = MT ? p.G * p.T : p.G;  // columns
   if (tid < G * nch) {
     const int g = tid / nch;
-    s_l[g][tid - g * nch] = load_agent(&p.part_lse[row0 + size_t(g) * p.num_chunks + (tid - g * nch)]);
+    s_l[g][tid - g * nch] =
+        load_agent(&p.part_lse[out_row<MT>(p, b, h, g) * p.num_chunks + (tid - g * nch)]);
   }
   const int g = min(tid / V, G - 1);
   const int v = tid % V;
-  const float* src = p.part_o + (row0 + size_t(g) * p.num_chunks) * D + 4 * v;
+  const float* src = p.part_o + out_row<MT>(p, b, h, g) * p.num_chunks * D + 4 * v;
   float o[kInMergeChunks][4];
 #pragma unroll
   for (int c = 0; c < kInMergeChunks; ++c) {
@@ -208,6 +220,8 @@ __device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
 #pragma unroll
   for (int c = 0; c < kInMergeChunks; ++c)
     if (c < nch) M = fmaxf(M, s_l[g][c]);
+  const bool none = MT && M == -INFINITY;
+  if (MT && none) M = 0.f;
   float ws = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < kInMergeChunks; ++c) {
@@ -219,19 +233,21 @@ __device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
     }
   }
   if (tid < G * V) {
-    const float inv = 1.f / ws;
-    const size_t orow = size_t(b) * p.H_qo + size_t(h) * G + g;
+    const float inv = none ? 0.f : 1.f / ws;
+    const size_t orow = out_row<MT>(p, b, h, g);
     uint16_t* dst = static_cast<uint16_t*>(p.out) + orow * D + 4 * v;
     *reinterpret_cast<uint2*>(dst) = make_uint2(
         uint32_t(f32_to_bf16(a[0] * inv)) | uint32_t(f32_to_bf16(a[1] * inv)) << 16,
         uint32_t(f32_to_bf16(a[2] * inv)) | uint32_t(f32_to_bf16(a[3] * inv)) << 16);
-    if (v == 0) p.lse[orow] = M + log2f(ws);
+    if (v == 0) p.lse[orow] = none ? kEmptyLse : M + log2f(ws);
   }
   __syncthreads();  // s_l is free again
 }
 
 // FUSED: the call also appends each sequence's new K/V row (p.new_k, p.new_v).
-template <int KVT, int D, int PS, int GP, bool ROPE, bool FUSED>
+// MT: several query tokens per sequence (p.T > 1; no RoPE, no window): the G T columns of the
+// MFMA B operand are token-major and each is causally capped.
+template <int KVT, int D, int PS, int GP, bool ROPE, bool FUSED, bool MT = false>
 __global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mfma_persist_kernel(DecodeParams p) {
   // items of 16 rows: a 32-row page is two items (half the registers per item in flight)
@@ -264,8 +280,11 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   const int l = tid & 63;
   const int B = p.B;
   const int G = p.G;
+  const int T = MT ? p.T : 1;
+  const int GC = G * T;  // q columns of the MFMA B operand
   C core;
   core.init_lane(l);
+  const int tok = MT ? core.n / G : 0;  // query token of this lane's MFMA column
   if constexpr (ROPE) {
     if (tid < D / 2) {
       float fhi, flo;
@@ -396,9 +415,9 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   // still gets its new row, written by append_last_row)
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
     if (tab.njobs[b] != 0) continue;
-    for (int idx = tid; idx < p.H_qo * D; idx += NT)
-      store_out<kBF16>(p.out, size_t(b) * p.H_qo * D + idx, 0.f);
-    for (int hq = tid; hq < p.H_qo; hq += NT) p.lse[size_t(b) * p.H_qo + hq] = kEmptyLse;
+    for (int idx = tid; idx < T * p.H_qo * D; idx += NT)
+      store_out<kBF16>(p.out, size_t(b) * T * p.H_qo * D + idx, 0.f);
+    for (int hq = tid; hq < T * p.H_qo; hq += NT) p.lse[size_t(b) * T * p.H_qo + hq] = kEmptyLse;
     if constexpr (FUSED) append_last_row<KVT, D, PS, NT>(p, b);
   }
 
@@ -411,9 +430,19 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   // This thread's share of J's q rows (words past the G rows repeat the last one; an invalid job
   // reads sequence 0's). Unconditional loads, consumed only when staged into LDS.
   auto q_words = [&](const Job& J, uint32_t (&qs)[QW]) {
-    const size_t base = (size_t(J.b) * p.H_qo + size_t(J.h) * G) * (D / 2);
+    if constexpr (MT) {
+      // column c's row is q[b, c / G, h G + c % G, :] (token-major columns)
 #pragma unroll
-    for (int i = 0; i < QW; ++i) qs[i] = qsrc[base + min(tid + i * NT, G * D / 2 - 1)];
+      for (int i = 0; i < QW; ++i) {
+        const int wd = min(tid + i * NT, GC * D / 2 - 1);
+        const int c = wd / (D / 2);
+        qs[i] = qsrc[out_row<true>(p, J.b, J.h, c) * (D / 2) + (wd - c * (D / 2))];
+      }
+    } else {
+      const size_t base = (size_t(J.b) * p.H_qo + size_t(J.h) * G) * (D / 2);
+#pragma unroll
+      for (int i = 0; i < QW; ++i) qs[i] = qsrc[base + min(tid + i * NT, G * D / 2 - 1)];
+    }
   };
 
   // ---- fused append (p.new_k set): thread t < 2 * D / 8 takes 8 elements of J's new K (t < D / 8)
@@ -490,7 +519,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   __syncthreads();
 
   if (J.valid) {
-    core.load_q(reinterpret_cast<const uint16_t*>(s_q[0]), G);
+    core.load_q(reinterpret_cast<const uint16_t*>(s_q[0]), GC);
     core.rope_q(J.qpos, s_freq);
     float scale = p.score_scale * (C::FP8 ? p.k_scale[J.h] : 1.0f);
     float vscale = C::FP8 ? p.v_scale[J.h] : 1.0f;
@@ -531,7 +560,14 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         // first one, so window pages shift by the rows the window skips (sink - win_off)
         const int pos0 = J.kro + j * PS + r0 +
                          (J.s_w + kPWaves * si < J.g.n0 ? 0 : J.g.sink - J.g.win_off);
-        if (lo < hi) core.process(cur, lo, hi, scale, s_pt[w], s_alpha[w], pos0, s_freq);
+        if constexpr (MT) {
+          // this lane's column (token n / G) sees positions <= total - T + n / G
+          const int cap = J.g.total - T + tok - (j * PS + r0);
+          if (lo < hi) core.template process<true>(cur, lo, hi, scale, s_pt[w], s_alpha[w], 0,
+                                                   nullptr, cap);
+        } else {
+          if (lo < hi) core.process(cur, lo, hi, scale, s_pt[w], s_alpha[w], pos0, s_freq);
+        }
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NLOADS));
     };
@@ -613,12 +649,16 @@ void decode_mfma_persist_kernel(DecodeParams p) {
 #pragma unroll
       for (int it = 0; it < (GP * D + NT - 1) / NT; ++it) {
         const int idx = tid + it * NT;
-        if (idx < G * D) {
+        if (idx < GC * D) {
           const int g = idx / D;
           const int d = idx - g * D;
           float M = -INFINITY;
 #pragma unroll
           for (int ww = 0; ww < kPWaves; ++ww) M = fmaxf(M, s_m[ww][g]);
+          // MT: a column whose token sees no row of this job (M = -inf) leaves out 0 and lse
+          // -5e4, or a partial of weight 0
+          const bool none = MT && M == -INFINITY;
+          if (MT && none) M = 0.f;
           float wsum = 0.f, o = 0.f;
 #pragma unroll
           for (int ww = 0; ww < kPWaves; ++ww) {
@@ -626,14 +666,14 @@ void decode_mfma_persist_kernel(DecodeParams p) {
             wsum = fmaf(f, s_d[ww][g], wsum);
             o = fmaf(f, s_o[ww][g][d], o);
           }
-          const int hq = J.h * G + g;
-          const float val = o / wsum * vscale;
-          const float l2 = M + log2f(wsum);
+          const size_t orow = out_row<MT>(p, J.b, J.h, g);
+          const float val = none ? 0.f : o / wsum * vscale;
+          const float l2 = none ? (J.nch == 1 ? kEmptyLse : -INFINITY) : M + log2f(wsum);
           if (J.nch == 1) {
-            store_out<kBF16>(p.out, (size_t(J.b) * p.H_qo + hq) * D + d, val);
-            if (d == 0) p.lse[size_t(J.b) * p.H_qo + hq] = l2;
+            store_out<kBF16>(p.out, orow * D + d, val);
+            if (d == 0) p.lse[orow] = l2;
           } else {
-            const size_t row = (size_t(J.b) * p.H_qo + hq) * p.num_chunks + J.c;
+            const size_t row = orow * p.num_chunks + J.c;
             if (in_merge) {
               store_agent(&p.part_o[row * D + d], val);
               if (d == 0) store_agent(&p.part_lse[row], l2);
@@ -646,7 +686,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       }
       __syncthreads();  // s_m / s_d / s_o / s_ticket are free again
       if (merge_prev) {
-        merge_split<D, GP, NT>(p, pb, ph, pnch);
+        merge_split<D, GP, NT, MT>(p, pb, ph, pnch);
         if (tid == 0)
           __hip_atomic_store(&p.counters[pb * p.H_kv + ph], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -665,7 +705,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
           }
           __syncthreads();
           if (s_ticket) {
-            merge_split<D, GP, NT>(p, pb, ph, pnch);
+            merge_split<D, GP, NT, MT>(p, pb, ph, pnch);
             if (tid == 0)
               __hip_atomic_store(&p.counters[pb * p.H_kv + ph], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
@@ -675,7 +715,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       // ---- move on: J1 becomes current; decode the job after it
       J = J1;
       par ^= 1;
-      core.load_q(reinterpret_cast<const uint16_t*>(s_q[par]), G);
+      core.load_q(reinterpret_cast<const uint16_t*>(s_q[par]), GC);
       core.rope_q(J.qpos, s_freq);
       if (C::FP8) {
         scale = p.score_scale * p.k_scale[J.h];
@@ -723,15 +763,15 @@ inline int resident_workgroups(const void* kernel, size_t lds) {
   return n;
 }
 
-template <int KVT, int D, int PS, int GP, bool ROPE, bool FUSED>
+template <int KVT, int D, int PS, int GP, bool ROPE, bool FUSED, bool MT = false>
 hipError_t launch_persist_k(const DecodeParams& p, long long max_jobs, hipStream_t st) {
   const void* k =
-      reinterpret_cast<const void*>(&decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE, FUSED>);
+      reinterpret_cast<const void*>(&decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE, FUSED, MT>);
   const size_t lds = seq_table_bytes(p.B);
   const int resident = resident_workgroups(k, lds);
   if (resident <= 0) return hipErrorInvalidConfiguration;
   const unsigned grid = static_cast<unsigned>((max_jobs < resident ? (max_jobs > 0 ? max_jobs : 1) : resident));
-  hipLaunchKernelGGL((decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE, FUSED>), dim3(grid),
+  hipLaunchKernelGGL((decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE, FUSED, MT>), dim3(grid),
                      dim3(64 * kPWaves), lds, st, p);
   return hipGetLastError();
 }
@@ -739,5 +779,10 @@ hipError_t launch_persist_k(const DecodeParams& p, long long max_jobs, hipStream
 // The fused-append instantiations of launch_persist_k (decode_fused.hip).
 template <int KVT, int D, int PS, int GP, bool ROPE>
 hipError_t launch_persist_fused(const DecodeParams& p, long long max_jobs, hipStream_t st);
+
+// The several-query-token instantiations of launch_persist_k (decode_multi.hip): no RoPE, no fused
+// append.
+template <int KVT, int D, int PS, int GP>
+hipError_t launch_persist_multi(const DecodeParams& p, long long max_jobs, hipStream_t st);
 
 }  // namespace pdk

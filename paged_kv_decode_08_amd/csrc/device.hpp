@@ -34,6 +34,8 @@ struct DecodeParams {
   const void* new_v;         // to each sequence's last position; null: attention only
   void* pages_w;             // fused append: the pool (the same memory as pages)
   int32_t B, H_qo, H_kv, G;
+  int32_t T;                 // query tokens per sequence (1: single-token decode); q, out and
+                             // lse are [B, T, H_qo, ...], token t sees positions <= total - T + t
   int32_t max_num_pages;     // page ids are clamped into the pool before any KV address is formed
   int32_t sliding, rotary;
   float rope_scale, rope_theta;

@@ -231,9 +231,12 @@ struct MfmaCore {
   // Online-softmax update with one page whose attended rows are [lo, hi) (lo < hi).
   // s_pt: this wave's [16][PT_STRIDE] P^T tile; s_alpha: this wave's 16 rescale factors.
   // RoPE: row r of the item is at position pos0 + r; s_freq as in rope_q.
+  // COLCAP (several query tokens): this lane's column also masks the rows above `cap`, so a
+  // column may have no row left in the item, or in the whole job so far (m = -inf).
+  template <bool COLCAP = false>
   __device__ __forceinline__ void process(const Buf& bf, int lo, int hi, float scale,
                                           float (*s_pt)[PT_STRIDE], float* s_alpha, int pos0 = 0,
-                                          const float2* s_freq = nullptr) {
+                                          const float2* s_freq = nullptr, int cap = 15) {
     // scores S^T[row][head] on the matrix cores
     f32x4_t acc[RB];
     if constexpr (ROPE) {
@@ -298,20 +301,22 @@ struct MfmaCore {
       for (int v = 0; v < 4; ++v) {
         const int row = rb * 16 + 4 * qg + v;
         float x = acc[rb][v] * scale;
-        x = (row >= lo && row < hi) ? x : -INFINITY;
+        x = (row >= lo && row < hi && (!COLCAP || row <= cap)) ? x : -INFINITY;
         sv[rb][v] = x;
         tmax = fmaxf(tmax, x);
       }
     tmax = xmax(xmax(tmax, 16), 32);
-    const float mn = fmaxf(m, tmax);  // finite: the page has at least one attended row
-    const float alpha = exp2_fast(m - mn);
+    const float mn = fmaxf(m, tmax);  // finite unless COLCAP: the page has an attended row
+    // a column with no row yet keeps m = -inf, O = 0, d = 0 (reference 0: every weight is 0)
+    const float mref = COLCAP && mn == -INFINITY ? 0.f : mn;
+    const float alpha = exp2_fast(m - mref);
     m = mn;
     float psum = 0.f;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        sv[rb][v] = exp2_fast(sv[rb][v] - mn);
+        sv[rb][v] = exp2_fast(sv[rb][v] - mref);
         psum += sv[rb][v];
       }
     dl = dl * alpha + psum;

@@ -244,6 +244,13 @@ CONFIGS = {
 }
 
 
+def multi_query(w, T, seed):
+    """q for T query tokens per sequence of workload w: [B, T, H_qo, D] in w.q_dtype storage,
+    N(0, 1) from its own seeded stream."""
+    rng = _rng(seed, 6)
+    return cast_f32(rng.standard_normal((w.B, T, w.H_qo, w.D), dtype=np.float32), w.q_dtype)
+
+
 def append_inputs(*, T, H_kv, D, page_size, max_num_pages, in_dtype, seed, skip_every=0,
                   slots=None):
     """New K/V rows [T, H_kv, D] in `in_dtype` storage and int32 slot ids: distinct slots drawn

@@ -168,3 +168,22 @@ def test_append_attention_argument_errors(L):
     assert call(desc(batch=0), nk=None, nv=None) == 0
     assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.1, FAKE, FAKE, FAKE, 0,
              None) == 1
+
+
+def test_attention_multi_argument_errors(L):
+    """pdecode_attention_multi: qo_len < 1, a sliding window, more than 8 MFMA columns (group
+    size x tokens), an fp32 pool and a batch beyond the persistent schedule are refused before
+    anything is launched; the workspace size grows with the tokens."""
+    f = L.pdecode_attention_multi
+
+    def call(d, T):
+        return f(ctypes.byref(d), T, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, FAKE, 1 << 30,
+                 None)
+    assert call(desc(), 0) == 1
+    assert call(desc(sliding_window=True), 2) == 2
+    assert call(desc(), 3) == 2                   # 4 q heads per KV head x 3 tokens > 8
+    assert call(desc(num_qo_heads=8, batch=2000), 4) == 2
+    assert call(desc(num_qo_heads=8, q_dtype="f32", kv_dtype="f32"), 4) == 2
+    wb = L.pdecode_workspace_bytes_multi
+    assert wb(ctypes.byref(desc()), 0) == 0
+    assert wb(ctypes.byref(desc()), 2) >= L.pdecode_workspace_bytes(ctypes.byref(desc()))

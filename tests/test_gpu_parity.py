@@ -663,3 +663,67 @@ def test_append_attention_no_attended_rows():
     w = synth.make_workload(name="fused_empty_win", B=3, H_qo=8, H_kv=2, D=128, page_size=16,
                             seq_lens=[40, 0, 16], seed=740, max_num_pages=64, window=0, sink=0)
     _fused_case(w, seed=75)
+
+
+# ---- several query tokens per sequence: pdecode_attention_multi
+
+def _multi_case(w, T, seed, num_kv_splits=0):
+    qm = synth.multi_query(w, T, seed)
+    kw = {k: v for k, v in w.oracle_kwargs().items() if k != "q"}
+    o_ref, l_ref = oracle.decode_multi(qo_len=T, q=qm, **kw)
+    dev = gu.upload(w)
+    desc = gu.desc_for(w, dev, num_kv_splits)
+    qd = gu.to_device_storage(qm, w.q_dtype)
+    out = torch.empty((w.B, T, w.H_qo, w.D), dtype=torch.bfloat16, device="cuda")
+    out.view(torch.int16).fill_(0x7FC0)
+    lse = torch.full((w.B, T, w.H_qo), float("nan"), dtype=torch.float32, device="cuda")
+    ws = pk.alloc_workspace_multi(desc, T)
+    pk.attention_multi(desc, T, qd, dev["pages"], dev["indptr"], dev["values"],
+                       dev["length_info"], out, lse, w.sm_scale, workspace=ws)
+    torch.cuda.synchronize()
+    tol_o, tol_l = gu.tolerance(w)
+    o_gpu, l_gpu = gu.to_np64(out), gu.to_np64(lse)
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(l_gpu)), w.name
+    do = np.abs(o_gpu - o_ref).max(initial=0)
+    dl = np.abs(l_gpu - l_ref).max(initial=0)
+    print(f"{w.name} T={T}: max|dout|={do:.3g} max|dlse|={dl:.3g}", flush=True)
+    assert do <= tol_o and dl <= tol_l, (w.name, T, do, dl)
+    return qd, desc, dev, out, lse, ws
+
+
+@pytest.mark.parametrize("kv,G,T,D,ps", [("bf16", 4, 2, 128, 16), ("bf16", 1, 8, 64, 32),
+                                         ("bf16", 2, 3, 128, 16), ("fp8", 2, 4, 128, 32),
+                                         ("fp8", 1, 2, 64, 16), ("bf16", 8, 1, 128, 16)])
+def test_attention_multi(kv, G, T, D, ps):
+    """T query tokens, causal over the new ones, against the oracle (each token = decode over its
+    visible prefix): sequences shorter than T (tokens with no row), an empty one, lengths around
+    page boundaries; T x G from 6 to 8 MFMA columns."""
+    lens = [1, T - 1, ps, ps + 1, 3 * ps - 1, 700, 0, 2 * ps + T]
+    w = synth.make_workload(name=f"multi_{kv}_G{G}_D{D}_ps{ps}", B=len(lens), H_qo=2 * G,
+                            H_kv=2, D=D, page_size=ps, seq_lens=lens, q_dtype="bf16",
+                            kv_dtype=kv, seed=800 + G + T + D + ps, max_num_pages=256)
+    _multi_case(w, T, seed=81 + T)
+
+
+@pytest.mark.parametrize("splits", [3, 12])
+def test_attention_multi_split(splits):
+    """Forced splits with two tokens: merged in the kernel (3 chunks) and by the split merge kernel
+    (12), including chunks where the first token sees no row."""
+    w = synth.make_workload(name=f"multi_split{splits}", B=4, H_qo=16, H_kv=4, D=128,
+                            page_size=16, seq_lens=[3000, 17, 1200, 641], seed=820 + splits,
+                            max_num_pages=512)
+    _multi_case(w, 2, seed=83, num_kv_splits=splits)
+
+
+def test_attention_multi_one_token_is_attention():
+    """qo_len = 1 through pdecode_attention_multi is pdecode_attention, bit for bit."""
+    w = synth.make_workload(name="multi_T1", B=5, H_qo=32, H_kv=8, D=128, page_size=16,
+                            seq_lens=[900, 1, 17, 4000, 33], seed=840, max_num_pages=512)
+    qd, desc, dev, out, lse, ws = _multi_case(w, 1, seed=84)
+    out1 = torch.empty((w.B, w.H_qo, w.D), dtype=torch.bfloat16, device="cuda")
+    lse1 = torch.empty((w.B, w.H_qo), dtype=torch.float32, device="cuda")
+    pk.attention(desc, qd.view(w.B, w.H_qo, w.D), dev["pages"], dev["indptr"], dev["values"],
+                 dev["length_info"], out1, lse1, w.sm_scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(w.B, w.H_qo, w.D).view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse.view(w.B, w.H_qo), lse1)

@@ -525,3 +525,40 @@ def test_append_then_decode_single_row_is_the_new_row():
     assert np.all(out[1] == 0) and np.all(lse[1] == -5e4)
     assert np.array_equal(pool[4, 0, :, 0], nk[0]) and np.array_equal(pool[1, 1, :, 0], nv[2])
     assert np.isnan(pool[4, 0, :, 1:]).all()  # nothing else written
+
+
+# ---- several query tokens per sequence (causal over the new tokens)
+
+@pytest.mark.parametrize("kv_dtype,q_dtype", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "bf16")])
+@pytest.mark.parametrize("T", [2, 3])
+def test_multi_token_matches_dense_causal_bruteforce(kv_dtype, q_dtype, T):
+    """Token t of a sequence of total rows L = textbook softmax over the flattened cache's rows
+    0 .. L - T + t; a token whose prefix is empty gets out = 0, lse = -5e4."""
+    w = small(B=4, kv_dtype=kv_dtype, q_dtype=q_dtype, page_order="shuffled",
+              seq_lens=[7, 1, 13, 0])
+    qm = synth.multi_query(w, T, seed=5)
+    out, lse = oracle.decode_multi(qo_len=T, q=qm, **{k: v for k, v in w.oracle_kwargs().items()
+                                                     if k != "q"})
+    G = w.H_qo // w.H_kv
+    q64 = to_f64(qm, w.q_dtype)
+    for b in range(w.B):
+        L = int(w.seq_lens[b])
+        for t in range(T):
+            n = L - T + t + 1
+            for hq in range(w.H_qo):
+                if n <= 0:
+                    assert np.all(out[b, t, hq] == 0) and lse[b, t, hq] == -5e4
+                    continue
+                K, V = contiguous_kv(w, b, hq // G)
+                o, l = dense_attention(q64[b, t, hq], K[:n], V[:n], w.sm_scale)
+                np.testing.assert_allclose(out[b, t, hq], o, rtol=0, atol=1e-12)
+                assert abs(lse[b, t, hq] - l) < 1e-12
+
+
+def test_multi_token_one_token_is_decode():
+    """qo_len = 1 is the single-token decode, bit for bit."""
+    w = small(seq_lens=[7, 1, 13])
+    out1, lse1 = oracle.decode_multi(qo_len=1, q=w.q[:, None], **{
+        k: v for k, v in w.oracle_kwargs().items() if k != "q"})
+    out, lse = run_oracle(w)
+    assert np.array_equal(out1[:, 0], out) and np.array_equal(lse1[:, 0], lse)
