@@ -44,11 +44,15 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_bf16",
                     choices=["llama3_8b_bf16", "long_ctx_bf16", "rope_swa_bf16", "fp8_gqa8",
                              "tiny_fp32", "gqa8_bf16"])
-    ap.add_argument("--op", choices=["merge_state", "append_kv", "append_attention"], default=None,
+    ap.add_argument("--op", choices=["merge_state", "append_kv", "append_attention", "multi"],
+                    default=None,
                     help="instead of the decode, time pdecode_merge_state_inplace or "
                          "pdecode_append_kv at a decode-step size and a bulk size, or a whole "
                          "decode step of --workload: pdecode_append_attention against "
-                         "pdecode_append_kv followed by pdecode_attention")
+                         "pdecode_append_kv followed by pdecode_attention, or --qo-len query "
+                         "tokens per sequence of --workload: one pdecode_attention_multi call "
+                         "against --qo-len pdecode_attention calls")
+    ap.add_argument("--qo-len", type=int, default=2, help="query tokens per sequence (--op multi)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the decode, run a plain 512 MiB device-to-device copy "
                          "(the reference point for the HBM byte counters) and exit")
@@ -165,6 +169,71 @@ def op_bench(op, steps, warmup):
                       "data": "synthetic", "results": results}), flush=True)
 
 
+def multi_bench(workload, T, steps, warmup, nsets):
+    """T query tokens per sequence (causal over the new tokens): one pdecode_attention_multi call,
+    which reads the KV once for all T tokens, against T pdecode_attention calls (one per token,
+    each over the whole sequence: the upper bound of the per-token work). K steps each between
+    synchronisations, input sets cycled as in the decode bench."""
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_08_amd as pk
+    import synth
+    from tests import gpu_util as gu
+
+    torch.cuda.set_device(0)
+    make = synth.CONFIGS[workload]
+    base = make()
+    nsets = nsets if base.kv_bytes < 512e6 else 1
+    lens = base.seq_lens.astype(np.int64)
+    sets = [base] + [make(seed=1002 + 100 * i, lens=lens) for i in range(1, nsets)]
+    devs = [gu.upload(w) for w in sets]
+    desc = gu.desc_for(base, devs[0])
+    ws = pk.alloc_workspace_multi(desc, T)
+    qm = gu.to_device_storage(synth.multi_query(base, T, seed=10), base.q_dtype)
+    out = torch.empty((base.B, T, base.H_qo, base.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((base.B, T, base.H_qo), dtype=torch.float32, device="cuda")
+    qt = [qm[:, t].contiguous() for t in range(T)]
+    outs = [torch.empty((base.B, base.H_qo, base.D), dtype=torch.bfloat16, device="cuda")
+            for _ in range(T)]
+    lses = [torch.empty((base.B, base.H_qo), dtype=torch.float32, device="cuda") for _ in range(T)]
+    stream = torch.cuda.current_stream()
+
+    def multi(i):
+        d = devs[i % len(devs)]
+        pk.attention_multi(desc, T, qm, d["pages"], d["indptr"], d["values"], d["length_info"],
+                           out, lse, base.sm_scale, workspace=ws, stream=stream)
+
+    def per_token(i):
+        d = devs[i % len(devs)]
+        for t in range(T):
+            pk.attention(desc, qt[t], d["pages"], d["indptr"], d["values"], d["length_info"],
+                         outs[t], lses[t], base.sm_scale, workspace=ws, stream=stream)
+
+    res = {}
+    for name, fn in (("per_token_calls", per_token), ("multi", multi),
+                     ("per_token_calls_again", per_token), ("multi_again", multi)):
+        for i in range(warmup):
+            fn(i)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = {"us_per_step_wall": round((time.perf_counter() - t0) * 1e6 / steps, 2),
+                     "us_per_step_events": round(ev0.elapsed_time(ev1) * 1e3 / steps, 2)}
+    us = res["multi"]["us_per_step_events"]
+    print(json.dumps({"op": "multi", "workload": base.name, "qo_len": T, "n_gpus": 1,
+                      "steps": steps, "warmup": warmup, "input_sets": len(sets),
+                      "kv_bytes_per_step": base.kv_bytes,
+                      "multi_kv_GBps_events": round(base.kv_bytes / (us * 1e-6) / 1e9, 1),
+                      "data": "synthetic", **res}), flush=True)
+
+
 def step_bench(workload, steps, warmup, nsets):
     """A whole decode step: the step's new K/V row of every (sequence, KV head) goes to the
     sequence's last position, then attention. Fused (one pdecode_append_attention launch) against
@@ -246,6 +315,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(max(args.steps, 1))
+        return
+    if args.op == "multi":
+        multi_bench(args.workload, args.qo_len, max(args.steps, 1), args.warmup, args.sets)
         return
     if args.op == "append_attention":
         step_bench(args.workload, max(args.steps, 1), args.warmup, args.sets)
