@@ -540,8 +540,8 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       return s_ids[par][w][si & 63];
     };
     // Computes item k from `cur` (rows 16 (k % SUB) .. + 16 of slot k / SUB; items past the
-    // wave's slots are unused), then retires `cur`: only the loads just issued stay in flight.
-    auto compute = [&](Buf& cur, int k) __attribute__((always_inline)) {
+    // wave's slots are unused).
+    auto process_item = [&](Buf& cur, int k) __attribute__((always_inline)) {
       const int si = k / SUB;
       if (si < J.nw) {
         int j, lo, hi;
@@ -569,6 +569,10 @@ void decode_mfma_persist_kernel(DecodeParams p) {
           if (lo < hi) core.process(cur, lo, hi, scale, s_pt[w], s_alpha[w], pos0, s_freq);
         }
       }
+    };
+    // process_item, then retires `cur`: only the loads just issued stay in flight.
+    auto compute = [&](Buf& cur, int k) __attribute__((always_inline)) {
+      process_item(cur, k);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NLOADS));
     };
     // Issues the loads of item `k`'s 16 rows (k % SUB selects the rows in the page).
@@ -589,6 +593,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
     // job's first item is always in flight in buf0 when a job ends: every path into the loops has
     // the same loads in flight and the compiler's wait counts stay exact.
     for (;;) {
+      int arrival = 0;  // this wave's arrival for the previous job's split sequence
       // ---- items 0 and 1, with the loads for the next job (its page ids and q words, staged into
       // LDS once item 1 is computed). The ticket of the job after the next one is taken in the
       // last pair of items, so a workgroup holds at most one job beyond the current one.
@@ -602,22 +607,23 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         int ticket_raw = 0;
         if (last && J1.valid && tid == 0) ticket_raw = atomicAdd(queue, 1);
         issue_id(buf1, item_id(1), J.h, 1);
-        compute(buf0, 0);
-        // the previous job's partial stores are older than the loads just waited for
-        int arrival = 0;
-        if (pb >= 0 && l == 0)
-          arrival = __hip_atomic_fetch_add(&p.counters[pb * p.H_kv + ph], 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+        // no wait after item 0: the next job's ids and q words were issued with item 1, and
+        // waiting for them here would leave only item 1 in flight while they arrive
+        process_item(buf0, 0);
         if (!last) issue_id(buf0, item_id(2), J.h, 2);
         else if (J1.valid) issue_id(buf0, __builtin_amdgcn_readlane(ids_n, 0), J1.h, 0);
         else issue_id(buf0, item_id(1), J.h, 1);
         compute(buf1, 1);
+        // the previous job's partial stores are older than the loads just waited for; the
+        // arrival's result is read at the end of this job
+        if (pb >= 0 && l == 0)
+          arrival = __hip_atomic_fetch_add(&p.counters[pb * p.H_kv + ph], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int i = 0; i < QW; ++i) s_q[par ^ 1][tid + i * NT] = qs[i];
         s_ids[par ^ 1][w][l] = ids_n;
         if constexpr (FUSED) stage_new(J1, nw1, s_new[par ^ 1]);
         if (last && tid == 0) s_ticket = 2 * int(gridDim.x) + ticket_raw;
-        if (l == 0) s_mrg[w] = pb >= 0 && arrival == pnch * kPWaves - 1;
       }
       // ---- items 2 .. nitems - 3
       for (int k = 2; k + 2 < J.nitems; k += 2) {
@@ -640,10 +646,11 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       }
 
       // ---- end of job J: merge the waves, store
+      if (l == 0) s_mrg[w] = pb >= 0 && arrival == pnch * kPWaves - 1;
       core.to_lds(s_m[w], s_d[w], s_o[w]);
       __syncthreads();
       const int next_ticket = s_ticket;
-      int merge_prev = 0;  // s_mrg: written in this job's first pair, rewritten after the next barrier
+      int merge_prev = 0;  // s_mrg: written before the barrier above, rewritten after the next one
 #pragma unroll
       for (int ww = 0; ww < kPWaves; ++ww) merge_prev |= s_mrg[ww];
 #pragma unroll
