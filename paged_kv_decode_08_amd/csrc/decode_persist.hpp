@@ -429,15 +429,22 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   const uint32_t* qsrc = static_cast<const uint32_t*>(p.q);
   // This thread's share of J's q rows (words past the G rows repeat the last one; an invalid job
   // reads sequence 0's). Unconditional loads, consumed only when staged into LDS.
+  // MT: column c's row is q[b, c / G, h G + c % G, :] (token-major columns); the part of this
+  // thread's word offsets that does not depend on the job, (t H_qo + g) D / 2 + word, is fixed
+  int qoff[MT ? QW : 1];
+  if constexpr (MT) {
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+      const int wd = min(tid + i * NT, GC * D / 2 - 1);
+      const int c = wd / (D / 2);
+      qoff[i] = ((c / G) * p.H_qo + c % G) * (D / 2) + (wd - c * (D / 2));
+    }
+  }
   auto q_words = [&](const Job& J, uint32_t (&qs)[QW]) {
     if constexpr (MT) {
-      // column c's row is q[b, c / G, h G + c % G, :] (token-major columns)
+      const size_t base = (size_t(J.b) * T * p.H_qo + size_t(J.h) * G) * (D / 2);
 #pragma unroll
-      for (int i = 0; i < QW; ++i) {
-        const int wd = min(tid + i * NT, GC * D / 2 - 1);
-        const int c = wd / (D / 2);
-        qs[i] = qsrc[out_row<true>(p, J.b, J.h, c) * (D / 2) + (wd - c * (D / 2))];
-      }
+      for (int i = 0; i < QW; ++i) qs[i] = qsrc[base + qoff[i]];
     } else {
       const size_t base = (size_t(J.b) * p.H_qo + size_t(J.h) * G) * (D / 2);
 #pragma unroll
