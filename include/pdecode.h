@@ -88,6 +88,13 @@ typedef struct pdecode_desc {
                              sequence's pages into at most n chunks merged by log-sum-exp         */
   const float *k_scale;   /* device fp32 [H_kv]; required iff kv_dtype is FP8: K = code * scale */
   const float *v_scale;   /* device fp32 [H_kv]; required iff kv_dtype is FP8: V = code * scale */
+  const float *sink_logits; /* device fp32 [H_qo] or NULL: learned attention sink per q head (the
+                             AWS attention_block_tkg page's `sink`, one value per q head). Read as
+                             a logit in the units of the scaled score: a sequence with attended
+                             rows gets out = sum_r e^{s_r} v_r / (e^{sink} + sum_r e^{s_r}) and
+                             lse = log2(e^{sink} + sum_r e^{s_r}); one without keeps out = 0,
+                             lse = -5e4. Attention calls on the persistent matrix-core schedule
+                             only (BF16 / FP8 pool, batch <= 1024); otherwise UNSUPPORTED.       */
 } pdecode_desc;
 
 /* Rotary embedding on Q and K inside the kernel; a NULL pointer to this struct means none.

@@ -61,6 +61,9 @@ def _c(a, dtype):
     return None if a is None else np.ascontiguousarray(a, dtype=dtype)
 
 
+LOG2E = 1.0 / np.log(2.0)
+
+
 class OracleError(RuntimeError):
     pass
 
@@ -129,6 +132,23 @@ def append_kv(*, pages, new_k, new_v, slots, H_kv, D, ps, in_dtype, kv_dtype, k_
     if rc != 0:
         raise OracleError(f"oracle_append_kv failed with code {rc}")
     return pages
+
+
+def apply_sink(out, lse, sink_logits):
+    """Folds a learned attention sink per q head (a logit in the units of the scaled score, with
+    no value row) into finished decode states (out [..., H_qo, D], lse [..., H_qo], base 2): the
+    softmax denominator gains e^sink, so lse' = log2(2^lse + 2^(sink log2 e)) and
+    out' = out 2^(lse - lse'). Rows with the empty convention (lse = -5e4, out = 0) are kept."""
+    out = np.array(out, np.float64)
+    lse = np.array(lse, np.float64)
+    s2 = np.asarray(sink_logits, np.float64) * LOG2E
+    s2 = np.broadcast_to(s2, lse.shape)
+    empty = lse == -5e4
+    m = np.maximum(lse, s2)
+    new = m + np.log2(np.exp2(lse - m) + np.exp2(s2 - m))
+    f = np.exp2(lse - new)
+    out = np.where(empty[..., None], out, out * f[..., None])
+    return out, np.where(empty, lse, new)
 
 
 def decode_multi(*, qo_len, q, **kw):

@@ -169,7 +169,7 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   if (!q || !pages || !page_indptr || !page_values || !length_info || !out || !lse)
     return PDECODE_ERR_INVALID_ARG;
   const Plan pl = make_plan(d, rotary, qo_len);
-  if ((fused || qo_len > 1) && !pl.persistent) return PDECODE_ERR_UNSUPPORTED;
+  if ((fused || qo_len > 1 || d->sink_logits) && !pl.persistent) return PDECODE_ERR_UNSUPPORTED;
   const int64_t grid = int64_t(pl.num_chunks) * d->batch * d->num_kv_heads;
   if (grid > INT_MAX) return PDECODE_ERR_UNSUPPORTED;
   if (pl.workspace_bytes() > 0) {
@@ -190,6 +190,7 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   p.new_k = new_k;
   p.new_v = new_v;
   p.pages_w = fused ? const_cast<void*>(pages) : nullptr;
+  p.sink = d->sink_logits;
   p.out = out;
   p.lse = lse;
   const bool ws = pl.workspace_bytes() > 0;

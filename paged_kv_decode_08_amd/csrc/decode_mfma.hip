@@ -246,15 +246,18 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
     acc.w += __shfl_xor(acc.w, o, 64);
   }
   if (nch <= 1) return;  // unsplit (or empty) sequence: the decode kernel wrote its row
+  float Mf = M;
+  float fo = 1.f;  // learned sink of the row's q head, folded once
+  if (p.sink != nullptr && !none) fo = fold_sink(p.sink[row % p.H_qo] * kLog2e, Mf, ws);
   if (lane < V) {
-    const float inv = none ? 0.f : 1.f / ws;
+    const float inv = none ? 0.f : fo / ws;
     uint16_t* dst = static_cast<uint16_t*>(p.out) + size_t(row) * D + 4 * lane;
     const uint2 packed = make_uint2(
         uint32_t(f32_to_bf16(acc.x * inv)) | uint32_t(f32_to_bf16(acc.y * inv)) << 16,
         uint32_t(f32_to_bf16(acc.z * inv)) | uint32_t(f32_to_bf16(acc.w * inv)) << 16);
     *reinterpret_cast<uint2*>(dst) = packed;
   }
-  if (lane == 0) p.lse[row] = none ? kEmptyLse : M + log2f(ws);
+  if (lane == 0) p.lse[row] = none ? kEmptyLse : Mf + log2f(ws);
 }
 
 // ------------------------------------------------------------------------------------------------

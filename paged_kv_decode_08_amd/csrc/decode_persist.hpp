@@ -233,8 +233,10 @@ __device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
     }
   }
   if (tid < G * V) {
-    const float inv = none ? 0.f : 1.f / ws;
     const size_t orow = out_row<MT>(p, b, h, g);
+    float fo = 1.f;  // learned sink: folded into the denominator once, here
+    if (p.sink != nullptr && !none) fo = fold_sink(p.sink[h * p.G + g % p.G] * kLog2e, M, ws);
+    const float inv = none ? 0.f : fo / ws;
     uint16_t* dst = static_cast<uint16_t*>(p.out) + orow * D + 4 * v;
     *reinterpret_cast<uint2*>(dst) = make_uint2(
         uint32_t(f32_to_bf16(a[0] * inv)) | uint32_t(f32_to_bf16(a[1] * inv)) << 16,
@@ -681,6 +683,9 @@ void decode_mfma_persist_kernel(DecodeParams p) {
             o = fmaf(f, s_o[ww][g][d], o);
           }
           const size_t orow = out_row<MT>(p, J.b, J.h, g);
+          // learned sink: folded into a finished row only (a split one gets it when merged)
+          if (p.sink != nullptr && J.nch == 1 && !none)
+            o *= fold_sink(p.sink[J.h * G + g % G] * kLog2e, M, wsum);
           const float val = none ? 0.f : o / wsum * vscale;
           const float l2 = none ? (J.nch == 1 ? kEmptyLse : -INFINITY) : M + log2f(wsum);
           if (J.nch == 1) {

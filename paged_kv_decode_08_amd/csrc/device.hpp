@@ -33,6 +33,7 @@ struct DecodeParams {
   const void* new_k;         // fused append: the step's K and V rows [B, H_kv, D] (bf16), written
   const void* new_v;         // to each sequence's last position; null: attention only
   void* pages_w;             // fused append: the pool (the same memory as pages)
+  const float* sink;         // learned sink logit per q head [H_qo] (natural-log units), or null
   int32_t B, H_qo, H_kv, G;
   int32_t T;                 // query tokens per sequence (1: single-token decode); q, out and
                              // lse are [B, T, H_qo, ...], token t sees positions <= total - T + t
@@ -43,6 +44,17 @@ struct DecodeParams {
   int32_t chunk_slots;       // page slots per chunk
   int32_t num_chunks;        // chunks in the grid; the last one takes every remaining slot
 };
+
+// Learned attention sink of one q head (logit sink2 in log2 units) folded into a finished state
+// (M, wsum = sum_r 2^(x_r - M)): the denominator gains 2^sink2 and no value row is added. Updates
+// M and wsum; returns the factor of the unnormalised output sum_r 2^(x_r - M) v_r.
+__device__ __forceinline__ float fold_sink(float sink2, float& M, float& wsum) {
+  const float Mn = fmaxf(M, sink2);
+  const float a = __builtin_amdgcn_exp2f(M - Mn);
+  wsum = wsum * a + __builtin_amdgcn_exp2f(sink2 - Mn);
+  M = Mn;
+  return a;
+}
 
 struct AppendParams {
   const void* new_k;

@@ -29,7 +29,7 @@ def upload(w, device="cuda"):
     return d
 
 
-def desc_for(w, dev, num_kv_splits=0, max_kv_len=None):
+def desc_for(w, dev, num_kv_splits=0, max_kv_len=None, sink_logits=None):
     if max_kv_len is None:
         max_kv_len = int(w.attended.max()) if w.B else 0
     return pk.make_desc(batch=w.B, num_qo_heads=w.H_qo, num_kv_heads=w.H_kv, head_dim=w.D,
@@ -37,7 +37,7 @@ def desc_for(w, dev, num_kv_splits=0, max_kv_len=None):
                         q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
                         sliding_window=w.sliding_window, max_kv_len=max_kv_len,
                         num_kv_splits=num_kv_splits, k_scale=dev["k_scale"],
-                        v_scale=dev["v_scale"])
+                        v_scale=dev["v_scale"], sink_logits=sink_logits)
 
 
 def run_attention(w, dev, num_kv_splits=0, max_kv_len=None, out=None, lse=None, stream=None):

@@ -187,3 +187,11 @@ def test_attention_multi_argument_errors(L):
     wb = L.pdecode_workspace_bytes_multi
     assert wb(ctypes.byref(desc()), 0) == 0
     assert wb(ctypes.byref(desc()), 2) >= L.pdecode_workspace_bytes(ctypes.byref(desc()))
+
+
+def test_sink_outside_the_persistent_schedule_is_unsupported(L):
+    """Learned sinks: an fp32 pool (vector-ALU kernel) and a batch above the persistent schedule's
+    bound are refused before anything is launched."""
+    for d in (desc(q_dtype="f32", kv_dtype="f32"), desc(batch=2000)):
+        d.sink_logits = FAKE
+        assert attention_status(L, d, workspace=FAKE, ws_bytes=1 << 30) == 2

@@ -727,3 +727,64 @@ def test_attention_multi_one_token_is_attention():
     torch.cuda.synchronize()
     assert torch.equal(out.view(w.B, w.H_qo, w.D).view(torch.int16), out1.view(torch.int16))
     assert torch.equal(lse.view(w.B, w.H_qo), lse1)
+
+
+# ---- learned attention sink per q head
+
+def _sink_case(w, sinks, num_kv_splits=0, T=1):
+    dev = gu.upload(w)
+    sk = torch.from_numpy(np.asarray(sinks, np.float32)).cuda()
+    desc = gu.desc_for(w, dev, num_kv_splits, sink_logits=sk)
+    kw = {k: v for k, v in w.oracle_kwargs().items()}
+    if T == 1:
+        o0, l0 = oracle.decode(**kw)
+        out = torch.empty((w.B, w.H_qo, w.D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.B, w.H_qo), dtype=torch.float32, device="cuda")
+        ws = pk.alloc_workspace(desc)
+        pk.attention(desc, dev["q"], dev["pages"], dev["indptr"], dev["values"],
+                     dev["length_info"], out, lse, w.sm_scale, workspace=ws)
+    else:
+        qm = synth.multi_query(w, T, seed=91)
+        kw.pop("q")
+        o0, l0 = oracle.decode_multi(qo_len=T, q=qm, **kw)
+        out = torch.empty((w.B, T, w.H_qo, w.D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.B, T, w.H_qo), dtype=torch.float32, device="cuda")
+        ws = pk.alloc_workspace_multi(desc, T)
+        pk.attention_multi(desc, T, gu.to_device_storage(qm, w.q_dtype), dev["pages"],
+                           dev["indptr"], dev["values"], dev["length_info"], out, lse, w.sm_scale,
+                           workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.apply_sink(o0, l0, sinks)
+    tol_o, tol_l = gu.tolerance(w)
+    o_gpu, l_gpu = gu.to_np64(out), gu.to_np64(lse)
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(l_gpu)), w.name
+    do = np.abs(o_gpu - o_ref).max(initial=0)
+    dl = np.abs(l_gpu - l_ref).max(initial=0)
+    print(f"{w.name} sink: max|dout|={do:.3g} max|dlse|={dl:.3g}", flush=True)
+    assert do <= tol_o and dl <= tol_l, (w.name, do, dl)
+
+
+@pytest.mark.parametrize("kv,G,ps,splits", [("bf16", 4, 16, 0), ("bf16", 4, 16, 3),
+                                            ("bf16", 4, 16, 12), ("fp8", 8, 32, 0),
+                                            ("bf16", 1, 32, 2)])
+def test_learned_sink(kv, G, ps, splits):
+    """Per-q-head sink logits, including one that dwarfs the scores (out ~ 0) and one far below
+    them (no effect), against the oracle's fold of the sink into the finished state; unsplit,
+    merged in the kernel (3 chunks) and by the split merge kernel (12); an empty sequence keeps
+    out = 0, lse = -5e4."""
+    lens = [1, 300, 2000, 0, 5 * ps + 3]
+    w = synth.make_workload(name=f"sink_{kv}_G{G}_ps{ps}_s{splits}", B=len(lens), H_qo=2 * G,
+                            H_kv=2, D=128, page_size=ps, seq_lens=lens, q_dtype="bf16",
+                            kv_dtype=kv, seed=900 + G + ps + splits, max_num_pages=512)
+    sinks = np.random.default_rng(92).normal(0.0, 2.0, w.H_qo).astype(np.float32)
+    sinks[0], sinks[-1] = 60.0, -60.0
+    _sink_case(w, sinks, splits)
+
+
+def test_learned_sink_multi_token():
+    """Sinks with two query tokens per sequence (each token's state gets its q head's sink)."""
+    w = synth.make_workload(name="sink_multi", B=4, H_qo=8, H_kv=2, D=128, page_size=16,
+                            seq_lens=[1, 40, 1500, 700], seed=930, max_num_pages=256)
+    sinks = np.random.default_rng(93).normal(0.0, 2.0, w.H_qo).astype(np.float32)
+    _sink_case(w, sinks, 3, T=2)
+    _sink_case(w, sinks, 0, T=2)

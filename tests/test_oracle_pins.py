@@ -562,3 +562,31 @@ def test_multi_token_one_token_is_decode():
         k: v for k, v in w.oracle_kwargs().items() if k != "q"})
     out, lse = run_oracle(w)
     assert np.array_equal(out1[:, 0], out) and np.array_equal(lse1[:, 0], lse)
+
+
+# ---- learned attention sink per q head
+
+@pytest.mark.parametrize("kv_dtype,q_dtype", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "bf16")])
+def test_sink_matches_dense_with_an_extra_logit(kv_dtype, q_dtype):
+    """A sink logit is one more softmax entry with a zero value row: textbook attention over the
+    scores plus the sink, on the flattened cache; the empty sequence keeps its convention."""
+    w = small(B=4, kv_dtype=kv_dtype, q_dtype=q_dtype, page_order="shuffled",
+              seq_lens=[7, 1, 13, 0])
+    sinks = np.array([0.5, -3.0, 2.5, 40.0], np.float32)  # 40: the sink takes almost everything
+    out0, lse0 = run_oracle(w)
+    out, lse = oracle.apply_sink(out0, lse0, sinks)
+    G = w.H_qo // w.H_kv
+    q64 = to_f64(w.q, w.q_dtype)
+    for b in range(w.B):
+        for hq in range(w.H_qo):
+            if w.seq_lens[b] == 0:
+                assert np.all(out[b, hq] == 0) and lse[b, hq] == -5e4
+                continue
+            K, V = contiguous_kv(w, b, hq // G)
+            s = np.concatenate([(K @ q64[b, hq]) * w.sm_scale, [float(sinks[hq])]])
+            Vx = np.vstack([V, np.zeros((1, w.D))])
+            m = s.max()
+            e = np.exp(s - m)
+            np.testing.assert_allclose(out[b, hq], (e[:, None] * Vx).sum(0) / e.sum(), rtol=0,
+                                       atol=1e-12)
+            assert abs(lse[b, hq] - (m + np.log(e.sum())) * LOG2E) < 1e-12
