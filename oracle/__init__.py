@@ -48,7 +48,7 @@ def lib():
         L.oracle_bf16_value.restype = ctypes.c_double
         L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
         L.oracle_rope_rotate.restype = None
-        L.oracle_rope_rotate.argtypes = [P, i32, ctypes.c_double, f32, f32]
+        L.oracle_rope_rotate.argtypes = [P, i32, ctypes.c_double, f32, f32, i32]
         _lib = L
     return _lib
 
@@ -246,7 +246,8 @@ def bf16_value(bits: int) -> float:
     return float(lib().oracle_bf16_value(bits))
 
 
-def rope_rotate(x, pos, rope_scale, rope_theta):
+def rope_rotate(x, pos, rope_scale, rope_theta, interleaved=False):
     x = np.array(x, dtype=np.float64, order="C")
-    lib().oracle_rope_rotate(_ptr(x), x.size, float(pos), float(rope_scale), float(rope_theta))
+    lib().oracle_rope_rotate(_ptr(x), x.size, float(pos), float(rope_scale), float(rope_theta),
+                             int(bool(interleaved)))
     return x

@@ -34,8 +34,10 @@
 //   * RoPE: rotate-half, pairing element i with i + D/2 (the attention_block_tkg docs, parameter
 //     rope_contiguous_layout, offer this split-in-halves layout besides an interleaved one),
 //     frequency theta^(-2i/D), angle = position * rope_scale * frequency; applied iff
-//     rotary_mode == 1; the K position is k_rope_pos_offset[b] + r (compacted row index r, as
-//     the page passes row_idx). PARITY UNPINNED against the pages: only invariants pin it.
+//     rotary_mode == 1; rotary_mode == 2 takes that interleaved layout instead, pairing elements
+//     2i and 2i + 1 with the same frequency i; the K position is k_rope_pos_offset[b] + r
+//     (compacted row index r, as the page passes row_idx). PARITY UNPINNED against the pages:
+//     only invariants pin it.
 //   * fp8 scales multiply the decoded payload, per KV head.
 #include <algorithm>
 #include <atomic>
@@ -95,16 +97,19 @@ uint8_t fp8_encode(float x) {
   return sign | static_cast<uint8_t>(best);
 }
 
-// Rotate-half RoPE on a D-vector in place (reading of the absent _rope helper, see header).
-void rope_rotate(double* x, int D, double pos, double rope_scale, double rope_theta) {
+// RoPE on a D-vector in place (reading of the absent _rope helper, see header): pair i is
+// (i, i + D/2) (rotate-half) or, interleaved, (2i, 2i + 1).
+void rope_rotate(double* x, int D, double pos, double rope_scale, double rope_theta,
+                 bool interleaved = false) {
   int half = D / 2;
   for (int i = 0; i < half; ++i) {
     double freq = std::pow(rope_theta, -2.0 * i / D);
     double ang = pos * rope_scale * freq;
     double c = std::cos(ang), s = std::sin(ang);
-    double a = x[i], b = x[i + half];
-    x[i] = a * c - b * s;
-    x[i + half] = b * c + a * s;
+    const int i0 = interleaved ? 2 * i : i, i1 = interleaved ? 2 * i + 1 : i + half;
+    double a = x[i0], b = x[i1];
+    x[i0] = a * c - b * s;
+    x[i1] = b * c + a * s;
   }
 }
 
@@ -162,8 +167,9 @@ int decode_one(const DecodeArgs& a, int b, int h_qo, double* out, double* lse) {
   std::vector<double> qv(D), kv(D), vv(D), acc(D, 0.0), scores(L);
   for (int d = 0; d < D; ++d)
     qv[d] = load_value(a.q, a.q_dtype, (static_cast<size_t>(b) * a.H_qo + h_qo) * D + d);
-  const bool rope = a.rotary_mode == 1;
-  if (rope) rope_rotate(qv.data(), D, a.q_rope_position[b], a.rope_scale, a.rope_theta);
+  const bool rope = a.rotary_mode == 1 || a.rotary_mode == 2;
+  const bool ilv = a.rotary_mode == 2;
+  if (rope) rope_rotate(qv.data(), D, a.q_rope_position[b], a.rope_scale, a.rope_theta, ilv);
   const double kscale = a.kv_dtype == DT_FP8 ? static_cast<double>(a.k_scale[h]) : 1.0;
   const double vscale = a.kv_dtype == DT_FP8 ? static_cast<double>(a.v_scale[h]) : 1.0;
 
@@ -186,7 +192,7 @@ int decode_one(const DecodeArgs& a, int b, int h_qo, double* out, double* lse) {
     for (int d = 0; d < D; ++d)
       kv[d] = load_value(a.pages, a.kv_dtype, pool_index(a, page, 0, h, off, d)) * kscale;
     if (rope) rope_rotate(kv.data(), D, static_cast<double>(a.k_rope_pos_offset[b]) + r,
-                          a.rope_scale, a.rope_theta);
+                          a.rope_scale, a.rope_theta, ilv);
     double s = 0.0;
     for (int d = 0; d < D; ++d) s += qv[d] * kv[d];
     s *= static_cast<double>(a.sm_scale);
@@ -218,8 +224,9 @@ uint8_t oracle_fp8_e4m3fn_encode(float x) { return fp8_encode(x); }
 double oracle_bf16_value(uint16_t bits) { return bf16_value(bits); }
 
 // Applies the RoPE reading to x[D] in place at position pos (exposed for the invariant pins).
-void oracle_rope_rotate(double* x, int32_t D, double pos, float rope_scale, float rope_theta) {
-  rope_rotate(x, D, pos, rope_scale, rope_theta);
+void oracle_rope_rotate(double* x, int32_t D, double pos, float rope_scale, float rope_theta,
+                        int32_t interleaved) {
+  rope_rotate(x, D, pos, rope_scale, rope_theta, interleaved != 0);
 }
 
 // Decode attention for the selected (b, h_qo) pairs (sel = [n_sel, 2]; n_sel == 0 means every

@@ -274,18 +274,24 @@ def test_rope_decode_uses_compacted_row_positions():
             assert abs(lse[b, hq] - l) < 1e-12
 
 
-def test_rope_only_mode_one_applies():
+def test_rope_only_modes_one_and_two_apply():
+    """rotary_mode 1 (rotate-half) and 2 (interleaved) apply RoPE; any other value applies none."""
     w = small(seq_lens=[13, 3, 16])
     out0, lse0 = run_oracle(w)
     pos = np.array([100, 7, 3], np.int32)
-    for mode in (0, 2, -1):
+    for mode in (1, 2):
+        out1, _ = run_oracle(w, rotary_mode=mode, q_rope_position=pos, k_rope_pos_offset=pos)
+        assert np.abs(out1 - out0).max() > 1e-3
+    for mode in (0, 3, -1):
         out1, lse1 = run_oracle(w, rotary_mode=mode, q_rope_position=pos, k_rope_pos_offset=pos)
         assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
 
 
-def test_rope_relative_position_invariance():
-    """Shifting the q position and the k offset by the same amount leaves every score unchanged."""
-    w = small(seq_lens=[13, 3, 16], rotary_mode=1, rope_theta=500000.0)
+@pytest.mark.parametrize("mode", [1, 2])
+def test_rope_relative_position_invariance(mode):
+    """Shifting the q position and the k offset by the same amount leaves every score unchanged
+    (both layouts)."""
+    w = small(seq_lens=[13, 3, 16], rotary_mode=mode, rope_theta=500000.0)
     qp = np.array([12, 2, 15], np.int32)
     ko = np.zeros(3, np.int32)
     out0, lse0 = run_oracle(w, q_rope_position=qp, k_rope_pos_offset=ko)
@@ -590,3 +596,21 @@ def test_sink_matches_dense_with_an_extra_logit(kv_dtype, q_dtype):
             np.testing.assert_allclose(out[b, hq], (e[:, None] * Vx).sum(0) / e.sum(), rtol=0,
                                        atol=1e-12)
             assert abs(lse[b, hq] - (m + np.log(e.sum())) * LOG2E) < 1e-12
+
+
+def test_interleaved_rope_is_rotate_half_of_the_deinterleaved_vector():
+    """The interleaved layout pairs (2i, 2i + 1) with frequency i; moving element 2i to i and
+    2i + 1 to i + D/2 turns it into rotate-half: R_ilv(x) = P^-1 R_half(P x) for every position,
+    scale and base; R_ilv(0) = I and pairs (2i, 2i + 1) keep their norms."""
+    rng = np.random.default_rng(2)
+    D = 64
+    x = rng.standard_normal(D)
+    perm = np.concatenate([np.arange(0, D, 2), np.arange(1, D, 2)])  # P x = x[perm]
+    for pos, scale, theta in ((0, 1.0, 1e4), (1, 1.0, 1e4), (37, 0.5, 5e5), (4099, 1.0, 1e4)):
+        y = oracle.rope_rotate(x, pos, scale, theta, interleaved=True)
+        z = np.empty(D)
+        z[perm] = oracle.rope_rotate(x[perm], pos, scale, theta)
+        np.testing.assert_allclose(y, z, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(y[0::2] ** 2 + y[1::2] ** 2, x[0::2] ** 2 + x[1::2] ** 2,
+                                   atol=1e-12)
+    assert np.array_equal(oracle.rope_rotate(x, 0, 1.0, 1e4, interleaved=True), x)
