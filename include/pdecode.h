@@ -98,10 +98,13 @@ typedef struct pdecode_desc {
 } pdecode_desc;
 
 /* Rotary embedding on Q and K inside the kernel; a NULL pointer to this struct means none.
- * Applied iff rotary_mode == 1 (any other value: none). Rotate-half over the two contiguous
- * halves of the head dimension: for i < D/2, angle = position * rope_scale * rope_theta^(-2i/D),
- * x'[i] = x[i] cos - x[i + D/2] sin, x'[i + D/2] = x[i + D/2] cos + x[i] sin. The rotated q and k
- * stay in fp32. */
+ * rotary_mode == 1: rotate-half over the two contiguous halves of the head dimension: for
+ * i < D/2, angle = position * rope_scale * rope_theta^(-2i/D), x'[i] = x[i] cos - x[i + D/2] sin,
+ * x'[i + D/2] = x[i + D/2] cos + x[i] sin. rotary_mode == 2: the interleaved layout (the AWS
+ * attention_block_tkg page's rope_contiguous_layout = False), the same rotation on the pairs
+ * (2i, 2i + 1); supported on the persistent matrix-core schedule (BF16 pool, or FP8 at head_dim
+ * 128; batch <= 1024), not with pdecode_append_attention; otherwise UNSUPPORTED. Any other value:
+ * no RoPE. The rotated q and k stay in fp32 (or a bf16 pair that holds them to 2^-16). */
 typedef struct pdecode_rope {
   int32_t rotary_mode;
   float rope_scale;

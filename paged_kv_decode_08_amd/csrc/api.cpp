@@ -160,7 +160,8 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   if (st != PDECODE_OK) return st;
   if ((st = check_attention_shape(d)) != PDECODE_OK) return st;
   if (!std::isfinite(sm_scale)) return PDECODE_ERR_INVALID_ARG;
-  const bool rotary = rope && rope->rotary_mode == 1;
+  // rotary_mode 1: rotate-half; 2: interleaved pairs; anything else: no RoPE
+  const bool rotary = rope && (rope->rotary_mode == 1 || rope->rotary_mode == 2);
   if (rotary && (!rope->q_rope_position || !rope->k_rope_pos_offset ||
                  !(rope->rope_theta > 0.f) || !std::isfinite(rope->rope_theta) ||
                  !std::isfinite(rope->rope_scale)))
@@ -170,6 +171,8 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
     return PDECODE_ERR_INVALID_ARG;
   const Plan pl = make_plan(d, rotary, qo_len);
   if ((fused || qo_len > 1 || d->sink_logits) && !pl.persistent) return PDECODE_ERR_UNSUPPORTED;
+  // interleaved RoPE: the persistent matrix-core kernels only, not fused with the append
+  if (rotary && rope->rotary_mode == 2 && (!pl.persistent || fused)) return PDECODE_ERR_UNSUPPORTED;
   const int64_t grid = int64_t(pl.num_chunks) * d->batch * d->num_kv_heads;
   if (grid > INT_MAX) return PDECODE_ERR_UNSUPPORTED;
   if (pl.workspace_bytes() > 0) {
@@ -206,7 +209,7 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   p.T = qo_len;
   p.max_num_pages = d->max_num_pages;
   p.sliding = d->sliding_window;
-  p.rotary = rotary ? 1 : 0;
+  p.rotary = rotary ? rope->rotary_mode : 0;
   p.rope_scale = rotary ? rope->rope_scale : 1.f;
   p.rope_theta = rotary ? rope->rope_theta : 1.f;
   p.score_scale = sm_scale * pdk::kLog2e;

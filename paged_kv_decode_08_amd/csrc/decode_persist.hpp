@@ -249,11 +249,12 @@ __device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
 // FUSED: the call also appends each sequence's new K/V row (p.new_k, p.new_v).
 // MT: several query tokens per sequence (p.T > 1; no RoPE, no window): the G T columns of the
 // MFMA B operand are token-major and each is causally capped.
-template <int KVT, int D, int PS, int GP, bool ROPE, bool FUSED, bool MT = false>
+// ILV (with ROPE): the interleaved RoPE layout (rotary_mode 2).
+template <int KVT, int D, int PS, int GP, bool ROPE, bool FUSED, bool MT = false, bool ILV = false>
 __global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mfma_persist_kernel(DecodeParams p) {
   // items of 16 rows: a 32-row page is two items (half the registers per item in flight)
-  using C = MfmaCore<KVT, D, 16, GP, ROPE>;
+  using C = MfmaCore<KVT, D, 16, GP, ROPE, ILV>;
   constexpr int SUB = PS / 16;
   constexpr int BLOCK = PS * C::ROW;  // bytes of one (page, K|V, head) block
   using Buf = typename C::Buf;
@@ -782,15 +783,15 @@ inline int resident_workgroups(const void* kernel, size_t lds) {
   return n;
 }
 
-template <int KVT, int D, int PS, int GP, bool ROPE, bool FUSED, bool MT = false>
+template <int KVT, int D, int PS, int GP, bool ROPE, bool FUSED, bool MT = false, bool ILV = false>
 hipError_t launch_persist_k(const DecodeParams& p, long long max_jobs, hipStream_t st) {
-  const void* k =
-      reinterpret_cast<const void*>(&decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE, FUSED, MT>);
+  const void* k = reinterpret_cast<const void*>(
+      &decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE, FUSED, MT, ILV>);
   const size_t lds = seq_table_bytes(p.B);
   const int resident = resident_workgroups(k, lds);
   if (resident <= 0) return hipErrorInvalidConfiguration;
   const unsigned grid = static_cast<unsigned>((max_jobs < resident ? (max_jobs > 0 ? max_jobs : 1) : resident));
-  hipLaunchKernelGGL((decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE, FUSED, MT>), dim3(grid),
+  hipLaunchKernelGGL((decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE, FUSED, MT, ILV>), dim3(grid),
                      dim3(64 * kPWaves), lds, st, p);
   return hipGetLastError();
 }
@@ -803,5 +804,10 @@ hipError_t launch_persist_fused(const DecodeParams& p, long long max_jobs, hipSt
 // append.
 template <int KVT, int D, int PS, int GP>
 hipError_t launch_persist_multi(const DecodeParams& p, long long max_jobs, hipStream_t st);
+
+// The interleaved-RoPE instantiations of launch_persist_k (decode_rope_ilv.hip): bf16 KV, and fp8
+// KV at D = 128.
+template <int KVT, int D, int PS, int GP>
+hipError_t launch_persist_ilv(const DecodeParams& p, long long max_jobs, hipStream_t st);
 
 }  // namespace pdk

@@ -82,7 +82,9 @@ __device__ __forceinline__ void split_bf16(float x, float y, uint32_t& hi, uint3
   lo = pack_bf16x2(x - bf16_lo(hi), y - bf16_hi(hi));
 }
 
-template <int KVT, int D, int PS, int GP, bool ROPE = false>
+// ILV (with ROPE): the interleaved RoPE layout, pairs (2i, 2i + 1), both in the 8 consecutive
+// dims a lane holds per k-step.
+template <int KVT, int D, int PS, int GP, bool ROPE = false, bool ILV = false>
 struct MfmaCore {
   static constexpr bool FP8 = KVT == kFP8;
   static constexpr int EB = FP8 ? 1 : 2;        // bytes per element
@@ -167,7 +169,26 @@ struct MfmaCore {
   // Rotates the q operand to position qpos (RoPE) and splits it into qop (high) and qlo.
   // s_freq[i] = (fhi, flo) of frequency i (rope_freq).
   __device__ __forceinline__ void rope_q(int qpos, const float2* s_freq) {
-    if constexpr (ROPE) {
+    if constexpr (ROPE && ILV) {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        float x[8], y[8];
+        Kv<kBF16>::unpack(qop[j], x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float2 f = s_freq[q_dim0(j) / 2 + e];
+          float c, sn;
+          rope_cs_hw(qpos, f.x, f.y, c, sn);
+          y[2 * e] = x[2 * e] * c - x[2 * e + 1] * sn;
+          y[2 * e + 1] = x[2 * e + 1] * c + x[2 * e] * sn;
+        }
+        uint32_t h[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_bf16(y[2 * e], y[2 * e + 1], h[e], lo[e]);
+        qop[j] = make_uint4(h[0], h[1], h[2], h[3]);
+        qlo[j] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      }
+    } else if constexpr (ROPE) {
 #pragma unroll
       for (int j = 0; j < KH; ++j) {
         float x1[8], x2[8];
@@ -242,6 +263,26 @@ struct MfmaCore {
     if constexpr (ROPE) {
       // this lane's K row (n) rotated to its position, split into high parts and remainders
       uint4 khi[KS], klo[KS];
+      if constexpr (ILV) {
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+          float x[8], y[8];
+          kstep_f32(bf, j, x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float2 f = s_freq[q_dim0(j) / 2 + e];
+            float c, sn;
+            rope_cs_hw(pos0 + n, f.x, f.y, c, sn);
+            y[2 * e] = x[2 * e] * c - x[2 * e + 1] * sn;
+            y[2 * e + 1] = x[2 * e + 1] * c + x[2 * e] * sn;
+          }
+          uint32_t h[4], lo[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) split_bf16(y[2 * e], y[2 * e + 1], h[e], lo[e]);
+          khi[j] = make_uint4(h[0], h[1], h[2], h[3]);
+          klo[j] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
+      } else {
 #pragma unroll
       for (int j = 0; j < KH; ++j) {
         float x1[8], x2[8];
@@ -266,6 +307,7 @@ struct MfmaCore {
         klo[j] = make_uint4(l1[0], l1[1], l1[2], l1[3]);
         khi[j + KH] = make_uint4(h2[0], h2[1], h2[2], h2[3]);
         klo[j + KH] = make_uint4(l2[0], l2[1], l2[2], l2[3]);
+      }
       }
       acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll

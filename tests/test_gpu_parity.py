@@ -788,3 +788,38 @@ def test_learned_sink_multi_token():
     sinks = np.random.default_rng(93).normal(0.0, 2.0, w.H_qo).astype(np.float32)
     _sink_case(w, sinks, 3, T=2)
     _sink_case(w, sinks, 0, T=2)
+
+
+# ---- interleaved RoPE (rotary_mode 2)
+
+@pytest.mark.parametrize("kv,G,D,ps", [("bf16", 4, 128, 16), ("bf16", 2, 64, 32),
+                                       ("bf16", 8, 128, 16), ("fp8", 4, 128, 32),
+                                       ("fp8", 8, 128, 16)])
+def test_rope_interleaved(kv, G, D, ps):
+    """Interleaved RoPE (pairs (2i, 2i + 1)) against the oracle, with a window and sink on half of
+    the cases, and large positions."""
+    lens = [1, 40, 5000, 2049, 3 * ps + 5]
+    win = dict(window=1024, sink=4) if G in (4, 8) and ps == 16 else {}
+    w = synth.make_workload(name=f"ilv_{kv}_G{G}_D{D}_ps{ps}", B=len(lens), H_qo=2 * G, H_kv=2,
+                            D=D, page_size=ps, seq_lens=lens, q_dtype="bf16", kv_dtype=kv,
+                            seed=950 + G + D + ps, max_num_pages=1024, rotary_mode=2,
+                            rope_theta=500000.0, **win)
+    dev = gu.upload(w)
+    out, lse = gu.run_attention(w, dev)
+    check(w, out, lse, label=w.name)
+    out3, lse3 = gu.run_attention(w, dev, num_kv_splits=3)
+    check(w, out3, lse3, label=w.name + " split3")
+
+
+def test_rope_interleaved_unsupported_where_not_built():
+    """Interleaved RoPE is refused (before any launch) on the fp32 pool's vector-ALU kernel and for
+    fp8 at head dim 64."""
+    import paged_kv_decode_08_amd as pk
+    for kv, D in (("f32", 64), ("fp8", 64)):
+        w = synth.make_workload(name=f"ilv_unsup_{kv}", B=2, H_qo=4, H_kv=2, D=D, page_size=16,
+                                seq_lens=[30, 7], q_dtype="f32" if kv == "f32" else "bf16",
+                                kv_dtype=kv, seed=960, max_num_pages=16, rotary_mode=2)
+        dev = gu.upload(w)
+        with pytest.raises(pk.PdecodeError) as e:
+            gu.run_attention(w, dev)
+        assert e.value.status == 2
