@@ -423,7 +423,8 @@ def main():
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                      "algorithmic_bytes": kv_bytes,
                      "kernel": ("pdecode_attention: the decode kernel, plus split_merge_kernel when the plan "
-                                "has more than 8 chunks per sequence"),
+                                "splits sequences and the decode kernel does not merge them itself "
+                                "(instantiations of at most 4 q columns, or more than 8 chunks)"),
                      "avg_launch_us": round(avg_call_s * 1e6, 3),
                      "single_call_event_us_p10": round(float(np.percentile(call_ms, 10)) * 1e3, 3),
                      "single_call_event_us_p90": round(float(np.percentile(call_ms, 90)) * 1e3, 3)},

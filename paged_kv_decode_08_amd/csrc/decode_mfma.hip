@@ -282,7 +282,7 @@ static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipS
     e = p.new_k != nullptr ? launch_persist_fused<KVT, D, PS, GP, ROPE>(p, max_jobs, st)
                            : launch_persist_k<KVT, D, PS, GP, ROPE, false>(p, max_jobs, st);
   }
-  if (e != hipSuccess || p.num_chunks <= 1 || p.num_chunks <= kInMergeChunks) return e;
+  if (e != hipSuccess || p.num_chunks <= 1 || merges_in_kernel<GP>(p.num_chunks)) return e;
   const unsigned rows = static_cast<unsigned>(p.B) * p.T * p.H_qo;
   hipLaunchKernelGGL((split_merge_kernel<D, PS>), dim3((rows + kMergeRows - 1) / kMergeRows),
                      dim3(64 * kMergeRows), 0, st, p);

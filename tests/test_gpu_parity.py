@@ -823,3 +823,17 @@ def test_rope_interleaved_unsupported_where_not_built():
         with pytest.raises(pk.PdecodeError) as e:
             gu.run_attention(w, dev)
         assert e.value.status == 2
+
+
+@pytest.mark.parametrize("kv,splits", [("bf16", 2), ("bf16", 5), ("bf16", 8), ("fp8", 3),
+                                       ("fp8", 8), ("bf16", 9)])
+def test_forced_splits_eight_heads(kv, splits):
+    """8 q heads per KV head: up to 8 chunks are merged inside the persistent kernel (the 4-head
+    and narrower kernels leave them to the split merge kernel), 9 go to the split merge kernel."""
+    lens = [5000, 1, 700, 2100, 33, 4096]
+    w = synth.make_workload(name=f"g8_splits{splits}_{kv}", B=len(lens), H_qo=16, H_kv=2, D=128,
+                            page_size=16 if kv == "bf16" else 32, seq_lens=lens, q_dtype="bf16",
+                            kv_dtype=kv, seed=970 + splits, max_num_pages=1024)
+    dev = gu.upload(w)
+    out, lse = gu.run_attention(w, dev, num_kv_splits=splits)
+    check(w, out, lse, label=w.name)
