@@ -15,10 +15,11 @@
 //    from the page table. The job after the current one is fetched, decoded and its page ids and q
 //    loaded while the current one streams, and its first page is in flight before the current
 //    job's last page is computed, so a workgroup's load stream does not stop at job boundaries.
-//    When the call has at most kInMergeChunks chunks per sequence, the workgroup whose waves
-//    complete a split sequence's count of arrivals merges it at the end of its next job (each wave
-//    arrives once its own partial stores are known complete, one job late, so no wait falls on the
-//    load stream); with more chunks a second, row-parallel kernel (split_merge_kernel) merges them.
+//    In the 8-column instantiations, when the call has at most kInMergeChunks chunks per sequence,
+//    the workgroup whose waves complete a split sequence's count of arrivals merges it at the end
+//    of its next job (each wave arrives once its own partial stores are known complete, a pair of
+//    items into the next job, so no wait falls on the load stream); otherwise a second,
+//    row-parallel kernel (split_merge_kernel) merges them (merges_in_kernel).
 //  * one workgroup per job (decode_mfma_kernel), for batches too large for the LDS job table: the
 //    last workgroup of a split sequence to finish merges it (split.hpp).
 #include "decode_persist.hpp"
