@@ -151,13 +151,13 @@ def apply_sink(out, lse, sink_logits):
     return out, np.where(empty, lse, new)
 
 
-def decode_multi(*, qo_len, q, **kw):
+def decode_multi(*, qo_len, q, select=None, **kw):
     """Decode with qo_len query tokens per sequence (q [B, qo_len, H_qo, D]), causal over the new
     tokens: the last qo_len positions of each sequence are the new tokens, and token t attends
     positions 0 .. total - qo_len + t, i.e. it is the TVM page's single-token decode over that
     prefix of the sequence (its first ceil(len / ps) pages, the last one holding len - (np - 1) ps
     rows). An empty prefix gives the empty convention. No window. Returns (out [B, T, H_qo, D],
-    lse [B, T, H_qo])."""
+    lse [B, T, H_qo]), or, for select = int array [n, 3] of (b, t, h_qo), (out [n, D], lse [n])."""
     B, T, ps = kw["B"], int(qo_len), kw["ps"]
     assert not kw.get("sliding_window"), "several query tokens: no sliding window"
     indptr = np.asarray(kw["indptr"], np.int64)
@@ -184,6 +184,9 @@ def decode_multi(*, qo_len, q, **kw):
     for key in ("q_rope_position", "k_rope_pos_offset"):
         kw.pop(key, None)
     kw.pop("rotary_mode", None)
+    if select is not None:
+        sel = np.asarray(select, np.int64).reshape(-1, 3)
+        return decode(select=np.stack([sel[:, 0] * T + sel[:, 1], sel[:, 2]], 1), **kw)
     out, lse = decode(**kw)
     return out.reshape(B, T, kw["H_qo"], kw["D"]), lse.reshape(B, T, kw["H_qo"])
 

@@ -837,3 +837,68 @@ def test_forced_splits_eight_heads(kv, splits):
     dev = gu.upload(w)
     out, lse = gu.run_attention(w, dev, num_kv_splits=splits)
     check(w, out, lse, label=w.name)
+
+
+# ---- the additions at the full Llama-3-8B-shaped size, on sampled outputs
+
+def test_full_size_fused_step_sampled():
+    """pdecode_append_attention on the full Llama-3-8B-shaped workload (NaN in every target row
+    beforehand): every appended row bit-exact, sampled outputs against the oracle's append then
+    decode, every output finite."""
+    w = synth.CONFIGS["llama3_8b_bf16"]()
+    _poison_last_rows(w)
+    nk, nv, _ = synth.append_inputs(T=w.B, H_kv=w.H_kv, D=w.D, page_size=w.page_size,
+                                    max_num_pages=w.max_num_pages, in_dtype="bf16", seed=77,
+                                    slots=np.zeros(w.B, np.int32))
+    sel = _sample_pairs(w, 48, 7)
+    o_ref, l_ref, pool_ref = oracle.append_then_decode(new_k=nk, new_v=nv, select=sel,
+                                                       **w.oracle_kwargs())
+    dev = gu.upload(w)
+    desc = gu.desc_for(w, dev)
+    out = torch.empty((w.B, w.H_qo, w.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H_qo), dtype=torch.float32, device="cuda")
+    pk.append_attention(desc, gu.to_device_storage(nk, "bf16"), gu.to_device_storage(nv, "bf16"),
+                        dev["q"], dev["pages"], dev["indptr"], dev["values"], dev["length_info"],
+                        out, lse, w.sm_scale, workspace=pk.alloc_workspace(desc))
+    torch.cuda.synchronize()
+    slots = oracle.last_position_slots(B=w.B, ps=w.page_size, indptr=w.page_indptr,
+                                       values=w.page_values, length_info=w.length_info)
+    pages_gpu = dev["pages"].view(torch.int16)
+    for s in slots:
+        pg, r = int(s) // w.page_size, int(s) % w.page_size
+        got = pages_gpu[pg, :, :, r, :].cpu().numpy()
+        assert np.array_equal(got, pool_ref[pg, :, :, r, :].view(np.int16)), (pg, r)
+    o_gpu, l_gpu = gu.to_np64(out), gu.to_np64(lse)
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(l_gpu))
+    do = np.abs(o_gpu[sel[:, 0], sel[:, 1]] - o_ref).max()
+    dl = np.abs(l_gpu[sel[:, 0], sel[:, 1]] - l_ref).max()
+    print(f"full-size fused: max|dout|={do:.3g} max|dlse|={dl:.3g}", flush=True)
+    assert do <= 2e-2 and dl <= 1e-3
+
+
+def test_full_size_multi_token_and_sink_sampled():
+    """pdecode_attention_multi (two tokens) with learned sinks on the full Llama-3-8B-shaped
+    workload: sampled (sequence, token, head) outputs against the oracle."""
+    w = synth.CONFIGS["llama3_8b_bf16"]()
+    T = 2
+    qm = synth.multi_query(w, T, seed=78)
+    sinks = np.random.default_rng(79).normal(0.0, 2.0, w.H_qo).astype(np.float32)
+    pairs = _sample_pairs(w, 48, 8)
+    sel = np.stack([pairs[:, 0], np.arange(len(pairs)) % T, pairs[:, 1]], 1).astype(np.int32)
+    kw = {k: v for k, v in w.oracle_kwargs().items() if k != "q"}
+    o0, l0 = oracle.decode_multi(qo_len=T, q=qm, select=sel, **kw)
+    o_ref, l_ref = oracle.apply_sink(o0, l0, sinks[sel[:, 2]])
+    dev = gu.upload(w)
+    desc = gu.desc_for(w, dev, sink_logits=torch.from_numpy(sinks).cuda())
+    out = torch.empty((w.B, T, w.H_qo, w.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, T, w.H_qo), dtype=torch.float32, device="cuda")
+    pk.attention_multi(desc, T, gu.to_device_storage(qm, "bf16"), dev["pages"], dev["indptr"],
+                       dev["values"], dev["length_info"], out, lse, w.sm_scale,
+                       workspace=pk.alloc_workspace_multi(desc, T))
+    torch.cuda.synchronize()
+    o_gpu, l_gpu = gu.to_np64(out), gu.to_np64(lse)
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(l_gpu))
+    do = np.abs(o_gpu[sel[:, 0], sel[:, 1], sel[:, 2]] - o_ref).max()
+    dl = np.abs(l_gpu[sel[:, 0], sel[:, 1], sel[:, 2]] - l_ref).max()
+    print(f"full-size multi + sink: max|dout|={do:.3g} max|dlse|={dl:.3g}", flush=True)
+    assert do <= 2e-2 and dl <= 1e-3

@@ -614,3 +614,15 @@ def test_interleaved_rope_is_rotate_half_of_the_deinterleaved_vector():
         np.testing.assert_allclose(y[0::2] ** 2 + y[1::2] ** 2, x[0::2] ** 2 + x[1::2] ** 2,
                                    atol=1e-12)
     assert np.array_equal(oracle.rope_rotate(x, 0, 1.0, 1e4, interleaved=True), x)
+
+
+def test_multi_token_select_matches_full():
+    """decode_multi on selected (b, t, h_qo) triples returns those rows of the full result."""
+    w = small(B=4, seq_lens=[7, 1, 13, 0])
+    qm = synth.multi_query(w, 3, seed=6)
+    kw = {k: v for k, v in w.oracle_kwargs().items() if k != "q"}
+    out, lse = oracle.decode_multi(qo_len=3, q=qm, **kw)
+    sel = np.array([[0, 2, 1], [2, 0, 3], [1, 0, 0], [3, 1, 2]], np.int32)
+    o, l = oracle.decode_multi(qo_len=3, q=qm, select=sel, **kw)
+    assert np.array_equal(o, out[sel[:, 0], sel[:, 1], sel[:, 2]])
+    assert np.array_equal(l, lse[sel[:, 0], sel[:, 1], sel[:, 2]])
