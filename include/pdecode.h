@@ -64,13 +64,19 @@ typedef enum pdecode_status {
 typedef enum pdecode_dtype {
   PDECODE_F32 = 0,
   PDECODE_BF16 = 1,
-  PDECODE_FP8_E4M3FN = 2                /* OCP e4m3fn: bias 7, no infinities, max 448            */
+  PDECODE_FP8_E4M3FN = 2,               /* OCP e4m3fn: bias 7, no infinities, max 448            */
+  PDECODE_FP8_E4M3 = 3                  /* IEEE-style e4m3: bias 7, exponent 15 = inf / NaN, max
+                                           240 (the AWS attention_block_tkg page's default
+                                           NON_OCP float8_e4m3). As a pool: the append writes it
+                                           (round to nearest even, saturating to +-240); a pool
+                                           read by the decode must hold finite codes, which have
+                                           their e4m3fn values. Not with pdecode_append_attention. */
 } pdecode_dtype;
 
 /* Problem description shared by pdecode_attention and pdecode_append_kv.
  * Supported set: head_dim in {64, 128}; page_size in {16, 32}; group size
  * num_qo_heads / num_kv_heads in 1..8; (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
- * (BF16, FP8_E4M3FN)}. The output dtype equals q_dtype. */
+ * (BF16, FP8_E4M3FN), (BF16, FP8_E4M3)}. The output dtype equals q_dtype. */
 typedef struct pdecode_desc {
   int32_t batch;          /* B >= 0                                                            */
   int32_t num_qo_heads;   /* H_qo > 0, a multiple of num_kv_heads                              */
@@ -86,8 +92,8 @@ typedef struct pdecode_desc {
                              sequence longer than the bound is still computed exactly.           */
   int32_t num_kv_splits;  /* 0 = automatic; 1 = never split a sequence; n > 1 = split each
                              sequence's pages into at most n chunks merged by log-sum-exp         */
-  const float *k_scale;   /* device fp32 [H_kv]; required iff kv_dtype is FP8: K = code * scale */
-  const float *v_scale;   /* device fp32 [H_kv]; required iff kv_dtype is FP8: V = code * scale */
+  const float *k_scale;   /* device fp32 [H_kv]; required iff kv_dtype is an FP8: K = code * scale */
+  const float *v_scale;   /* device fp32 [H_kv]; required iff kv_dtype is an FP8: V = code * scale */
   const float *sink_logits; /* device fp32 [H_qo] or NULL: learned attention sink per q head (the
                              AWS attention_block_tkg page's `sink`, one value per q head). Read as
                              a logit in the units of the scaled score: a sequence with attended

@@ -45,6 +45,10 @@ def lib():
         L.oracle_fp8_e4m3fn_value.argtypes = [ctypes.c_uint8]
         L.oracle_fp8_e4m3fn_encode.restype = ctypes.c_uint8
         L.oracle_fp8_e4m3fn_encode.argtypes = [f32]
+        L.oracle_fp8_e4m3_value.restype = ctypes.c_double
+        L.oracle_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_fp8_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_fp8_e4m3_encode.argtypes = [f32]
         L.oracle_bf16_value.restype = ctypes.c_double
         L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
         L.oracle_rope_rotate.restype = None
@@ -243,6 +247,15 @@ def fp8_encode_array(x):
     x = np.asarray(x, np.float32).ravel()
     f = lib().oracle_fp8_e4m3fn_encode
     return np.array([f(float(v)) for v in x], np.uint8)
+
+
+def fp8_e4m3_value(code: int) -> float:
+    """IEEE-style e4m3 (the NON_OCP float8_e4m3, max 240): value of a code."""
+    return float(lib().oracle_fp8_e4m3_value(code))
+
+
+def fp8_e4m3_encode(x: float) -> int:
+    return int(lib().oracle_fp8_e4m3_encode(x))
 
 
 def bf16_value(bits: int) -> float:

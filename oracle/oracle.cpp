@@ -25,7 +25,9 @@
 //     write with the all-ones uint32 value, which reads as -1 in int32).
 //   * fp8: OCP float8 e4m3fn (bias 7, no infinities, S.1111.111 = NaN, max 448), the OCP variant
 //     named in the attention_block_tkg docs (dtype_mode). Encode = round to nearest, ties to even,
-//     saturating to +-448.
+//     saturating to +-448. The same docs' default NON_OCP mode takes float8_e4m3 with max 240:
+//     read as the IEEE-style e4m3 (bias 7, exponent 15 = infinity / NaN), encoded the same way
+//     with saturation to +-240.
 //
 // Readings where the pages are silent (the helper bodies _get_kv_chunk_len, _get_seq_offset and
 // _rope are imported but not shown):
@@ -49,9 +51,12 @@
 
 namespace {
 
-enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+// DT_FP8: OCP e4m3fn (max 448); DT_FP8_E4M3: the IEEE-style e4m3 of the attention_block_tkg
+// page's default NON_OCP dtype mode (max 240: exponent 15 holds infinities and NaN).
+enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_FP8_E4M3 = 3 };
+bool is_fp8(int dt) { return dt == DT_FP8 || dt == DT_FP8_E4M3; }
 
-int elem_bytes(int dt) { return dt == DT_F32 ? 4 : dt == DT_BF16 ? 2 : dt == DT_FP8 ? 1 : 0; }
+int elem_bytes(int dt) { return dt == DT_F32 ? 4 : dt == DT_BF16 ? 2 : is_fp8(dt) ? 1 : 0; }
 
 // bfloat16 is the upper 16 bits of an IEEE binary32.
 double bf16_value(uint16_t h) {
@@ -72,9 +77,26 @@ double fp8_value(uint8_t c) {
   return s ? -mag : mag;
 }
 
+// IEEE-style e4m3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is subnormal;
+// exponent 15 is infinity (mantissa 0) or NaN; the largest finite value is 1.75 * 2^7 = 240.
+double fp8_e4m3_value(uint8_t c) {
+  int s = (c >> 7) & 1, e = (c >> 3) & 15, m = c & 7;
+  double mag;
+  if (e == 15) {
+    if (m != 0) return std::nan("");
+    mag = HUGE_VAL;
+  } else if (e == 0) {
+    mag = std::ldexp(m / 8.0, -6);
+  } else {
+    mag = std::ldexp(1.0 + m / 8.0, e - 7);
+  }
+  return s ? -mag : mag;
+}
+
 double load_value(const void* base, int dt, size_t idx) {
   if (dt == DT_F32) return static_cast<const float*>(base)[idx];
   if (dt == DT_BF16) return bf16_value(static_cast<const uint16_t*>(base)[idx]);
+  if (dt == DT_FP8_E4M3) return fp8_e4m3_value(static_cast<const uint8_t*>(base)[idx]);
   return fp8_value(static_cast<const uint8_t*>(base)[idx]);
 }
 
@@ -89,6 +111,25 @@ uint8_t fp8_encode(float x) {
   double best_err = a;  // code 0 is +0
   for (int c = 1; c <= 0x7E; ++c) {
     double err = std::fabs(a - fp8_value(static_cast<uint8_t>(c)));
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return sign | static_cast<uint8_t>(best);
+}
+
+// Nearest IEEE-style e4m3 code to a float, ties to the even code, saturating to +-240 (finite
+// codes only). Brute force over the 120 non-negative finite codes.
+uint8_t fp8_e4m3_encode(float x) {
+  if (std::isnan(x)) return 0x7F;
+  uint8_t sign = std::signbit(x) ? 0x80 : 0x00;
+  double a = std::fabs(static_cast<double>(x));
+  if (a >= 240.0) return sign | 0x77;
+  int best = 0;
+  double best_err = a;
+  for (int c = 1; c <= 0x77; ++c) {
+    double err = std::fabs(a - fp8_e4m3_value(static_cast<uint8_t>(c)));
     if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
       best = c;
       best_err = err;
@@ -170,8 +211,8 @@ int decode_one(const DecodeArgs& a, int b, int h_qo, double* out, double* lse) {
   const bool rope = a.rotary_mode == 1 || a.rotary_mode == 2;
   const bool ilv = a.rotary_mode == 2;
   if (rope) rope_rotate(qv.data(), D, a.q_rope_position[b], a.rope_scale, a.rope_theta, ilv);
-  const double kscale = a.kv_dtype == DT_FP8 ? static_cast<double>(a.k_scale[h]) : 1.0;
-  const double vscale = a.kv_dtype == DT_FP8 ? static_cast<double>(a.v_scale[h]) : 1.0;
+  const double kscale = is_fp8(a.kv_dtype) ? static_cast<double>(a.k_scale[h]) : 1.0;
+  const double vscale = is_fp8(a.kv_dtype) ? static_cast<double>(a.v_scale[h]) : 1.0;
 
   auto locate = [&](int64_t r, int64_t* page, int* off) -> int {
     int64_t pos = (r < sink) ? r : r - sink + win_off;
@@ -221,6 +262,8 @@ extern "C" {
 
 double oracle_fp8_e4m3fn_value(uint8_t code) { return fp8_value(code); }
 uint8_t oracle_fp8_e4m3fn_encode(float x) { return fp8_encode(x); }
+double oracle_fp8_e4m3_value(uint8_t code) { return fp8_e4m3_value(code); }
+uint8_t oracle_fp8_e4m3_encode(float x) { return fp8_e4m3_encode(x); }
 double oracle_bf16_value(uint16_t bits) { return bf16_value(bits); }
 
 // Applies the RoPE reading to x[D] in place at position pos (exposed for the invariant pins).
@@ -243,7 +286,7 @@ int32_t oracle_decode(int32_t B, int32_t H_qo, int32_t H_kv, int32_t D, int32_t 
   if (B < 0 || H_kv <= 0 || H_qo <= 0 || H_qo % H_kv != 0 || D <= 0 || D % 2 != 0 || ps <= 0)
     return 4;
   if (elem_bytes(q_dtype) == 0 || elem_bytes(kv_dtype) == 0) return 4;
-  if (kv_dtype == DT_FP8 && (k_scale == nullptr || v_scale == nullptr)) return 4;
+  if (is_fp8(kv_dtype) && (k_scale == nullptr || v_scale == nullptr)) return 4;
   DecodeArgs a{B, H_qo, H_kv, D, ps, max_num_pages, q_dtype, kv_dtype, q, pages, indptr, values,
                nnz, length_info, sliding_window, rotary_mode, rope_scale, rope_theta,
                q_rope_position, k_rope_pos_offset, sm_scale, k_scale, v_scale};
@@ -296,8 +339,8 @@ int32_t oracle_append_kv(int32_t T, int32_t H_kv, int32_t D, int32_t ps, int32_t
   if (T < 0 || H_kv <= 0 || D <= 0 || ps <= 0) return 4;
   const int ib = elem_bytes(in_dtype), kb = elem_bytes(kv_dtype);
   if (ib == 0 || kb == 0) return 4;
-  if (kv_dtype != DT_FP8 && in_dtype != kv_dtype) return 4;
-  if (kv_dtype == DT_FP8 && (in_dtype == DT_FP8 || !k_scale || !v_scale)) return 4;
+  if (!is_fp8(kv_dtype) && in_dtype != kv_dtype) return 4;
+  if (is_fp8(kv_dtype) && (is_fp8(in_dtype) || !k_scale || !v_scale)) return 4;
   for (int t = 0; t < T; ++t) {
     int64_t s = slots[t];
     if (s < 0) continue;
@@ -309,10 +352,11 @@ int32_t oracle_append_kv(int32_t T, int32_t H_kv, int32_t D, int32_t ps, int32_t
         for (int d = 0; d < D; ++d) {
           size_t si = (static_cast<size_t>(t) * H_kv + h) * D + d;
           size_t di = ((((static_cast<size_t>(page) * 2 + kv) * H_kv + h) * ps + off) * D) + d;
-          if (kv_dtype == DT_FP8) {
+          if (is_fp8(kv_dtype)) {
             float x = static_cast<float>(load_value(src, in_dtype, si));
             float sc = kv == 0 ? k_scale[h] : v_scale[h];
-            static_cast<uint8_t*>(pages)[di] = fp8_encode(x / sc);
+            static_cast<uint8_t*>(pages)[di] =
+                kv_dtype == DT_FP8 ? fp8_encode(x / sc) : fp8_e4m3_encode(x / sc);
           } else {
             std::memcpy(static_cast<uint8_t*>(pages) + di * kb,
                         static_cast<const uint8_t*>(src) + si * ib, kb);

@@ -28,9 +28,11 @@ struct Plan {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+bool is_fp8(int kv) { return kv == PDECODE_FP8_E4M3FN || kv == PDECODE_FP8_E4M3; }
+
 bool supported_pair(int q, int kv) {
   return (q == PDECODE_F32 && kv == PDECODE_F32) || (q == PDECODE_BF16 && kv == PDECODE_BF16) ||
-         (q == PDECODE_BF16 && kv == PDECODE_FP8_E4M3FN);
+         (q == PDECODE_BF16 && is_fp8(kv));
 }
 
 pdecode_status check_desc(const pdecode_desc* d) {
@@ -40,10 +42,9 @@ pdecode_status check_desc(const pdecode_desc* d) {
     return PDECODE_ERR_INVALID_ARG;
   if (d->num_qo_heads % d->num_kv_heads != 0) return PDECODE_ERR_INVALID_ARG;
   if (d->sliding_window != 0 && d->sliding_window != 1) return PDECODE_ERR_INVALID_ARG;
-  if (d->q_dtype < 0 || d->q_dtype > 2 || d->kv_dtype < 0 || d->kv_dtype > 2)
+  if (d->q_dtype < 0 || d->q_dtype > 2 || d->kv_dtype < 0 || d->kv_dtype > 3)
     return PDECODE_ERR_INVALID_ARG;
-  if (d->kv_dtype == PDECODE_FP8_E4M3FN && (!d->k_scale || !d->v_scale))
-    return PDECODE_ERR_INVALID_ARG;
+  if (is_fp8(d->kv_dtype) && (!d->k_scale || !d->v_scale)) return PDECODE_ERR_INVALID_ARG;
   if (!supported_pair(d->q_dtype, d->kv_dtype)) return PDECODE_ERR_UNSUPPORTED;
   return PDECODE_OK;
 }
@@ -68,7 +69,7 @@ Plan make_plan(const pdecode_desc* d, bool rope, int qo_len = 1) {
   const int64_t max_slots = (max_len + ps - 1) / ps + (d->sliding_window ? 2 : 0);
   const int64_t units = int64_t(d->batch) * d->num_kv_heads;
 
-  const bool persistent = (d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN) &&
+  const bool persistent = (d->kv_dtype == PDECODE_BF16 || is_fp8(d->kv_dtype)) &&
                           d->batch <= kPersistMaxBatch &&
                           (!rope || d->kv_dtype == PDECODE_BF16 || d->head_dim == 128);
   int64_t chunk;
@@ -171,6 +172,8 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
     return PDECODE_ERR_INVALID_ARG;
   const Plan pl = make_plan(d, rotary, qo_len);
   if ((fused || qo_len > 1 || d->sink_logits) && !pl.persistent) return PDECODE_ERR_UNSUPPORTED;
+  // the fused append writes e4m3fn codes only
+  if (fused && d->kv_dtype == PDECODE_FP8_E4M3) return PDECODE_ERR_UNSUPPORTED;
   // interleaved RoPE: the persistent matrix-core kernels only, not fused with the append
   if (rotary && rope->rotary_mode == 2 && (!pl.persistent || fused)) return PDECODE_ERR_UNSUPPORTED;
   const int64_t grid = int64_t(pl.num_chunks) * d->batch * d->num_kv_heads;
@@ -221,13 +224,16 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   // bf16 / fp8 KV: q.K on the matrix cores (4-wave workgroups, persistent over a job queue up to
   // kPersistMaxBatch sequences, else one per chunk), RoPE included for bf16 KV and for fp8 KV at
   // head_dim 128; otherwise the vector-ALU kernel (one wave per chunk; RoPE rotates K in fp32).
-  const bool mfma = (d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN) &&
+  // An IEEE-style e4m3 pool holds finite codes only (a precondition; the append saturates to
+  // +-240), and every finite code has its e4m3fn value: the decode kernels read it as e4m3fn.
+  const int kv_read = d->kv_dtype == PDECODE_FP8_E4M3 ? PDECODE_FP8_E4M3FN : d->kv_dtype;
+  const bool mfma = (kv_read == PDECODE_BF16 || kv_read == PDECODE_FP8_E4M3FN) &&
                     (!rotary || d->kv_dtype == PDECODE_BF16 || d->head_dim == 128);
   if (mfma)
-    st = hip_status(pdk::launch_decode_mfma(p, d->kv_dtype, d->head_dim, d->page_size, gp,
+    st = hip_status(pdk::launch_decode_mfma(p, kv_read, d->head_dim, d->page_size, gp,
                                             pl.persistent, rotary, grid, s));
   else
-    st = hip_status(pdk::launch_decode_valu(p, d->kv_dtype, d->head_dim, d->page_size, gp,
+    st = hip_status(pdk::launch_decode_valu(p, kv_read, d->head_dim, d->page_size, gp,
                                             static_cast<unsigned>(grid), s));
   return st;
 }
@@ -276,7 +282,7 @@ pdecode_status pdecode_append_attention(const pdecode_desc* d, const void* new_k
                                         size_t workspace_bytes, void* stream) {
   if (d && d->batch > 0 && (!new_k || !new_v)) return PDECODE_ERR_INVALID_ARG;
   if (d && d->batch > 0 &&
-      !(d->kv_dtype == PDECODE_BF16 || d->kv_dtype == PDECODE_FP8_E4M3FN))
+      !(d->kv_dtype == PDECODE_BF16 || is_fp8(d->kv_dtype)))
     return check_desc(d) != PDECODE_OK ? check_desc(d) : PDECODE_ERR_UNSUPPORTED;
   return attention_impl(d, new_k, new_v, q, pages, page_indptr, page_values, length_info, rope,
                         sm_scale, out, lse, workspace, workspace_bytes, stream);
@@ -300,8 +306,7 @@ pdecode_status pdecode_append_kv(const pdecode_desc* d, const void* new_k, const
                                  void* stream) {
   pdecode_status st = check_desc(d);
   // Append also quantises fp32 rows into an fp8 pool.
-  if (st == PDECODE_ERR_UNSUPPORTED && d->q_dtype == PDECODE_F32 &&
-      d->kv_dtype == PDECODE_FP8_E4M3FN)
+  if (st == PDECODE_ERR_UNSUPPORTED && d->q_dtype == PDECODE_F32 && is_fp8(d->kv_dtype))
     st = PDECODE_OK;
   if (st != PDECODE_OK) return st;
   if (num_tokens < 0) return PDECODE_ERR_INVALID_ARG;

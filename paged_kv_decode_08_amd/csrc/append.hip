@@ -24,6 +24,7 @@ __device__ __forceinline__ bool append_slot(const AppendParams& p, int t, size_t
 template <int IT, int KVT>
 __global__ __launch_bounds__(256) void append_vec_kernel(AppendParams p, int vpr, long long total) {
   constexpr int EPV = KVT == kF32 ? 4 : KVT == kBF16 ? 8 : 16;  // elements per 16-byte output
+  constexpr bool E4M3 = KVT == kFP8E4M3;
   const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const int v = static_cast<int>(i % vpr);
@@ -53,13 +54,14 @@ __global__ __launch_bounds__(256) void append_vec_kernel(AppendParams p, int vpr
 #pragma unroll
       for (int q = 0; q < 2; ++q) Kv<kBF16>::unpack(s4[q], x + 8 * q);
     }
+    auto enc = [](float v) { return E4M3 ? f32_to_fp8_e4m3(v) : f32_to_fp8(v); };
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      w[q] = uint32_t(f32_to_fp8(__fdiv_rn(x[4 * q], sc))) |
-             uint32_t(f32_to_fp8(__fdiv_rn(x[4 * q + 1], sc))) << 8 |
-             uint32_t(f32_to_fp8(__fdiv_rn(x[4 * q + 2], sc))) << 16 |
-             uint32_t(f32_to_fp8(__fdiv_rn(x[4 * q + 3], sc))) << 24;
+      w[q] = uint32_t(enc(__fdiv_rn(x[4 * q], sc))) |
+             uint32_t(enc(__fdiv_rn(x[4 * q + 1], sc))) << 8 |
+             uint32_t(enc(__fdiv_rn(x[4 * q + 2], sc))) << 16 |
+             uint32_t(enc(__fdiv_rn(x[4 * q + 3], sc))) << 24;
     o = make_uint4(w[0], w[1], w[2], w[3]);
   }
   reinterpret_cast<uint4*>(p.pages)[dst_row * vpr + v] = o;
@@ -86,7 +88,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     } else {
       const float x = load_q<IT>(in, src);
       const float sc = kv ? p.v_scale[h] : p.k_scale[h];
-      static_cast<uint8_t*>(p.pages)[dst] = f32_to_fp8(__fdiv_rn(x, sc));
+      const float y = __fdiv_rn(x, sc);
+      static_cast<uint8_t*>(p.pages)[dst] = KVT == kFP8E4M3 ? f32_to_fp8_e4m3(y) : f32_to_fp8(y);
     }
   }
 }
@@ -114,6 +117,8 @@ hipError_t launch_append(const AppendParams& p, int in_dtype, int kv_dtype, hipS
   if (in_dtype == kBF16 && kv_dtype == kBF16) return launch_it<kBF16, kBF16>(p, st);
   if (in_dtype == kBF16 && kv_dtype == kFP8) return launch_it<kBF16, kFP8>(p, st);
   if (in_dtype == kF32 && kv_dtype == kFP8) return launch_it<kF32, kFP8>(p, st);
+  if (in_dtype == kBF16 && kv_dtype == kFP8E4M3) return launch_it<kBF16, kFP8E4M3>(p, st);
+  if (in_dtype == kF32 && kv_dtype == kFP8E4M3) return launch_it<kF32, kFP8E4M3>(p, st);
   return hipErrorInvalidValue;
 }
 

@@ -6,7 +6,9 @@
 
 namespace pdk {
 
-enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+// kFP8: OCP e4m3fn; kFP8E4M3: the IEEE-style e4m3 (max 240), written only by the append kernel
+// (its finite codes decode as e4m3fn codes do, so the decode kernels read it as kFP8)
+enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kFP8E4M3 = 3 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kEmptyLse = -5e4f;  // lse of a sequence with no attended rows
@@ -115,6 +117,14 @@ __device__ __forceinline__ uint8_t f32_to_fp8(float x) {
   // smallest normal, code 0x08)
   const uint32_t m = static_cast<uint32_t>(rintf(__uint_as_float(u) * 512.0f));
   return static_cast<uint8_t>(sign | m);
+}
+
+// IEEE-style e4m3 (bias 7, exponent 15 reserved for infinity and NaN, max 240), round to nearest
+// even with saturation to +-240: below 248 in magnitude the e4m3fn code is the e4m3 code; from 248
+// up e4m3fn rounds to 256 or more (exponent 15), which saturates to 240. NaN stays NaN (0x7F).
+__device__ __forceinline__ uint8_t f32_to_fp8_e4m3(float x) {
+  const uint8_t c = f32_to_fp8(x);
+  return ((c & 0x78) == 0x78 && (c & 0x7F) != 0x7F) ? static_cast<uint8_t>((c & 0x80) | 0x77) : c;
 }
 
 // A 16-byte vector of KV elements decoded to fp32.

@@ -24,10 +24,13 @@ import math
 import numpy as np
 import torch
 
-DTYPE_CODE = {"f32": 0, "bf16": 1, "fp8": 2}
-STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
-ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
-POISON = {"f32": np.float32(np.nan).view(np.uint32), "bf16": 0x7FC0, "fp8": 0x7F}
+# "fp8": OCP e4m3fn codes; "fp8e4m3": IEEE-style e4m3 codes (max 240), drawn within +-240 where
+# both formats give the same code to every value
+DTYPE_CODE = {"f32": 0, "bf16": 1, "fp8": 2, "fp8e4m3": 3}
+STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "fp8e4m3": np.uint8}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "fp8e4m3": 1}
+POISON = {"f32": np.float32(np.nan).view(np.uint32), "bf16": 0x7FC0, "fp8": 0x7F,
+          "fp8e4m3": 0x7F}
 
 
 def _rng(seed: int, stream: int) -> np.random.Generator:
@@ -44,6 +47,8 @@ def cast_f32(x: np.ndarray, dtype: str) -> np.ndarray:
         return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     if dtype == "fp8":
         return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    if dtype == "fp8e4m3":  # within +-240 the e4m3fn code is the e4m3 code
+        return torch.clamp(t, -240.0, 240.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     raise ValueError(dtype)
 
 
@@ -141,7 +146,7 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
     pool = poisoned_pool(max_num_pages, H_kv, ps, D, kv_dtype)
     order = np.sort(ids)
     k_scale = v_scale = None
-    if kv_dtype == "fp8":
+    if kv_dtype in ("fp8", "fp8e4m3"):
         rng_sc = _rng(seed, 4)
         k_scale = rng_sc.uniform(*scale_range, size=H_kv).astype(np.float32)
         v_scale = rng_sc.uniform(*scale_range, size=H_kv).astype(np.float32)
@@ -150,7 +155,7 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
     def fill(i):
         blk = order[i * CH:(i + 1) * CH]
         x = _rng(seed, 1000 + i).standard_normal((blk.size, 2, H_kv, ps, D), dtype=np.float32)
-        if kv_dtype == "fp8":
+        if kv_dtype in ("fp8", "fp8e4m3"):
             x *= np.float32(fp8_payload_sigma)
             np.clip(x, -448.0, 448.0, out=x)
         elif kv_sigma != 1.0:

@@ -195,3 +195,16 @@ def test_sink_outside_the_persistent_schedule_is_unsupported(L):
     for d in (desc(q_dtype="f32", kv_dtype="f32"), desc(batch=2000)):
         d.sink_logits = FAKE
         assert attention_status(L, d, workspace=FAKE, ws_bytes=1 << 30) == 2
+
+
+def test_fp8_e4m3_pool_checks(L):
+    """The IEEE-style e4m3 pool needs its scales, and is refused by the fused append (which writes
+    e4m3fn codes only) before anything is launched."""
+    assert attention_status(L, desc(kv_dtype="fp8e4m3")) == 1
+    f = L.pdecode_append_attention
+    ks = FAKE
+    d = desc(kv_dtype="fp8e4m3")
+    d.k_scale = ks
+    d.v_scale = ks
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.1, FAKE, FAKE,
+             FAKE, 1 << 30, None) == 2

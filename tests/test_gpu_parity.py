@@ -902,3 +902,52 @@ def test_full_size_multi_token_and_sink_sampled():
     dl = np.abs(l_gpu[sel[:, 0], sel[:, 1], sel[:, 2]] - l_ref).max()
     print(f"full-size multi + sink: max|dout|={do:.3g} max|dlse|={dl:.3g}", flush=True)
     assert do <= 2e-2 and dl <= 1e-3
+
+
+# ---- IEEE-style e4m3 pool (PDECODE_FP8_E4M3, max 240)
+
+@pytest.mark.parametrize("G,ps,splits", [(4, 32, 0), (8, 16, 3), (2, 32, 12)])
+def test_fp8_e4m3_pool_decode(G, ps, splits):
+    """Decode over an IEEE-style e4m3 pool (finite codes within +-240) against the oracle."""
+    lens = [1, 300, 2000, 0, 5 * ps + 3]
+    w = synth.make_workload(name=f"e4m3_G{G}_ps{ps}_s{splits}", B=len(lens), H_qo=2 * G, H_kv=2,
+                            D=128, page_size=ps, seq_lens=lens, q_dtype="bf16",
+                            kv_dtype="fp8e4m3", seed=990 + G + ps, max_num_pages=512)
+    run_and_check(w, num_kv_splits=splits)
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_append_fp8_e4m3_rounding_exhaustive(in_dtype):
+    """Every finite e4m3 value, the midpoints between neighbours (ties to even), values at and
+    beyond 240 (saturation from 248 up) and tiny values, quantised by the GPU append into an
+    e4m3 pool, match the oracle's encoder bit for bit."""
+    import ctypes
+    import paged_kv_decode_08_amd as pk
+    table = np.array([oracle.fp8_e4m3_value(c) for c in range(0x78)])
+    mids = (table[:-1] + table[1:]) / 2
+    xs = np.concatenate([table, mids, -table, -mids, [240.5, 247.99, 248.0, 250.0, 1e4, -1e4,
+                                                      1e-4, 2e-3, -3e-3]]).astype(np.float32)
+    D, ps = 64, 16
+    T = (xs.size + D - 1) // D
+    x = np.zeros(T * D, np.float32)
+    x[:xs.size] = xs
+    x = synth.cast_f32(x.reshape(T, 1, D), in_dtype)
+    ks = np.array([1.0], np.float32)
+    P = (T + ps - 1) // ps
+    pool = synth.poisoned_pool(P, 1, ps, D, "fp8e4m3")
+    slots = np.arange(T, dtype=np.int32)
+    desc = pk.make_desc(batch=1, num_qo_heads=1, num_kv_heads=1, head_dim=D, page_size=ps,
+                        max_num_pages=P, q_dtype=in_dtype, kv_dtype="fp8e4m3",
+                        k_scale=torch.from_numpy(ks).cuda(), v_scale=torch.from_numpy(ks).cuda())
+    tpool = torch.from_numpy(pool).cuda()
+    tx = gu.to_device_storage(x, in_dtype)
+    tslots = torch.from_numpy(slots).cuda()
+    st = pk.lib().pdecode_append_kv(ctypes.byref(desc), pk._ptr(tx), pk._ptr(tx), pk._ptr(tslots),
+                                    T, pk._ptr(tpool), pk._stream(None))
+    assert st == 0
+    torch.cuda.synchronize()
+    got = tpool.cpu().numpy()
+    ref = oracle.append_kv(pages=pool.copy(), new_k=x, new_v=x, slots=slots, H_kv=1, D=D, ps=ps,
+                           in_dtype=synth.DTYPE_CODE[in_dtype], kv_dtype=3, k_scale=ks,
+                           v_scale=ks)
+    assert got.tobytes() == ref.tobytes()

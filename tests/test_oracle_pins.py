@@ -4,6 +4,8 @@ Each test checks the oracle against something other than itself: brute force on 
 closed forms, invariants, the pages' own online recurrences run in fp64, and library routines
 (torch's fp8 / bf16 conversions).
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -626,3 +628,57 @@ def test_multi_token_select_matches_full():
     o, l = oracle.decode_multi(qo_len=3, q=qm, select=sel, **kw)
     assert np.array_equal(o, out[sel[:, 0], sel[:, 1], sel[:, 2]])
     assert np.array_equal(l, lse[sel[:, 0], sel[:, 1], sel[:, 2]])
+
+
+# ---- IEEE-style e4m3 (the NON_OCP float8_e4m3, max 240)
+
+def test_fp8_e4m3_values_and_relation_to_e4m3fn():
+    """Every code: exponent below 15 has the e4m3fn value (pinned against torch); exponent 15 is
+    infinity (mantissa 0) or NaN; the fixture's values (max 240) hold."""
+    for c in range(256):
+        e, m = (c >> 3) & 15, c & 7
+        v = oracle.fp8_e4m3_value(c)
+        if e < 15:
+            assert v == oracle.fp8_value(c), c
+        elif m == 0:
+            assert np.isinf(v) and (v < 0) == bool(c & 0x80), c
+        else:
+            assert np.isnan(v), c
+    path = os.path.join(os.path.dirname(__file__), "golden", "fp8_e4m3_values.txt")
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        code, val = line.split()
+        got = oracle.fp8_e4m3_value(int(code, 16))
+        want = float(val)
+        assert (np.isnan(got) and np.isnan(want)) or got == want, (code, got, want)
+
+
+def test_fp8_e4m3_encode_is_e4m3fn_rounding_saturated_at_240():
+    """Below 248 in magnitude the nearest-even e4m3 code is torch's e4m3fn cast (the two formats
+    share every code up to 240 and 248 is the midpoint to the next e4m3fn value); from 248 up the
+    encode saturates to +-240; NaN stays NaN."""
+    import torch
+    table = np.array([oracle.fp8_e4m3_value(c) for c in range(0x78)])
+    mids = (table[:-1] + table[1:]) / 2
+    xs = np.concatenate([table, mids, -table, -mids, [240.5, 247.99, 1e-4, 3e-3, -7e-4]]).astype(np.float32)
+    ref = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.fp8_e4m3_encode(float(x)) for x in xs], np.uint8)
+    assert np.array_equal(got, ref)
+    for x in (248.0, 250.0, 448.0, 1e4, np.inf):
+        assert oracle.fp8_e4m3_encode(x) == 0x77 and oracle.fp8_e4m3_encode(-x) == 0xF7
+    assert oracle.fp8_e4m3_encode(float("nan")) == 0x7F
+
+
+def test_fp8_e4m3_pool_matches_dense_bruteforce():
+    """Decode over an IEEE-style e4m3 pool against the textbook softmax on the flattened cache."""
+    w = small(kv_dtype="fp8e4m3", q_dtype="bf16", page_order="shuffled", seq_lens=[7, 1, 13])
+    out, lse = run_oracle(w)
+    G = w.H_qo // w.H_kv
+    q64 = to_f64(w.q, w.q_dtype)
+    for b in range(w.B):
+        for hq in range(w.H_qo):
+            K, V = contiguous_kv(w, b, hq // G)
+            o, l = dense_attention(q64[b, hq], K, V, w.sm_scale)
+            np.testing.assert_allclose(out[b, hq], o, rtol=0, atol=1e-12)
+            assert abs(lse[b, hq] - l) < 1e-12
