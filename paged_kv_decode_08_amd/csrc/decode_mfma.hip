@@ -15,7 +15,7 @@
 //    from the page table. The job after the current one is fetched, decoded and its page ids and q
 //    loaded while the current one streams, and its first page is in flight before the current
 //    job's last page is computed, so a workgroup's load stream does not stop at job boundaries.
-//    In the 8-column instantiations, when the call has at most kInMergeChunks chunks per sequence,
+//    In the single-token 8-column instantiations, when the call has at most kInMergeChunks chunks,
 //    the workgroup whose waves complete a split sequence's count of arrivals merges it at the end
 //    of its next job (each wave arrives once its own partial stores are known complete, a pair of
 //    items into the next job, so no wait falls on the load stream); otherwise a second,
@@ -283,7 +283,7 @@ static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipS
     e = p.new_k != nullptr ? launch_persist_fused<KVT, D, PS, GP, ROPE>(p, max_jobs, st)
                            : launch_persist_k<KVT, D, PS, GP, ROPE, false>(p, max_jobs, st);
   }
-  if (e != hipSuccess || p.num_chunks <= 1 || merges_in_kernel<GP>(p.num_chunks)) return e;
+  if (e != hipSuccess || p.num_chunks <= 1 || merges_in_kernel<GP>(p.num_chunks, p.T > 1)) return e;
   const unsigned rows = static_cast<unsigned>(p.B) * p.T * p.H_qo;
   hipLaunchKernelGGL((split_merge_kernel<D, PS>), dim3((rows + kMergeRows - 1) / kMergeRows),
                      dim3(64 * kMergeRows), 0, st, p);

@@ -174,14 +174,15 @@ __device__ void append_last_row(const DecodeParams& p, int b) {
 }
 
 // Split sequences of calls with at most this many chunks are merged inside the persistent kernel
-// by its 8-column instantiations (8 q heads, or q heads x tokens); the others leave every split
-// sequence to split_merge_kernel. Measured on the same box: with 4 columns the separate merge
-// kernel was faster (Llama-3-8B shape 68.0-68.5 against 68.9-69.5 us), with 8 columns the
-// in-kernel merge was (bf16 and fp8 8-head shapes, 2-4 us and 3-8 us).
+// by its single-token 8-column instantiations (8 q heads per KV head); the others leave every
+// split sequence to split_merge_kernel. Measured on the same box: with 4 columns the separate
+// merge kernel was faster (Llama-3-8B shape 68.0-68.5 against 68.9-69.5 us), and so it was with
+// 4 q heads x 2 tokens (75.1 against 78.6-78.8 us); with 8 heads the in-kernel merge was (bf16 and
+// fp8 8-head shapes, 2-4 us and 3-8 us).
 constexpr int kInMergeChunks = 8;
 template <int GP>
-constexpr bool merges_in_kernel(int num_chunks) {
-  return GP >= 8 && num_chunks <= kInMergeChunks;
+constexpr bool merges_in_kernel(int num_chunks, bool several_tokens) {
+  return GP >= 8 && !several_tokens && num_chunks <= kInMergeChunks;
 }
 
 // Merges the nch (2 .. kInMergeChunks) chunk states of (sequence b, KV head h), stored with
@@ -604,7 +605,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
     // pair, where they are older than the loads waited for); the workgroup whose wave brings the
     // count to chunks x waves merges the sequence at the end of that next job. pb < 0: no
     // arrival pending.
-    const bool in_merge = merges_in_kernel<GP>(p.num_chunks);
+    const bool in_merge = merges_in_kernel<GP>(p.num_chunks, MT);
     int pb = -1, ph = 0, pnch = 0;
 
     // Every job has an even number of items per wave, item k in buf0 for even k, so the next
