@@ -951,3 +951,17 @@ def test_append_fp8_e4m3_rounding_exhaustive(in_dtype):
                            in_dtype=synth.DTYPE_CODE[in_dtype], kv_dtype=3, k_scale=ks,
                            v_scale=ks)
     assert got.tobytes() == ref.tobytes()
+
+
+def test_append_attention_fp8_rope_window():
+    """Fused append into an fp8 pool with RoPE and a window: the substituted row holds the encoded
+    codes, which are converted and rotated like every other K row."""
+    w = synth.make_workload(name="fused_fp8_rope_swa", B=4, H_qo=16, H_kv=2, D=128, page_size=32,
+                            seq_lens=[3000, 200, 4100, 1], seed=760, max_num_pages=512,
+                            q_dtype="bf16", kv_dtype="fp8", window=1024, sink=4, rotary_mode=1,
+                            rope_theta=500000.0)
+    _fused_case(w, seed=76)
+    w2 = synth.make_workload(name="fused_fp8_rope_split", B=3, H_qo=8, H_kv=2, D=128,
+                             page_size=16, seq_lens=[2500, 33, 900], seed=761, max_num_pages=512,
+                             q_dtype="bf16", kv_dtype="fp8", rotary_mode=1, rope_theta=10000.0)
+    _fused_case(w2, seed=77, num_kv_splits=5)
