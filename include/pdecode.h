@@ -156,18 +156,21 @@ pdecode_status pdecode_attention(const pdecode_desc *d, const void *q, const voi
  * page, _attention_decode); a token whose prefix is empty (total_b < qo_len - t) gets out = 0 and
  * lse = -5e4, as a sequence without pages does.
  * q, out: device [batch, qo_len, num_qo_heads, head_dim] (q_dtype); lse: fp32 [batch, qo_len,
- * num_qo_heads]. The other arguments are those of pdecode_attention, without RoPE; the workspace
- * is sized by pdecode_workspace_bytes_multi(d, qo_len), with the same reuse rules.
+ * num_qo_heads]. The other arguments are those of pdecode_attention; the workspace is sized by
+ * pdecode_workspace_bytes_multi(d, qo_len), with the same reuse rules. With rotate-half RoPE
+ * (rotary_mode 1), token t's query sits at position q_rope_position[b] + t; the keys are placed as
+ * in pdecode_attention.
  * qo_len == 1 is pdecode_attention. Supported for qo_len > 1: no sliding window,
- * (num_qo_heads / num_kv_heads) * qo_len <= 8, and the persistent matrix-core schedule (BF16 or
- * FP8_E4M3FN pool, batch <= 1024); otherwise UNSUPPORTED. Errors: as pdecode_attention, and
- * INVALID_ARG for qo_len < 1. */
+ * (num_qo_heads / num_kv_heads) * qo_len <= 8, no interleaved RoPE, and the persistent
+ * matrix-core schedule (BF16 or FP8 pool, batch <= 1024; with RoPE, an FP8 pool at head_dim 128
+ * only); otherwise UNSUPPORTED. Errors: as pdecode_attention, and INVALID_ARG for qo_len < 1. */
 size_t pdecode_workspace_bytes_multi(const pdecode_desc *d, int32_t qo_len);
 pdecode_status pdecode_attention_multi(const pdecode_desc *d, int32_t qo_len, const void *q,
                                        const void *pages, const int32_t *page_indptr,
                                        const int32_t *page_values, const int32_t *length_info,
-                                       float sm_scale, void *out, float *lse, void *workspace,
-                                       size_t workspace_bytes, void *stream);
+                                       const pdecode_rope *rope, float sm_scale, void *out,
+                                       float *lse, void *workspace, size_t workspace_bytes,
+                                       void *stream);
 
 /* One decode step with its KV append fused into the attention launch: for every sequence b with
  * pages and every KV head h, new_k[b, h, :] and new_v[b, h, :] are written to the sequence's row

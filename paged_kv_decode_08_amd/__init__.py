@@ -68,7 +68,8 @@ def lib() -> ctypes.CDLL:
         L.pdecode_workspace_bytes_multi.argtypes = [ctypes.POINTER(Desc), _c_i32]
         L.pdecode_attention_multi.restype = _c_i32
         L.pdecode_attention_multi.argtypes = [ctypes.POINTER(Desc), _c_i32, P, P, P, P, P,
-                                              ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+                                              ctypes.POINTER(Rope), ctypes.c_float, P, P, P,
+                                              ctypes.c_size_t, P]
         L.pdecode_append_attention.restype = _c_i32
         L.pdecode_append_attention.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P, P, P,
                                                ctypes.POINTER(Rope), ctypes.c_float, P, P, P,
@@ -170,12 +171,15 @@ def alloc_workspace_multi(desc: Desc, qo_len: int, device="cuda") -> torch.Tenso
 
 
 def attention_multi(desc: Desc, qo_len: int, q, pages, page_indptr, page_values, length_info,
-                    out, lse, sm_scale, workspace=None, stream=None) -> None:
+                    out, lse, sm_scale, rope: Rope | None = None, workspace=None,
+                    stream=None) -> None:
     """pdecode_attention_multi: q/out [B, qo_len, H_qo, D], lse [B, qo_len, H_qo]; token t of a
-    sequence attends its positions up to total - qo_len + t."""
+    sequence attends its positions up to total - qo_len + t (with RoPE, its query sits at
+    q_rope_position[b] + t)."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().pdecode_attention_multi(ctypes.byref(desc), int(qo_len), _ptr(q), _ptr(pages),
                                        _ptr(page_indptr), _ptr(page_values), _ptr(length_info),
+                                       None if rope is None else ctypes.byref(rope),
                                        float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                        ws_bytes, _stream(stream))
     if st:

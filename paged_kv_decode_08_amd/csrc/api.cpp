@@ -149,7 +149,8 @@ namespace {
 
 // pdecode_attention, and with new_k / new_v set the fused append of pdecode_append_attention
 // (the persistent matrix-core schedule only).
-// qo_len > 1: several query tokens per sequence (pdecode_attention_multi; no RoPE, no window).
+// qo_len > 1: several query tokens per sequence (pdecode_attention_multi; rotate-half RoPE only,
+// no window).
 pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const void* new_v,
                               const void* q, const void* pages, const int32_t* page_indptr,
                               const int32_t* page_values, const int32_t* length_info,
@@ -175,7 +176,8 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   // the fused append writes e4m3fn codes only
   if (fused && d->kv_dtype == PDECODE_FP8_E4M3) return PDECODE_ERR_UNSUPPORTED;
   // interleaved RoPE: the persistent matrix-core kernels only, not fused with the append
-  if (rotary && rope->rotary_mode == 2 && (!pl.persistent || fused)) return PDECODE_ERR_UNSUPPORTED;
+  if (rotary && rope->rotary_mode == 2 && (!pl.persistent || fused || qo_len > 1))
+    return PDECODE_ERR_UNSUPPORTED;
   const int64_t grid = int64_t(pl.num_chunks) * d->batch * d->num_kv_heads;
   if (grid > INT_MAX) return PDECODE_ERR_UNSUPPORTED;
   if (pl.workspace_bytes() > 0) {
@@ -260,18 +262,19 @@ size_t pdecode_workspace_bytes_multi(const pdecode_desc* d, int32_t qo_len) {
 pdecode_status pdecode_attention_multi(const pdecode_desc* d, int32_t qo_len, const void* q,
                                        const void* pages, const int32_t* page_indptr,
                                        const int32_t* page_values, const int32_t* length_info,
-                                       float sm_scale, void* out, float* lse, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
+                                       const pdecode_rope* rope, float sm_scale, void* out,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
   pdecode_status st = check_desc(d);
   if (st != PDECODE_OK) return st;
   if (qo_len < 1) return PDECODE_ERR_INVALID_ARG;
   if (qo_len == 1)
     return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
-                          nullptr, sm_scale, out, lse, workspace, workspace_bytes, stream);
+                          rope, sm_scale, out, lse, workspace, workspace_bytes, stream);
   if (d->sliding_window) return PDECODE_ERR_UNSUPPORTED;
   if (int64_t(qo_len) * (d->num_qo_heads / d->num_kv_heads) > 8) return PDECODE_ERR_UNSUPPORTED;
   return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
-                        nullptr, sm_scale, out, lse, workspace, workspace_bytes, stream, qo_len);
+                        rope, sm_scale, out, lse, workspace, workspace_bytes, stream, qo_len);
 }
 
 pdecode_status pdecode_append_attention(const pdecode_desc* d, const void* new_k,

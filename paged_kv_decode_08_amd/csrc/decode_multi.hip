@@ -1,32 +1,36 @@
 // Decode with several query tokens per sequence (pdecode_attention_multi): the MT instantiations
 // of the persistent matrix-core decode kernel (decode_persist.hpp), built apart from
 // decode_mfma.hip. The G q heads of a KV head times the T tokens fill up to 8 columns of the MFMA
-// B operand (group bound GP 2, 4 or 8).
+// B operand (group bound GP 2, 4 or 8). With rotate-half RoPE (bf16 KV, or fp8 KV at head dim
+// 128), token t of a sequence is rotated t positions after the sequence's first query position.
 #include "decode_persist.hpp"
 
 namespace pdk {
 
-template <int KVT, int D, int PS, int GP>
+template <int KVT, int D, int PS, int GP, bool ROPE>
 hipError_t launch_persist_multi(const DecodeParams& p, long long max_jobs, hipStream_t st) {
   if constexpr (GP < 2) return hipErrorInvalidValue;
-  else return launch_persist_k<KVT, D, PS, GP, false, false, true>(p, max_jobs, st);
+  else return launch_persist_k<KVT, D, PS, GP, ROPE, false, true>(p, max_jobs, st);
 }
 
-#define PDK_MULTI(KVT, D, PS, GP)                                                                  \
-  template hipError_t launch_persist_multi<KVT, D, PS, GP>(const DecodeParams&, long long,         \
-                                                           hipStream_t);
-#define PDK_MULTI_GP(KVT, D, PS) \
-  PDK_MULTI(KVT, D, PS, 1)       \
-  PDK_MULTI(KVT, D, PS, 2)       \
-  PDK_MULTI(KVT, D, PS, 4)       \
-  PDK_MULTI(KVT, D, PS, 8)
-#define PDK_MULTI_SHAPES(KVT)  \
-  PDK_MULTI_GP(KVT, 64, 16)    \
-  PDK_MULTI_GP(KVT, 64, 32)    \
-  PDK_MULTI_GP(KVT, 128, 16)   \
-  PDK_MULTI_GP(KVT, 128, 32)
+#define PDK_MULTI(KVT, D, PS, GP, ROPE)                                                           \
+  template hipError_t launch_persist_multi<KVT, D, PS, GP, ROPE>(const DecodeParams&, long long, \
+                                                                 hipStream_t);
+#define PDK_MULTI_GP(KVT, D, PS, ROPE) \
+  PDK_MULTI(KVT, D, PS, 1, ROPE)       \
+  PDK_MULTI(KVT, D, PS, 2, ROPE)       \
+  PDK_MULTI(KVT, D, PS, 4, ROPE)       \
+  PDK_MULTI(KVT, D, PS, 8, ROPE)
+#define PDK_MULTI_SHAPES(KVT, ROPE)  \
+  PDK_MULTI_GP(KVT, 64, 16, ROPE)    \
+  PDK_MULTI_GP(KVT, 64, 32, ROPE)    \
+  PDK_MULTI_GP(KVT, 128, 16, ROPE)   \
+  PDK_MULTI_GP(KVT, 128, 32, ROPE)
 
-PDK_MULTI_SHAPES(kBF16)
-PDK_MULTI_SHAPES(kFP8)
+PDK_MULTI_SHAPES(kBF16, false)
+PDK_MULTI_SHAPES(kBF16, true)
+PDK_MULTI_SHAPES(kFP8, false)
+PDK_MULTI_GP(kFP8, 128, 16, true)
+PDK_MULTI_GP(kFP8, 128, 32, true)
 
 }  // namespace pdk

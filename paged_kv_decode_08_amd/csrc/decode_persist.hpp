@@ -539,7 +539,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
 
   if (J.valid) {
     core.load_q(reinterpret_cast<const uint16_t*>(s_q[0]), GC);
-    core.rope_q(J.qpos, s_freq);
+    core.rope_q(J.qpos + tok, s_freq);  // several tokens: token tok sits tok positions later
     float scale = p.score_scale * (C::FP8 ? p.k_scale[J.h] : 1.0f);
     float vscale = C::FP8 ? p.v_scale[J.h] : 1.0f;
     core.reset();
@@ -582,8 +582,8 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         if constexpr (MT) {
           // this lane's column (token n / G) sees positions <= total - T + n / G
           const int cap = J.g.total - T + tok - (j * PS + r0);
-          if (lo < hi) core.template process<true>(cur, lo, hi, scale, s_pt[w], s_alpha[w], 0,
-                                                   nullptr, cap);
+          if (lo < hi) core.template process<true>(cur, lo, hi, scale, s_pt[w], s_alpha[w], pos0,
+                                                   s_freq, cap);
         } else {
           if (lo < hi) core.process(cur, lo, hi, scale, s_pt[w], s_alpha[w], pos0, s_freq);
         }
@@ -745,7 +745,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       J = J1;
       par ^= 1;
       core.load_q(reinterpret_cast<const uint16_t*>(s_q[par]), GC);
-      core.rope_q(J.qpos, s_freq);
+      core.rope_q(J.qpos + tok, s_freq);  // several tokens: token tok sits tok positions later
       if (C::FP8) {
         scale = p.score_scale * p.k_scale[J.h];
         vscale = p.v_scale[J.h];
@@ -809,9 +809,9 @@ hipError_t launch_persist_k(const DecodeParams& p, long long max_jobs, hipStream
 template <int KVT, int D, int PS, int GP, bool ROPE>
 hipError_t launch_persist_fused(const DecodeParams& p, long long max_jobs, hipStream_t st);
 
-// The several-query-token instantiations of launch_persist_k (decode_multi.hip): no RoPE, no fused
-// append.
-template <int KVT, int D, int PS, int GP>
+// The several-query-token instantiations of launch_persist_k (decode_multi.hip): without and with
+// rotate-half RoPE (bf16 KV, or fp8 KV at D = 128); no fused append.
+template <int KVT, int D, int PS, int GP, bool ROPE>
 hipError_t launch_persist_multi(const DecodeParams& p, long long max_jobs, hipStream_t st);
 
 // The interleaved-RoPE instantiations of launch_persist_k (decode_rope_ilv.hip): bf16 KV, and fp8

@@ -172,14 +172,22 @@ def test_append_attention_argument_errors(L):
 
 def test_attention_multi_argument_errors(L):
     """pdecode_attention_multi: qo_len < 1, a sliding window, more than 8 MFMA columns (group
-    size x tokens), an fp32 pool and a batch beyond the persistent schedule are refused before
-    anything is launched; the workspace size grows with the tokens."""
+    size x tokens), an fp32 pool, a batch beyond the persistent schedule, interleaved RoPE and
+    RoPE over an fp8 pool at head dim 64 are refused before anything is launched; the workspace
+    size grows with the tokens."""
     f = L.pdecode_attention_multi
 
-    def call(d, T):
-        return f(ctypes.byref(d), T, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, FAKE, 1 << 30,
+    def call(d, T, rope=None):
+        return f(ctypes.byref(d), T, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 None if rope is None else ctypes.byref(rope), 0.1, FAKE, FAKE, FAKE, 1 << 30,
                  None)
     assert call(desc(), 0) == 1
+    assert call(desc(), 2, pk.Rope(2, 1.0, 5e5, FAKE, FAKE)) == 2
+    d8 = desc(kv_dtype="fp8", head_dim=64)
+    d8.k_scale = FAKE
+    d8.v_scale = FAKE
+    assert call(d8, 2, pk.Rope(1, 1.0, 5e5, FAKE, FAKE)) == 2
+    assert call(desc(), 2, pk.Rope(1, 1.0, -1.0, FAKE, FAKE)) == 1
     assert call(desc(sliding_window=True), 2) == 2
     assert call(desc(), 3) == 2                   # 4 q heads per KV head x 3 tokens > 8
     assert call(desc(num_qo_heads=8, batch=2000), 4) == 2

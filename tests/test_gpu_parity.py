@@ -678,8 +678,13 @@ def _multi_case(w, T, seed, num_kv_splits=0):
     out.view(torch.int16).fill_(0x7FC0)
     lse = torch.full((w.B, T, w.H_qo), float("nan"), dtype=torch.float32, device="cuda")
     ws = pk.alloc_workspace_multi(desc, T)
+    rope = None
+    if w.rotary_mode:
+        rope = pk.make_rope(rotary_mode=w.rotary_mode, rope_scale=w.rope_scale,
+                            rope_theta=w.rope_theta, q_rope_position=dev["q_pos"],
+                            k_rope_pos_offset=dev["k_off"])
     pk.attention_multi(desc, T, qd, dev["pages"], dev["indptr"], dev["values"],
-                       dev["length_info"], out, lse, w.sm_scale, workspace=ws)
+                       dev["length_info"], out, lse, w.sm_scale, rope=rope, workspace=ws)
     torch.cuda.synchronize()
     tol_o, tol_l = gu.tolerance(w)
     o_gpu, l_gpu = gu.to_np64(out), gu.to_np64(lse)
@@ -713,6 +718,23 @@ def test_attention_multi_split(splits):
                             page_size=16, seq_lens=[3000, 17, 1200, 641], seed=820 + splits,
                             max_num_pages=512)
     _multi_case(w, 2, seed=83, num_kv_splits=splits)
+
+
+@pytest.mark.parametrize("kv,G,T,D,ps,splits", [("bf16", 4, 2, 128, 16, 0),
+                                                ("bf16", 2, 3, 64, 32, 0),
+                                                ("fp8", 2, 4, 128, 16, 0),
+                                                ("bf16", 4, 2, 128, 16, 12),
+                                                ("fp8", 1, 8, 128, 32, 3)])
+def test_attention_multi_rope(kv, G, T, D, ps, splits):
+    """Rotate-half RoPE with several tokens: token t's query at q_rope_position + t (oracle
+    reading), Llama-3 base; lengths around page boundaries, tokens with no row, split sequences
+    merged in the kernel and by the split merge kernel."""
+    lens = [1, T - 1, ps, ps + 1, 3 * ps - 1, 2500, 0, 2 * ps + T]
+    w = synth.make_workload(name=f"multi_rope_{kv}_G{G}_T{T}_D{D}_ps{ps}_s{splits}", B=len(lens),
+                            H_qo=2 * G, H_kv=2, D=D, page_size=ps, seq_lens=lens, q_dtype="bf16",
+                            kv_dtype=kv, seed=860 + G + T + D + ps + splits, max_num_pages=512,
+                            rotary_mode=1, rope_theta=500000.0)
+    _multi_case(w, T, seed=86 + T, num_kv_splits=splits)
 
 
 def test_attention_multi_one_token_is_attention():

@@ -563,6 +563,42 @@ def test_multi_token_matches_dense_causal_bruteforce(kv_dtype, q_dtype, T):
                 assert abs(lse[b, t, hq] - l) < 1e-12
 
 
+@pytest.mark.parametrize("kv_dtype,q_dtype", [("f32", "f32"), ("bf16", "bf16")])
+def test_multi_token_rope_matches_dense_causal_bruteforce(kv_dtype, q_dtype):
+    """Rotate-half RoPE with several tokens: token t's query rotated to q_rope_position + t, the
+    flattened cache's row r to k_rope_pos_offset + r, then the causal brute force as above."""
+    T = 3
+    w = small(B=4, kv_dtype=kv_dtype, q_dtype=q_dtype, page_order="shuffled",
+              seq_lens=[7, 1, 13, 0], rotary_mode=1, rope_theta=1e4)
+    qm = synth.multi_query(w, T, seed=7)
+    qp = np.array([40, 0, 12, 3], np.int32)
+    ko = np.array([33, 5, 0, 0], np.int32)
+    kw = {k: v for k, v in w.oracle_kwargs().items() if k != "q"}
+    kw.update(q_rope_position=qp, k_rope_pos_offset=ko)
+    out, lse = oracle.decode_multi(qo_len=T, q=qm, **kw)
+    G = w.H_qo // w.H_kv
+    q64 = to_f64(qm, w.q_dtype)
+    for b in range(w.B):
+        L = int(w.seq_lens[b])
+        for t in range(T):
+            n = L - T + t + 1
+            for hq in range(w.H_qo):
+                if n <= 0:
+                    assert np.all(out[b, t, hq] == 0) and lse[b, t, hq] == -5e4
+                    continue
+                K, V = contiguous_kv(w, b, hq // G)
+                Kr = np.stack([oracle.rope_rotate(K[r], ko[b] + r, 1.0, 1e4) for r in range(n)])
+                qr = oracle.rope_rotate(q64[b, t, hq], qp[b] + t, 1.0, 1e4)
+                o, l = dense_attention(qr, Kr, V[:n], w.sm_scale)
+                np.testing.assert_allclose(out[b, t, hq], o, rtol=0, atol=1e-12)
+                assert abs(lse[b, t, hq] - l) < 1e-12
+    # and the positions matter: without RoPE the result differs
+    kw0 = {k: v for k, v in w.oracle_kwargs().items() if k != "q"}
+    kw0["rotary_mode"] = 0
+    out0, _ = oracle.decode_multi(qo_len=T, q=qm, **kw0)
+    assert np.abs(out0 - out).max() > 1e-3
+
+
 def test_multi_token_one_token_is_decode():
     """qo_len = 1 is the single-token decode, bit for bit."""
     w = small(seq_lens=[7, 1, 13])
