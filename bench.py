@@ -53,6 +53,8 @@ def parse():
                          "tokens per sequence of --workload: one pdecode_attention_multi call "
                          "against --qo-len pdecode_attention calls")
     ap.add_argument("--qo-len", type=int, default=2, help="query tokens per sequence (--op multi)")
+    ap.add_argument("--multi-rope", action="store_true",
+                    help="--op multi: rotate-half RoPE (base 5e5), token t at position L - T + t")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the decode, run a plain 512 MiB device-to-device copy "
                          "(the reference point for the HBM byte counters) and exit")
@@ -169,7 +171,7 @@ def op_bench(op, steps, warmup):
                       "data": "synthetic", "results": results}), flush=True)
 
 
-def multi_bench(workload, T, steps, warmup, nsets):
+def multi_bench(workload, T, steps, warmup, nsets, rope=False):
     """T query tokens per sequence (causal over the new tokens): one pdecode_attention_multi call,
     which reads the KV once for all T tokens, against T pdecode_attention calls (one per token,
     each over the whole sequence: the upper bound of the per-token work). K steps each between
@@ -198,17 +200,27 @@ def multi_bench(workload, T, steps, warmup, nsets):
             for _ in range(T)]
     lses = [torch.empty((base.B, base.H_qo), dtype=torch.float32, device="cuda") for _ in range(T)]
     stream = torch.cuda.current_stream()
+    ropes = [None] * T  # per-token calls: token t's query at L - T + t
+    mrope = None
+    if rope:
+        qpos = [torch.from_numpy(np.maximum(lens - T + t, 0).astype(np.int32)).cuda()
+                for t in range(T)]
+        koff = torch.zeros(base.B, dtype=torch.int32, device="cuda")
+        ropes = [pk.make_rope(rotary_mode=1, rope_scale=1.0, rope_theta=500000.0,
+                              q_rope_position=qpos[t], k_rope_pos_offset=koff) for t in range(T)]
+        mrope = ropes[0]
 
     def multi(i):
         d = devs[i % len(devs)]
         pk.attention_multi(desc, T, qm, d["pages"], d["indptr"], d["values"], d["length_info"],
-                           out, lse, base.sm_scale, workspace=ws, stream=stream)
+                           out, lse, base.sm_scale, rope=mrope, workspace=ws, stream=stream)
 
     def per_token(i):
         d = devs[i % len(devs)]
         for t in range(T):
             pk.attention(desc, qt[t], d["pages"], d["indptr"], d["values"], d["length_info"],
-                         outs[t], lses[t], base.sm_scale, workspace=ws, stream=stream)
+                         outs[t], lses[t], base.sm_scale, rope=ropes[t], workspace=ws,
+                         stream=stream)
 
     res = {}
     for name, fn in (("per_token_calls", per_token), ("multi", multi),
@@ -227,7 +239,8 @@ def multi_bench(workload, T, steps, warmup, nsets):
         res[name] = {"us_per_step_wall": round((time.perf_counter() - t0) * 1e6 / steps, 2),
                      "us_per_step_events": round(ev0.elapsed_time(ev1) * 1e3 / steps, 2)}
     us = res["multi"]["us_per_step_events"]
-    print(json.dumps({"op": "multi", "workload": base.name, "qo_len": T, "n_gpus": 1,
+    print(json.dumps({"op": "multi", "workload": base.name, "qo_len": T, "rope": bool(rope),
+                      "n_gpus": 1,
                       "steps": steps, "warmup": warmup, "input_sets": len(sets),
                       "kv_bytes_per_step": base.kv_bytes,
                       "multi_kv_GBps_events": round(base.kv_bytes / (us * 1e-6) / 1e9, 1),
@@ -317,7 +330,8 @@ def main():
         copy_calibration(max(args.steps, 1))
         return
     if args.op == "multi":
-        multi_bench(args.workload, args.qo_len, max(args.steps, 1), args.warmup, args.sets)
+        multi_bench(args.workload, args.qo_len, max(args.steps, 1), args.warmup, args.sets,
+                    rope=args.multi_rope)
         return
     if args.op == "append_attention":
         step_bench(args.workload, max(args.steps, 1), args.warmup, args.sets)
