@@ -926,6 +926,39 @@ def test_full_size_multi_token_and_sink_sampled():
     assert do <= 2e-2 and dl <= 1e-3
 
 
+def test_full_size_multi_token_rope_sampled():
+    """pdecode_attention_multi (two tokens) with rotate-half RoPE (Llama-3 base, token t at
+    L - 2 + t, keys from position 0) on the full Llama-3-8B-shaped workload: sampled
+    (sequence, token, head) outputs against the oracle."""
+    import dataclasses
+    w0 = synth.CONFIGS["llama3_8b_bf16"]()
+    T = 2
+    w = dataclasses.replace(w0, rotary_mode=1, rope_theta=500000.0, rope_scale=1.0,
+                            q_rope_position=np.maximum(w0.seq_lens - T, 0).astype(np.int32),
+                            k_rope_pos_offset=np.zeros(w0.B, np.int32))
+    qm = synth.multi_query(w, T, seed=87)
+    pairs = _sample_pairs(w, 48, 8)
+    sel = np.stack([pairs[:, 0], np.arange(len(pairs)) % T, pairs[:, 1]], 1).astype(np.int32)
+    kw = {k: v for k, v in w.oracle_kwargs().items() if k != "q"}
+    o_ref, l_ref = oracle.decode_multi(qo_len=T, q=qm, select=sel, **kw)
+    dev = gu.upload(w)
+    desc = gu.desc_for(w, dev)
+    rope = pk.make_rope(rotary_mode=1, rope_scale=1.0, rope_theta=500000.0,
+                        q_rope_position=dev["q_pos"], k_rope_pos_offset=dev["k_off"])
+    out = torch.empty((w.B, T, w.H_qo, w.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, T, w.H_qo), dtype=torch.float32, device="cuda")
+    pk.attention_multi(desc, T, gu.to_device_storage(qm, "bf16"), dev["pages"], dev["indptr"],
+                       dev["values"], dev["length_info"], out, lse, w.sm_scale, rope=rope,
+                       workspace=pk.alloc_workspace_multi(desc, T))
+    torch.cuda.synchronize()
+    o_gpu, l_gpu = gu.to_np64(out), gu.to_np64(lse)
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(l_gpu))
+    do = np.abs(o_gpu[sel[:, 0], sel[:, 1], sel[:, 2]] - o_ref).max()
+    dl = np.abs(l_gpu[sel[:, 0], sel[:, 1], sel[:, 2]] - l_ref).max()
+    print(f"full-size multi + RoPE: max|dout|={do:.3g} max|dlse|={dl:.3g}", flush=True)
+    assert do <= 2e-2 and dl <= 1e-3
+
+
 # ---- IEEE-style e4m3 pool (PDECODE_FP8_E4M3, max 240)
 
 @pytest.mark.parametrize("G,ps,splits", [(4, 32, 0), (8, 16, 3), (2, 32, 12)])
