@@ -162,8 +162,7 @@ pdecode_status pdecode_attention(const pdecode_desc *d, const void *q, const voi
  * in pdecode_attention.
  * qo_len == 1 is pdecode_attention. Supported for qo_len > 1: no sliding window,
  * (num_qo_heads / num_kv_heads) * qo_len <= 8, no interleaved RoPE, and the persistent
- * matrix-core schedule (BF16 or FP8 pool, batch <= 1024; with RoPE, an FP8 pool at head_dim 128
- * only); otherwise UNSUPPORTED. Errors: as pdecode_attention, and INVALID_ARG for qo_len < 1. */
+ * matrix-core schedule (BF16 or FP8 pool, batch <= 1024); otherwise UNSUPPORTED. Errors: as pdecode_attention, and INVALID_ARG for qo_len < 1. */
 size_t pdecode_workspace_bytes_multi(const pdecode_desc *d, int32_t qo_len);
 pdecode_status pdecode_attention_multi(const pdecode_desc *d, int32_t qo_len, const void *q,
                                        const void *pages, const int32_t *page_indptr,
@@ -183,8 +182,7 @@ pdecode_status pdecode_attention_multi(const pdecode_desc *d, int32_t qo_len, co
  * new_k, new_v: device [batch, num_kv_heads, head_dim] of q_dtype (BF16); pages is written; the
  * other arguments, the workspace rules and the results are those of pdecode_attention.
  * Supported: the calls pdecode_attention runs on its persistent matrix-core schedule (BF16 or
- * FP8_E4M3FN pool, batch <= 1024; with RoPE, an FP8 pool needs head_dim 128); otherwise
- * UNSUPPORTED. Errors: as pdecode_attention, and INVALID_ARG for a null new_k / new_v. */
+ * FP8_E4M3FN pool, batch <= 1024); otherwise UNSUPPORTED. Errors: as pdecode_attention, and INVALID_ARG for a null new_k / new_v. */
 pdecode_status pdecode_append_attention(const pdecode_desc *d, const void *new_k,
                                         const void *new_v, const void *q, void *pages,
                                         const int32_t *page_indptr, const int32_t *page_values,

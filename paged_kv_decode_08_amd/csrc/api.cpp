@@ -60,8 +60,8 @@ pdecode_status check_attention_shape(const pdecode_desc* d) {
 // Chunking of each sequence's page slots. A sequence with n slots uses ceil(n / chunk_slots)
 // chunks, capped at num_chunks (the last chunk then takes every remaining slot), so any length
 // is computed exactly; max_kv_len only sizes the grid.
-// rope: the call applies RoPE (bf16 KV, or fp8 KV at head_dim 128: the matrix-core kernels, planned
-// as without RoPE; otherwise the vector-ALU kernel).
+// rope: the call applies RoPE (bf16 or fp8 KV: the matrix-core kernels, planned as without RoPE;
+// fp32 KV: the vector-ALU kernel).
 Plan make_plan(const pdecode_desc* d, bool rope, int qo_len = 1) {
   Plan pl;
   const int64_t ps = d->page_size;
@@ -70,8 +70,7 @@ Plan make_plan(const pdecode_desc* d, bool rope, int qo_len = 1) {
   const int64_t units = int64_t(d->batch) * d->num_kv_heads;
 
   const bool persistent = (d->kv_dtype == PDECODE_BF16 || is_fp8(d->kv_dtype)) &&
-                          d->batch <= kPersistMaxBatch &&
-                          (!rope || d->kv_dtype == PDECODE_BF16 || d->head_dim == 128);
+                          d->batch <= kPersistMaxBatch;
   int64_t chunk;
   if (d->num_kv_splits == 1) {
     chunk = max_slots;
@@ -224,13 +223,12 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   const int gp = cols <= 1 ? 1 : cols <= 2 ? 2 : cols <= 4 ? 4 : 8;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // bf16 / fp8 KV: q.K on the matrix cores (4-wave workgroups, persistent over a job queue up to
-  // kPersistMaxBatch sequences, else one per chunk), RoPE included for bf16 KV and for fp8 KV at
-  // head_dim 128; otherwise the vector-ALU kernel (one wave per chunk; RoPE rotates K in fp32).
+  // kPersistMaxBatch sequences, else one per chunk), RoPE included; fp32 KV: the vector-ALU kernel
+  // (one wave per chunk; RoPE rotates K in fp32).
   // An IEEE-style e4m3 pool holds finite codes only (a precondition; the append saturates to
   // +-240), and every finite code has its e4m3fn value: the decode kernels read it as e4m3fn.
   const int kv_read = d->kv_dtype == PDECODE_FP8_E4M3 ? PDECODE_FP8_E4M3FN : d->kv_dtype;
-  const bool mfma = (kv_read == PDECODE_BF16 || kv_read == PDECODE_FP8_E4M3FN) &&
-                    (!rotary || d->kv_dtype == PDECODE_BF16 || d->head_dim == 128);
+  const bool mfma = kv_read == PDECODE_BF16 || kv_read == PDECODE_FP8_E4M3FN;
   if (mfma)
     st = hip_status(pdk::launch_decode_mfma(p, kv_read, d->head_dim, d->page_size, gp,
                                             pl.persistent, rotary, grid, s));

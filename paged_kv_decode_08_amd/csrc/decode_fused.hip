@@ -10,7 +10,7 @@ hipError_t launch_persist_fused(const DecodeParams& p, long long max_jobs, hipSt
 }
 
 // Every (KV dtype, head dim, page size, group bound, RoPE) the persistent schedule launches; RoPE
-// with fp8 KV runs on the matrix cores at head dim 128 only.
+// included for bf16 and fp8 KV.
 #define PDK_FUSED_GP(KVT, D, PS, ROPE)                                                            \
   template hipError_t launch_persist_fused<KVT, D, PS, 1, ROPE>(const DecodeParams&, long long,  \
                                                                 hipStream_t);                    \
@@ -29,7 +29,6 @@ hipError_t launch_persist_fused(const DecodeParams& p, long long max_jobs, hipSt
 PDK_FUSED_SHAPES(kBF16, false)
 PDK_FUSED_SHAPES(kBF16, true)
 PDK_FUSED_SHAPES(kFP8, false)
-PDK_FUSED_GP(kFP8, 128, 16, true)
-PDK_FUSED_GP(kFP8, 128, 32, true)
+PDK_FUSED_SHAPES(kFP8, true)
 
 }  // namespace pdk

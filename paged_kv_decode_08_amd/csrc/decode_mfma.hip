@@ -290,17 +290,13 @@ static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipS
   return hipGetLastError();
 }
 
-// RoPE on the matrix cores: bf16 KV, or fp8 KV at D = 128.
+// RoPE on the matrix cores: bf16 or fp8 KV, every head dim.
 template <int KVT, int D, int PS, int GP>
 static hipError_t launch_sched(const DecodeParams& p, bool persistent, bool rope, long long grid,
                                hipStream_t st) {
-  if (rope) {
-    if constexpr (KVT == kBF16 || D == 128) {
-      return persistent ? launch_persist<KVT, D, PS, GP, true>(p, grid, st)
-                        : launch_chunked<KVT, D, PS, GP, true>(p, static_cast<unsigned>(grid), st);
-    }
-    return hipErrorInvalidValue;
-  }
+  if (rope)
+    return persistent ? launch_persist<KVT, D, PS, GP, true>(p, grid, st)
+                      : launch_chunked<KVT, D, PS, GP, true>(p, static_cast<unsigned>(grid), st);
   return persistent ? launch_persist<KVT, D, PS, GP, false>(p, grid, st)
                     : launch_chunked<KVT, D, PS, GP, false>(p, static_cast<unsigned>(grid), st);
 }

@@ -1,8 +1,8 @@
 // Decode with several query tokens per sequence (pdecode_attention_multi): the MT instantiations
 // of the persistent matrix-core decode kernel (decode_persist.hpp), built apart from
 // decode_mfma.hip. The G q heads of a KV head times the T tokens fill up to 8 columns of the MFMA
-// B operand (group bound GP 2, 4 or 8). With rotate-half RoPE (bf16 KV, or fp8 KV at head dim
-// 128), token t of a sequence is rotated t positions after the sequence's first query position.
+// B operand (group bound GP 2, 4 or 8). With rotate-half RoPE, token t of a sequence is rotated
+// t positions after the sequence's first query position.
 #include "decode_persist.hpp"
 
 namespace pdk {
@@ -30,7 +30,6 @@ hipError_t launch_persist_multi(const DecodeParams& p, long long max_jobs, hipSt
 PDK_MULTI_SHAPES(kBF16, false)
 PDK_MULTI_SHAPES(kBF16, true)
 PDK_MULTI_SHAPES(kFP8, false)
-PDK_MULTI_GP(kFP8, 128, 16, true)
-PDK_MULTI_GP(kFP8, 128, 32, true)
+PDK_MULTI_SHAPES(kFP8, true)
 
 }  // namespace pdk

@@ -810,12 +810,11 @@ template <int KVT, int D, int PS, int GP, bool ROPE>
 hipError_t launch_persist_fused(const DecodeParams& p, long long max_jobs, hipStream_t st);
 
 // The several-query-token instantiations of launch_persist_k (decode_multi.hip): without and with
-// rotate-half RoPE (bf16 KV, or fp8 KV at D = 128); no fused append.
+// rotate-half RoPE; no fused append.
 template <int KVT, int D, int PS, int GP, bool ROPE>
 hipError_t launch_persist_multi(const DecodeParams& p, long long max_jobs, hipStream_t st);
 
-// The interleaved-RoPE instantiations of launch_persist_k (decode_rope_ilv.hip): bf16 KV, and fp8
-// KV at D = 128.
+// The interleaved-RoPE instantiations of launch_persist_k (decode_rope_ilv.hip): bf16 and fp8 KV.
 template <int KVT, int D, int PS, int GP>
 hipError_t launch_persist_ilv(const DecodeParams& p, long long max_jobs, hipStream_t st);
 

@@ -6,8 +6,7 @@ namespace pdk {
 
 template <int KVT, int D, int PS, int GP>
 hipError_t launch_persist_ilv(const DecodeParams& p, long long max_jobs, hipStream_t st) {
-  if constexpr (KVT == kFP8 && D != 128) return hipErrorInvalidValue;
-  else return launch_persist_k<KVT, D, PS, GP, true, false, false, true>(p, max_jobs, st);
+  return launch_persist_k<KVT, D, PS, GP, true, false, false, true>(p, max_jobs, st);
 }
 
 #define PDK_ILV(KVT, D, PS, GP)                                                                    \

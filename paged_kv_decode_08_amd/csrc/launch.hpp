@@ -11,7 +11,7 @@ hipError_t launch_decode_valu(const DecodeParams& p, int kv_dtype, int D, int PS
                               unsigned grid, hipStream_t st);
 // persistent: grid = the jobs upper bound (units x num_chunks), capped at the workgroups that fit
 // on the device; otherwise one workgroup per (chunk, unit) and grid is that count.
-// rope: apply RoPE (bf16 KV, or fp8 KV at D = 128; persistent schedule only).
+// rope: apply RoPE (bf16 or fp8 KV).
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int D, int PS, int gp,
                               bool persistent, bool rope, long long grid, hipStream_t st);
 hipError_t launch_merge_state(const MergeParams& p, int v_dtype, hipStream_t st);

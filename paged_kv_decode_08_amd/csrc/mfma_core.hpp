@@ -17,9 +17,10 @@
 //    pairs with P rounded to bf16 (fp8 V: two rows' bytes interleaved with v_perm, converted
 //    exactly to bf16; bf16 V with 8 heads: two rows' elements regrouped with v_perm).
 //  * fp8: k_scale multiplies the scores, v_scale the output.
-//  * RoPE (ROPE = true; bf16 KV, or fp8 KV at D = 128): rotate-half pairs dims i and i + D/2, and
-//    the MFMA layout puts both in the same lane (k-steps j and j + KS/2; fp8 codes are converted
-//    exactly to fp32 first), so q (once per job) and each K row (per item)
+//  * RoPE (ROPE = true): rotate-half pairs dims i and i + D/2, and the MFMA layout puts both in
+//    the same lane (k-steps j and j + KS/2; fp8 codes are converted exactly to fp32 first), except
+//    for fp8 at D = 64, where the partner is in lane l ^ 32 and is fetched with a lane exchange
+//    (XLANE); so q (once per job) and each K row (per item)
 //    are rotated in registers in fp32 (angles: rope_cs_hw). The rotated values no longer
 //    fit bf16, so each is split into a bf16 high part and a bf16 remainder, and the scores take
 //    three products: q_hi.k_hi + q_hi.k_lo + q_lo.k_hi (the dropped q_lo.k_lo is below 2^-16 of
@@ -101,9 +102,11 @@ struct MfmaCore {
   static constexpr int PT_STRIDE = PS + 4;      // P^T row stride in floats (bank-conflict-free)
   using VT = typename VVec<KVT>::type;
   static_assert(GP <= 16 && (NI == 2 || NI % 4 == 0), "unsupported shape");
-  // RoPE needs dims i and i + D/2 in one lane: true for bf16, and for fp8 at D = 128
-  static_assert(!ROPE || (RB == 1 && (!FP8 || D == 128)), "RoPE on the matrix cores: 16-row items, bf16 or fp8 at D = 128");
+  static_assert(!ROPE || RB == 1, "RoPE on the matrix cores: 16-row items");
   static constexpr int KH = KS / 2;             // k-steps of the lower half of the head dim
+  // Rotate-half RoPE finds dims i and i + D/2 in one lane for bf16, and for fp8 at D = 128; fp8 at
+  // D = 64 holds dims [16 qg, +16) per lane, so each dim's partner sits in lane l ^ 32.
+  static constexpr bool XLANE = ROPE && !ILV && FP8 && D == 64;
   // P.V with P rounded to bf16 and row pairs through v_dot2_f32_bf16: fp8 V always, bf16 V with 8
   // heads (fp32 P for 8 heads would take the kernel past 256 VGPRs, one wave per SIMD)
   static constexpr bool PBF16 = FP8 || GP >= 8;
@@ -152,18 +155,47 @@ struct MfmaCore {
       qop[j] = n < G ? *reinterpret_cast<const uint4*>(qr + q_dim0(j)) : make_uint4(0, 0, 0, 0);
   }
 
+  // The 8 fp8 codes of k-step jj (even: words x, y; odd: z, w) of a 16-code load, in fp32.
+  __device__ __forceinline__ static void fp8_kstep(const uint4& raw, int jj, float (&x)[8]) {
+    const uint32_t w0 = (jj % 2) ? raw.z : raw.x, w1 = (jj % 2) ? raw.w : raw.y;
+    fp8x2_to_f32<false>(w0, x[0], x[1]);
+    fp8x2_to_f32<true>(w0, x[2], x[3]);
+    fp8x2_to_f32<false>(w1, x[4], x[5]);
+    fp8x2_to_f32<true>(w1, x[6], x[7]);
+  }
+
   // The 8 K elements of k-step jj of this lane's row, in fp32 (fp8 codes convert exactly).
   __device__ __forceinline__ void kstep_f32(const Buf& bf, int jj, float (&x)[8]) const {
-    if constexpr (FP8) {
-      const uint4 raw = bf.k[jj / 2];
-      const uint32_t w0 = (jj % 2) ? raw.z : raw.x, w1 = (jj % 2) ? raw.w : raw.y;
-      fp8x2_to_f32<false>(w0, x[0], x[1]);
-      fp8x2_to_f32<true>(w0, x[2], x[3]);
-      fp8x2_to_f32<false>(w1, x[4], x[5]);
-      fp8x2_to_f32<true>(w1, x[6], x[7]);
-    } else {
-      Kv<kBF16>::unpack(bf.k[jj], x);
+    if constexpr (FP8) fp8_kstep(bf.k[jj / 2], jj, x);
+    else Kv<kBF16>::unpack(bf.k[jj], x);
+  }
+
+  // The same words of lane l ^ 32 (the other half of the wave).
+  __device__ __forceinline__ static uint4 other_half(const uint4& v) {
+    return make_uint4(uint32_t(__shfl_xor(int(v.x), 32)), uint32_t(__shfl_xor(int(v.y), 32)),
+                      uint32_t(__shfl_xor(int(v.z), 32)), uint32_t(__shfl_xor(int(v.w), 32)));
+  }
+
+  // XLANE rotate-half at position pos: x holds this lane's 8 dims of k-step j, xp the same
+  // k-step of lane l ^ 32, i.e. the dims D/2 away. Lanes of the lower half (qg < 2) compute
+  // x c - xp s, the upper half x c + xp s; the result is split into bf16 high parts and
+  // remainders.
+  __device__ __forceinline__ void rope_xlane(const float (&x)[8], const float (&xp)[8], int j,
+                                             int pos, const float2* s_freq, uint4& hi,
+                                             uint4& lo) const {
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float2 f = s_freq[(q_dim0(j) + e) % (D / 2)];
+      float c, sn;
+      rope_cs_hw(pos, f.x, f.y, c, sn);
+      y[e] = qg < 2 ? x[e] * c - xp[e] * sn : x[e] * c + xp[e] * sn;
     }
+    uint32_t h[4], l4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_bf16(y[2 * e], y[2 * e + 1], h[e], l4[e]);
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l4[0], l4[1], l4[2], l4[3]);
   }
 
   // Rotates the q operand to position qpos (RoPE) and splits it into qop (high) and qlo.
@@ -187,6 +219,14 @@ struct MfmaCore {
         for (int e = 0; e < 4; ++e) split_bf16(y[2 * e], y[2 * e + 1], h[e], lo[e]);
         qop[j] = make_uint4(h[0], h[1], h[2], h[3]);
         qlo[j] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      }
+    } else if constexpr (XLANE) {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        float x[8], xp[8];
+        Kv<kBF16>::unpack(qop[j], x);
+        Kv<kBF16>::unpack(other_half(qop[j]), xp);
+        rope_xlane(x, xp, j, qpos, s_freq, qop[j], qlo[j]);
       }
     } else if constexpr (ROPE) {
 #pragma unroll
@@ -281,6 +321,15 @@ struct MfmaCore {
           for (int e = 0; e < 4; ++e) split_bf16(y[2 * e], y[2 * e + 1], h[e], lo[e]);
           khi[j] = make_uint4(h[0], h[1], h[2], h[3]);
           klo[j] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
+      } else if constexpr (XLANE) {
+        const uint4 oth = other_half(bf.k[0]);  // one 16-code load per row at D = 64
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+          float x[8], xp[8];
+          fp8_kstep(bf.k[0], j, x);
+          fp8_kstep(oth, j, xp);
+          rope_xlane(x, xp, j, pos0 + n, s_freq, khi[j], klo[j]);
         }
       } else {
 #pragma unroll

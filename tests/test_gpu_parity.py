@@ -540,10 +540,11 @@ def test_large_batch_one_workgroup_per_chunk(kv, G, ps):
     run_and_check(w)
 
 
-@pytest.mark.parametrize("G,D,ps", [(8, 128, 32), (4, 128, 16), (1, 128, 32), (4, 64, 16)])
+@pytest.mark.parametrize("G,D,ps", [(8, 128, 32), (4, 128, 16), (1, 128, 32), (4, 64, 16),
+                                    (8, 64, 32), (1, 64, 16), (2, 64, 32)])
 def test_rope_fp8_kv(G, D, ps):
-    """RoPE with fp8 KV: on the matrix cores at D = 128 (codes converted exactly to fp32 before
-    the rotation), on the vector-ALU kernel at D = 64 (rotation partners in different lanes)."""
+    """RoPE with fp8 KV on the matrix cores (codes converted exactly to fp32 before the rotation);
+    at D = 64 each dim's rotation partner is fetched from the other half of the wave."""
     lens = [2500, 33, 0, 700, 4100]
     w = synth.make_workload(name=f"rope_fp8_G{G}_D{D}_ps{ps}", B=len(lens), H_qo=2 * G, H_kv=2,
                             D=D, page_size=ps, seq_lens=lens, seed=900 + G + D + ps,
@@ -724,7 +725,9 @@ def test_attention_multi_split(splits):
                                                 ("bf16", 2, 3, 64, 32, 0),
                                                 ("fp8", 2, 4, 128, 16, 0),
                                                 ("bf16", 4, 2, 128, 16, 12),
-                                                ("fp8", 1, 8, 128, 32, 3)])
+                                                ("fp8", 1, 8, 128, 32, 3),
+                                                ("fp8", 2, 3, 64, 32, 0),
+                                                ("fp8", 4, 2, 64, 16, 12)])
 def test_attention_multi_rope(kv, G, T, D, ps, splits):
     """Rotate-half RoPE with several tokens: token t's query at q_rope_position + t (oracle
     reading), Llama-3 base; lengths around page boundaries, tokens with no row, split sequences
@@ -816,7 +819,8 @@ def test_learned_sink_multi_token():
 
 @pytest.mark.parametrize("kv,G,D,ps", [("bf16", 4, 128, 16), ("bf16", 2, 64, 32),
                                        ("bf16", 8, 128, 16), ("fp8", 4, 128, 32),
-                                       ("fp8", 8, 128, 16)])
+                                       ("fp8", 8, 128, 16), ("fp8", 4, 64, 16),
+                                       ("fp8", 2, 64, 32)])
 def test_rope_interleaved(kv, G, D, ps):
     """Interleaved RoPE (pairs (2i, 2i + 1)) against the oracle, with a window and sink on half of
     the cases, and large positions."""
@@ -834,10 +838,9 @@ def test_rope_interleaved(kv, G, D, ps):
 
 
 def test_rope_interleaved_unsupported_where_not_built():
-    """Interleaved RoPE is refused (before any launch) on the fp32 pool's vector-ALU kernel and for
-    fp8 at head dim 64."""
+    """Interleaved RoPE is refused (before any launch) on the fp32 pool's vector-ALU kernel."""
     import paged_kv_decode_08_amd as pk
-    for kv, D in (("f32", 64), ("fp8", 64)):
+    for kv, D in (("f32", 64),):
         w = synth.make_workload(name=f"ilv_unsup_{kv}", B=2, H_qo=4, H_kv=2, D=D, page_size=16,
                                 seq_lens=[30, 7], q_dtype="f32" if kv == "f32" else "bf16",
                                 kv_dtype=kv, seed=960, max_num_pages=16, rotary_mode=2)
@@ -1020,3 +1023,7 @@ def test_append_attention_fp8_rope_window():
                              page_size=16, seq_lens=[2500, 33, 900], seed=761, max_num_pages=512,
                              q_dtype="bf16", kv_dtype="fp8", rotary_mode=1, rope_theta=10000.0)
     _fused_case(w2, seed=77, num_kv_splits=5)
+    w3 = synth.make_workload(name="fused_fp8_rope_d64", B=4, H_qo=8, H_kv=2, D=64, page_size=16,
+                             seq_lens=[2500, 1, 900, 17], seed=762, max_num_pages=512,
+                             q_dtype="bf16", kv_dtype="fp8", rotary_mode=1, rope_theta=500000.0)
+    _fused_case(w3, seed=78)
