@@ -125,9 +125,9 @@ typedef struct pdecode_rope {
  * invalid description. */
 size_t pdecode_workspace_bytes(const pdecode_desc *d);
 
-/* The split plan for `d` in calls without RoPE: rows are processed in chunks of *chunk_pages page
- * slots and a sequence uses at most *num_chunks chunks (calls with RoPE use smaller chunks; the
- * workspace size covers both). Returns PDECODE_OK or an argument error. */
+/* The split plan for `d` (with or without RoPE): rows are processed in chunks of *chunk_pages page
+ * slots and a sequence uses at most *num_chunks chunks. Returns PDECODE_OK or an argument
+ * error. */
 pdecode_status pdecode_plan(const pdecode_desc *d, int32_t *chunk_pages, int32_t *num_chunks);
 
 /* Decode attention (see the header comment for the computation and layouts).

@@ -22,7 +22,7 @@ struct Plan {
   size_t part_o_bytes = 0;
   size_t part_lse_bytes = 0;
   size_t counter_bytes = 0;
-  bool persistent = false;  // matrix-core kernel on the persistent schedule (when no RoPE)
+  bool persistent = false;  // matrix-core kernel on the persistent schedule
   size_t workspace_bytes() const { return part_o_bytes + part_lse_bytes + counter_bytes; }
 };
 
@@ -60,9 +60,8 @@ pdecode_status check_attention_shape(const pdecode_desc* d) {
 // Chunking of each sequence's page slots. A sequence with n slots uses ceil(n / chunk_slots)
 // chunks, capped at num_chunks (the last chunk then takes every remaining slot), so any length
 // is computed exactly; max_kv_len only sizes the grid.
-// rope: the call applies RoPE (bf16 or fp8 KV: the matrix-core kernels, planned as without RoPE;
-// fp32 KV: the vector-ALU kernel).
-Plan make_plan(const pdecode_desc* d, bool rope, int qo_len = 1) {
+// The plan does not depend on RoPE: calls with and without it run the same kernel family.
+Plan make_plan(const pdecode_desc* d, int qo_len = 1) {
   Plan pl;
   const int64_t ps = d->page_size;
   const int64_t max_len = d->max_kv_len > 0 ? d->max_kv_len : int64_t(d->max_num_pages) * ps;
@@ -99,9 +98,9 @@ Plan make_plan(const pdecode_desc* d, bool rope, int qo_len = 1) {
     pl.part_lse_bytes = align256(rows * sizeof(float));
   }
   // split arrival counters [B * H_kv], then the two job-queue counters of the persistent schedule.
-  // They lead the workspace, at the same offset and size in every plan of a description (with or
-  // without RoPE), so a workspace alternating between those plans keeps its counters apart from
-  // the partial states.
+  // They lead the workspace, at the same offset and size in every plan of a description (any
+  // query-token count), so a workspace alternating between those plans keeps its counters apart
+  // from the partial states.
   if (pl.num_chunks > 1 || pl.persistent)
     pl.counter_bytes = align256((size_t(d->batch) * d->num_kv_heads + 2) * sizeof(int32_t));
   return pl;
@@ -126,9 +125,7 @@ const char* pdecode_status_string(pdecode_status s) {
 
 size_t pdecode_workspace_bytes(const pdecode_desc* d) {
   if (check_desc(d) != PDECODE_OK || check_attention_shape(d) != PDECODE_OK) return 0;
-  // enough for calls with and without RoPE
-  const size_t a = make_plan(d, false).workspace_bytes(), b = make_plan(d, true).workspace_bytes();
-  return a > b ? a : b;
+  return make_plan(d).workspace_bytes();
 }
 
 pdecode_status pdecode_plan(const pdecode_desc* d, int32_t* chunk_pages, int32_t* num_chunks) {
@@ -136,7 +133,7 @@ pdecode_status pdecode_plan(const pdecode_desc* d, int32_t* chunk_pages, int32_t
   if (st != PDECODE_OK) return st;
   if ((st = check_attention_shape(d)) != PDECODE_OK) return st;
   if (!chunk_pages || !num_chunks) return PDECODE_ERR_INVALID_ARG;
-  const Plan pl = make_plan(d, false);
+  const Plan pl = make_plan(d);
   *chunk_pages = pl.chunk_slots;
   *num_chunks = pl.num_chunks;
   return PDECODE_OK;
@@ -170,7 +167,7 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   if (d->batch == 0) return PDECODE_OK;
   if (!q || !pages || !page_indptr || !page_values || !length_info || !out || !lse)
     return PDECODE_ERR_INVALID_ARG;
-  const Plan pl = make_plan(d, rotary, qo_len);
+  const Plan pl = make_plan(d, qo_len);
   if ((fused || qo_len > 1 || d->sink_logits) && !pl.persistent) return PDECODE_ERR_UNSUPPORTED;
   // the fused append writes e4m3fn codes only
   if (fused && d->kv_dtype == PDECODE_FP8_E4M3) return PDECODE_ERR_UNSUPPORTED;
@@ -254,7 +251,7 @@ pdecode_status pdecode_attention(const pdecode_desc* d, const void* q, const voi
 size_t pdecode_workspace_bytes_multi(const pdecode_desc* d, int32_t qo_len) {
   if (qo_len < 1) return 0;
   if (check_desc(d) != PDECODE_OK || check_attention_shape(d) != PDECODE_OK) return 0;
-  return make_plan(d, false, qo_len).workspace_bytes();
+  return make_plan(d, qo_len).workspace_bytes();
 }
 
 pdecode_status pdecode_attention_multi(const pdecode_desc* d, int32_t qo_len, const void* q,
