@@ -964,14 +964,29 @@ def test_full_size_multi_token_rope_sampled():
 
 # ---- IEEE-style e4m3 pool (PDECODE_FP8_E4M3, max 240)
 
-@pytest.mark.parametrize("G,ps,splits", [(4, 32, 0), (8, 16, 3), (2, 32, 12)])
-def test_fp8_e4m3_pool_decode(G, ps, splits):
-    """Decode over an IEEE-style e4m3 pool (finite codes within +-240) against the oracle."""
+@pytest.mark.parametrize("G,ps,splits,D,rot", [(4, 32, 0, 128, 0), (8, 16, 3, 128, 0),
+                                               (2, 32, 12, 128, 0), (4, 16, 0, 128, 1),
+                                               (8, 32, 3, 64, 1), (2, 16, 0, 64, 2)])
+def test_fp8_e4m3_pool_decode(G, ps, splits, D, rot):
+    """Decode over an IEEE-style e4m3 pool (finite codes within +-240) against the oracle, also
+    with rotate-half and interleaved RoPE at head dims 128 and 64."""
     lens = [1, 300, 2000, 0, 5 * ps + 3]
-    w = synth.make_workload(name=f"e4m3_G{G}_ps{ps}_s{splits}", B=len(lens), H_qo=2 * G, H_kv=2,
-                            D=128, page_size=ps, seq_lens=lens, q_dtype="bf16",
-                            kv_dtype="fp8e4m3", seed=990 + G + ps, max_num_pages=512)
+    w = synth.make_workload(name=f"e4m3_G{G}_ps{ps}_s{splits}_D{D}_r{rot}", B=len(lens),
+                            H_qo=2 * G, H_kv=2, D=D, page_size=ps, seq_lens=lens, q_dtype="bf16",
+                            kv_dtype="fp8e4m3", seed=990 + G + ps + D + rot, max_num_pages=512,
+                            rotary_mode=rot, rope_theta=500000.0)
     run_and_check(w, num_kv_splits=splits)
+
+
+@pytest.mark.parametrize("G,T,D,rot", [(2, 4, 128, 0), (4, 2, 64, 1)])
+def test_fp8_e4m3_pool_multi_token(G, T, D, rot):
+    """Several query tokens over an IEEE-style e4m3 pool, without and with RoPE."""
+    lens = [1, T - 1, 16, 700, 0, 2500]
+    w = synth.make_workload(name=f"e4m3_multi_G{G}_T{T}_D{D}_r{rot}", B=len(lens), H_qo=2 * G,
+                            H_kv=2, D=D, page_size=16, seq_lens=lens, q_dtype="bf16",
+                            kv_dtype="fp8e4m3", seed=995 + G + T + D, max_num_pages=512,
+                            rotary_mode=rot, rope_theta=500000.0)
+    _multi_case(w, T, seed=99 + T)
 
 
 @pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
