@@ -356,14 +356,27 @@ struct MfmaCore {
         klo[j] = make_uint4(l1[0], l1[1], l1[2], l1[3]);
         khi[j + KH] = make_uint4(h2[0], h2[1], h2[2], h2[3]);
         klo[j + KH] = make_uint4(l2[0], l2[1], l2[2], l2[3]);
-      }
-      }
-      acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (COLCAP) {
+          // several tokens: each rotated k-step pair goes to the matrix cores at once, so the
+          // rotated K pieces are not all live together (the 8-column kernel is at 256 VGPRs)
+          if (j == 0) acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jj = 0; jj < KS; ++jj) {
-        acc[0] = mfma_16x16x32_bf16(khi[jj], qop[jj], acc[0]);
-        acc[0] = mfma_16x16x32_bf16(klo[jj], qop[jj], acc[0]);
-        acc[0] = mfma_16x16x32_bf16(khi[jj], qlo[jj], acc[0]);
+          for (int jj = j; jj < KS; jj += KH) {
+            acc[0] = mfma_16x16x32_bf16(khi[jj], qop[jj], acc[0]);
+            acc[0] = mfma_16x16x32_bf16(klo[jj], qop[jj], acc[0]);
+            acc[0] = mfma_16x16x32_bf16(khi[jj], qlo[jj], acc[0]);
+          }
+        }
+      }
+      }
+      if constexpr (!COLCAP || ILV || XLANE) {
+        acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < KS; ++jj) {
+          acc[0] = mfma_16x16x32_bf16(khi[jj], qop[jj], acc[0]);
+          acc[0] = mfma_16x16x32_bf16(klo[jj], qop[jj], acc[0]);
+          acc[0] = mfma_16x16x32_bf16(khi[jj], qlo[jj], acc[0]);
+        }
       }
     } else {
 #pragma unroll
