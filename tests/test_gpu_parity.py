@@ -554,16 +554,18 @@ def test_rope_fp8_kv(G, D, ps):
     run_and_check(w, num_kv_splits=4)
 
 
-@pytest.mark.parametrize("kv,G,ps", [("bf16", 4, 16), ("fp8", 8, 32)])
-def test_large_batch_rope(kv, G, ps):
+@pytest.mark.parametrize("kv,G,ps,D", [("bf16", 4, 16, 128), ("fp8", 8, 32, 128),
+                                        ("fp8", 4, 16, 64)])
+def test_large_batch_rope(kv, G, ps, D):
     """RoPE with more sequences than the persistent job table holds: the one-workgroup-per-chunk
-    matrix-core kernel rotates q and K in registers too (window + sink, split sequences)."""
+    matrix-core kernel rotates q and K in registers too (window + sink, split sequences; fp8 at
+    head dim 64 through the lane exchange)."""
     B = 1100
     rng = np.random.default_rng(850 + G + ps)
     lens = rng.integers(0, 200, size=B)
     lens[rng.integers(0, B, size=30)] = 2500
     pages = int(np.sum((lens + ps - 1) // ps)) + 8
-    w = synth.make_workload(name=f"bigB_rope_{kv}_G{G}_ps{ps}", B=B, H_qo=2 * G, H_kv=2, D=128,
+    w = synth.make_workload(name=f"bigB_rope_{kv}_G{G}_ps{ps}_D{D}", B=B, H_qo=2 * G, H_kv=2, D=D,
                             page_size=ps, seq_lens=lens, seed=860 + G + ps, max_num_pages=pages,
                             kv_dtype=kv, rotary_mode=1, rope_theta=500000.0, window=1500, sink=4)
     run_and_check(w)
