@@ -108,9 +108,9 @@ typedef struct pdecode_desc {
  * i < D/2, angle = position * rope_scale * rope_theta^(-2i/D), x'[i] = x[i] cos - x[i + D/2] sin,
  * x'[i + D/2] = x[i + D/2] cos + x[i] sin. rotary_mode == 2: the interleaved layout (the AWS
  * attention_block_tkg page's rope_contiguous_layout = False), the same rotation on the pairs
- * (2i, 2i + 1); supported on the persistent matrix-core schedule (BF16 pool, or FP8 at head_dim
- * 128; batch <= 1024), not with pdecode_append_attention; otherwise UNSUPPORTED. Any other value:
- * no RoPE. The rotated q and k stay in fp32 (or a bf16 pair that holds them to 2^-16). */
+ * (2i, 2i + 1); supported on the persistent matrix-core schedule (BF16 or FP8 pool, batch
+ * <= 1024), including pdecode_append_attention, with one query token; otherwise UNSUPPORTED. Any
+ * other value: no RoPE. The rotated q and k stay in fp32 (or a bf16 pair that holds them to 2^-16). */
 typedef struct pdecode_rope {
   int32_t rotary_mode;
   float rope_scale;

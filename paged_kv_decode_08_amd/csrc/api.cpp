@@ -171,8 +171,8 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   if ((fused || qo_len > 1 || d->sink_logits) && !pl.persistent) return PDECODE_ERR_UNSUPPORTED;
   // the fused append writes e4m3fn codes only
   if (fused && d->kv_dtype == PDECODE_FP8_E4M3) return PDECODE_ERR_UNSUPPORTED;
-  // interleaved RoPE: the persistent matrix-core kernels only, not fused with the append
-  if (rotary && rope->rotary_mode == 2 && (!pl.persistent || fused || qo_len > 1))
+  // interleaved RoPE: the persistent matrix-core kernels only, one query token
+  if (rotary && rope->rotary_mode == 2 && (!pl.persistent || qo_len > 1))
     return PDECODE_ERR_UNSUPPORTED;
   const int64_t grid = int64_t(pl.num_chunks) * d->batch * d->num_kv_heads;
   if (grid > INT_MAX) return PDECODE_ERR_UNSUPPORTED;

@@ -278,7 +278,7 @@ static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipS
     if (ROPE && p.rotary == 2) return hipErrorInvalidValue;  // several tokens: rotate-half only
     e = launch_persist_multi<KVT, D, PS, GP, ROPE>(p, max_jobs, st);
   } else if (ROPE && p.rotary == 2) {
-    e = launch_persist_ilv<KVT, D, PS, GP>(p, max_jobs, st);  // interleaved RoPE, not fused
+    e = launch_persist_ilv<KVT, D, PS, GP>(p, max_jobs, st);  // interleaved RoPE, plain or fused
   } else {
     e = p.new_k != nullptr ? launch_persist_fused<KVT, D, PS, GP, ROPE>(p, max_jobs, st)
                            : launch_persist_k<KVT, D, PS, GP, ROPE, false>(p, max_jobs, st);

@@ -814,7 +814,8 @@ hipError_t launch_persist_fused(const DecodeParams& p, long long max_jobs, hipSt
 template <int KVT, int D, int PS, int GP, bool ROPE>
 hipError_t launch_persist_multi(const DecodeParams& p, long long max_jobs, hipStream_t st);
 
-// The interleaved-RoPE instantiations of launch_persist_k (decode_rope_ilv.hip): bf16 and fp8 KV.
+// The interleaved-RoPE instantiations of launch_persist_k (decode_rope_ilv.hip): bf16 and fp8 KV,
+// plain and fused.
 template <int KVT, int D, int PS, int GP>
 hipError_t launch_persist_ilv(const DecodeParams& p, long long max_jobs, hipStream_t st);
 

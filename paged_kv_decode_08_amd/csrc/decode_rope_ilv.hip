@@ -1,11 +1,15 @@
 // Decode with interleaved RoPE (rotary_mode 2, pairs (2i, 2i + 1)): the ILV instantiations of the
-// persistent matrix-core decode kernel (decode_persist.hpp), built apart from decode_mfma.hip.
+// persistent matrix-core decode kernel (decode_persist.hpp), plain and with the fused append,
+// built apart from decode_mfma.hip.
 #include "decode_persist.hpp"
 
 namespace pdk {
 
 template <int KVT, int D, int PS, int GP>
 hipError_t launch_persist_ilv(const DecodeParams& p, long long max_jobs, hipStream_t st) {
+  // with the fused append: the new row is substituted in its raw form, before the rotation
+  if (p.new_k != nullptr)
+    return launch_persist_k<KVT, D, PS, GP, true, true, false, true>(p, max_jobs, st);
   return launch_persist_k<KVT, D, PS, GP, true, false, false, true>(p, max_jobs, st);
 }
 

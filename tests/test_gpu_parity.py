@@ -660,6 +660,19 @@ def test_append_attention_rope_window():
     _fused_case(w, seed=74)
 
 
+@pytest.mark.parametrize("kv,D,ps,splits", [("bf16", 128, 16, 0), ("fp8", 64, 32, 5),
+                                             ("bf16", 64, 16, 12)])
+def test_append_attention_interleaved_rope(kv, D, ps, splits):
+    """Fused append with interleaved RoPE: the new row is substituted in its raw form and rotated
+    in pairs (2i, 2i + 1) like every other K row; a window and sink on the first case."""
+    win = dict(window=1024, sink=4) if splits == 0 else {}
+    w = synth.make_workload(name=f"fused_ilv_{kv}_D{D}_ps{ps}_s{splits}", B=4, H_qo=16, H_kv=4,
+                            D=D, page_size=ps, seq_lens=[3000, 1, 700, 2 * ps + 1], seed=770 + D,
+                            max_num_pages=512, q_dtype="bf16", kv_dtype=kv, rotary_mode=2,
+                            rope_theta=500000.0, **win)
+    _fused_case(w, seed=79, num_kv_splits=splits)
+
+
 def test_append_attention_no_attended_rows():
     """An empty window without a sink: no row is attended (out = 0, lse = -5e4), yet every
     sequence with pages still gets its new row."""
