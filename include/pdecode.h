@@ -109,8 +109,8 @@ typedef struct pdecode_desc {
  * x'[i + D/2] = x[i + D/2] cos + x[i] sin. rotary_mode == 2: the interleaved layout (the AWS
  * attention_block_tkg page's rope_contiguous_layout = False), the same rotation on the pairs
  * (2i, 2i + 1); supported on the persistent matrix-core schedule (BF16 or FP8 pool, batch
- * <= 1024), including pdecode_append_attention, with one query token; otherwise UNSUPPORTED. Any
- * other value: no RoPE. The rotated q and k stay in fp32 (or a bf16 pair that holds them to 2^-16). */
+ * <= 1024), including pdecode_append_attention and pdecode_attention_multi; otherwise
+ * UNSUPPORTED. Any other value: no RoPE. The rotated q and k stay in fp32 (or a bf16 pair that holds them to 2^-16). */
 typedef struct pdecode_rope {
   int32_t rotary_mode;
   float rope_scale;
@@ -157,11 +157,11 @@ pdecode_status pdecode_attention(const pdecode_desc *d, const void *q, const voi
  * lse = -5e4, as a sequence without pages does.
  * q, out: device [batch, qo_len, num_qo_heads, head_dim] (q_dtype); lse: fp32 [batch, qo_len,
  * num_qo_heads]. The other arguments are those of pdecode_attention; the workspace is sized by
- * pdecode_workspace_bytes_multi(d, qo_len), with the same reuse rules. With rotate-half RoPE
- * (rotary_mode 1), token t's query sits at position q_rope_position[b] + t; the keys are placed as
- * in pdecode_attention.
+ * pdecode_workspace_bytes_multi(d, qo_len), with the same reuse rules. With RoPE (either
+ * rotary_mode), token t's query sits at position q_rope_position[b] + t; the keys are placed as in
+ * pdecode_attention.
  * qo_len == 1 is pdecode_attention. Supported for qo_len > 1: no sliding window,
- * (num_qo_heads / num_kv_heads) * qo_len <= 8, no interleaved RoPE, and the persistent
+ * (num_qo_heads / num_kv_heads) * qo_len <= 8, and the persistent
  * matrix-core schedule (BF16 or FP8 pool, batch <= 1024); otherwise UNSUPPORTED. Errors: as pdecode_attention, and INVALID_ARG for qo_len < 1. */
 size_t pdecode_workspace_bytes_multi(const pdecode_desc *d, int32_t qo_len);
 pdecode_status pdecode_attention_multi(const pdecode_desc *d, int32_t qo_len, const void *q,

@@ -160,8 +160,8 @@ def decode_multi(*, qo_len, q, select=None, **kw):
     tokens: the last qo_len positions of each sequence are the new tokens, and token t attends
     positions 0 .. total - qo_len + t, i.e. it is the TVM page's single-token decode over that
     prefix of the sequence (its first ceil(len / ps) pages, the last one holding len - (np - 1) ps
-    rows). An empty prefix gives the empty convention. No window. With rotate-half RoPE (the
-    page's decode RoPE, rotary_mode 1), token t's query is at position q_rope_position[b] + t (the
+    rows). An empty prefix gives the empty convention. No window. With RoPE (rotary_mode 1,
+    rotate-half, or 2, interleaved), token t's query is at position q_rope_position[b] + t (the
     new tokens are consecutive) and the keys keep the sequence's k_rope_pos_offset[b]. Returns
     (out [B, T, H_qo, D], lse [B, T, H_qo]), or, for select = int array [n, 3] of (b, t, h_qo),
     (out [n, D], lse [n])."""
@@ -188,13 +188,12 @@ def decode_multi(*, qo_len, q, select=None, **kw):
     kw.update(B=B * T, indptr=np.array(ip2, np.int32), values=np.array(val2, np.int32),
               length_info=np.array(last2, np.int32), q=np.ascontiguousarray(q).reshape(
                   B * T, kw["H_qo"], kw["D"]))
-    if kw.get("rotary_mode", 0) == 1:
+    if kw.get("rotary_mode", 0) in (1, 2):
         qrp = np.asarray(kw["q_rope_position"], np.int64).reshape(-1)[:B]
         kro = np.asarray(kw["k_rope_pos_offset"], np.int64).reshape(-1)[:B]
         kw["q_rope_position"] = (qrp[:, None] + np.arange(T)[None, :]).reshape(-1).astype(np.int32)
         kw["k_rope_pos_offset"] = np.repeat(kro, T).astype(np.int32)
     else:
-        assert kw.get("rotary_mode", 0) == 0, "several query tokens: rotate-half RoPE only"
         for key in ("q_rope_position", "k_rope_pos_offset", "rotary_mode"):
             kw.pop(key, None)
     if select is not None:

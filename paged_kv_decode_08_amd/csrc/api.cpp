@@ -145,8 +145,7 @@ namespace {
 
 // pdecode_attention, and with new_k / new_v set the fused append of pdecode_append_attention
 // (the persistent matrix-core schedule only).
-// qo_len > 1: several query tokens per sequence (pdecode_attention_multi; rotate-half RoPE only,
-// no window).
+// qo_len > 1: several query tokens per sequence (pdecode_attention_multi; no window).
 pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const void* new_v,
                               const void* q, const void* pages, const int32_t* page_indptr,
                               const int32_t* page_values, const int32_t* length_info,
@@ -171,8 +170,8 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   if ((fused || qo_len > 1 || d->sink_logits) && !pl.persistent) return PDECODE_ERR_UNSUPPORTED;
   // the fused append writes e4m3fn codes only
   if (fused && d->kv_dtype == PDECODE_FP8_E4M3) return PDECODE_ERR_UNSUPPORTED;
-  // interleaved RoPE: the persistent matrix-core kernels only, one query token
-  if (rotary && rope->rotary_mode == 2 && (!pl.persistent || qo_len > 1))
+  // interleaved RoPE: the persistent matrix-core kernels only
+  if (rotary && rope->rotary_mode == 2 && !pl.persistent)
     return PDECODE_ERR_UNSUPPORTED;
   const int64_t grid = int64_t(pl.num_chunks) * d->batch * d->num_kv_heads;
   if (grid > INT_MAX) return PDECODE_ERR_UNSUPPORTED;

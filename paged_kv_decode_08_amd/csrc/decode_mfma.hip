@@ -275,8 +275,7 @@ template <int KVT, int D, int PS, int GP, bool ROPE>
 static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipStream_t st) {
   hipError_t e;
   if (p.T > 1) {
-    if (ROPE && p.rotary == 2) return hipErrorInvalidValue;  // several tokens: rotate-half only
-    e = launch_persist_multi<KVT, D, PS, GP, ROPE>(p, max_jobs, st);
+    e = launch_persist_multi<KVT, D, PS, GP, ROPE>(p, max_jobs, st);  // either RoPE layout
   } else if (ROPE && p.rotary == 2) {
     e = launch_persist_ilv<KVT, D, PS, GP>(p, max_jobs, st);  // interleaved RoPE, plain or fused
   } else {

@@ -1,8 +1,8 @@
 // Decode with several query tokens per sequence (pdecode_attention_multi): the MT instantiations
 // of the persistent matrix-core decode kernel (decode_persist.hpp), built apart from
 // decode_mfma.hip. The G q heads of a KV head times the T tokens fill up to 8 columns of the MFMA
-// B operand (group bound GP 2, 4 or 8). With rotate-half RoPE, token t of a sequence is rotated
-// t positions after the sequence's first query position.
+// B operand (group bound GP 2, 4 or 8). With RoPE (rotate-half or interleaved), token t of a
+// sequence is rotated t positions after the sequence's first query position.
 #include "decode_persist.hpp"
 
 namespace pdk {
@@ -10,7 +10,13 @@ namespace pdk {
 template <int KVT, int D, int PS, int GP, bool ROPE>
 hipError_t launch_persist_multi(const DecodeParams& p, long long max_jobs, hipStream_t st) {
   if constexpr (GP < 2) return hipErrorInvalidValue;
-  else return launch_persist_k<KVT, D, PS, GP, ROPE, false, true>(p, max_jobs, st);
+  else if constexpr (ROPE) {
+    if (p.rotary == 2)  // interleaved pairs
+      return launch_persist_k<KVT, D, PS, GP, true, false, true, true>(p, max_jobs, st);
+    return launch_persist_k<KVT, D, PS, GP, true, false, true>(p, max_jobs, st);
+  } else {
+    return launch_persist_k<KVT, D, PS, GP, false, false, true>(p, max_jobs, st);
+  }
 }
 
 #define PDK_MULTI(KVT, D, PS, GP, ROPE)                                                           \

@@ -256,7 +256,7 @@ __device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
 }
 
 // FUSED: the call also appends each sequence's new K/V row (p.new_k, p.new_v).
-// MT: several query tokens per sequence (p.T > 1; no RoPE, no window): the G T columns of the
+// MT: several query tokens per sequence (p.T > 1; no window): the G T columns of the
 // MFMA B operand are token-major and each is causally capped.
 // ILV (with ROPE): the interleaved RoPE layout (rotary_mode 2).
 template <int KVT, int D, int PS, int GP, bool ROPE, bool FUSED, bool MT = false, bool ILV = false>
@@ -810,7 +810,7 @@ template <int KVT, int D, int PS, int GP, bool ROPE>
 hipError_t launch_persist_fused(const DecodeParams& p, long long max_jobs, hipStream_t st);
 
 // The several-query-token instantiations of launch_persist_k (decode_multi.hip): without and with
-// rotate-half RoPE; no fused append.
+// RoPE in either layout; no fused append.
 template <int KVT, int D, int PS, int GP, bool ROPE>
 hipError_t launch_persist_multi(const DecodeParams& p, long long max_jobs, hipStream_t st);
 

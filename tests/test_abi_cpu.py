@@ -172,9 +172,8 @@ def test_append_attention_argument_errors(L):
 
 def test_attention_multi_argument_errors(L):
     """pdecode_attention_multi: qo_len < 1, a sliding window, more than 8 MFMA columns (group
-    size x tokens), an fp32 pool, a batch beyond the persistent schedule, interleaved RoPE and an
-    invalid RoPE base are refused before anything is launched; the workspace size grows with the
-    tokens."""
+    size x tokens), an fp32 pool, a batch beyond the persistent schedule and an invalid RoPE base
+    are refused before anything is launched; the workspace size grows with the tokens."""
     f = L.pdecode_attention_multi
 
     def call(d, T, rope=None):
@@ -182,7 +181,6 @@ def test_attention_multi_argument_errors(L):
                  None if rope is None else ctypes.byref(rope), 0.1, FAKE, FAKE, FAKE, 1 << 30,
                  None)
     assert call(desc(), 0) == 1
-    assert call(desc(), 2, pk.Rope(2, 1.0, 5e5, FAKE, FAKE)) == 2
     assert call(desc(), 2, pk.Rope(1, 1.0, -1.0, FAKE, FAKE)) == 1
     assert call(desc(sliding_window=True), 2) == 2
     assert call(desc(), 3) == 2                   # 4 q heads per KV head x 3 tokens > 8

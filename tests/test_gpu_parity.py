@@ -736,22 +736,26 @@ def test_attention_multi_split(splits):
     _multi_case(w, 2, seed=83, num_kv_splits=splits)
 
 
-@pytest.mark.parametrize("kv,G,T,D,ps,splits", [("bf16", 4, 2, 128, 16, 0),
-                                                ("bf16", 2, 3, 64, 32, 0),
-                                                ("fp8", 2, 4, 128, 16, 0),
-                                                ("bf16", 4, 2, 128, 16, 12),
-                                                ("fp8", 1, 8, 128, 32, 3),
-                                                ("fp8", 2, 3, 64, 32, 0),
-                                                ("fp8", 4, 2, 64, 16, 12)])
-def test_attention_multi_rope(kv, G, T, D, ps, splits):
-    """Rotate-half RoPE with several tokens: token t's query at q_rope_position + t (oracle
-    reading), Llama-3 base; lengths around page boundaries, tokens with no row, split sequences
-    merged in the kernel and by the split merge kernel."""
+@pytest.mark.parametrize("kv,G,T,D,ps,splits,rot", [("bf16", 4, 2, 128, 16, 0, 1),
+                                                    ("bf16", 2, 3, 64, 32, 0, 1),
+                                                    ("fp8", 2, 4, 128, 16, 0, 1),
+                                                    ("bf16", 4, 2, 128, 16, 12, 1),
+                                                    ("fp8", 1, 8, 128, 32, 3, 1),
+                                                    ("fp8", 2, 3, 64, 32, 0, 1),
+                                                    ("fp8", 4, 2, 64, 16, 12, 1),
+                                                    ("bf16", 4, 2, 128, 16, 0, 2),
+                                                    ("bf16", 1, 8, 64, 32, 5, 2),
+                                                    ("fp8", 2, 4, 64, 16, 12, 2),
+                                                    ("fp8", 8, 1, 128, 32, 0, 2)])
+def test_attention_multi_rope(kv, G, T, D, ps, splits, rot):
+    """RoPE with several tokens (rotate-half, or interleaved for rot = 2): token t's query at
+    q_rope_position + t (oracle reading), Llama-3 base; lengths around page boundaries, tokens
+    with no row, split sequences merged by the split merge kernel."""
     lens = [1, T - 1, ps, ps + 1, 3 * ps - 1, 2500, 0, 2 * ps + T]
-    w = synth.make_workload(name=f"multi_rope_{kv}_G{G}_T{T}_D{D}_ps{ps}_s{splits}", B=len(lens),
-                            H_qo=2 * G, H_kv=2, D=D, page_size=ps, seq_lens=lens, q_dtype="bf16",
-                            kv_dtype=kv, seed=860 + G + T + D + ps + splits, max_num_pages=512,
-                            rotary_mode=1, rope_theta=500000.0)
+    w = synth.make_workload(name=f"multi_rope{rot}_{kv}_G{G}_T{T}_D{D}_ps{ps}_s{splits}",
+                            B=len(lens), H_qo=2 * G, H_kv=2, D=D, page_size=ps, seq_lens=lens,
+                            q_dtype="bf16", kv_dtype=kv, seed=860 + G + T + D + ps + splits + rot,
+                            max_num_pages=512, rotary_mode=rot, rope_theta=500000.0)
     _multi_case(w, T, seed=86 + T, num_kv_splits=splits)
 
 

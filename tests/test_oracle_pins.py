@@ -563,13 +563,16 @@ def test_multi_token_matches_dense_causal_bruteforce(kv_dtype, q_dtype, T):
                 assert abs(lse[b, t, hq] - l) < 1e-12
 
 
+@pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("kv_dtype,q_dtype", [("f32", "f32"), ("bf16", "bf16")])
-def test_multi_token_rope_matches_dense_causal_bruteforce(kv_dtype, q_dtype):
-    """Rotate-half RoPE with several tokens: token t's query rotated to q_rope_position + t, the
-    flattened cache's row r to k_rope_pos_offset + r, then the causal brute force as above."""
+def test_multi_token_rope_matches_dense_causal_bruteforce(kv_dtype, q_dtype, mode):
+    """RoPE (rotate-half or interleaved) with several tokens: token t's query rotated to
+    q_rope_position + t, the flattened cache's row r to k_rope_pos_offset + r, then the causal
+    brute force as above."""
     T = 3
+    ilv = mode == 2
     w = small(B=4, kv_dtype=kv_dtype, q_dtype=q_dtype, page_order="shuffled",
-              seq_lens=[7, 1, 13, 0], rotary_mode=1, rope_theta=1e4)
+              seq_lens=[7, 1, 13, 0], rotary_mode=mode, rope_theta=1e4)
     qm = synth.multi_query(w, T, seed=7)
     qp = np.array([40, 0, 12, 3], np.int32)
     ko = np.array([33, 5, 0, 0], np.int32)
@@ -587,8 +590,9 @@ def test_multi_token_rope_matches_dense_causal_bruteforce(kv_dtype, q_dtype):
                     assert np.all(out[b, t, hq] == 0) and lse[b, t, hq] == -5e4
                     continue
                 K, V = contiguous_kv(w, b, hq // G)
-                Kr = np.stack([oracle.rope_rotate(K[r], ko[b] + r, 1.0, 1e4) for r in range(n)])
-                qr = oracle.rope_rotate(q64[b, t, hq], qp[b] + t, 1.0, 1e4)
+                Kr = np.stack([oracle.rope_rotate(K[r], ko[b] + r, 1.0, 1e4, interleaved=ilv)
+                               for r in range(n)])
+                qr = oracle.rope_rotate(q64[b, t, hq], qp[b] + t, 1.0, 1e4, interleaved=ilv)
                 o, l = dense_attention(qr, Kr, V[:n], w.sm_scale)
                 np.testing.assert_allclose(out[b, t, hq], o, rtol=0, atol=1e-12)
                 assert abs(lse[b, t, hq] - l) < 1e-12
