@@ -780,13 +780,18 @@ def _sink_case(w, sinks, num_kv_splits=0, T=1):
     sk = torch.from_numpy(np.asarray(sinks, np.float32)).cuda()
     desc = gu.desc_for(w, dev, num_kv_splits, sink_logits=sk)
     kw = {k: v for k, v in w.oracle_kwargs().items()}
+    rope = None
+    if w.rotary_mode:
+        rope = pk.make_rope(rotary_mode=w.rotary_mode, rope_scale=w.rope_scale,
+                            rope_theta=w.rope_theta, q_rope_position=dev["q_pos"],
+                            k_rope_pos_offset=dev["k_off"])
     if T == 1:
         o0, l0 = oracle.decode(**kw)
         out = torch.empty((w.B, w.H_qo, w.D), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((w.B, w.H_qo), dtype=torch.float32, device="cuda")
         ws = pk.alloc_workspace(desc)
         pk.attention(desc, dev["q"], dev["pages"], dev["indptr"], dev["values"],
-                     dev["length_info"], out, lse, w.sm_scale, workspace=ws)
+                     dev["length_info"], out, lse, w.sm_scale, rope=rope, workspace=ws)
     else:
         qm = synth.multi_query(w, T, seed=91)
         kw.pop("q")
@@ -796,7 +801,7 @@ def _sink_case(w, sinks, num_kv_splits=0, T=1):
         ws = pk.alloc_workspace_multi(desc, T)
         pk.attention_multi(desc, T, gu.to_device_storage(qm, w.q_dtype), dev["pages"],
                            dev["indptr"], dev["values"], dev["length_info"], out, lse, w.sm_scale,
-                           workspace=ws)
+                           rope=rope, workspace=ws)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.apply_sink(o0, l0, sinks)
     tol_o, tol_l = gu.tolerance(w)
@@ -823,6 +828,19 @@ def test_learned_sink(kv, G, ps, splits):
     sinks = np.random.default_rng(92).normal(0.0, 2.0, w.H_qo).astype(np.float32)
     sinks[0], sinks[-1] = 60.0, -60.0
     _sink_case(w, sinks, splits)
+
+
+@pytest.mark.parametrize("kv,D,rot,T,splits", [("bf16", 128, 1, 1, 3), ("fp8", 64, 2, 1, 12),
+                                               ("bf16", 64, 2, 2, 0), ("fp8", 128, 1, 2, 5)])
+def test_learned_sink_with_rope(kv, D, rot, T, splits):
+    """Sinks with RoPE (rotate-half or interleaved), one or two query tokens, split or not: the
+    sink is folded into the state of the rotated scores."""
+    w = synth.make_workload(name=f"sink_rope{rot}_{kv}_D{D}_T{T}_s{splits}", B=4, H_qo=8, H_kv=2,
+                            D=D, page_size=16, seq_lens=[1, 40, 1500, 700], seed=940 + D + rot,
+                            max_num_pages=256, q_dtype="bf16", kv_dtype=kv, rotary_mode=rot,
+                            rope_theta=500000.0)
+    sinks = np.random.default_rng(94).normal(0.0, 2.0, w.H_qo).astype(np.float32)
+    _sink_case(w, sinks, splits, T=T)
 
 
 def test_learned_sink_multi_token():
