@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--qo-len", type=int, default=2, help="query tokens per sequence (--op multi)")
     ap.add_argument("--multi-rope", action="store_true",
                     help="--op multi: rotate-half RoPE (base 5e5), token t at position L - T + t")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="instead of the decode, print the streaming-read ceiling sweep (every "
+                         "launch shape of pdecode_bench_stream_read over a 2 GiB buffer, and a "
+                         "plain read of the workload's KV bytes per step) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the decode, run a plain 512 MiB device-to-device copy "
                          "(the reference point for the HBM byte counters) and exit")
@@ -92,6 +96,66 @@ def recorded_traffic(workload):
     if not sha or not val or sha.group(1) != kernel_source_hash():
         return None
     return float(val.group(1))
+
+
+CEILING_BYTES = 2 << 30  # well above the 256 MB last-level cache
+
+
+def _time_launches(fn, reps, stream):
+    """Mean duration of fn() over `reps` launches, from one HIP event pair on `stream`."""
+    import torch
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(reps):
+        fn(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e-3 / reps
+
+
+def measure_ceiling(step_bytes=None, verbose=False):
+    """Streaming-read ceiling of this device (pdecode_bench_stream_read): the best rate over a
+    sweep of launch shapes (workgroups per CU, 16-byte loads per lane per round, nontemporal
+    hint), each reading a 2 GiB buffer once per launch, 10 timed launches after 3 warm-up ones.
+    With step_bytes, the best shape also reads exactly that many bytes per launch, cycling over 4
+    buffers so that no launch finds its bytes in the last-level cache: the time one launch of a
+    step's size needs at best, launch ramp and drain included."""
+    import torch
+
+    import paged_kv_decode_08_amd as pk
+    stream = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.zeros(CEILING_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(cus * 16 * 256, dtype=torch.int32, device="cuda")
+    sweep = []
+    for per_cu in (1, 2, 4, 8):
+        for u in (2, 4, 8, 16):
+            for nt in (0, 1):
+                fn = lambda i: pk.bench_stream_read(buf, u, nt, cus * per_cu, sink, stream=stream)
+                for i in range(3):
+                    fn(i)
+                dt = _time_launches(fn, 10, stream)
+                sweep.append({"workgroups_per_cu": per_cu, "loads_per_lane": u, "nontemporal": nt,
+                              "us": round(dt * 1e6, 2), "GBps": round(CEILING_BYTES / dt / 1e9, 1)})
+    best = max(sweep, key=lambda r: r["GBps"])
+    res = {"GBps": best["GBps"], "bytes_per_launch": CEILING_BYTES,
+           "shape": {k: best[k] for k in ("workgroups_per_cu", "loads_per_lane", "nontemporal")}}
+    if verbose:
+        res["sweep"] = sweep
+    del buf
+    if step_bytes:
+        n = (int(step_bytes) + 15) // 16 * 16
+        bufs = [torch.zeros(n, dtype=torch.uint8, device="cuda") for _ in range(4)]
+        fn = lambda i: pk.bench_stream_read(bufs[i % 4], best["loads_per_lane"],
+                                            best["nontemporal"], cus * best["workgroups_per_cu"],
+                                            sink, stream=stream)
+        for i in range(8):
+            fn(i)
+        dt = _time_launches(fn, 100, stream)
+        res["step_size_read"] = {"bytes": n, "us": round(dt * 1e6, 2),
+                                 "GBps": round(n / dt / 1e9, 1)}
+    return res
 
 
 def copy_calibration(steps):
@@ -329,6 +393,14 @@ def main():
     if args.copy_calibration:
         copy_calibration(max(args.steps, 1))
         return
+    if args.ceiling:
+        import synth
+        import torch
+        torch.cuda.set_device(0)
+        kvb = synth.CONFIGS[args.workload]().kv_bytes
+        print(json.dumps({"ceiling": measure_ceiling(step_bytes=kvb, verbose=True),
+                          "workload": args.workload}), flush=True)
+        return
     if args.op == "multi":
         multi_bench(args.workload, args.qo_len, max(args.steps, 1), args.warmup, args.sets,
                     rope=args.multi_rope)
@@ -406,6 +478,8 @@ def main():
     achieved = kv_bytes / avg_call_s / 1e9
     cp, nc = pk.plan(desc)
 
+    ceiling = measure_ceiling(step_bytes=kv_bytes)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(base, args.cpu_seconds)
@@ -440,6 +514,9 @@ def main():
                                 "splits sequences and the decode kernel does not merge them itself "
                                 "(instantiations of at most 4 q columns, or more than 8 chunks)"),
                      "avg_launch_us": round(avg_call_s * 1e6, 3),
+                     "ceiling_GBps": ceiling["GBps"],
+                     "frac_of_ceiling": round(achieved / ceiling["GBps"], 4),
+                     "ceiling": ceiling,
                      "single_call_event_us_p10": round(float(np.percentile(call_ms, 10)) * 1e3, 3),
                      "single_call_event_us_p90": round(float(np.percentile(call_ms, 90)) * 1e3, 3)},
         "cpu_baseline": cpu,

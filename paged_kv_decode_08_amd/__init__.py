@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.pdecode_merge_state_inplace.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, P, P, P, P, P]
         L.pdecode_append_kv.restype = _c_i32
         L.pdecode_append_kv.argtypes = [ctypes.POINTER(Desc), P, P, P, _c_i32, P, P]
+        L.pdecode_bench_stream_read.restype = _c_i32
+        L.pdecode_bench_stream_read.argtypes = [P, ctypes.c_size_t, _c_i32, _c_i32, _c_i32, P, P]
         L.pdecode_status_string.restype = ctypes.c_char_p
         L.pdecode_status_string.argtypes = [_c_i32]
         _lib = L
@@ -225,3 +227,17 @@ def append_kv(desc: Desc, new_k, new_v, slot_ids, pages, stream=None) -> None:
                                  int(slot_ids.numel()), _ptr(pages), _stream(stream))
     if st:
         raise PdecodeError(st, "pdecode_append_kv")
+
+
+def bench_stream_read(buf, loads_per_lane, nontemporal, workgroups, sink, stream=None) -> None:
+    """pdecode_bench_stream_read (include/pdecode_bench.h): one streaming read of the whole of
+    `buf` (a contiguous GPU tensor whose byte size is a multiple of 16); sink: uint32 or int32
+    [workgroups * 256] on the GPU."""
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() * sink.element_size() < 4 * 256 * int(workgroups):
+        raise ValueError("sink must hold workgroups * 256 uint32 values")
+    st = lib().pdecode_bench_stream_read(_ptr(buf), nbytes, int(loads_per_lane),
+                                         int(bool(nontemporal)), int(workgroups), _ptr(sink),
+                                         _stream(stream))
+    if st:
+        raise PdecodeError(st, "pdecode_bench_stream_read")

@@ -129,9 +129,9 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     const char* kb = pool + (size_t(page) * 2 * p.H_kv + h) * BLOCK_BYTES + lane * 16;
     const char* vb = kb + size_t(p.H_kv) * BLOCK_BYTES;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kr[i] = *reinterpret_cast<const uint4*>(kb + i * 1024);
+    for (int i = 0; i < NI; ++i) kr[i] = kv_load(reinterpret_cast<const uint4*>(kb + i * 1024));
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vr[i] = *reinterpret_cast<const uint4*>(vb + i * 1024);
+    for (int i = 0; i < NI; ++i) vr[i] = kv_load(reinterpret_cast<const uint4*>(vb + i * 1024));
   };
 
   uint4 kc[NI], vc[NI], kn[NI], vn[NI];

@@ -45,6 +45,7 @@ __device__ __forceinline__ float xmax(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 
+
 // Raw v_exp_f32: 2^x, results below the smallest normal flush to zero (softmax weights only).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -266,11 +267,11 @@ struct MfmaCore {
       for (int j = 0; j < KL; ++j) {
         // bf16: 16 B = k-step j; fp8: 16 codes = k-steps 2j and 2j + 1
         const int off = FP8 ? 64 * j + 16 * qg : (4 * j + qg) * 16;
-        bf.k[rb * KL + j] = *reinterpret_cast<const uint4*>(kb + (rb * 16 + n) * ROW + off);
+        bf.k[rb * KL + j] = kv_load(reinterpret_cast<const uint4*>(kb + (rb * 16 + n) * ROW + off));
       }
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      bf.v[i] = *reinterpret_cast<const VT*>(vb + (NI * rg + i) * ROW + cv * 8 * EB);
+      bf.v[i] = kv_load(reinterpret_cast<const VT*>(vb + (NI * rg + i) * ROW + cv * 8 * EB));
   }
 
   // Fused append: row rn of the item (loaded from the pool, whatever it held) is replaced by the

@@ -21,14 +21,19 @@ def L():
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "pdecode.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pdecode_[a-z_]+)\s*\(", text)))
+    """Every pdecode_* function declared in a header under include/."""
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, h)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(pdecode_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) >= 6
+    assert len(names) >= 10 and "pdecode_bench_stream_read" in names
     for n in names:
         assert hasattr(L, n), n
 
@@ -210,3 +215,16 @@ def test_fp8_e4m3_pool_checks(L):
     d.v_scale = ks
     assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.1, FAKE, FAKE,
              FAKE, 1 << 30, None) == 2
+
+
+def test_stream_read_argument_errors(L):
+    """The ceiling helper checks its arguments on the host before launching anything."""
+    sink = FAKE
+    assert L.pdecode_bench_stream_read(None, 1 << 20, 4, 0, 8, sink, None) == 1
+    assert L.pdecode_bench_stream_read(FAKE, 1 << 20, 4, 0, 8, None, None) == 1
+    assert L.pdecode_bench_stream_read(FAKE, 1 << 20, 4, 0, 0, sink, None) == 1
+    assert L.pdecode_bench_stream_read(FAKE, 8, 4, 0, 8, sink, None) == 1      # < 16 bytes
+    assert L.pdecode_bench_stream_read(FAKE, 1000, 4, 0, 8, sink, None) == 1   # not 16-multiple
+    assert L.pdecode_bench_stream_read(ctypes.c_void_p(0x1008), 1 << 20, 4, 0, 8, sink,
+                                       None) == 1                            # misaligned
+    assert L.pdecode_bench_stream_read(FAKE, 1 << 20, 3, 0, 8, sink, None) == 2

@@ -251,7 +251,7 @@ def test_window_zero_reduces_to_plain():
     assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
 
 
-# ---------------------------------------------------------------- RoPE (parity unpinned: invariants)
+# ---------------------------------------------------------------- RoPE invariants
 def test_rope_position_zero_is_identity():
     rng = np.random.default_rng(2)
     x = rng.standard_normal(128)
@@ -326,6 +326,138 @@ def test_rope_two_dims_is_plane_rotation():
     for p in (0.0, 1.0, 2.5, 100.0):
         y = oracle.rope_rotate(np.array([1.0, 0.0]), p, 1.0, 1e4)
         np.testing.assert_allclose(y, [np.cos(p), np.sin(p)], atol=1e-15)
+
+
+# ---------------------------------------------------------------- RoPE against common implementations
+# The pages import the rotation helper without showing it, so its convention (which dims pair up,
+# the frequency schedule, the sign of the rotation) is pinned here against the two layouts that the
+# attention_block_tkg page names, as the transformers library implements them: Llama's rotate-half
+# (contiguous halves) and GPT-J's rotate-every-two (interleaved pairs), with their own frequency
+# schedules. Positions reach 131 071, so a wrong schedule (theta^(-i/D), theta^(-2i/(D-2)), ...),
+# a swapped pairing or a flipped sign fails by O(1).
+RPOS = np.array([0, 1, 2, 17, 100, 4095, 4096, 65537, 131071], np.int64)
+
+
+def _llama_inv_freq64(D, theta, rope_type="default", factor=None):
+    """transformers' Llama inverse frequencies, evaluated with the library's own formula in
+    float64 (its arange dtype, torch.float, patched to float64 for the call)."""
+    import torch
+    from unittest import mock
+    from transformers import LlamaConfig
+    from transformers.modeling_rope_utils import ROPE_INIT_FUNCTIONS
+    from transformers.models.llama import modeling_llama as ml
+    params = {"rope_type": rope_type, "rope_theta": float(theta)}
+    if factor is not None:
+        params["factor"] = float(factor)
+    cfg = LlamaConfig(hidden_size=D, num_attention_heads=1, head_dim=D, rope_parameters=params)
+    fn = (ml.LlamaRotaryEmbedding.compute_default_rope_parameters if rope_type == "default"
+          else ROPE_INIT_FUNCTIONS[rope_type])
+    with mock.patch.object(torch, "float", torch.float64):
+        inv, _ = fn(cfg, None)
+    assert inv.dtype == torch.float64 and inv.shape == (D // 2,)
+    return inv
+
+
+def _oracle_rows(x, pos, scale, theta, interleaved=False):
+    return np.stack([oracle.rope_rotate(x[i], float(pos[i]), scale, theta, interleaved=interleaved)
+                     for i in range(len(pos))])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("theta", [1e4, 5e5])
+def test_rope_rotate_half_matches_transformers_llama(D, theta):
+    """Rotate-half against transformers' Llama rotate_half / apply_rotary_pos_emb with its
+    default inverse frequencies (float64), at positions up to 131 071."""
+    torch = pytest.importorskip("torch")
+    ml = pytest.importorskip("transformers.models.llama.modeling_llama")
+    rng = np.random.default_rng(int(D + theta) % 1000)
+    x = rng.standard_normal((len(RPOS), D))
+    inv = _llama_inv_freq64(D, theta)
+    freqs = torch.from_numpy(RPOS.astype(np.float64))[:, None] * inv[None, :]
+    emb = torch.cat((freqs, freqs), dim=-1)[None]  # [1, n, D], as the library's forward builds it
+    xt = torch.from_numpy(x)[None, None]  # [1, 1, n, D]
+    ref, _ = ml.apply_rotary_pos_emb(xt, xt, emb.cos(), emb.sin(), unsqueeze_dim=1)
+    got = _oracle_rows(x, RPOS, 1.0, theta)
+    np.testing.assert_allclose(got, ref[0, 0].numpy(), rtol=0, atol=1e-9)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_rope_rotate_half_matches_transformers_llama_fp32_pipeline(D):
+    """The same against the library's whole float32 path (LlamaRotaryEmbedding.forward, then
+    apply_rotary_pos_emb) at positions where float32 angles stay within 2e-3 rad."""
+    torch = pytest.importorskip("torch")
+    ml = pytest.importorskip("transformers.models.llama.modeling_llama")
+    from transformers import LlamaConfig
+    pos = np.array([0, 1, 3, 50, 511, 2047], np.int64)
+    cfg = LlamaConfig(hidden_size=D, num_attention_heads=1, head_dim=D,
+                      rope_parameters={"rope_type": "default", "rope_theta": 500000.0})
+    rot = ml.LlamaRotaryEmbedding(cfg)
+    x = np.random.default_rng(5).standard_normal((len(pos), D)).astype(np.float32)
+    xt = torch.from_numpy(x)[None, None]
+    cos, sin = rot(xt, torch.from_numpy(pos)[None])
+    ref, _ = ml.apply_rotary_pos_emb(xt, xt, cos, sin, unsqueeze_dim=1)
+    got = _oracle_rows(x.astype(np.float64), pos, 1.0, 500000.0)
+    np.testing.assert_allclose(got, ref[0, 0].double().numpy(), rtol=0, atol=5e-3)
+
+
+def test_rope_scale_matches_transformers_linear_scaling():
+    """rope_scale multiplies the position: transformers' 'linear' RoPE with factor 4 divides every
+    frequency by 4, which is rope_scale = 0.25."""
+    torch = pytest.importorskip("torch")
+    ml = pytest.importorskip("transformers.models.llama.modeling_llama")
+    D, theta = 128, 1e4
+    inv = _llama_inv_freq64(D, theta, rope_type="linear", factor=4.0)
+    x = np.random.default_rng(9).standard_normal((len(RPOS), D))
+    freqs = torch.from_numpy(RPOS.astype(np.float64))[:, None] * inv[None, :]
+    emb = torch.cat((freqs, freqs), dim=-1)[None]
+    xt = torch.from_numpy(x)[None, None]
+    ref, _ = ml.apply_rotary_pos_emb(xt, xt, emb.cos(), emb.sin(), unsqueeze_dim=1)
+    got = _oracle_rows(x, RPOS, 0.25, theta)
+    np.testing.assert_allclose(got, ref[0, 0].numpy(), rtol=0, atol=1e-9)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("theta", [1e4, 5e5])
+def test_rope_interleaved_matches_transformers_gptj(D, theta):
+    """Interleaved pairs against transformers' GPT-J rotate_every_two / apply_rotary_pos_emb
+    (sin and cos repeated per pair), float64, with the inverse frequencies of the Llama schedule,
+    which GPT-J's own table uses (pinned at base 1e4 by the float32 test below)."""
+    torch = pytest.importorskip("torch")
+    mg = pytest.importorskip("transformers.models.gptj.modeling_gptj")
+    inv = _llama_inv_freq64(D, theta)
+    x = np.random.default_rng(int(theta) % 997 + D).standard_normal((len(RPOS), D))
+    ang = torch.from_numpy(RPOS.astype(np.float64))[:, None] * inv[None, :]  # [n, D/2]
+    xt = torch.from_numpy(x)[None, :, None, :]  # [batch, seq, heads, D]
+    ref = mg.apply_rotary_pos_emb(xt, ang.sin()[None], ang.cos()[None])
+    got = _oracle_rows(x, RPOS, 1.0, theta, interleaved=True)
+    np.testing.assert_allclose(got, ref[0, :, 0].numpy(), rtol=0, atol=1e-9)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_rope_interleaved_matches_gptj_sinusoid_table(D):
+    """Interleaved pairs against GPT-J's whole float32 path: its sinusoid table
+    (create_sinusoidal_positions, base 1e4), split into sin and cos, then apply_rotary_pos_emb."""
+    torch = pytest.importorskip("torch")
+    mg = pytest.importorskip("transformers.models.gptj.modeling_gptj")
+    pos = np.array([0, 1, 3, 50, 511, 2047], np.int64)
+    table = mg.create_sinusoidal_positions(2048, D)  # [pos, D] = (sin | cos)
+    sincos = table[torch.from_numpy(pos)][None]
+    sin, cos = torch.split(sincos, D // 2, dim=-1)
+    x = np.random.default_rng(6).standard_normal((len(pos), D)).astype(np.float32)
+    ref = mg.apply_rotary_pos_emb(torch.from_numpy(x)[None, :, None, :], sin, cos)
+    got = _oracle_rows(x.astype(np.float64), pos, 1.0, 1e4, interleaved=True)
+    np.testing.assert_allclose(got, ref[0, :, 0].double().numpy(), rtol=0, atol=5e-3)
+
+
+def test_rope_wrong_schedules_fail_the_pin():
+    """The pins above separate the schedule from plausible mistakes: at the positions they use,
+    theta^(-i/D) and theta^(-2i/(D-2)) move some element by far more than their tolerances."""
+    D, theta = 128, 5e5
+    i = np.arange(D // 2)
+    right = theta ** (-2.0 * i / D)
+    for wrong in (theta ** (-1.0 * i / D), theta ** (-2.0 * i / (D - 2))):
+        dphi = np.abs(np.outer(RPOS, wrong - right))
+        assert np.abs(np.sin(dphi / 2)).max() > 0.1
 
 
 # ---------------------------------------------------------------- fp8 e4m3fn and bf16 codecs
