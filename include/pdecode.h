@@ -149,6 +149,25 @@ pdecode_status pdecode_attention(const pdecode_desc *d, const void *q, const voi
                                  float sm_scale, void *out, float *lse, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): pdecode_attention without a workspace. The split and job-queue counters
+ * and the split partial states live in a device array inside the library, one per GPU, held from
+ * the first call on that GPU until the process ends: a counter region of 64 KiB (room for
+ * batch * num_kv_heads <= 16382) and a partial-state region of 32 MiB. The arguments, results and
+ * supported set are those of pdecode_attention; the array is used on the device current at the
+ * call, which must be the device of `stream`, q and the other buffers. Nothing is allocated (no
+ * hipMalloc, no allocating library call): the first call on a device takes the array's device
+ * address and clears its counters once (a kernel on `stream`); every call leaves the counters at
+ * zero. All calls on one GPU share the array and it keeps the last call's partial states, so calls
+ * that may run at the same time on one GPU (other streams, other threads) race: serialise them.
+ * Errors: those of pdecode_attention; PDECODE_ERR_WORKSPACE_TOO_SMALL (nothing launched) when the
+ * plan needs more counters or partial state than the array holds (use pdecode_attention with a
+ * workspace then); PDECODE_ERR_HIP when the array's address cannot be taken. */
+pdecode_status pdecode_attention_noalloc(const pdecode_desc *d, const void *q, const void *pages,
+                                         const int32_t *page_indptr, const int32_t *page_values,
+                                         const int32_t *length_info, const pdecode_rope *rope,
+                                         float sm_scale, void *out, float *lse, void *stream);
+
 /* Decode with qo_len query tokens per sequence, causal over the new tokens (speculative
  * verification, chunked decode): the sequence's last qo_len positions hold the new tokens, already
  * in the pool, and token t (0-based) attends the positions 0 .. total_b - qo_len + t. Each token's

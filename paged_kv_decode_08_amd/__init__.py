@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.pdecode_merge_state_inplace.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, P, P, P, P, P]
         L.pdecode_append_kv.restype = _c_i32
         L.pdecode_append_kv.argtypes = [ctypes.POINTER(Desc), P, P, P, _c_i32, P, P]
+        L.pdecode_attention_noalloc.restype = _c_i32
+        L.pdecode_attention_noalloc.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P,
+                                                ctypes.POINTER(Rope), ctypes.c_float, P, P, P]
         L.pdecode_bench_stream_read.restype = _c_i32
         L.pdecode_bench_stream_read.argtypes = [P, ctypes.c_size_t, _c_i32, _c_i32, _c_i32, P, P]
         L.pdecode_status_string.restype = ctypes.c_char_p
@@ -164,6 +167,18 @@ def attention(desc: Desc, q, pages, page_indptr, page_values, length_info, out, 
                                  ws_bytes, _stream(stream))
     if st:
         raise PdecodeError(st, "pdecode_attention")
+
+
+def attention_noalloc(desc: Desc, q, pages, page_indptr, page_values, length_info, out, lse,
+                      sm_scale, rope: Rope | None = None, stream=None) -> None:
+    """pdecode_attention_noalloc: pdecode_attention with the library's own per-GPU scratch (no
+    workspace, nothing allocated); calls that may overlap on one GPU race."""
+    st = lib().pdecode_attention_noalloc(ctypes.byref(desc), _ptr(q), _ptr(pages),
+                                         _ptr(page_indptr), _ptr(page_values), _ptr(length_info),
+                                         None if rope is None else ctypes.byref(rope),
+                                         float(sm_scale), _ptr(out), _ptr(lse), _stream(stream))
+    if st:
+        raise PdecodeError(st, "pdecode_attention_noalloc")
 
 
 def alloc_workspace_multi(desc: Desc, qo_len: int, device="cuda") -> torch.Tensor | None:

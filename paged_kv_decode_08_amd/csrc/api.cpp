@@ -7,6 +7,7 @@
 #include <climits>
 #include <cmath>
 
+#include "api_internal.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -146,12 +147,15 @@ namespace {
 // pdecode_attention, and with new_k / new_v set the fused append of pdecode_append_attention
 // (the persistent matrix-core schedule only).
 // qo_len > 1: several query tokens per sequence (pdecode_attention_multi; no window).
+// fixed: the caller's scratch split into a counter region and a partial-state region at fixed
+// places (pdecode_attention_noalloc) instead of one workspace laid out by the plan.
 pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const void* new_v,
                               const void* q, const void* pages, const int32_t* page_indptr,
                               const int32_t* page_values, const int32_t* length_info,
                               const pdecode_rope* rope, float sm_scale, void* out, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream,
-                              int qo_len = 1) {
+                              int qo_len = 1, const pdk::FixedScratch* fixed = nullptr,
+                              bool check_only = false) {
   const bool fused = new_k != nullptr;
   pdecode_status st = check_desc(d);
   if (st != PDECODE_OK) return st;
@@ -175,10 +179,15 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
     return PDECODE_ERR_UNSUPPORTED;
   const int64_t grid = int64_t(pl.num_chunks) * d->batch * d->num_kv_heads;
   if (grid > INT_MAX) return PDECODE_ERR_UNSUPPORTED;
-  if (pl.workspace_bytes() > 0) {
+  if (fixed) {
+    if (pl.counter_bytes > fixed->counter_bytes ||
+        pl.part_o_bytes + pl.part_lse_bytes > fixed->partial_bytes)
+      return PDECODE_ERR_WORKSPACE_TOO_SMALL;
+  } else if (pl.workspace_bytes() > 0) {
     if (!workspace || workspace_bytes < pl.workspace_bytes()) return PDECODE_ERR_WORKSPACE_TOO_SMALL;
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PDECODE_ERR_INVALID_ARG;
   }
+  if (check_only) return PDECODE_OK;
 
   pdk::DecodeParams p{};
   p.q = q;
@@ -197,10 +206,18 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   p.out = out;
   p.lse = lse;
   const bool ws = pl.workspace_bytes() > 0;
-  char* wsb = static_cast<char*>(workspace);
-  p.counters = ws ? reinterpret_cast<int*>(wsb) : nullptr;
-  p.part_o = ws ? reinterpret_cast<float*>(wsb + pl.counter_bytes) : nullptr;
-  p.part_lse = ws ? reinterpret_cast<float*>(wsb + pl.counter_bytes + pl.part_o_bytes) : nullptr;
+  if (fixed) {
+    p.counters = ws ? fixed->counters : nullptr;
+    p.part_o = ws ? fixed->partials : nullptr;
+    p.part_lse = ws ? reinterpret_cast<float*>(reinterpret_cast<char*>(fixed->partials) +
+                                               pl.part_o_bytes)
+                    : nullptr;
+  } else {
+    char* wsb = static_cast<char*>(workspace);
+    p.counters = ws ? reinterpret_cast<int*>(wsb) : nullptr;
+    p.part_o = ws ? reinterpret_cast<float*>(wsb + pl.counter_bytes) : nullptr;
+    p.part_lse = ws ? reinterpret_cast<float*>(wsb + pl.counter_bytes + pl.part_o_bytes) : nullptr;
+  }
   p.queue = ws ? p.counters + size_t(d->batch) * d->num_kv_heads : nullptr;
   p.B = d->batch;
   p.H_qo = d->num_qo_heads;
@@ -235,6 +252,19 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
 }
 
 }  // namespace
+
+namespace pdk {
+
+pdecode_status attention_fixed_scratch(const pdecode_desc* d, const void* q, const void* pages,
+                                       const int32_t* page_indptr, const int32_t* page_values,
+                                       const int32_t* length_info, const pdecode_rope* rope,
+                                       float sm_scale, void* out, float* lse,
+                                       const FixedScratch* fixed, void* stream, bool check_only) {
+  return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
+                        rope, sm_scale, out, lse, nullptr, 0, stream, 1, fixed, check_only);
+}
+
+}  // namespace pdk
 
 extern "C" {
 

@@ -228,3 +228,25 @@ def test_stream_read_argument_errors(L):
     assert L.pdecode_bench_stream_read(ctypes.c_void_p(0x1008), 1 << 20, 4, 0, 8, sink,
                                        None) == 1                            # misaligned
     assert L.pdecode_bench_stream_read(FAKE, 1 << 20, 3, 0, 8, sink, None) == 2
+
+
+def noalloc_status(L, d, ptrs=True):
+    P = FAKE if ptrs else None
+    return L.pdecode_attention_noalloc(ctypes.byref(d) if d is not None else None, P, P, P, P, P,
+                                       None, 0.1, P, P, None)
+
+
+def test_noalloc_refuses_plans_beyond_its_scratch(L):
+    """pdecode_attention_noalloc checks its description and plan on the host first: a plan whose
+    partial states exceed the 32 MiB region, or whose counters exceed the 64 KiB one, is refused
+    with WORKSPACE_TOO_SMALL before the device is touched; bad arguments as pdecode_attention."""
+    big = desc(batch=1024, num_qo_heads=64, num_kv_heads=8, max_num_pages=1 << 20,
+               max_kv_len=65536)
+    assert noalloc_status(L, big) == 3
+    many = desc(batch=2100, num_qo_heads=8, num_kv_heads=8, max_num_pages=1 << 20,
+                max_kv_len=64, num_kv_splits=2)  # 16802 counters, 4.3 MB of partial states
+    assert noalloc_status(L, many) == 3
+    assert noalloc_status(L, None) == 1
+    assert noalloc_status(L, desc(num_qo_heads=30)) == 1
+    assert noalloc_status(L, desc(), ptrs=False) == 1
+    assert noalloc_status(L, desc(head_dim=96)) == 2
