@@ -20,8 +20,10 @@
  *
  * Conventions for every call:
  *   - Tensor pointers are DEVICE pointers owned by the caller; host structs are read during the
- *     call only. The library allocates nothing, never synchronises and keeps no state between
- *     calls (it is reentrant). Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     call only. The library allocates nothing, never synchronises and keeps no per-call state
+ *     (it is reentrant). Its only state is a thread-safe cache of how many workgroups of each
+ *     kernel fit on a device (keyed by kernel, device and LDS size), and, for
+ *     pdecode_attention_noalloc only, each device's scratch array and its address. Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and runs asynchronously.
  *   - Arguments are checked on the host before anything is launched; on error nothing is
  *     launched and the call returns a status other than PDECODE_OK. Device-resident data

@@ -8,8 +8,9 @@ Every function takes and returns host NumPy arrays. Floating-point results are f
 dtype codes: 0 = fp32, 1 = bf16 (raw uint16 bits), 2 = fp8 e4m3fn (raw uint8 bits).
 
 What each function follows is cited in ``oracle.cpp``. Parity against the pages is pinned by the
-``-m "not gpu"`` tests, except the RoPE convention, whose helper body the pages do not show:
-parity unpinned (only invariants pin it).
+``-m "not gpu"`` tests. The RoPE convention, whose helper body the pages do not show, is pinned
+to transformers' Llama rotate_half and GPT-J rotate_every_two instead: parity unpinned against
+the pages themselves.
 """
 import ctypes
 import os

@@ -38,8 +38,9 @@
 //     frequency theta^(-2i/D), angle = position * rope_scale * frequency; applied iff
 //     rotary_mode == 1; rotary_mode == 2 takes that interleaved layout instead, pairing elements
 //     2i and 2i + 1 with the same frequency i; the K position is k_rope_pos_offset[b] + r
-//     (compacted row index r, as the page passes row_idx). PARITY UNPINNED against the pages:
-//     only invariants pin it.
+//     (compacted row index r, as the page passes row_idx). Pinned to transformers' Llama
+//     rotate_half (default inverse frequencies) and GPT-J's rotate_every_two by the CPU tests;
+//     PARITY UNPINNED against the pages themselves, which do not show the helper.
 //   * fp8 scales multiply the decoded payload, per KV head.
 #include <algorithm>
 #include <atomic>
