@@ -40,8 +40,7 @@ void decode_mfma_kernel(DecodeParams p) {
   constexpr int BLOCK = PS * C::ROW;  // bytes of one (page, K|V, head) block
   using Buf = typename C::Buf;
   constexpr int NT = 64 * kWaves;
-  __shared__ __attribute__((aligned(16))) float s_pt[kWaves][16][C::PT_STRIDE];
-  __shared__ float s_alpha[kWaves][16];
+  __shared__ __attribute__((aligned(16))) unsigned char s_tile[kWaves][C::TILE_BYTES];  // V tiles
   __shared__ float s_m[kWaves][GP];
   __shared__ float s_d[kWaves][GP];
   __shared__ __attribute__((aligned(16))) float s_o[kWaves][GP][D];
@@ -139,7 +138,7 @@ void decode_mfma_kernel(DecodeParams p) {
         // RoPE position of the item's row 0 (attended rows numbered from the sequence's first)
         const int pos0 = kro + j * PS + r0 +
                          (slot_of((k + r) / SUB) < sg.n0 ? 0 : sg.sink - sg.win_off);
-        if (lo < hi) core.process(buf[r], lo, hi, scale, s_pt[w], s_alpha[w], pos0, s_freq);
+        if (lo < hi) core.process(buf[r], lo, hi, scale, s_tile[w], pos0, s_freq);
       }
     }
   }

@@ -272,8 +272,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   constexpr int QWORDS = GP * D / 2;
   constexpr int QW = (QWORDS + NT - 1) / NT;
   extern __shared__ __attribute__((aligned(16))) int s_dyn[];
-  __shared__ __attribute__((aligned(16))) float s_pt[kPWaves][16][C::PT_STRIDE];
-  __shared__ float s_alpha[kPWaves][16];
+  __shared__ __attribute__((aligned(16))) unsigned char s_tile[kPWaves][C::TILE_BYTES];  // V tiles
   __shared__ float s_m[kPWaves][GP];
   __shared__ float s_d[kPWaves][GP];
   __shared__ __attribute__((aligned(16))) float s_o[kPWaves][GP][D];
@@ -582,10 +581,9 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         if constexpr (MT) {
           // this lane's column (token n / G) sees positions <= total - T + n / G
           const int cap = J.g.total - T + tok - (j * PS + r0);
-          if (lo < hi) core.template process<true>(cur, lo, hi, scale, s_pt[w], s_alpha[w], pos0,
-                                                   s_freq, cap);
+          if (lo < hi) core.template process<true>(cur, lo, hi, scale, s_tile[w], pos0, s_freq, cap);
         } else {
-          if (lo < hi) core.process(cur, lo, hi, scale, s_pt[w], s_alpha[w], pos0, s_freq);
+          if (lo < hi) core.process(cur, lo, hi, scale, s_tile[w], pos0, s_freq);
         }
       }
     };

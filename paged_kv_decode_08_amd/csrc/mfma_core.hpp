@@ -11,11 +11,13 @@
 //    j; fp8: 16 codes [64 j' + 16 (l/16), +16) converted exactly to bf16 for k-steps 2j', 2j'+1.
 //    The accumulator gives lane l the scores of rows 4 (l/16) + {0..3} for head l % 16.
 //  * softmax: the tile max per head needs two cross-row exchanges; one exp2 per score.
-//  * P.V: P goes through LDS (transposed, [head][row]) to the V layout, where lane l holds 8
-//    consecutive dims of NI consecutive rows (each V load instruction reads whole rows);
-//    O[g][dims] accumulates in fp32 FMAs (bf16 V, up to 4 heads) or in v_dot2_f32_bf16 over row
-//    pairs with P rounded to bf16 (fp8 V: two rows' bytes interleaved with v_perm, converted
-//    exactly to bf16; bf16 V with 8 heads: two rows' elements regrouped with v_perm).
+//  * P.V on the matrix cores too: O^T[dims][heads] += V^T P, one v_mfma_f32_16x16x16_bf16 per 16
+//    dims. P is the B operand as it stands in the score accumulator (lane l: rows 4 (l/16) + {0..3}
+//    of head l % 16), rounded to bf16. V (lane l loads 8 consecutive dims of NI consecutive rows,
+//    so each load instruction reads whole rows; fp8 codes are converted exactly to bf16) goes to
+//    a per-wave LDS tile and is read back transposed with ds_read_b64_tr_b16 as the A operand.
+//    The accumulators hold the 16 columns' outputs whatever the number of heads, and the rescale
+//    of a column's output by its softmax correction is lane-local.
 //  * fp8: k_scale multiplies the scores, v_scale the output.
 //  * RoPE (ROPE = true): rotate-half pairs dims i and i + D/2, and the MFMA layout puts both in
 //    the same lane (k-steps j and j + KS/2; fp8 codes are converted exactly to fp32 first), except
@@ -40,6 +42,22 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(const uint4& a, const uint
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+// v_mfma_f32_16x16x16_bf16: A lane l = A[m = l % 16][k = 4 (l / 16) .. + 4], B lane l =
+// B[k = 4 (l / 16) .. + 4][n = l % 16], accumulator lane l = D[m = 4 (l / 16) + v][n = l % 16].
+__device__ __forceinline__ f32x4_t mfma_16x16x16_bf16(const i16x4_t& a, const uint2& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element i % 4 of the 8-byte
+// chunks that lanes 4e + i / 4 address, for e = 0..3 (measured on gfx950).
+__device__ __forceinline__ i16x4_t lds_read_tr16(const unsigned char* p) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+
 
 __device__ __forceinline__ float xmax(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
@@ -72,11 +90,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};  // round to nearest even
   return __builtin_bit_cast(uint32_t, v);
 }
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
 
 // Splits x into a bf16 high part and a bf16 remainder (x - hi), both rounded to nearest even.
 __device__ __forceinline__ void split_bf16(float x, float y, uint32_t& hi, uint32_t& lo) {
@@ -100,17 +113,19 @@ struct MfmaCore {
   static constexpr int RPI = 64 / VPR;          // V rows per load instruction
   static constexpr int NI = PS / RPI;           // V loads per lane per page (consecutive rows)
   static constexpr int NLOADS = NK + NI;        // vector-memory instructions per page
-  static constexpr int PT_STRIDE = PS + 4;      // P^T row stride in floats (bank-conflict-free)
+  // P.V on the matrix cores: V goes through a per-wave LDS tile [16 rows][VSTRIDE bytes] of
+  // bf16 (rows padded by 32 bytes against bank conflicts of the transposed reads) and comes back
+  // transposed as the A operand; P stays in registers.
+  static constexpr int VSTRIDE = D * 2 + 32;
+  static constexpr int TILE_BYTES = 16 * VSTRIDE;  // this wave's V tile
+  static constexpr int NB = D / 16;             // 16-dim blocks of the output
   using VT = typename VVec<KVT>::type;
   static_assert(GP <= 16 && (NI == 2 || NI % 4 == 0), "unsupported shape");
-  static_assert(!ROPE || RB == 1, "RoPE on the matrix cores: 16-row items");
+  static_assert(RB == 1, "16-row items");
   static constexpr int KH = KS / 2;             // k-steps of the lower half of the head dim
   // Rotate-half RoPE finds dims i and i + D/2 in one lane for bf16, and for fp8 at D = 128; fp8 at
   // D = 64 holds dims [16 qg, +16) per lane, so each dim's partner sits in lane l ^ 32.
   static constexpr bool XLANE = ROPE && !ILV && FP8 && D == 64;
-  // P.V with P rounded to bf16 and row pairs through v_dot2_f32_bf16: fp8 V always, bf16 V with 8
-  // heads (fp32 P for 8 heads would take the kernel past 256 VGPRs, one wave per SIMD)
-  static constexpr bool PBF16 = FP8 || GP >= 8;
 
   struct Buf {
     uint4 k[NK];
@@ -122,7 +137,7 @@ struct MfmaCore {
   uint4 qlo[ROPE ? KS : 1];  // with RoPE: the bf16 remainder of the rotated q
   float m;               // running max of head n (MFMA layout, identical across qg)
   float dl;              // partial denominator over this lane's rows
-  float O[GP][8];
+  f32x4_t OT[NB];         // O^T of head (column) n: dims 16 b + 4 qg + v of block b
 
   __device__ __forceinline__ void init_lane(int lane) {
     l = lane;
@@ -136,9 +151,7 @@ struct MfmaCore {
     m = -INFINITY;
     dl = 0.f;
 #pragma unroll
-    for (int g = 0; g < GP; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) O[g][e] = 0.f;
+    for (int b = 0; b < NB; ++b) OT[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   // Element offset, within one q row, of the 8 dims that k-step j of k-group qg holds:
@@ -291,13 +304,13 @@ struct MfmaCore {
   }
 
   // Online-softmax update with one page whose attended rows are [lo, hi) (lo < hi).
-  // s_pt: this wave's [16][PT_STRIDE] P^T tile; s_alpha: this wave's 16 rescale factors.
+  // tile: this wave's LDS V tile (TILE_BYTES, 16-byte aligned).
   // RoPE: row r of the item is at position pos0 + r; s_freq as in rope_q.
   // COLCAP (several query tokens): this lane's column also masks the rows above `cap`, so a
   // column may have no row left in the item, or in the whole job so far (m = -inf).
   template <bool COLCAP = false>
   __device__ __forceinline__ void process(const Buf& bf, int lo, int hi, float scale,
-                                          float (*s_pt)[PT_STRIDE], float* s_alpha, int pos0 = 0,
+                                          unsigned char* tile, int pos0 = 0,
                                           const float2* s_freq = nullptr, int cap = 15) {
     // scores S^T[row][head] on the matrix cores
     f32x4_t acc[RB];
@@ -425,119 +438,35 @@ struct MfmaCore {
         psum += sv[rb][v];
       }
     dl = dl * alpha + psum;
+    // O^T[dims][head n] += V^T . P on the matrix cores. P (this lane: rows 4 qg .. + 4 of head n,
+    // where the QK accumulator left them) is the B operand as bf16; V goes to this wave's LDS tile
+    // (rows outside [lo, hi) as zeros: 0 x NaN would poison O) and comes back transposed, 16 dims
+    // per read, as the A operand.
+    const uint2 pb = make_uint2(pack_bf16x2(sv[0][0], sv[0][1]), pack_bf16x2(sv[0][2], sv[0][3]));
+    if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      *reinterpret_cast<float4*>(&s_pt[n][rb * 16 + 4 * qg]) =
-          make_float4(sv[rb][0], sv[rb][1], sv[rb][2], sv[rb][3]);
-    if (qg == 0) s_alpha[n] = alpha;
-    const bool rescale = __ballot(alpha != 1.0f) != 0;
-    wave_lds_fence();
-    if (rescale) {
-#pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        const float a = s_alpha[g];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) O[g][e] *= a;
-      }
+      for (int b = 0; b < NB; ++b) OT[b] *= alpha;
     }
-    // this lane's rows of P, per head: fp32 (bf16 V) or bf16 row pairs (fp8 V)
-    float pv[PBF16 ? 1 : GP][NI];
-    uint32_t pp[PBF16 ? GP : 1][NI / 2];
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      const float* src = &s_pt[g][NI * rg];
-      float t[NI];
-      if constexpr (NI == 2) {
-        const float2 v2 = *reinterpret_cast<const float2*>(src);
-        t[0] = v2.x;
-        t[1] = v2.y;
-      } else {
-#pragma unroll
-        for (int i4 = 0; i4 < NI; i4 += 4) {
-          const float4 v4 = *reinterpret_cast<const float4*>(src + i4);
-          t[i4] = v4.x;
-          t[i4 + 1] = v4.y;
-          t[i4 + 2] = v4.z;
-          t[i4 + 3] = v4.w;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        if constexpr (PBF16) {
-          if (i % 2) pp[g][i / 2] = pack_bf16x2(t[i - 1], t[i]);
-        } else {
-          pv[g][i] = t[i];
-        }
-      }
-    }
-    wave_lds_fence();
     const bool partial = lo > 0 || hi < PS;
-    if constexpr (FP8) {
-      VT vv[NI];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        vv[i] = bf.v[i];
-        if (partial && !(NI * rg + i >= lo && NI * rg + i < hi)) vv[i] = make_uint2(0, 0);
+    for (int i = 0; i < NI; ++i) {
+      const int row = NI * rg + i;
+      uint4 x;
+      if constexpr (FP8) {
+        const uint2 c8 = bf.v[i];
+        x = make_uint4(fp8x2_to_bf16x2<false>(c8.x), fp8x2_to_bf16x2<true>(c8.x),
+                       fp8x2_to_bf16x2<false>(c8.y), fp8x2_to_bf16x2<true>(c8.y));
+      } else {
+        x = bf.v[i];
       }
-#pragma unroll
-      for (int ip = 0; ip < NI / 2; ++ip) {
-        // rows (2 ip, 2 ip + 1): P as a bf16 pair per head, V as a bf16 pair per dim
-        const uint32_t a[2] = {vv[2 * ip].x, vv[2 * ip].y};
-        const uint32_t bb[2] = {vv[2 * ip + 1].x, vv[2 * ip + 1].y};
-#pragma unroll
-        for (int wi = 0; wi < 2; ++wi) {
-          const uint32_t lo4 = __builtin_amdgcn_perm(bb[wi], a[wi], 0x05010400u);  // a0 b0 a1 b1
-          const uint32_t hi4 = __builtin_amdgcn_perm(bb[wi], a[wi], 0x07030602u);  // a2 b2 a3 b3
-          const uint32_t vp[4] = {fp8x2_to_bf16x2<false>(lo4), fp8x2_to_bf16x2<true>(lo4),
-                                  fp8x2_to_bf16x2<false>(hi4), fp8x2_to_bf16x2<true>(hi4)};
-#pragma unroll
-          for (int g = 0; g < GP; ++g)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              O[g][4 * wi + e] = dot2_bf16(pp[g][ip], vp[e], O[g][4 * wi + e]);
-        }
-      }
-    } else if constexpr (PBF16) {
-      VT vv[NI];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        vv[i] = bf.v[i];
-        if (partial && !(NI * rg + i >= lo && NI * rg + i < hi)) vv[i] = make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int ip = 0; ip < NI / 2; ++ip) {
-        // rows (2 ip, 2 ip + 1): P as a bf16 pair per head; V dims (2w, 2w + 1) of both rows
-        // regrouped into one bf16 pair per dim
-        const uint32_t a[4] = {vv[2 * ip].x, vv[2 * ip].y, vv[2 * ip].z, vv[2 * ip].w};
-        const uint32_t bb[4] = {vv[2 * ip + 1].x, vv[2 * ip + 1].y, vv[2 * ip + 1].z,
-                                vv[2 * ip + 1].w};
-#pragma unroll
-        for (int wi = 0; wi < 4; ++wi) {
-          const uint32_t d0 = __builtin_amdgcn_perm(bb[wi], a[wi], 0x05040100u);  // a.lo b.lo
-          const uint32_t d1 = __builtin_amdgcn_perm(bb[wi], a[wi], 0x07060302u);  // a.hi b.hi
-#pragma unroll
-          for (int g = 0; g < GP; ++g) {
-            O[g][2 * wi] = dot2_bf16(pp[g][ip], d0, O[g][2 * wi]);
-            O[g][2 * wi + 1] = dot2_bf16(pp[g][ip], d1, O[g][2 * wi + 1]);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float vf[8];
-        Kv<kBF16>::unpack(bf.v[i], vf);
-        if (partial) {
-          const bool ok = NI * rg + i >= lo && NI * rg + i < hi;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vf[e] = ok ? vf[e] : 0.f;
-        }
-#pragma unroll
-        for (int g = 0; g < GP; ++g)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) O[g][e] = fmaf(pv[g][i], vf[e], O[g][e]);
-      }
+      if (partial && !(row >= lo && row < hi)) x = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(tile + row * VSTRIDE + cv * 16) = x;
     }
+    wave_lds_fence();
+    const unsigned char* src = tile + (4 * qg + n / 4) * VSTRIDE + 8 * (n % 4);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) OT[b] = mfma_16x16x16_bf16(lds_read_tr16(src + 32 * b), pb, OT[b]);
+    wave_lds_fence();  // the tile is free for the next item
   }
 
   // Reduces this wave's state over its lanes (d over the row quads, O over the row groups) and
@@ -546,23 +475,15 @@ struct MfmaCore {
     float d = dl;
     d += __shfl_xor(d, 16, 64);
     d += __shfl_xor(d, 32, 64);
-#pragma unroll
-    for (int msk = VPR; msk < 64; msk <<= 1)
-#pragma unroll
-      for (int g = 0; g < GP; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) O[g][e] += __shfl_xor(O[g][e], msk, 64);
     if (qg == 0 && n < GP) {
       s_m[n] = m;
       s_d[n] = d;
     }
-    if (rg == 0) {
+    if (n < GP) {
 #pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        *reinterpret_cast<float4*>(&s_o[g][cv * 8]) = make_float4(O[g][0], O[g][1], O[g][2], O[g][3]);
-        *reinterpret_cast<float4*>(&s_o[g][cv * 8 + 4]) =
-            make_float4(O[g][4], O[g][5], O[g][6], O[g][7]);
-      }
+      for (int b = 0; b < NB; ++b)
+        *reinterpret_cast<float4*>(&s_o[n][16 * b + 4 * qg]) =
+            make_float4(OT[b][0], OT[b][1], OT[b][2], OT[b][3]);
     }
   }
 };
