@@ -182,7 +182,7 @@ pdecode_status pdecode_attention_noalloc(const pdecode_desc *d, const void *q, c
  * rotary_mode), token t's query sits at position q_rope_position[b] + t; the keys are placed as in
  * pdecode_attention.
  * qo_len == 1 is pdecode_attention. Supported for qo_len > 1: no sliding window,
- * (num_qo_heads / num_kv_heads) * qo_len <= 8, and the persistent
+ * (num_qo_heads / num_kv_heads) * qo_len <= 16, and the persistent
  * matrix-core schedule (BF16 or FP8 pool, batch <= 1024); otherwise UNSUPPORTED. Errors: as pdecode_attention, and INVALID_ARG for qo_len < 1. */
 size_t pdecode_workspace_bytes_multi(const pdecode_desc *d, int32_t qo_len);
 pdecode_status pdecode_attention_multi(const pdecode_desc *d, int32_t qo_len, const void *q,

@@ -233,7 +233,7 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   p.chunk_slots = pl.chunk_slots;
   p.num_chunks = pl.num_chunks;
   const int cols = p.G * qo_len;  // q columns of the matrix-core B operand
-  const int gp = cols <= 1 ? 1 : cols <= 2 ? 2 : cols <= 4 ? 4 : 8;
+  const int gp = cols <= 1 ? 1 : cols <= 2 ? 2 : cols <= 4 ? 4 : cols <= 8 ? 8 : 16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // bf16 / fp8 KV: q.K on the matrix cores (4-wave workgroups, persistent over a job queue up to
   // kPersistMaxBatch sequences, else one per chunk), RoPE included; fp32 KV: the vector-ALU kernel
@@ -296,7 +296,7 @@ pdecode_status pdecode_attention_multi(const pdecode_desc* d, int32_t qo_len, co
     return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
                           rope, sm_scale, out, lse, workspace, workspace_bytes, stream);
   if (d->sliding_window) return PDECODE_ERR_UNSUPPORTED;
-  if (int64_t(qo_len) * (d->num_qo_heads / d->num_kv_heads) > 8) return PDECODE_ERR_UNSUPPORTED;
+  if (int64_t(qo_len) * (d->num_qo_heads / d->num_kv_heads) > 16) return PDECODE_ERR_UNSUPPORTED;
   return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
                         rope, sm_scale, out, lse, workspace, workspace_bytes, stream, qo_len);
 }

@@ -273,7 +273,10 @@ static hipError_t launch_chunked(const DecodeParams& p, unsigned grid, hipStream
 template <int KVT, int D, int PS, int GP, bool ROPE>
 static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipStream_t st) {
   hipError_t e;
-  if (p.T > 1) {
+  if constexpr (GP == 16) {  // 16 q columns: several query tokens only
+    if (p.T <= 1) return hipErrorInvalidValue;
+    e = launch_persist_multi<KVT, D, PS, GP, ROPE>(p, max_jobs, st);
+  } else if (p.T > 1) {
     e = launch_persist_multi<KVT, D, PS, GP, ROPE>(p, max_jobs, st);  // either RoPE layout
   } else if (ROPE && p.rotary == 2) {
     e = launch_persist_ilv<KVT, D, PS, GP>(p, max_jobs, st);  // interleaved RoPE, plain or fused
@@ -292,6 +295,11 @@ static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipS
 template <int KVT, int D, int PS, int GP>
 static hipError_t launch_sched(const DecodeParams& p, bool persistent, bool rope, long long grid,
                                hipStream_t st) {
+  if constexpr (GP == 16) {  // several query tokens on the persistent schedule only
+    if (!persistent) return hipErrorInvalidValue;
+    return rope ? launch_persist<KVT, D, PS, GP, true>(p, grid, st)
+                : launch_persist<KVT, D, PS, GP, false>(p, grid, st);
+  }
   if (rope)
     return persistent ? launch_persist<KVT, D, PS, GP, true>(p, grid, st)
                       : launch_chunked<KVT, D, PS, GP, true>(p, static_cast<unsigned>(grid), st);
@@ -307,6 +315,7 @@ static hipError_t launch_g(const DecodeParams& p, int gp, bool persistent, bool 
     case 2: return launch_sched<KVT, D, PS, 2>(p, persistent, rope, grid, st);
     case 4: return launch_sched<KVT, D, PS, 4>(p, persistent, rope, grid, st);
     case 8: return launch_sched<KVT, D, PS, 8>(p, persistent, rope, grid, st);
+    case 16: return launch_sched<KVT, D, PS, 16>(p, persistent, rope, grid, st);
   }
   return hipErrorInvalidValue;
 }

@@ -1,7 +1,7 @@
 // Decode with several query tokens per sequence (pdecode_attention_multi): the MT instantiations
 // of the persistent matrix-core decode kernel (decode_persist.hpp), built apart from
-// decode_mfma.hip. The G q heads of a KV head times the T tokens fill up to 8 columns of the MFMA
-// B operand (group bound GP 2, 4 or 8). With RoPE (rotate-half or interleaved), token t of a
+// decode_mfma.hip. The G q heads of a KV head times the T tokens fill up to 16 columns of the MFMA
+// B operand (group bound GP 2, 4, 8 or 16). With RoPE (rotate-half or interleaved), token t of a
 // sequence is rotated t positions after the sequence's first query position.
 #include "decode_persist.hpp"
 
@@ -26,7 +26,8 @@ hipError_t launch_persist_multi(const DecodeParams& p, long long max_jobs, hipSt
   PDK_MULTI(KVT, D, PS, 1, ROPE)       \
   PDK_MULTI(KVT, D, PS, 2, ROPE)       \
   PDK_MULTI(KVT, D, PS, 4, ROPE)       \
-  PDK_MULTI(KVT, D, PS, 8, ROPE)
+  PDK_MULTI(KVT, D, PS, 8, ROPE)       \
+  PDK_MULTI(KVT, D, PS, 16, ROPE)
 #define PDK_MULTI_SHAPES(KVT, ROPE)  \
   PDK_MULTI_GP(KVT, 64, 16, ROPE)    \
   PDK_MULTI_GP(KVT, 64, 32, ROPE)    \

@@ -728,10 +728,12 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         }
       }
       __syncthreads();  // s_m / s_d / s_o / s_ticket are free again
-      if (merge_prev) {
-        merge_split<D, GP, NT, MT>(p, pb, ph, pnch);
-        if (tid == 0)
-          __hip_atomic_store(&p.counters[pb * p.H_kv + ph], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if constexpr (!MT) {  // several tokens never merge in the kernel (merges_in_kernel)
+        if (merge_prev) {
+          merge_split<D, GP, NT, MT>(p, pb, ph, pnch);
+          if (tid == 0)
+            __hip_atomic_store(&p.counters[pb * p.H_kv + ph], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
       pb = in_merge && J.nch > 1 ? J.b : -1;
       ph = J.h;
@@ -747,10 +749,12 @@ void decode_mfma_persist_kernel(DecodeParams p) {
             s_ticket = t == (pnch - 1) * kPWaves;
           }
           __syncthreads();
-          if (s_ticket) {
-            merge_split<D, GP, NT, MT>(p, pb, ph, pnch);
-            if (tid == 0)
-              __hip_atomic_store(&p.counters[pb * p.H_kv + ph], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if constexpr (!MT) {
+            if (s_ticket) {
+              merge_split<D, GP, NT, MT>(p, pb, ph, pnch);
+              if (tid == 0)
+                __hip_atomic_store(&p.counters[pb * p.H_kv + ph], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
         }
         break;

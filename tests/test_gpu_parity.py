@@ -759,11 +759,15 @@ def _multi_case(w, T, seed, num_kv_splits=0):
 
 @pytest.mark.parametrize("kv,G,T,D,ps", [("bf16", 4, 2, 128, 16), ("bf16", 1, 8, 64, 32),
                                          ("bf16", 2, 3, 128, 16), ("fp8", 2, 4, 128, 32),
-                                         ("fp8", 1, 2, 64, 16), ("bf16", 8, 1, 128, 16)])
+                                         ("fp8", 1, 2, 64, 16), ("bf16", 8, 1, 128, 16),
+                                         ("bf16", 4, 4, 128, 16), ("bf16", 8, 2, 128, 16),
+                                         ("fp8", 8, 2, 128, 32), ("bf16", 1, 16, 64, 16),
+                                         ("fp8", 4, 3, 64, 32), ("bf16", 5, 3, 128, 32)])
 def test_attention_multi(kv, G, T, D, ps):
     """T query tokens, causal over the new ones, against the oracle (each token = decode over its
     visible prefix): sequences shorter than T (tokens with no row), an empty one, lengths around
-    page boundaries; T x G from 6 to 8 MFMA columns."""
+    page boundaries; T x G from 6 to 16 MFMA columns (Llama-3-8B group with 4 tokens, GQA 8 with
+    2, one head with 16)."""
     lens = [1, T - 1, ps, ps + 1, 3 * ps - 1, 700, 0, 2 * ps + T]
     w = synth.make_workload(name=f"multi_{kv}_G{G}_D{D}_ps{ps}", B=len(lens), H_qo=2 * G,
                             H_kv=2, D=D, page_size=ps, seq_lens=lens, q_dtype="bf16",
@@ -781,6 +785,16 @@ def test_attention_multi_split(splits):
     _multi_case(w, 2, seed=83, num_kv_splits=splits)
 
 
+@pytest.mark.parametrize("splits", [0, 4, 13])
+def test_attention_multi_sixteen_columns_split(splits):
+    """Four tokens on the Llama-3-8B group (16 columns) with forced splits merged by the split
+    merge kernel."""
+    w = synth.make_workload(name=f"multi16_split{splits}", B=5, H_qo=16, H_kv=4, D=128,
+                            page_size=16, seq_lens=[3000, 3, 1200, 641, 4], seed=840 + splits,
+                            max_num_pages=512)
+    _multi_case(w, 4, seed=85, num_kv_splits=splits)
+
+
 @pytest.mark.parametrize("kv,G,T,D,ps,splits,rot", [("bf16", 4, 2, 128, 16, 0, 1),
                                                     ("bf16", 2, 3, 64, 32, 0, 1),
                                                     ("fp8", 2, 4, 128, 16, 0, 1),
@@ -791,7 +805,11 @@ def test_attention_multi_split(splits):
                                                     ("bf16", 4, 2, 128, 16, 0, 2),
                                                     ("bf16", 1, 8, 64, 32, 5, 2),
                                                     ("fp8", 2, 4, 64, 16, 12, 2),
-                                                    ("fp8", 8, 1, 128, 32, 0, 2)])
+                                                    ("fp8", 8, 1, 128, 32, 0, 2),
+                                                    ("bf16", 4, 4, 128, 16, 0, 1),
+                                                    ("bf16", 8, 2, 128, 16, 7, 2),
+                                                    ("fp8", 8, 2, 128, 32, 12, 1),
+                                                    ("fp8", 4, 4, 64, 16, 0, 2)])
 def test_attention_multi_rope(kv, G, T, D, ps, splits, rot):
     """RoPE with several tokens (rotate-half, or interleaved for rot = 2): token t's query at
     q_rope_position + t (oracle reading), Llama-3 base; lengths around page boundaries, tokens
@@ -971,11 +989,11 @@ def test_full_size_fused_step():
     assert_close(w, o_ref, l_ref, gu.to_np64(out), gu.to_np64(lse), "full-size fused")
 
 
-def test_full_size_multi_token_and_sink():
-    """pdecode_attention_multi (two tokens) with learned sinks on the full Llama-3-8B-shaped
-    workload: every (sequence, token, head) output against the oracle."""
+@pytest.mark.parametrize("T", [2, 4])
+def test_full_size_multi_token_and_sink(T):
+    """pdecode_attention_multi (two tokens, and four: 16 MFMA columns) with learned sinks on the
+    full Llama-3-8B-shaped workload: every (sequence, token, head) output against the oracle."""
     w = synth.CONFIGS["llama3_8b_bf16"]()
-    T = 2
     qm = synth.multi_query(w, T, seed=78)
     sinks = np.random.default_rng(79).normal(0.0, 2.0, w.H_qo).astype(np.float32)
     kw = {k: v for k, v in w.oracle_kwargs().items() if k != "q"}
