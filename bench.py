@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="num_kv_splits (0 = automatic plan)")
+    ap.add_argument("--no-hint", action="store_true",
+                    help="max_kv_len = 0 in the description (no length hint)")
     ap.add_argument("--workload", default="llama3_8b_bf16",
                     choices=["llama3_8b_bf16", "long_ctx_bf16", "rope_swa_bf16", "fp8_gqa8",
                              "tiny_fp32", "gqa8_bf16"])
@@ -426,7 +428,8 @@ def main():
     sets = [base] + [make(seed=1002 + 100 * i, lens=lens) for i in range(1, nsets)]
     devs = [gu.upload(w) for w in sets]
     kv_bytes = base.kv_bytes
-    desc = gu.desc_for(base, devs[0], num_kv_splits=args.splits)
+    desc = gu.desc_for(base, devs[0], num_kv_splits=args.splits,
+                       max_kv_len=0 if args.no_hint else None)
     ws = pk.alloc_workspace(desc)
     out = torch.empty((base.B, base.H_qo, base.D), dtype=gu.TORCH_STORAGE[base.q_dtype],
                       device="cuda")
@@ -504,15 +507,17 @@ def main():
                    "page_size": base.page_size, "kv_dtype": base.kv_dtype,
                    "ctx_len": CTX_DESC.get(args.workload, ""),
                    "kv_bytes_per_step": kv_bytes, "input_sets": len(sets),
-                   "chunk_pages": cp, "num_chunks": nc},
+                   "split_plan": (f"chunks sized on the device from the call's lengths, at most "
+                                  f"{nc} per sequence" if cp == 0 else
+                                  f"chunks of {cp} page slots, at most {nc} per sequence"),
+                   "max_kv_len_hint": int(desc.max_kv_len)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(args.workload),
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                      "algorithmic_bytes": kv_bytes,
-                     "kernel": ("pdecode_attention: the decode kernel, plus split_merge_kernel when the plan "
-                                "splits sequences and the decode kernel does not merge them itself "
-                                "(instantiations of at most 4 q columns, or more than 8 chunks)"),
+                     "kernel": ("pdecode_attention: one launch of the persistent decode kernel, "
+                                "which also merges the split sequences"),
                      "avg_launch_us": round(avg_call_s * 1e6, 3),
                      "ceiling_GBps": ceiling["GBps"],
                      "frac_of_ceiling": round(achieved / ceiling["GBps"], 4),

@@ -90,10 +90,15 @@ typedef struct pdecode_desc {
   int32_t kv_dtype;       /* pdecode_dtype of the pool                                         */
   int32_t sliding_window; /* 0: length_info is [B]; 1: length_info is [3, B]                   */
   int32_t max_kv_len;     /* host-side upper bound on attended rows per sequence, used only to
-                             plan the split-KV grid; 0 = take max_num_pages * page_size. A
-                             sequence longer than the bound is still computed exactly.           */
-  int32_t num_kv_splits;  /* 0 = automatic; 1 = never split a sequence; n > 1 = split each
-                             sequence's pages into at most n chunks merged by log-sum-exp         */
+                             plan the split-KV grid of the fixed-split and fp32 / large-batch
+                             plans; 0 = take max_num_pages * page_size. The automatic plan of the
+                             bf16 / fp8 kernels (batch <= 1024) ignores it. A sequence longer than
+                             the bound is still computed exactly.                               */
+  int32_t num_kv_splits;  /* 0 = automatic: for bf16 / fp8 KV and batch <= 1024 the chunk size is
+                             chosen on the device at each call from the lengths (about one or two
+                             jobs per resident workgroup); 1 = never split a sequence; n > 1 =
+                             split each sequence's pages into at most n chunks merged by
+                             log-sum-exp                                                        */
   const float *k_scale;   /* device fp32 [H_kv]; required iff kv_dtype is an FP8: K = code * scale */
   const float *v_scale;   /* device fp32 [H_kv]; required iff kv_dtype is an FP8: V = code * scale */
   const float *sink_logits; /* device fp32 [H_qo] or NULL: learned attention sink per q head (the
@@ -128,8 +133,9 @@ typedef struct pdecode_rope {
 size_t pdecode_workspace_bytes(const pdecode_desc *d);
 
 /* The split plan for `d` (with or without RoPE): rows are processed in chunks of *chunk_pages page
- * slots and a sequence uses at most *num_chunks chunks. Returns PDECODE_OK or an argument
- * error. */
+ * slots and a sequence uses at most *num_chunks chunks. *chunk_pages = 0: the chunk size is chosen
+ * on the device at each call (automatic plan of the bf16 / fp8 kernels), within *num_chunks
+ * chunks per sequence. Returns PDECODE_OK or an argument error. */
 pdecode_status pdecode_plan(const pdecode_desc *d, int32_t *chunk_pages, int32_t *num_chunks);
 
 /* Decode attention (see the header comment for the computation and layouts).

@@ -140,8 +140,13 @@ def workspace_bytes(desc: Desc) -> int:
     return int(lib().pdecode_workspace_bytes(ctypes.byref(desc)))
 
 
+def workspace_bytes_multi(desc: Desc, qo_len: int) -> int:
+    return int(lib().pdecode_workspace_bytes_multi(ctypes.byref(desc), int(qo_len)))
+
+
 def plan(desc: Desc):
-    """(chunk_pages, num_chunks) the library plans for this description."""
+    """(chunk_pages, num_chunks) the library plans for this description; (0, 0) when the
+    chunk size is chosen on the device at each call (the persistent schedule's automatic plan)."""
     cp, nc = _c_i32(0), _c_i32(0)
     st = lib().pdecode_plan(ctypes.byref(desc), ctypes.byref(cp), ctypes.byref(nc))
     if st:
@@ -183,7 +188,7 @@ def attention_noalloc(desc: Desc, q, pages, page_indptr, page_values, length_inf
 
 def alloc_workspace_multi(desc: Desc, qo_len: int, device="cuda") -> torch.Tensor | None:
     """A zero-filled workspace of pdecode_workspace_bytes_multi(desc, qo_len) bytes, or None."""
-    n = int(lib().pdecode_workspace_bytes_multi(ctypes.byref(desc), int(qo_len)))
+    n = workspace_bytes_multi(desc, qo_len)
     return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 

@@ -12,14 +12,22 @@
 
 namespace {
 
-constexpr int kTargetWorkgroups = 2048;  // one-wave workgroups of the vector-ALU kernel
-constexpr int kTargetJobs = 1024;         // jobs of the persistent matrix-core schedule
+constexpr int kTargetWorkgroups = 2048;  // workgroups of the one-workgroup-per-chunk kernels
 constexpr int kMinChunkRows = 256;
-constexpr int kPersistMaxBatch = 1024;  // the persistent schedule keeps a per-sequence table in LDS
+// The persistent schedule (decode_persist.hpp): its LDS job table holds kPersistMaxBatch
+// sequences and it runs at most kPersistMaxGrid workgroups, so its automatic plan never wants
+// more than 2 kPersistMaxGrid jobs (kAutoJobRoom); the 8-column instantiations merge split
+// sequences themselves up to kInMergeChunks chunks each.
+constexpr int kPersistMaxBatch = 1024;
+constexpr int kPersistMaxGrid = 1024;
+constexpr int64_t kAutoJobRoom = 4 * kPersistMaxGrid;
+constexpr int kInMergeChunks = 8;
 
 struct Plan {
   int32_t chunk_slots = 1;
   int32_t num_chunks = 1;
+  bool auto_chunk = false;  // persistent schedule: the chunk size is chosen on the device
+  int64_t max_jobs = 1;     // jobs of the call at most (the one-workgroup-per-chunk grid)
   size_t part_o_bytes = 0;
   size_t part_lse_bytes = 0;
   size_t counter_bytes = 0;
@@ -61,6 +69,9 @@ pdecode_status check_attention_shape(const pdecode_desc* d) {
 // Chunking of each sequence's page slots. A sequence with n slots uses ceil(n / chunk_slots)
 // chunks, capped at num_chunks (the last chunk then takes every remaining slot), so any length
 // is computed exactly; max_kv_len only sizes the grid.
+// The persistent schedule's automatic plan (num_kv_splits 0) is made on the device at each call,
+// from the call's lengths (auto_chunk_slots in decode_persist.hpp); the host only sizes its
+// partial states, and max_kv_len plays no part.
 // The plan does not depend on RoPE: calls with and without it run the same kernel family.
 Plan make_plan(const pdecode_desc* d, int qo_len = 1) {
   Plan pl;
@@ -68,35 +79,50 @@ Plan make_plan(const pdecode_desc* d, int qo_len = 1) {
   const int64_t max_len = d->max_kv_len > 0 ? d->max_kv_len : int64_t(d->max_num_pages) * ps;
   const int64_t max_slots = (max_len + ps - 1) / ps + (d->sliding_window ? 2 : 0);
   const int64_t units = int64_t(d->batch) * d->num_kv_heads;
+  const int64_t min_chunk = (kMinChunkRows + ps - 1) / ps;
+  const size_t cols = size_t(qo_len) * (d->num_qo_heads / d->num_kv_heads);
 
   const bool persistent = (d->kv_dtype == PDECODE_BF16 || is_fp8(d->kv_dtype)) &&
                           d->batch <= kPersistMaxBatch;
-  int64_t chunk;
-  if (d->num_kv_splits == 1) {
-    chunk = max_slots;
-  } else if (d->num_kv_splits > 1) {
-    chunk = (max_slots + d->num_kv_splits - 1) / d->num_kv_splits;
-  } else {
-    const int64_t min_chunk = (kMinChunkRows + ps - 1) / ps;
-    // about two jobs per resident workgroup of the persistent schedule, and at least two per
-    // (sequence, KV head) (long jobs amortise the job switch and need fewer split merges; the
-    // queue hands out the longest first)
-    const int64_t target =
-        persistent ? (kTargetJobs > 2 * units ? kTargetJobs : 2 * units) : kTargetWorkgroups;
-    chunk = (units * max_slots + target - 1) / target;
-    if (chunk < min_chunk) chunk = min_chunk;
-  }
-  if (chunk < 1) chunk = 1;
-  int64_t n = (max_slots + chunk - 1) / chunk;
-  if (n < 1) n = 1;
-  if (n > INT_MAX / 2) n = INT_MAX / 2;
-  pl.chunk_slots = static_cast<int32_t>(chunk > INT_MAX ? INT_MAX : chunk);
-  pl.num_chunks = static_cast<int32_t>(n);
   pl.persistent = persistent;
+  if (persistent && d->num_kv_splits == 0) {
+    // chunks per sequence at most: room for kAutoJobRoom jobs over the (sequence, KV head)
+    // pairs, at least 2 (the device plan's fallback halves the longest sequence); the 8-column
+    // single-token kernels keep to kInMergeChunks (and merge in the kernel) when that still leaves
+    // room for 2 kPersistMaxGrid jobs
+    int64_t cap = (kAutoJobRoom + units - 1) / (units > 0 ? units : 1);
+    if (cap < 2) cap = 2;
+    const bool eight_cols = qo_len == 1 && d->num_qo_heads / d->num_kv_heads > 4;
+    if (eight_cols && cap > kInMergeChunks && units * kInMergeChunks >= 2 * kPersistMaxGrid)
+      cap = kInMergeChunks;
+    pl.auto_chunk = true;
+    pl.chunk_slots = static_cast<int32_t>(min_chunk);
+    pl.num_chunks = static_cast<int32_t>(cap);
+    pl.max_jobs = units * cap;
+  } else {
+    int64_t chunk;
+    if (d->num_kv_splits == 1) {
+      chunk = max_slots;
+    } else if (d->num_kv_splits > 1) {
+      chunk = (max_slots + d->num_kv_splits - 1) / d->num_kv_splits;
+    } else {
+      // about kTargetWorkgroups workgroups
+      chunk = (units * max_slots + kTargetWorkgroups - 1) / kTargetWorkgroups;
+      if (chunk < min_chunk) chunk = min_chunk;
+    }
+    if (chunk < 1) chunk = 1;
+    int64_t n = (max_slots + chunk - 1) / chunk;
+    if (n < 1) n = 1;
+    if (n > INT_MAX / 2) n = INT_MAX / 2;
+    pl.chunk_slots = static_cast<int32_t>(chunk > INT_MAX ? INT_MAX : chunk);
+    pl.num_chunks = static_cast<int32_t>(n);
+    pl.max_jobs = units * n;
+  }
+  // split partial states [B, T, H_qo, num_chunks, D]
   if (pl.num_chunks > 1) {
-    const size_t rows = size_t(d->batch) * qo_len * d->num_qo_heads * pl.num_chunks;
+    const size_t rows = size_t(pl.max_jobs) * cols;
     pl.part_o_bytes = align256(rows * d->head_dim * sizeof(float));
-    pl.part_lse_bytes = align256(rows * sizeof(float));
+    pl.part_lse_bytes = align256((rows + 1) * sizeof(float));  // + the plan word
   }
   // split arrival counters [B * H_kv], then the two job-queue counters of the persistent schedule.
   // They lead the workspace, at the same offset and size in every plan of a description (any
@@ -135,7 +161,7 @@ pdecode_status pdecode_plan(const pdecode_desc* d, int32_t* chunk_pages, int32_t
   if ((st = check_attention_shape(d)) != PDECODE_OK) return st;
   if (!chunk_pages || !num_chunks) return PDECODE_ERR_INVALID_ARG;
   const Plan pl = make_plan(d);
-  *chunk_pages = pl.chunk_slots;
+  *chunk_pages = pl.auto_chunk ? 0 : pl.chunk_slots;
   *num_chunks = pl.num_chunks;
   return PDECODE_OK;
 }
@@ -177,7 +203,7 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   // interleaved RoPE: the persistent matrix-core kernels only
   if (rotary && rope->rotary_mode == 2 && !pl.persistent)
     return PDECODE_ERR_UNSUPPORTED;
-  const int64_t grid = int64_t(pl.num_chunks) * d->batch * d->num_kv_heads;
+  const int64_t grid = pl.max_jobs;  // persistent schedule: a bound on its workgroups
   if (grid > INT_MAX) return PDECODE_ERR_UNSUPPORTED;
   if (fixed) {
     if (pl.counter_bytes > fixed->counter_bytes ||
@@ -219,6 +245,10 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
     p.part_lse = ws ? reinterpret_cast<float*>(wsb + pl.counter_bytes + pl.part_o_bytes) : nullptr;
   }
   p.queue = ws ? p.counters + size_t(d->batch) * d->num_kv_heads : nullptr;
+  // the word after the partial lse rows [B, T, H_qo, num_chunks]
+  p.plan_word = pl.part_lse_bytes > 0 ? reinterpret_cast<int32_t*>(
+                    p.part_lse + size_t(pl.max_jobs) * qo_len * (d->num_qo_heads / d->num_kv_heads))
+                                      : nullptr;
   p.B = d->batch;
   p.H_qo = d->num_qo_heads;
   p.H_kv = d->num_kv_heads;
@@ -232,6 +262,7 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   p.score_scale = sm_scale * pdk::kLog2e;
   p.chunk_slots = pl.chunk_slots;
   p.num_chunks = pl.num_chunks;
+  p.auto_chunk = pl.auto_chunk ? 1 : 0;
   const int cols = p.G * qo_len;  // q columns of the matrix-core B operand
   const int gp = cols <= 1 ? 1 : cols <= 2 ? 2 : cols <= 4 ? 4 : cols <= 8 ? 8 : 16;
   hipStream_t s = static_cast<hipStream_t>(stream);

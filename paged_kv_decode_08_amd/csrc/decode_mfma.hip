@@ -1,6 +1,6 @@
-// Paged-KV decode attention for bf16 or fp8-e4m3fn KV (bf16 q) on gfx950: q.K on the matrix cores,
-// softmax and P.V on the vector ALUs, optional RoPE on q and K in registers (per-item steps:
-// mfma_core.hpp).
+// Paged-KV decode attention for bf16 or fp8-e4m3fn KV (bf16 q) on gfx950: q.K and P.V on the
+// matrix cores, the softmax on the vector ALUs, optional RoPE on q and K in registers (per-item
+// steps: mfma_core.hpp).
 //
 // Work unit ("job"): one chunk of page slots of one (sequence, KV head), done by one workgroup of
 // 4 wavefronts (kWaves, kPWaves); wave w takes slots w, w + 4, ... of the chunk and the waves' states are
@@ -15,11 +15,13 @@
 //    from the page table. The job after the current one is fetched, decoded and its page ids and q
 //    loaded while the current one streams, and its first page is in flight before the current
 //    job's last page is computed, so a workgroup's load stream does not stop at job boundaries.
-//    In the single-token 8-column instantiations, when the call has at most kInMergeChunks chunks,
-//    the workgroup whose waves complete a split sequence's count of arrivals merges it at the end
-//    of its next job (each wave arrives once its own partial stores are known complete, a pair of
-//    items into the next job, so no wait falls on the load stream); otherwise a second,
-//    row-parallel kernel (split_merge_kernel) merges them (merges_in_kernel).
+//    In the single-token 8-column instantiations, when the call has at most kInMergeChunks chunks
+//    per sequence, the workgroup whose waves complete a split sequence's count of arrivals merges
+//    it at the end of its next job (each wave arrives once its own partial stores are known
+//    complete, a pair of items into the next job, so no wait falls on the load stream); otherwise
+//    a second, row-parallel kernel (split_merge_kernel) merges them (merges_in_kernel). The chunk
+//    size is chosen on the device from the call's lengths (auto_chunk_slots) unless the caller
+//    fixed the split count.
 //  * one workgroup per job (decode_mfma_kernel), for batches too large for the LDS job table: the
 //    last workgroup of a split sequence to finish merges it (split.hpp).
 #include "decode_persist.hpp"
@@ -187,7 +189,7 @@ template <int D, int PS>
 __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodeParams p) {
   constexpr int V = D / 4;      // float4 per partial row
   constexpr int CPW = 64 / V;   // chunks per wave-wide load
-  constexpr int NB = 8;         // float4 loads per lane per batch
+  constexpr int NB = 4;         // float4 loads per lane per batch
   constexpr int CB = NB * CPW;  // chunks per batch
   static_assert(64 % CB == 0 || CB % 64 == 0, "batches and lse words line up");
   const int lane = threadIdx.x & 63;
@@ -206,8 +208,11 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
   };
   const float lse_l = lse_c[min(lane, nc - 1)];
   load_batch(0);
+  // automatic plan: the chunk size the decode kernel chose (its workgroup 0 stored it after the
+  // partial lse); loaded with the rest, used only once everything has arrived
+  const int cs = p.auto_chunk ? *p.plan_word : p.chunk_slots;
   const SeqGeom sg = seq_geom(p.indptr, p.length_info, p.B, b, PS, p.sliding);
-  const int nch = chunks_used(sg.n_slots, p.chunk_slots, nc);
+  const int nch = persist_chunks<PS>(sg.n_slots, cs, nc);
 
   float mx = lane < nch ? lse_l : -INFINITY;
   for (int c = 64 + lane; c < nch; c += 64) mx = fmaxf(mx, lse_c[c]);

@@ -15,6 +15,7 @@ namespace pdk {
 
 constexpr int kPWaves = 4;              // wavefronts per workgroup of the persistent schedule
 constexpr int kPersistMaxBatch = 1024;  // sequences the persistent schedule's LDS table holds
+constexpr int kPersistMaxGrid = 1024;   // workgroups of the persistent schedule, at most
 
 // ------------------------------------------------------------------------------------------------
 // Persistent workgroups over a job queue.
@@ -27,7 +28,7 @@ constexpr int kPersistMaxBatch = 1024;  // sequences the persistent schedule's L
 struct SeqTable {
   int4* geo;    // [B] by sequence: beg, np, total, win_off (multi-wave build only)
   int4* rgeo;   // [B] by rank: the same
-  int4* rsb;    // [B] by rank: sink, sequence, chunks, slots per chunk (rounded down)
+  int4* rsb;    // [B] by rank: sink, sequence, chunks, slot units per chunk (rounded down)
   int* pre;     // [B + 1] by rank: first job of each rank (exclusive prefix); pre[B] = all jobs
   int* njobs;   // [B] by sequence: chunks x H_kv
   int* rnj;     // [B] by rank: the same
@@ -56,6 +57,35 @@ __device__ inline SeqTable seq_table(int* base, int B) {
   return t;
 }
 
+// Chunk shape of the persistent schedule. A chunk's page slots are dealt to the four waves in
+// turn, so a chunk of A = 8 / SUB slots (eight 16-row items) gives each wave the same, even number
+// of items: no wave idles at the job's closing barrier and none pads its item pairs with a re-read.
+// Chunks are whole multiples of A slots (the u = n / A units are dealt evenly), and the last chunk
+// also takes the n mod A leftover slots. A sequence never has more chunks than units.
+template <int PS>
+constexpr int slot_unit() { return PS == 16 ? 8 : 4; }
+
+template <int PS>
+__host__ __device__ inline int persist_chunks(int n_slots, int chunk_slots, int num_chunks) {
+  if (n_slots <= 0) return 0;
+  int nch = (n_slots + chunk_slots - 1) / chunk_slots;
+  if (nch > num_chunks) nch = num_chunks;
+  const int u = n_slots / slot_unit<PS>();
+  return nch > 1 && nch > u ? (u > 1 ? u : 1) : nch;
+}
+
+// Slots [begin, end) of chunk c of nch, uq = (n_slots / A) / nch units per chunk (the first
+// units % nch chunks take one unit more).
+template <int PS>
+__device__ __forceinline__ void persist_bounds(int n_slots, int nch, int uq, int c, int& begin,
+                                               int& end) {
+  constexpr int A = slot_unit<PS>();
+  const int u = n_slots / A;
+  const int urem = u - uq * nch;
+  begin = A * (c * uq + min(c, urem));
+  end = c == nch - 1 ? n_slots : begin + A * (uq + (c < urem ? 1 : 0));
+}
+
 // A job as one wave sees it (wave-uniform values).
 struct Job {
   int valid;
@@ -69,6 +99,65 @@ struct Job {
 };
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ long long wave_sum64(long long x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// Chunk size in page slots of the automatic plan, chosen from the call's own lengths: N attended
+// slots over the n_seq sequences that have any, at most n_max in one; H KV heads (a job is one
+// chunk of one KV head); P workgroups; at least min_chunk slots and at most max_chunks chunks per
+// sequence (the partial states have room for that many). jobs(c) is the call's job count with
+// chunks of c slots (non-increasing in c); every thread that calls this calls it with the same
+// values.
+// * One job per workgroup, if no job is then above 5/4 of the mean work of a workgroup (few
+//   sequences of similar length: long contexts, sliding windows); measured 7 us (6 %) faster than
+//   two per workgroup on the long-context shape.
+// * Otherwise about max(2 P, 2 pairs) chunks of the longest sequence's size over the
+//   (sequence, KV head) pairs: what the host plans from a tight length hint, whose chunk size was
+//   tuned on the Llama-3-8B shape (64 slots there; 61 and 44 slots measured 2.4 and 2.8 us
+//   slower). With more pairs than workgroups this halves the longest sequence.
+template <typename Jobs>
+__device__ int auto_chunk_slots(float N, int n_seq, int n_max, int H, int P, int min_chunk,
+                                int max_chunks, Jobs jobs) {
+  // Every workgroup runs this in its prologue, so it decides from single-precision estimates
+  // (the same on every workgroup) and counts jobs at most twice: 64-bit divisions and a search
+  // here measured 2.3 us per call on the Llama-3-8B shape.
+  if (n_max <= 0) return max(min_chunk, 1);
+  min_chunk = max(min_chunk, (n_max + max_chunks - 1) / max_chunks);
+  auto up = [](float x) { return int(fminf(ceilf(x), 1073741824.f)); };
+  const float NH = N * float(H);
+  const float pairs = float(n_seq) * float(H);
+  if (pairs <= float(P)) {
+    const float lim = 1.25f * NH / float(P);  // the largest job a balanced one-per-workgroup plan has
+    // about the smallest chunk giving P jobs, a sequence's last chunk taken as half full; whole
+    // sequences (n_max) give pairs <= P jobs
+    int c = max(min_chunk, up(NH / (float(P) - 0.5f * pairs)));
+    if (c < n_max && float(c) <= lim) {
+      const long long J = jobs(c);
+      if (J > P) {  // grow by the excess once
+        c = up(float(c) * float(J) / float(P));
+        if (c < n_max && jobs(c) > P) c = n_max;
+      }
+    }
+    c = min(c, n_max);
+    if (float(c) <= lim) return c;
+  }
+  const float target = fmaxf(2.f * float(P), 2.f * pairs);
+  return max(min_chunk, up(pairs * float(n_max) / target));
+}
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory operations are
 // outstanding, and not for the export or LDS/scalar counters.
@@ -127,8 +216,7 @@ __device__ __forceinline__ Job decode_job(const DecodeParams& p, const SeqTable&
     J.kro = uni(rp.y);
   }
   int sb, se;
-  const int q = uni(sk_b.w);
-  chunk_bounds_q(q, g.n_slots - q * J.nch, J.c, sb, se);
+  persist_bounds<PS>(g.n_slots, J.nch, uni(sk_b.w), J.c, sb, se);
   J.s_first = sb;
   J.s_w = sb + w;
   J.nw = J.s_w < se ? (se - J.s_w + kPWaves - 1) / kPWaves : 0;
@@ -173,22 +261,18 @@ __device__ void append_last_row(const DecodeParams& p, int b) {
   }
 }
 
-// Split sequences of calls with at most this many chunks are merged inside the persistent kernel
-// by its single-token 8-column instantiations (8 q heads per KV head); the others leave every
-// split sequence to split_merge_kernel. Measured on the same box: with 4 columns the separate
-// merge kernel was faster (Llama-3-8B shape 68.0-68.5 against 68.9-69.5 us), and so it was with
-// 4 q heads x 2 tokens (75.1 against 78.6-78.8 us); with 8 heads the in-kernel merge was (bf16 and
-// fp8 8-head shapes, 2-4 us and 3-8 us).
+// Split sequences of calls with at most this many chunks per sequence are merged inside the
+// persistent kernel by its single-token 8-column instantiations (8 q heads per KV head); the
+// others leave every split sequence to split_merge_kernel. Measured on the same box: with 4
+// columns the separate merge kernel was faster (Llama-3-8B shape 62.5-62.8 against 63.8-65.8 us
+// with 4 chunks), and so it was with 4 q heads x 2 tokens (75.1 against 78.6-78.8 us); with 8
+// heads the in-kernel merge was (bf16 and fp8 8-head shapes, 2-4 us and 3-8 us).
 constexpr int kInMergeChunks = 8;
 template <int GP>
 constexpr bool merges_in_kernel(int num_chunks, bool several_tokens) {
-  return GP >= 8 && !several_tokens && num_chunks <= kInMergeChunks;
+  return GP == 8 && !several_tokens && num_chunks <= kInMergeChunks;
 }
 
-// Merges the nch (2 .. kInMergeChunks) chunk states of (sequence b, KV head h), stored with
-// store_agent() and complete, into out and lse: M = max_c lse_c, w_c = 2^(lse_c - M),
-// out = sum_c w_c O_c / sum_c w_c, lse = M + log2(sum_c w_c). Thread t produces 4 dims of one q
-// head; every load is issued before any is used (one memory round trip). All threads take part.
 // Output row of q column c of (sequence b, KV head h): columns are token-major (token c / G, q
 // head h G + c % G); with one token, c is the q head's index in the group.
 template <bool MT>
@@ -199,49 +283,59 @@ __device__ __forceinline__ size_t out_row(const DecodeParams& p, int b, int h, i
     return size_t(b) * p.H_qo + size_t(h) * p.G + c;
 }
 
+// Merges the nch (2 .. kInMergeChunks) chunk states of (sequence b, KV head h), stored with
+// store_agent() and complete, into out and lse (TVM relax decode-kernels page,
+// _merge_state_inplace, applied over all chunks): M = max_c lse_c, w_c = 2^(lse_c - M),
+// out = sum_c w_c O_c / sum_c w_c, lse = M + log2(sum_c w_c). Thread t produces 4 dims of one q
+// column and loads the chunks present, 8 at a time, before using any (one memory round trip per
+// 8 chunks; the state is rescaled as the running maximum grows). All threads take part.
 // MT: several query tokens (p.T): G T columns, and a column whose token sees no row of the
 // sequence (all chunk lse -inf) gives out = 0, lse = -5e4.
 template <int D, int GP, int NT, bool MT = false>
 __device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
   constexpr int V = D / 4;
-  static_assert(GP * V <= NT, "one float4 of output per thread");
-  __shared__ float s_l[GP][kInMergeChunks];
-  const int tid = threadIdx.x;
-  const int G = MT ? p.G * p.T : p.G;  // columns
-  if (tid < G * nch) {
-    const int g = tid / nch;
-    s_l[g][tid - g * nch] =
-        load_agent(&p.part_lse[out_row<MT>(p, b, h, g) * p.num_chunks + (tid - g * nch)]);
-  }
-  const int g = min(tid / V, G - 1);
-  const int v = tid % V;
-  const float* src = p.part_o + out_row<MT>(p, b, h, g) * p.num_chunks * D + 4 * v;
-  float o[kInMergeChunks][4];
+  constexpr int CB = 8;  // chunks per batch of loads
+  const int GC = MT ? p.G * p.T : p.G;  // columns
+  for (int it = threadIdx.x; it < GC * V; it += NT) {
+    const int g = it / V;
+    const int v = it - g * V;
+    float M = -INFINITY, ws = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < nch; c0 += CB) {
+      float l[CB], o[CB][4];
 #pragma unroll
-  for (int c = 0; c < kInMergeChunks; ++c) {
-    if (c < nch) {
+      for (int u = 0; u < CB; ++u) {
+        l[u] = -INFINITY;
+        o[u][0] = o[u][1] = o[u][2] = o[u][3] = 0.f;
+        if (c0 + u < nch) {  // uniform over the workgroup
+          const size_t row = out_row<MT>(p, b, h, g) * p.num_chunks + c0 + u;
+          l[u] = load_agent(&p.part_lse[row]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) o[c][k] = load_agent(src + size_t(c) * D + k);
+          for (int k = 0; k < 4; ++k) o[u][k] = load_agent(&p.part_o[row * D + 4 * v + k]);
+        }
+      }
+      float Mn = M;
+#pragma unroll
+      for (int u = 0; u < CB; ++u)
+        if (c0 + u < nch) Mn = fmaxf(Mn, l[u]);
+      // MT: every chunk so far may be -inf (the column's token sees none of their rows)
+      const float Ms = Mn == -INFINITY ? 0.f : Mn;
+      const float r = exp2_fast(M - Ms);  // 0 while M is -inf
+      ws *= r;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[k] *= r;
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        if (c0 + u < nch) {
+          const float wc = exp2_fast(l[u] - Ms);
+          ws += wc;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) a[k] = fmaf(wc, o[u][k], a[k]);
+        }
+      }
+      M = Mn;
     }
-  }
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int c = 0; c < kInMergeChunks; ++c)
-    if (c < nch) M = fmaxf(M, s_l[g][c]);
-  const bool none = MT && M == -INFINITY;
-  if (MT && none) M = 0.f;
-  float ws = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < kInMergeChunks; ++c) {
-    if (c < nch) {
-      const float wc = exp2_fast(s_l[g][c] - M);
-      ws += wc;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) a[k] = fmaf(wc, o[c][k], a[k]);
-    }
-  }
-  if (tid < G * V) {
+    const bool none = MT && M == -INFINITY;
+    if (none) M = 0.f;
     const size_t orow = out_row<MT>(p, b, h, g);
     float fo = 1.f;  // learned sink: folded into the denominator once, here
     if (p.sink != nullptr && !none) fo = fold_sink(p.sink[h * p.G + g % p.G] * kLog2e, M, ws);
@@ -252,7 +346,6 @@ __device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
         uint32_t(f32_to_bf16(a[2] * inv)) | uint32_t(f32_to_bf16(a[3] * inv)) << 16);
     if (v == 0) p.lse[orow] = none ? kEmptyLse : M + log2f(ws);
   }
-  __syncthreads();  // s_l is free again
 }
 
 // FUSED: the call also appends each sequence's new K/V row (p.new_k, p.new_v).
@@ -308,21 +401,31 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   // jobs (chunks x H_kv) in rank order
   const SeqTable tab = seq_table(s_dyn, B);
   {
+    constexpr int kUnit = slot_unit<PS>();
     // size class of a sequence: 0 for chunks above 7/8 of chunk_slots, .. 3 for 5/8 and below
-    auto size_class = [&](int n_slots, int nch) {
+    auto size_class = [&](int n_slots, int nch, int cs) {
       const int sz = nch > 0 ? (n_slots + nch - 1) / nch : 0;
-      return 8 * sz > 7 * p.chunk_slots ? 0 : 8 * sz > 6 * p.chunk_slots ? 1
-             : 8 * sz > 5 * p.chunk_slots ? 2 : 3;
+      return 8 * sz > 7 * cs ? 0 : 8 * sz > 6 * cs ? 1 : 8 * sz > 5 * cs ? 2 : 3;
     };
+    const int P = int(gridDim.x);
     if (B <= 64) {
       // One wave, lane b for sequence b: the rank counts the sequences of lower classes (ballots)
       // and those of the same class before b (mbcnt); the job prefix is a wave scan.
       if (w == 0) {
         const bool ok = l < B;
         const SeqGeom g = seq_geom(p.indptr, p.length_info, B, ok ? l : B - 1, PS, p.sliding);
-        const int nch = chunks_used(g.n_slots, p.chunk_slots, p.num_chunks);
+        const int n = ok ? g.n_slots : 0;
+        int cs = p.chunk_slots;
+        if (p.auto_chunk)
+          cs = auto_chunk_slots(wave_sum_f(float(n)), __popcll(__ballot(n > 0)), wave_max(n), p.H_kv, P,
+                                p.chunk_slots, p.num_chunks, [&](int cc) {
+                                  return p.H_kv * wave_sum64(persist_chunks<PS>(n, cc, p.num_chunks));
+                                });
+        // the split merge kernel reads the chunk size after the job counters
+        if (p.auto_chunk && blockIdx.x == 0 && l == 0 && p.plan_word) *p.plan_word = cs;
+        const int nch = persist_chunks<PS>(n, cs, p.num_chunks);
         const int nj = nch * p.H_kv;
-        const int c = ok ? size_class(g.n_slots, nch) : 4;
+        const int c = ok ? size_class(n, nch, cs) : 4;
         int rank = 0;
         unsigned long long same = 0;
 #pragma unroll
@@ -336,7 +439,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         if (ok) {
           tab.njobs[l] = nj;
           tab.rgeo[rank] = make_int4(g.beg, g.np, g.total, g.win_off);
-          tab.rsb[rank] = make_int4(g.sink, l, nch, nch > 0 ? g.n_slots / nch : 0);
+          tab.rsb[rank] = make_int4(g.sink, l, nch, nch > 0 ? g.n_slots / kUnit / nch : 0);
           tab.rnj[rank] = nj;
           if constexpr (ROPE) tab.rpos[rank] = make_int2(p.q_pos[l], p.k_off[l]);
         }
@@ -356,14 +459,52 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       // scanned over the workgroup.
       const int per = (B + NT - 1) / NT;
       const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
-      unsigned long long cnt = 0;  // this thread's sequences per class, 16 bits each
+      // Sums over the workgroup (every thread calls them alike; s_scan64 is free again after).
+      auto block_sum = [&](long long x) {
+        x = wave_sum64(x);
+        if (l == 0) s_scan64[w] = static_cast<unsigned long long>(x);
+        __syncthreads();
+        long long t = 0;
+#pragma unroll
+        for (int ww = 0; ww < kPWaves; ++ww) t += static_cast<long long>(s_scan64[ww]);
+        __syncthreads();
+        return t;
+      };
+      long long n_sum = 0;
+      int n_seq = 0, n_max = 0;
       for (int b = b0; b < b1; ++b) {
         const SeqGeom g = seq_geom(p.indptr, p.length_info, B, b, PS, p.sliding);
         tab.geo[b] = make_int4(g.beg, g.np, g.total, g.win_off);
         tab.sink[b] = g.sink;
-        const int nch = chunks_used(g.n_slots, p.chunk_slots, p.num_chunks);
+        tab.njobs[b] = g.n_slots;  // replaced by the job count below
+        n_sum += g.n_slots;
+        n_seq += g.n_slots > 0;
+        n_max = max(n_max, g.n_slots);
+      }
+      int cs = p.chunk_slots;
+      if (p.auto_chunk) {
+        // the longest sequence: per-wave maxima through s_scan (block_sum's barriers order it)
+        const int wmax = wave_max(n_max);
+        if (l == 0) s_scan[w] = wmax;
+        const long long tot = block_sum(n_sum);  // its barriers order s_scan
+        int bmax = 0;
+#pragma unroll
+        for (int ww = 0; ww < kPWaves; ++ww) bmax = max(bmax, s_scan[ww]);
+        const long long nseq = block_sum(n_seq);
+        cs = auto_chunk_slots(float(tot), int(nseq), bmax, p.H_kv, P, p.chunk_slots, p.num_chunks, [&](int cc) {
+          long long x = 0;
+          for (int b = b0; b < b1; ++b) x += persist_chunks<PS>(tab.njobs[b], cc, p.num_chunks);
+          return p.H_kv * block_sum(x);
+        });
+        __syncthreads();  // s_scan is read above before the prefix below rewrites it
+        if (blockIdx.x == 0 && tid == 0 && p.plan_word) *p.plan_word = cs;  // for split_merge_kernel
+      }
+      unsigned long long cnt = 0;  // this thread's sequences per class, 16 bits each
+      for (int b = b0; b < b1; ++b) {
+        const int n = tab.njobs[b];
+        const int nch = persist_chunks<PS>(n, cs, p.num_chunks);
         tab.njobs[b] = nch * p.H_kv;
-        cnt += 1ull << (16 * size_class(g.n_slots, nch));
+        cnt += 1ull << (16 * size_class(n, nch, cs));
       }
       unsigned long long x = cnt;
 #pragma unroll
@@ -392,9 +533,9 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         const int n0 = (sk + PS - 1) / PS;
         const int n_slots = gg.y > 0 ? n0 + (gg.w < gg.z ? gg.y - gg.w / PS : 0) : 0;
         const int nch = tab.njobs[b] / p.H_kv;
-        const int rank = cls_start[size_class(n_slots, nch)]++;
+        const int rank = cls_start[size_class(n_slots, nch, cs)]++;
         tab.rgeo[rank] = gg;
-        tab.rsb[rank] = make_int4(sk, b, nch, nch > 0 ? n_slots / nch : 0);
+        tab.rsb[rank] = make_int4(sk, b, nch, nch > 0 ? n_slots / kUnit / nch : 0);
         tab.rnj[rank] = tab.njobs[b];
         if constexpr (ROPE) tab.rpos[rank] = make_int2(p.q_pos[b], p.k_off[b]);
       }
@@ -817,7 +958,9 @@ hipError_t launch_persist_k(const DecodeParams& p, long long max_jobs, hipStream
   const size_t lds = seq_table_bytes(p.B);
   const int resident = resident_workgroups(k, lds);
   if (resident <= 0) return hipErrorInvalidConfiguration;
-  const unsigned grid = static_cast<unsigned>((max_jobs < resident ? (max_jobs > 0 ? max_jobs : 1) : resident));
+  long long g = resident < kPersistMaxGrid ? resident : kPersistMaxGrid;
+  if (max_jobs < g) g = max_jobs > 0 ? max_jobs : 1;
+  const unsigned grid = static_cast<unsigned>(g);
   hipLaunchKernelGGL((decode_mfma_persist_kernel<KVT, D, PS, GP, ROPE, FUSED, MT, ILV>), dim3(grid),
                      dim3(64 * kPWaves), lds, st, p);
   return hipGetLastError();

@@ -27,11 +27,14 @@ struct DecodeParams {
   const float* v_scale;
   void* out;
   float* lse;
-  float* part_o;             // split-KV partial outputs [B, H_qo, num_chunks, D] (normalised)
-  float* part_lse;           // split-KV partial lse [B, H_qo, num_chunks]
+  float* part_o;             // split-KV partial outputs [B, T, H_qo, num_chunks, D] (normalised)
+  float* part_lse;           // split-KV partial lse [B, T, H_qo, num_chunks]
   int* counters;             // split-KV arrival counters [B, H_kv]; zero between calls
   int* queue;                // persistent schedule: [0] next job ticket, [1] workgroups done;
                              // zero between calls
+  int* plan_word;            // automatic persistent plan: the call's chunk size, written by the
+                             // decode kernel's workgroup 0 for the split merge kernel (the word
+                             // after the partial lse; need not be zero)
   const void* new_k;         // fused append: the step's K and V rows [B, H_kv, D] (bf16), written
   const void* new_v;         // to each sequence's last position; null: attention only
   void* pages_w;             // fused append: the pool (the same memory as pages)
@@ -43,8 +46,10 @@ struct DecodeParams {
   int32_t sliding, rotary;
   float rope_scale, rope_theta;
   float score_scale;         // sm_scale * log2(e): scores are kept in log2 units
-  int32_t chunk_slots;       // page slots per chunk
+  int32_t chunk_slots;       // page slots per chunk (automatic persistent plan: the least chunk)
   int32_t num_chunks;        // chunks in the grid; the last one takes every remaining slot
+  int32_t auto_chunk;        // persistent schedule: 1 = the chunk size is chosen on the device
+                             // from the call's lengths
 };
 
 // Learned attention sink of one q head (logit sink2 in log2 units) folded into a finished state

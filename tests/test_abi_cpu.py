@@ -114,14 +114,19 @@ def test_plan_and_workspace(L):
     assert nc == 5 and cp * 5 >= 4096 // 16
     ws = pk.workspace_bytes(d)
     assert ws >= 4 * 32 * 5 * (128 + 1) * 4 and ws % 256 == 0
-    # automatic plan: chunks of at least 256 rows, sized so the grid has about 2048 workgroups
-    cp, nc = pk.plan(desc(batch=2, max_kv_len=131072))
-    assert nc > 1 and cp * 16 >= 256 and cp * nc * 16 >= 131072
-    cp, nc = pk.plan(desc(batch=1, num_qo_heads=4, num_kv_heads=1, max_kv_len=64))
-    assert nc == 1
-    cp, nc = pk.plan(desc())
+    # automatic plan of the persistent schedule: the chunk size is chosen on the device at each
+    # call (reported as 0); a sequence takes at most ceil(4096 / (B H_kv)) chunks (at least 2; at
+    # most 8 for 8 q heads per KV head when B H_kv >= 256), whatever the length hint, so
+    # max_kv_len = 0 plans exactly as a tight hint does
+    assert pk.plan(desc(batch=2, max_kv_len=131072)) == (0, 256)
+    assert pk.plan(desc(batch=1, num_qo_heads=4, num_kv_heads=1, max_kv_len=64)) == (0, 4096)
+    assert pk.plan(desc(batch=32)) == (0, 16)
+    assert pk.plan(desc(batch=32, num_qo_heads=64)) == (0, 8)
+    assert pk.plan(desc(batch=256, num_qo_heads=64)) == (0, 2)
     ws = pk.workspace_bytes(desc())
-    assert ws >= 4 * 32 * nc * (128 + 1) * 4 + 4 * 8 * 4 and ws % 256 == 0
+    assert ws >= 4 * 32 * 128 * (128 + 1) * 4 + (4 * 8 + 2) * 4 and ws % 256 == 0
+    assert pk.workspace_bytes(desc(max_kv_len=0)) == ws == pk.workspace_bytes(desc(max_kv_len=64))
+    assert pk.workspace_bytes_multi(desc(), 4) >= 4 * 4 * 32 * 128 * (128 + 1) * 4
     # fp32 / fp8 KV: chunks of at least 256 rows; long contexts split, tiny ones do not
     cp, nc = pk.plan(desc(q_dtype="f32", kv_dtype="f32", batch=2, max_kv_len=131072))
     assert nc > 1 and cp * 16 >= 256

@@ -423,6 +423,22 @@ def test_full_size_config(name):
         assert np.abs(gu.to_np64(lse) - gu.to_np64(l1)).max() <= 1e-3
 
 
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "fp8_gqa8"])
+def test_no_length_hint(name):
+    """max_kv_len = 0 (no length hint): the persistent schedule sizes its chunks on the device from
+    the call's lengths, so the call is bit-identical to the one with a tight hint (and as fast);
+    every output against the oracle."""
+    w = synth.CONFIGS[name]()
+    dev = gu.upload(w)
+    out0, lse0 = gu.run_attention(w, dev, max_kv_len=0)
+    out1, lse1 = gu.run_attention(w, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(out0.view(torch.uint8), out1.view(torch.uint8))
+    assert torch.equal(lse0, lse1)
+    if name == "llama3_8b_bf16":
+        check(w, out0, lse0, label=name + " no hint")
+
+
 def test_fp8_unit_sigma():
     """fp8 KV whose dequantised K and V have sigma near 1 (scales ~ U[0.9, 1.1] / 112 on payloads
     drawn as N(0, 1) * 112): outputs and scores of the size the bf16 workloads have, at the fp8
@@ -501,8 +517,8 @@ def test_batch_sizes_around_schedule_limits(B):
 
 @pytest.mark.parametrize("splits", [4, 8, 9])
 def test_split_counters_reset_across_calls(splits):
-    """Split sequences merged inside the persistent kernel (up to 8 chunks) or by the merge
-    kernel (more): the arrival counters and the job queue are back at zero after every call, so
+    """Split sequences merged inside the persistent kernel (up to 8 chunks in one round trip,
+    more in several): the arrival counters and the job queue are back at zero after every call, so
     repeated calls on one workspace give identical results, and a smaller batch reusing the
     workspace is exact too."""
     lens = np.random.default_rng(500 + splits).integers(300, 3000, size=12)
@@ -694,7 +710,7 @@ def test_append_attention(kv, G, D, ps):
 
 @pytest.mark.parametrize("splits", [3, 12])
 def test_append_attention_split(splits):
-    """Forced splits: merged in the kernel (3 chunks) and by the split merge kernel (12)."""
+    """Forced splits (3 and 12 chunks), merged in the kernel."""
     w = synth.make_workload(name=f"fused_split{splits}", B=4, H_qo=16, H_kv=4, D=128,
                             page_size=16, seq_lens=[3000, 17, 1200, 640], seed=720 + splits,
                             max_num_pages=512)
@@ -777,8 +793,8 @@ def test_attention_multi(kv, G, T, D, ps):
 
 @pytest.mark.parametrize("splits", [3, 12])
 def test_attention_multi_split(splits):
-    """Forced splits with two tokens: merged in the kernel (3 chunks) and by the split merge kernel
-    (12), including chunks where the first token sees no row."""
+    """Forced splits with two tokens (3 and 12 chunks), merged in the kernel, including chunks
+    where the first token sees no row."""
     w = synth.make_workload(name=f"multi_split{splits}", B=4, H_qo=16, H_kv=4, D=128,
                             page_size=16, seq_lens=[3000, 17, 1200, 641], seed=820 + splits,
                             max_num_pages=512)
@@ -787,8 +803,8 @@ def test_attention_multi_split(splits):
 
 @pytest.mark.parametrize("splits", [0, 4, 13])
 def test_attention_multi_sixteen_columns_split(splits):
-    """Four tokens on the Llama-3-8B group (16 columns) with forced splits merged by the split
-    merge kernel."""
+    """Four tokens on the Llama-3-8B group (16 columns): automatic plan and forced splits, merged
+    in the kernel."""
     w = synth.make_workload(name=f"multi16_split{splits}", B=5, H_qo=16, H_kv=4, D=128,
                             page_size=16, seq_lens=[3000, 3, 1200, 641, 4], seed=840 + splits,
                             max_num_pages=512)
@@ -813,7 +829,7 @@ def test_attention_multi_sixteen_columns_split(splits):
 def test_attention_multi_rope(kv, G, T, D, ps, splits, rot):
     """RoPE with several tokens (rotate-half, or interleaved for rot = 2): token t's query at
     q_rope_position + t (oracle reading), Llama-3 base; lengths around page boundaries, tokens
-    with no row, split sequences merged by the split merge kernel."""
+    with no row, split sequences."""
     lens = [1, T - 1, ps, ps + 1, 3 * ps - 1, 2500, 0, 2 * ps + T]
     w = synth.make_workload(name=f"multi_rope{rot}_{kv}_G{G}_T{T}_D{D}_ps{ps}_s{splits}",
                             B=len(lens), H_qo=2 * G, H_kv=2, D=D, page_size=ps, seq_lens=lens,
@@ -876,8 +892,8 @@ def _sink_case(w, sinks, num_kv_splits=0, T=1):
                                             ("bf16", 1, 32, 2)])
 def test_learned_sink(kv, G, ps, splits):
     """Per-q-head sink logits, including one that dwarfs the scores (out ~ 0) and one far below
-    them (no effect), against the oracle's fold of the sink into the finished state; unsplit,
-    merged in the kernel (3 chunks) and by the split merge kernel (12); an empty sequence keeps
+    them (no effect), against the oracle's fold of the sink into the finished state; unsplit and
+    split (3 and 12 chunks, the sink folded once at the merge); an empty sequence keeps
     out = 0, lse = -5e4."""
     lens = [1, 300, 2000, 0, 5 * ps + 3]
     w = synth.make_workload(name=f"sink_{kv}_G{G}_ps{ps}_s{splits}", B=len(lens), H_qo=2 * G,
@@ -948,8 +964,8 @@ def test_rope_interleaved_unsupported_where_not_built():
 @pytest.mark.parametrize("kv,splits", [("bf16", 2), ("bf16", 5), ("bf16", 8), ("fp8", 3),
                                        ("fp8", 8), ("bf16", 9)])
 def test_forced_splits_eight_heads(kv, splits):
-    """8 q heads per KV head: up to 8 chunks are merged inside the persistent kernel (the 4-head
-    and narrower kernels leave them to the split merge kernel), 9 go to the split merge kernel."""
+    """8 q heads per KV head, forced splits: up to 8 chunks are merged in one round trip of loads,
+    9 in two."""
     lens = [5000, 1, 700, 2100, 33, 4096]
     w = synth.make_workload(name=f"g8_splits{splits}_{kv}", B=len(lens), H_qo=16, H_kv=2, D=128,
                             page_size=16 if kv == "bf16" else 32, seq_lens=lens, q_dtype="bf16",

@@ -61,7 +61,7 @@ def _check(w, splits=0):
 
 
 def test_noalloc_two_calls_second_smaller():
-    """The Llama-3-8B-shaped workload (split sequences, merge kernel), then a smaller batch with
+    """The Llama-3-8B-shaped workload (split sequences), then a smaller batch with
     more KV heads per q head and forced splits: the second call finds the first one's partial
     states in the scratch and must not be disturbed by them."""
     _check(synth.CONFIGS["llama3_8b_bf16"]())
