@@ -36,7 +36,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed calls first (a cold GPU takes on the order of a hundred calls "
+                         "of the larger workloads to reach its steady rate)")
     ap.add_argument("--sets", type=int, default=4, help="independent input sets cycled per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -57,6 +59,8 @@ def parse():
     ap.add_argument("--qo-len", type=int, default=2, help="query tokens per sequence (--op multi)")
     ap.add_argument("--multi-rope", action="store_true",
                     help="--op multi: rotate-half RoPE (base 5e5), token t at position L - T + t")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling sweep (profiler runs)")
     ap.add_argument("--ceiling", action="store_true",
                     help="instead of the decode, print the streaming-read ceiling sweep (every "
                          "launch shape of pdecode_bench_stream_read over a 2 GiB buffer, and a "
@@ -481,7 +485,7 @@ def main():
     achieved = kv_bytes / avg_call_s / 1e9
     cp, nc = pk.plan(desc)
 
-    ceiling = measure_ceiling(step_bytes=kv_bytes)
+    ceiling = None if args.no_ceiling else measure_ceiling(step_bytes=kv_bytes)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -519,8 +523,8 @@ def main():
                      "kernel": ("pdecode_attention: one launch of the persistent decode kernel, "
                                 "which also merges the split sequences"),
                      "avg_launch_us": round(avg_call_s * 1e6, 3),
-                     "ceiling_GBps": ceiling["GBps"],
-                     "frac_of_ceiling": round(achieved / ceiling["GBps"], 4),
+                     "ceiling_GBps": ceiling["GBps"] if ceiling else None,
+                     "frac_of_ceiling": round(achieved / ceiling["GBps"], 4) if ceiling else None,
                      "ceiling": ceiling,
                      "single_call_event_us_p10": round(float(np.percentile(call_ms, 10)) * 1e3, 3),
                      "single_call_event_us_p90": round(float(np.percentile(call_ms, 90)) * 1e3, 3)},
@@ -529,18 +533,35 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, budget_s):
-    """The oracle on the host, on a bounded sample of (sequence, q head) outputs of the same
-    workload; reported in KV GB/s over the KV bytes the sample reads."""
-    import numpy as np
+# Host threads for the oracle leg: every CPU this process may run on, up to the 16 that one GPU's
+# share of the host is (the GPU hosts give each GPU 16 CPUs and set OMP_NUM_THREADS to match).
+HOST_THREAD_SHARE = 16
 
-    import oracle
+
+def host_threads():
     cores = os.cpu_count() or 1
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         pass
-    cores = min(cores, 16)
+    return max(1, min(cores, HOST_THREAD_SHARE))
+
+
+def cpu_baseline(w, budget_s, threads=None):
+    """The oracle on the host, on a bounded sample of (sequence, q head) outputs of the same
+    workload; reported in KV GB/s over the KV bytes the sample reads. threads: host threads
+    (default: host_threads()); a second, shorter run on one thread is reported beside it."""
+    out = _cpu_baseline_run(w, budget_s, threads or host_threads())
+    one = _cpu_baseline_run(w, max(2.0, budget_s / 3), 1)
+    out["single_thread"] = {k: one[k] for k in ("value", "unit", "cores", "seconds",
+                                                 "us_per_step", "sample")}
+    return out
+
+
+def _cpu_baseline_run(w, budget_s, cores):
+    import numpy as np
+
+    import oracle
     rng = np.random.default_rng(0)
     G = w.H_qo // w.H_kv
     groups = np.array([(b, h) for b in range(w.B) for h in range(w.H_kv)], np.int32)

@@ -15,8 +15,8 @@
 //    from the page table. The job after the current one is fetched, decoded and its page ids and q
 //    loaded while the current one streams, and its first page is in flight before the current
 //    job's last page is computed, so a workgroup's load stream does not stop at job boundaries.
-//    In the single-token 8-column instantiations, when the call has at most kInMergeChunks chunks
-//    per sequence, the workgroup whose waves complete a split sequence's count of arrivals merges
+//    In the single-token instantiations, when the call has at most kInMergeChunks chunks per
+//    sequence, the workgroup whose waves complete a split sequence's count of arrivals merges
 //    it at the end of its next job (each wave arrives once its own partial stores are known
 //    complete, a pair of items into the next job, so no wait falls on the load stream); otherwise
 //    a second, row-parallel kernel (split_merge_kernel) merges them (merges_in_kernel). The chunk

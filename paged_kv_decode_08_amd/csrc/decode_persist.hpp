@@ -110,6 +110,11 @@ __device__ __forceinline__ float wave_sum_f(float x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
 __device__ __forceinline__ int wave_max(int x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
@@ -261,16 +266,19 @@ __device__ void append_last_row(const DecodeParams& p, int b) {
   }
 }
 
-// Split sequences of calls with at most this many chunks per sequence are merged inside the
-// persistent kernel by its single-token 8-column instantiations (8 q heads per KV head); the
-// others leave every split sequence to split_merge_kernel. Measured on the same box: with 4
-// columns the separate merge kernel was faster (Llama-3-8B shape 62.5-62.8 against 63.8-65.8 us
-// with 4 chunks), and so it was with 4 q heads x 2 tokens (75.1 against 78.6-78.8 us); with 8
-// heads the in-kernel merge was (bf16 and fp8 8-head shapes, 2-4 us and 3-8 us).
+// Split sequences of calls with at most this many chunks per sequence (the plan's cap) are merged
+// inside the persistent kernel by its single-token instantiations; with a larger cap, and with
+// several query tokens, every split sequence goes to split_merge_kernel. Measured on the same box:
+// where sequences do split, the separate kernel was faster for 4 q columns (Llama-3-8B shape with
+// the cap forced to 8: 61.8 against 63.4 us) and the in-kernel merge for 8 (0.6-4 us on the bf16
+// and fp8 8-head shapes), and so it was with 4 q heads x 2 tokens (75.1 against 78.6 us). Where
+// the automatic plan splits nothing (one job per workgroup) the second launch alone costs about
+// 4 us (RoPE + window shape: 165.4 against 169.0 us), so a cap of at most 8 merges in the kernel
+// at any width.
 constexpr int kInMergeChunks = 8;
 template <int GP>
 constexpr bool merges_in_kernel(int num_chunks, bool several_tokens) {
-  return GP == 8 && !several_tokens && num_chunks <= kInMergeChunks;
+  return GP <= 8 && !several_tokens && num_chunks <= kInMergeChunks;
 }
 
 // Output row of q column c of (sequence b, KV head h): columns are token-major (token c / G, q
@@ -483,20 +491,31 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       }
       int cs = p.chunk_slots;
       if (p.auto_chunk) {
-        // the longest sequence: per-wave maxima through s_scan (block_sum's barriers order it)
+        // totals over the workgroup in one barrier: per-wave fp32 sum and sequence count in
+        // s_scan64, maximum in s_scan
+        const float wsum = wave_sum_f(float(n_sum));
+        const int wcnt = wave_sum_i(n_seq);
         const int wmax = wave_max(n_max);
-        if (l == 0) s_scan[w] = wmax;
-        const long long tot = block_sum(n_sum);  // its barriers order s_scan
-        int bmax = 0;
+        if (l == 0) {
+          s_scan64[w] = (static_cast<unsigned long long>(static_cast<uint32_t>(wcnt)) << 32) |
+                        __float_as_uint(wsum);
+          s_scan[w] = wmax;
+        }
+        __syncthreads();
+        float tot = 0.f;
+        int bmax = 0, nseq = 0;
 #pragma unroll
-        for (int ww = 0; ww < kPWaves; ++ww) bmax = max(bmax, s_scan[ww]);
-        const long long nseq = block_sum(n_seq);
-        cs = auto_chunk_slots(float(tot), int(nseq), bmax, p.H_kv, P, p.chunk_slots, p.num_chunks, [&](int cc) {
+        for (int ww = 0; ww < kPWaves; ++ww) {
+          tot += __uint_as_float(static_cast<uint32_t>(s_scan64[ww]));
+          nseq += static_cast<int>(s_scan64[ww] >> 32);
+          bmax = max(bmax, s_scan[ww]);
+        }
+        __syncthreads();  // s_scan64 is free again (block_sum below)
+        cs = auto_chunk_slots(tot, nseq, bmax, p.H_kv, P, p.chunk_slots, p.num_chunks, [&](int cc) {
           long long x = 0;
           for (int b = b0; b < b1; ++b) x += persist_chunks<PS>(tab.njobs[b], cc, p.num_chunks);
           return p.H_kv * block_sum(x);
         });
-        __syncthreads();  // s_scan is read above before the prefix below rewrites it
         if (blockIdx.x == 0 && tid == 0 && p.plan_word) *p.plan_word = cs;  // for split_merge_kernel
       }
       unsigned long long cnt = 0;  // this thread's sequences per class, 16 bits each
@@ -748,7 +767,19 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::NLOADS));
     };
     // Issues the loads of item `k`'s 16 rows (k % SUB selects the rows in the page).
-    auto issue_id = [&](Buf& nxt, int raw, int hh, int k) __attribute__((always_inline)) {
+    // Items are computed in pairs, so a wave with an odd number of items in a job loads one more
+    // that it does not compute, and after its last job a wave loads one item that no job uses.
+    // Those padding items read a fixed block (page 0, KV head 0), which stays in L2, instead of
+    // re-reading a page of the job: with non-temporal K/V loads that page has usually left L2 by
+    // then, and the re-read went to HBM (about 12 MB per call on the Llama-3-8B shape: 0.9 us). A
+    // wave without slots keeps reading the chunk's first page, which wave 0 loads at the same
+    // time (on the fp8 GQA-8 shape, where most short chunks leave three waves idle, the fixed block
+    // there was about 1 us slower).
+    auto pad_item = [&](const Job& JJ, int k) __attribute__((always_inline)) {
+      return JJ.nw > 0 && k / SUB >= JJ.nw;
+    };
+    auto issue_id = [&](Buf& nxt, int raw, int hh, int k, bool pad = false) __attribute__((always_inline)) {
+      if (pad) raw = hh = 0;
       core.issue(nxt, block_of(clamp_page(p, uni(raw)), uni(hh)) + (k % SUB) * 16 * C::ROW,
                  kv_stride);
     };
@@ -780,13 +811,13 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         if constexpr (FUSED) new_words(J1, nw1);
         int ticket_raw = 0;
         if (last && J1.valid && tid == 0) ticket_raw = atomicAdd(queue, 1);
-        issue_id(buf1, item_id(1), J.h, 1);
+        issue_id(buf1, item_id(1), J.h, 1, pad_item(J, 1));
         // no wait after item 0: the next job's ids and q words were issued with item 1, and
         // waiting for them here would leave only item 1 in flight while they arrive
         process_item(buf0, 0);
-        if (!last) issue_id(buf0, item_id(2), J.h, 2);
+        if (!last) issue_id(buf0, item_id(2), J.h, 2, pad_item(J, 2));
         else if (J1.valid) issue_id(buf0, __builtin_amdgcn_readlane(ids_n, 0), J1.h, 0);
-        else issue_id(buf0, item_id(1), J.h, 1);
+        else issue_id(buf0, item_id(1), J.h, 1, true);
         compute(buf1, 1);
         // the previous job's partial stores are older than the loads just waited for; the
         // arrival's result is read at the end of this job
@@ -801,9 +832,9 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       }
       // ---- items 2 .. nitems - 3
       for (int k = 2; k + 2 < J.nitems; k += 2) {
-        issue_id(buf1, item_id(k + 1), J.h, k + 1);
+        issue_id(buf1, item_id(k + 1), J.h, k + 1, pad_item(J, k + 1));
         compute(buf0, k);
-        issue_id(buf0, item_id(k + 2), J.h, k + 2);
+        issue_id(buf0, item_id(k + 2), J.h, k + 2, pad_item(J, k + 2));
         compute(buf1, k + 1);
       }
       // ---- the last pair takes the ticket and issues the next job's first item
@@ -811,10 +842,10 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         const int k = J.nitems - 2;
         int ticket_raw = 0;
         if (J1.valid && tid == 0) ticket_raw = atomicAdd(queue, 1);
-        issue_id(buf1, item_id(k + 1), J.h, k + 1);
+        issue_id(buf1, item_id(k + 1), J.h, k + 1, pad_item(J, k + 1));
         compute(buf0, k);
         if (J1.valid) issue_id(buf0, s_ids[par ^ 1][w][0], J1.h, 0);
-        else issue_id(buf0, item_id(k + 1), J.h, k + 1);
+        else issue_id(buf0, item_id(k + 1), J.h, k + 1, true);
         compute(buf1, k + 1);
         if (tid == 0) s_ticket = 2 * int(gridDim.x) + ticket_raw;
       }
