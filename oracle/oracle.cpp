@@ -171,6 +171,8 @@ struct DecodeArgs {
   float sm_scale;
   const float* k_scale;
   const float* v_scale;
+  const float* k_scale_page;  // [max_num_pages, H_kv] or null: per (page, KV head) scales
+  const float* v_scale_page;
 };
 
 // Index of element (page, kv, head, off, dim) in the pages[P, 2, H_kv, ps, D] pool.
@@ -212,8 +214,14 @@ int decode_one(const DecodeArgs& a, int b, int h_qo, double* out, double* lse) {
   const bool rope = a.rotary_mode == 1 || a.rotary_mode == 2;
   const bool ilv = a.rotary_mode == 2;
   if (rope) rope_rotate(qv.data(), D, a.q_rope_position[b], a.rope_scale, a.rope_theta, ilv);
-  const double kscale = is_fp8(a.kv_dtype) ? static_cast<double>(a.k_scale[h]) : 1.0;
-  const double vscale = is_fp8(a.kv_dtype) ? static_cast<double>(a.v_scale[h]) : 1.0;
+  // fp8 pool: a stored value is code * scale, the scale of the row's KV head, or of its
+  // (page, KV head) block when per-page scales are given (they replace the per-head ones)
+  const bool per_page = is_fp8(a.kv_dtype) && a.k_scale_page != nullptr;
+  auto scale_of = [&](const float* per_head, const float* per_page_tab, int64_t page) -> double {
+    if (!is_fp8(a.kv_dtype)) return 1.0;
+    if (per_page) return static_cast<double>(per_page_tab[page * a.H_kv + h]);
+    return static_cast<double>(per_head[h]);
+  };
 
   auto locate = [&](int64_t r, int64_t* page, int* off) -> int {
     int64_t pos = (r < sink) ? r : r - sink + win_off;
@@ -231,6 +239,7 @@ int decode_one(const DecodeArgs& a, int b, int h_qo, double* out, double* lse) {
     int64_t page;
     int off;
     if (int rc = locate(r, &page, &off)) return rc;
+    const double kscale = scale_of(a.k_scale, a.k_scale_page, page);
     for (int d = 0; d < D; ++d)
       kv[d] = load_value(a.pages, a.kv_dtype, pool_index(a, page, 0, h, off, d)) * kscale;
     if (rope) rope_rotate(kv.data(), D, static_cast<double>(a.k_rope_pos_offset[b]) + r,
@@ -249,6 +258,7 @@ int decode_one(const DecodeArgs& a, int b, int h_qo, double* out, double* lse) {
     if (int rc = locate(r, &page, &off)) return rc;
     double w = std::exp(scores[r] - M);
     Z += w;
+    const double vscale = scale_of(a.v_scale, a.v_scale_page, page);
     for (int d = 0; d < D; ++d)
       acc[d] += w * load_value(a.pages, a.kv_dtype, pool_index(a, page, 1, h, off, d)) * vscale;
   }
@@ -282,15 +292,19 @@ int32_t oracle_decode(int32_t B, int32_t H_qo, int32_t H_kv, int32_t D, int32_t 
                       const int32_t* length_info, int32_t sliding_window, int32_t rotary_mode,
                       float rope_scale, float rope_theta, const int32_t* q_rope_position,
                       const int32_t* k_rope_pos_offset, float sm_scale, const float* k_scale,
-                      const float* v_scale, int32_t n_sel, const int32_t* sel, double* out,
-                      double* lse, int32_t nthreads) {
+                      const float* v_scale, const float* k_scale_page, const float* v_scale_page,
+                      int32_t n_sel, const int32_t* sel, double* out, double* lse,
+                      int32_t nthreads) {
   if (B < 0 || H_kv <= 0 || H_qo <= 0 || H_qo % H_kv != 0 || D <= 0 || D % 2 != 0 || ps <= 0)
     return 4;
   if (elem_bytes(q_dtype) == 0 || elem_bytes(kv_dtype) == 0) return 4;
-  if (is_fp8(kv_dtype) && (k_scale == nullptr || v_scale == nullptr)) return 4;
+  if ((k_scale_page == nullptr) != (v_scale_page == nullptr)) return 4;
+  if (is_fp8(kv_dtype) && k_scale_page == nullptr && (k_scale == nullptr || v_scale == nullptr))
+    return 4;
   DecodeArgs a{B, H_qo, H_kv, D, ps, max_num_pages, q_dtype, kv_dtype, q, pages, indptr, values,
                nnz, length_info, sliding_window, rotary_mode, rope_scale, rope_theta,
-               q_rope_position, k_rope_pos_offset, sm_scale, k_scale, v_scale};
+               q_rope_position, k_rope_pos_offset, sm_scale, k_scale, v_scale, k_scale_page,
+               v_scale_page};
   const int64_t n = n_sel > 0 ? n_sel : static_cast<int64_t>(B) * H_qo;
   std::atomic<int64_t> next{0};
   std::atomic<int32_t> status{0};
@@ -330,18 +344,21 @@ void oracle_merge_state(int32_t N, int32_t H, int32_t D, double* v, double* s,
 
 // KV append: for token t with slot s >= 0, page = s / ps, off = s % ps, and every head h:
 // pages[page, 0, h, off, :] = k[t, h, :], pages[page, 1, h, off, :] = v[t, h, :].
-// Same dtype: the bits are copied. fp8 pool: the element is divided by its head's scale in fp32
-// and encoded to e4m3fn (nearest, ties to even, saturating). Returns 0, or 2 for a slot whose page
-// is out of range, 4 for bad arguments.
+// Same dtype: the bits are copied. fp8 pool: the element is divided by its head's scale (or its
+// (page, head) block's scale when per-page scales are given) in fp32 and encoded to e4m3fn
+// (nearest, ties to even, saturating). Returns 0, or 2 for a slot whose page is out of range, 4
+// for bad arguments.
 int32_t oracle_append_kv(int32_t T, int32_t H_kv, int32_t D, int32_t ps, int32_t max_num_pages,
                          int32_t in_dtype, int32_t kv_dtype, const void* new_k, const void* new_v,
                          const int32_t* slots, const float* k_scale, const float* v_scale,
-                         void* pages) {
+                         const float* k_scale_page, const float* v_scale_page, void* pages) {
   if (T < 0 || H_kv <= 0 || D <= 0 || ps <= 0) return 4;
   const int ib = elem_bytes(in_dtype), kb = elem_bytes(kv_dtype);
   if (ib == 0 || kb == 0) return 4;
   if (!is_fp8(kv_dtype) && in_dtype != kv_dtype) return 4;
-  if (is_fp8(kv_dtype) && (is_fp8(in_dtype) || !k_scale || !v_scale)) return 4;
+  if ((k_scale_page == nullptr) != (v_scale_page == nullptr)) return 4;
+  if (is_fp8(kv_dtype) && (is_fp8(in_dtype) || (!k_scale_page && (!k_scale || !v_scale))))
+    return 4;
   for (int t = 0; t < T; ++t) {
     int64_t s = slots[t];
     if (s < 0) continue;
@@ -355,7 +372,8 @@ int32_t oracle_append_kv(int32_t T, int32_t H_kv, int32_t D, int32_t ps, int32_t
           size_t di = ((((static_cast<size_t>(page) * 2 + kv) * H_kv + h) * ps + off) * D) + d;
           if (is_fp8(kv_dtype)) {
             float x = static_cast<float>(load_value(src, in_dtype, si));
-            float sc = kv == 0 ? k_scale[h] : v_scale[h];
+            const float* tab = kv == 0 ? k_scale_page : v_scale_page;
+            float sc = tab ? tab[page * H_kv + h] : (kv == 0 ? k_scale[h] : v_scale[h]);
             static_cast<uint8_t*>(pages)[di] =
                 kv_dtype == DT_FP8 ? fp8_encode(x / sc) : fp8_e4m3_encode(x / sc);
           } else {

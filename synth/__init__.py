@@ -87,6 +87,9 @@ class Workload:
     k_scale: np.ndarray | None
     v_scale: np.ndarray | None
     used_pages: np.ndarray        # int32 ids of pages holding data
+    # fp8 pools with per-(page, KV head) scales [max_num_pages, H_kv] (replace k_scale / v_scale)
+    k_scale_page: np.ndarray | None = None
+    v_scale_page: np.ndarray | None = None
 
     @property
     def kv_bytes(self) -> int:
@@ -102,20 +105,23 @@ class Workload:
                     rotary_mode=self.rotary_mode, rope_scale=self.rope_scale,
                     rope_theta=self.rope_theta, q_rope_position=self.q_rope_position,
                     k_rope_pos_offset=self.k_rope_pos_offset, sm_scale=self.sm_scale,
-                    k_scale=self.k_scale, v_scale=self.v_scale)
+                    k_scale=self.k_scale, v_scale=self.v_scale, k_scale_page=self.k_scale_page,
+                    v_scale_page=self.v_scale_page)
 
 
 def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_num_pages=None,
                   q_dtype="bf16", kv_dtype="bf16", seed=0, sm_scale=None, window=None, sink=0,
                   rotary_mode=0, rope_theta=1e4, rope_scale=1.0, q_rope_position=None,
                   k_rope_pos_offset=None, page_order="shuffled", kv_sigma=1.0,
-                  fp8_payload_sigma=112.0, scale_range=(0.5 / 448, 2.0 / 448)) -> Workload:
+                  fp8_payload_sigma=112.0, scale_range=(0.5 / 448, 2.0 / 448),
+                  page_scales=False) -> Workload:
     """Draws a workload. seq_lens: total tokens per sequence (0 = empty sequence).
     window: None (length_info [B]) or W (length_info [3, B]: last_page_len, max(sink', L - W),
     sink') with sink' = min(sink, L).
     page_order: 'shuffled' (a seeded permutation of the pool, consecutive slices per sequence) or
     'identity' (pages 0, 1, 2, ... in order). fp8 KV: payload codes are fp8(clip(N(0,1) *
-    fp8_payload_sigma, +-448)); per-KV-head scales ~ U[scale_range]."""
+    fp8_payload_sigma, +-448)); per-KV-head scales ~ U[scale_range], and with page_scales a scale
+    per (page, KV head) ~ U[scale_range] as well (for every page of the pool)."""
     seq_lens = np.asarray(seq_lens, np.int64)
     assert seq_lens.shape == (B,)
     ps = page_size
@@ -150,6 +156,12 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
         rng_sc = _rng(seed, 4)
         k_scale = rng_sc.uniform(*scale_range, size=H_kv).astype(np.float32)
         v_scale = rng_sc.uniform(*scale_range, size=H_kv).astype(np.float32)
+    k_scale_page = v_scale_page = None
+    if page_scales:
+        assert kv_dtype in ("fp8", "fp8e4m3"), "per-page scales are for fp8 pools"
+        rng_ps = _rng(seed, 5)
+        k_scale_page = rng_ps.uniform(*scale_range, size=(max_num_pages, H_kv)).astype(np.float32)
+        v_scale_page = rng_ps.uniform(*scale_range, size=(max_num_pages, H_kv)).astype(np.float32)
     CH = 512
 
     def fill(i):
@@ -188,7 +200,8 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
                     rope_scale=float(rope_scale), rope_theta=float(rope_theta),
                     q_rope_position=np.asarray(q_rope_position, np.int32),
                     k_rope_pos_offset=np.asarray(k_rope_pos_offset, np.int32),
-                    sm_scale=float(sm_scale), k_scale=k_scale, v_scale=v_scale, used_pages=order)
+                    sm_scale=float(sm_scale), k_scale=k_scale, v_scale=v_scale, used_pages=order,
+                    k_scale_page=k_scale_page, v_scale_page=v_scale_page)
 
 
 # The five benchmark workloads. Their sizes follow the decode settings the pages describe

@@ -33,8 +33,15 @@ def contiguous_kv(w, b, h):
     K = blk[:, 0, h].reshape(-1, w.D)[:total]
     V = blk[:, 1, h].reshape(-1, w.D)[:total]
     if w.kv_dtype in ("fp8", "fp8e4m3"):
-        K = K * float(w.k_scale[h])
-        V = V * float(w.v_scale[h])
+        if getattr(w, "k_scale_page", None) is not None:
+            # row r of the flattened cache sits on page r // ps of the sequence
+            ks = np.repeat(w.k_scale_page[pages, h].astype(np.float64), w.page_size)[:total]
+            vs = np.repeat(w.v_scale_page[pages, h].astype(np.float64), w.page_size)[:total]
+            K = K * ks[:, None]
+            V = V * vs[:, None]
+        else:
+            K = K * float(w.k_scale[h])
+            V = V * float(w.v_scale[h])
     return K, V
 
 

@@ -854,3 +854,79 @@ def test_fp8_e4m3_pool_matches_dense_bruteforce():
             o, l = dense_attention(q64[b, hq], K, V, w.sm_scale)
             np.testing.assert_allclose(out[b, hq], o, rtol=0, atol=1e-12)
             assert abs(lse[b, hq] - l) < 1e-12
+
+
+# ---------------------------------------------------------------- fp8 pools with per-page scales
+# A scale per (page, KV head) block, in place of one per KV head: a stored value is still code x
+# scale, with the scale of the block that holds the row.
+@pytest.mark.parametrize("kv_dtype", ["fp8", "fp8e4m3"])
+@pytest.mark.parametrize("window", [None, 5])
+def test_page_scales_match_dense_bruteforce(kv_dtype, window):
+    """Paged oracle == textbook attention over the flattened cache, each row dequantised with its
+    own page's scale (sequences span pages of different scales; with a window and a sink the
+    attended rows skip pages)."""
+    w = small(kv_dtype=kv_dtype, q_dtype="bf16", page_scales=True, seq_lens=[7, 1, 13],
+              window=window, sink=2 if window else 0)
+    out, lse = run_oracle(w)
+    G = w.H_qo // w.H_kv
+    q64 = to_f64(w.q, w.q_dtype)
+    for b in range(w.B):
+        for hq in range(w.H_qo):
+            K, V = contiguous_kv(w, b, hq // G)
+            if window:
+                off, sink = int(w.length_info[1, b]), int(w.length_info[2, b])
+                rows = np.r_[0:sink, off:int(w.seq_lens[b])]
+                K, V = K[rows], V[rows]
+            o, l = dense_attention(q64[b, hq], K, V, w.sm_scale)
+            np.testing.assert_allclose(out[b, hq], o, rtol=0, atol=1e-12)
+            assert abs(lse[b, hq] - l) < 1e-12
+
+
+def test_page_scales_equal_to_head_scales_are_per_head():
+    """Every page given its KV head's scale: exactly the per-head result; random page scales
+    change it."""
+    w = small(kv_dtype="fp8", q_dtype="bf16", page_scales=True, seq_lens=[9, 4, 13])
+    ksp = np.ascontiguousarray(np.broadcast_to(w.k_scale, w.k_scale_page.shape))
+    vsp = np.ascontiguousarray(np.broadcast_to(w.v_scale, w.v_scale_page.shape))
+    o_e, l_e = run_oracle(w, k_scale_page=ksp, v_scale_page=vsp)
+    o_h, l_h = run_oracle(w, k_scale_page=None, v_scale_page=None)
+    assert np.array_equal(o_e, o_h) and np.array_equal(l_e, l_h)
+    o_p, _ = run_oracle(w)
+    assert np.abs(o_p - o_h).max() > 1e-3
+
+
+def test_page_v_scales_doubled_double_out():
+    """Every page's V scale times 2 (exact in fp32 and fp64): out doubles exactly, lse stays."""
+    w = small(kv_dtype="fp8", q_dtype="bf16", page_scales=True, seq_lens=[9, 4, 13])
+    o1, l1 = run_oracle(w)
+    o2, l2 = run_oracle(w, v_scale_page=w.v_scale_page * np.float32(2))
+    assert np.array_equal(o2, 2 * o1) and np.array_equal(l1, l2)
+
+
+def test_append_with_page_scales_matches_library_quantization():
+    """Append into an fp8 pool with per-page scales: each element is x / (its slot's page scale)
+    in fp32, encoded by torch's e4m3fn conversion (inputs kept inside +-448)."""
+    import torch
+    H_kv, D, ps, P = 2, 16, 8, 6
+    pool = synth.poisoned_pool(P, H_kv, ps, D, "fp8")
+    k, v, slots = synth.append_inputs(T=11, H_kv=H_kv, D=D, page_size=ps, max_num_pages=P,
+                                      in_dtype="bf16", seed=9, skip_every=4)
+    rng = np.random.default_rng(90)
+    ksp = rng.uniform(1.0 / 112, 2.0 / 112, size=(P, H_kv)).astype(np.float32)
+    vsp = rng.uniform(1.0 / 112, 2.0 / 112, size=(P, H_kv)).astype(np.float32)
+    before = pool.copy()
+    oracle.append_kv(pages=pool, new_k=k, new_v=v, slots=slots, H_kv=H_kv, D=D, ps=ps,
+                     in_dtype=1, kv_dtype=2, k_scale_page=ksp, v_scale_page=vsp)
+    kf = to_f64(k, "bf16").astype(np.float32)
+    vf = to_f64(v, "bf16").astype(np.float32)
+    expect = before.copy()
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        page = s // ps
+        for kv, x, sc in ((0, kf, ksp), (1, vf, vsp)):
+            y = x[t] / sc[page][:, None]
+            assert np.abs(y).max() <= 448
+            expect[page, kv, :, s % ps, :] = (torch.from_numpy(np.ascontiguousarray(y))
+                                              .to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert expect.tobytes() == pool.tobytes()
