@@ -108,6 +108,16 @@ typedef struct pdecode_desc {
                              lse = log2(e^{sink} + sum_r e^{s_r}); one without keeps out = 0,
                              lse = -5e4. Attention calls on the persistent matrix-core schedule
                              only (BF16 / FP8 pool, batch <= 1024); otherwise UNSUPPORTED.       */
+  const float *k_scale_page; /* device fp32 [max_num_pages, H_kv] or NULL, FP8 pools only: a scale
+                             per (page, KV head) block, K = code * k_scale_page[page][h]; with
+                             v_scale_page (set both or neither, else INVALID_ARG) it replaces
+                             k_scale / v_scale, which may then be NULL. An extension of the
+                             pages' single K and V scale (AWS attention_block_tkg page, k_scale /
+                             v_scale) to one scale per page block. pdecode_append_kv stores a
+                             row as x / (its page's scale). Attention calls on the persistent
+                             matrix-core schedule (batch <= 1024), not pdecode_append_attention;
+                             otherwise UNSUPPORTED.                                             */
+  const float *v_scale_page; /* device fp32 [max_num_pages, H_kv] or NULL: V's, as k_scale_page    */
 } pdecode_desc;
 
 /* Rotary embedding on Q and K inside the kernel; a NULL pointer to this struct means none.

@@ -53,7 +53,12 @@ pdecode_status check_desc(const pdecode_desc* d) {
   if (d->sliding_window != 0 && d->sliding_window != 1) return PDECODE_ERR_INVALID_ARG;
   if (d->q_dtype < 0 || d->q_dtype > 2 || d->kv_dtype < 0 || d->kv_dtype > 3)
     return PDECODE_ERR_INVALID_ARG;
-  if (is_fp8(d->kv_dtype) && (!d->k_scale || !d->v_scale)) return PDECODE_ERR_INVALID_ARG;
+  // fp8 scales: per KV head, or per (page, KV head) (both tables or neither; fp8 pools only)
+  const bool page_scales = d->k_scale_page != nullptr || d->v_scale_page != nullptr;
+  if (page_scales && (!d->k_scale_page || !d->v_scale_page || !is_fp8(d->kv_dtype)))
+    return PDECODE_ERR_INVALID_ARG;
+  if (is_fp8(d->kv_dtype) && !page_scales && (!d->k_scale || !d->v_scale))
+    return PDECODE_ERR_INVALID_ARG;
   if (!supported_pair(d->q_dtype, d->kv_dtype)) return PDECODE_ERR_UNSUPPORTED;
   return PDECODE_OK;
 }
@@ -198,8 +203,10 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
     return PDECODE_ERR_INVALID_ARG;
   const Plan pl = make_plan(d, qo_len);
   if ((fused || qo_len > 1 || d->sink_logits) && !pl.persistent) return PDECODE_ERR_UNSUPPORTED;
-  // the fused append writes e4m3fn codes only
+  // the fused append writes e4m3fn codes only, with per-KV-head scales
   if (fused && d->kv_dtype == PDECODE_FP8_E4M3) return PDECODE_ERR_UNSUPPORTED;
+  // per-page fp8 scales: the persistent schedule, attention without the fused append
+  if (d->k_scale_page && (!pl.persistent || fused)) return PDECODE_ERR_UNSUPPORTED;
   // interleaved RoPE: the persistent matrix-core kernels only
   if (rotary && rope->rotary_mode == 2 && !pl.persistent)
     return PDECODE_ERR_UNSUPPORTED;
@@ -225,6 +232,8 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   p.k_off = rotary ? rope->k_rope_pos_offset : nullptr;
   p.k_scale = d->k_scale;
   p.v_scale = d->v_scale;
+  p.k_scale_page = d->k_scale_page;
+  p.v_scale_page = d->v_scale_page;
   p.new_k = new_k;
   p.new_v = new_v;
   p.pages_w = fused ? const_cast<void*>(pages) : nullptr;
@@ -371,7 +380,8 @@ pdecode_status pdecode_append_kv(const pdecode_desc* d, const void* new_k, const
   if (num_tokens == 0) return PDECODE_OK;
   if (!new_k || !new_v || !slot_ids || !pages) return PDECODE_ERR_INVALID_ARG;
   pdk::AppendParams p{new_k, new_v, slot_ids, pages, d->k_scale, d->v_scale, num_tokens,
-                      d->num_kv_heads, d->head_dim, d->page_size, d->max_num_pages};
+                      d->num_kv_heads, d->head_dim, d->page_size, d->max_num_pages,
+                      d->k_scale_page, d->v_scale_page};
   return hip_status(pdk::launch_append(p, d->q_dtype, d->kv_dtype, static_cast<hipStream_t>(stream)));
 }
 

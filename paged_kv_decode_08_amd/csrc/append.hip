@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void append_vec_kernel(AppendParams p, int vpr
     static_assert(IT == KVT, "same element type in and out");
     o = *reinterpret_cast<const uint4*>(static_cast<const char*>(in) + src * (KVT == kF32 ? 4 : 2));
   } else {
-    const float sc = kv ? p.v_scale[h] : p.k_scale[h];
+    const float sc = append_scale(p, kv, page, h);
     float x[16];
     if constexpr (IT == kF32) {
       const uint4* s4 = reinterpret_cast<const uint4*>(static_cast<const float*>(in) + src);
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
       static_cast<uint16_t*>(p.pages)[dst] = static_cast<const uint16_t*>(in)[src];
     } else {
       const float x = load_q<IT>(in, src);
-      const float sc = kv ? p.v_scale[h] : p.k_scale[h];
+      const float sc = append_scale(p, kv, page, h);
       const float y = __fdiv_rn(x, sc);
       static_cast<uint8_t*>(p.pages)[dst] = KVT == kFP8E4M3 ? f32_to_fp8_e4m3(y) : f32_to_fp8(y);
     }

@@ -699,11 +699,22 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   if (J.valid) {
     core.load_q(reinterpret_cast<const uint16_t*>(s_q[0]), GC);
     core.rope_q(J.qpos + tok, s_freq);  // several tokens: token tok sits tok positions later
-    float scale = p.score_scale * (C::FP8 ? p.k_scale[J.h] : 1.0f);
-    float vscale = C::FP8 ? p.v_scale[J.h] : 1.0f;
+    // fp8: the KV head's scales, or 1 with per-page scales (applied per item)
+    const bool page_scales = C::FP8 && p.k_scale_page != nullptr;
+    float scale = p.score_scale * (C::FP8 && !page_scales ? p.k_scale[J.h] : 1.0f);
+    float vscale = C::FP8 && !page_scales ? p.v_scale[J.h] : 1.0f;
     core.reset();
     Buf buf0, buf1;
-    core.issue(buf0, block_of(clamp_page(p, uni(s_ids[0][w][0])), J.h), kv_stride);
+    {
+      const int page0 = clamp_page(p, uni(s_ids[0][w][0]));
+      core.issue(buf0, block_of(page0, J.h), kv_stride);
+      if constexpr (C::FP8) {
+        if (page_scales) {
+          buf0.ks = p.k_scale_page[size_t(page0) * p.H_kv + J.h];
+          buf0.vs = p.v_scale_page[size_t(page0) * p.H_kv + J.h];
+        }
+      }
+    }
 
     // Page id of item k of the current job (slot k / SUB of the wave; refilled per 64 slots from
     // the page table).
@@ -738,12 +749,21 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         // first one, so window pages shift by the rows the window skips (sink - win_off)
         const int pos0 = J.kro + j * PS + r0 +
                          (J.s_w + kPWaves * si < J.g.n0 ? 0 : J.g.sink - J.g.win_off);
+        // fp8 pool with per-page scales: this item's block scales (the job's are 1)
+        float isc = scale, ivf = 1.f;
+        if constexpr (C::FP8) {
+          if (page_scales) {
+            isc = p.score_scale * cur.ks;
+            ivf = cur.vs;
+          }
+        }
         if constexpr (MT) {
           // this lane's column (token n / G) sees positions <= total - T + n / G
           const int cap = J.g.total - T + tok - (j * PS + r0);
-          if (lo < hi) core.template process<true>(cur, lo, hi, scale, s_tile[w], pos0, s_freq, cap);
+          if (lo < hi)
+            core.template process<true>(cur, lo, hi, isc, s_tile[w], pos0, s_freq, cap, ivf);
         } else {
-          if (lo < hi) core.process(cur, lo, hi, scale, s_tile[w], pos0, s_freq);
+          if (lo < hi) core.process(cur, lo, hi, isc, s_tile[w], pos0, s_freq, 15, ivf);
         }
       }
     };
@@ -780,8 +800,15 @@ void decode_mfma_persist_kernel(DecodeParams p) {
     };
     auto issue_id = [&](Buf& nxt, int raw, int hh, int k, bool pad = false) __attribute__((always_inline)) {
       if (pad) raw = hh = 0;
-      core.issue(nxt, block_of(clamp_page(p, uni(raw)), uni(hh)) + (k % SUB) * 16 * C::ROW,
-                 kv_stride);
+      const int page = clamp_page(p, uni(raw));
+      core.issue(nxt, block_of(page, uni(hh)) + (k % SUB) * 16 * C::ROW, kv_stride);
+      if constexpr (C::FP8) {
+        if (page_scales) {  // the item's block scales, loaded with its rows
+          const size_t e = size_t(page) * p.H_kv + uni(hh);
+          nxt.ks = p.k_scale_page[e];
+          nxt.vs = p.v_scale_page[e];
+        }
+      }
     };
 
     // Split sequences are merged here when the call has few chunks. Each wave arrives at its
@@ -936,7 +963,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       par ^= 1;
       core.load_q(reinterpret_cast<const uint16_t*>(s_q[par]), GC);
       core.rope_q(J.qpos + tok, s_freq);  // several tokens: token tok sits tok positions later
-      if (C::FP8) {
+      if (C::FP8 && !page_scales) {
         scale = p.score_scale * p.k_scale[J.h];
         vscale = p.v_scale[J.h];
       }

@@ -25,6 +25,8 @@ struct DecodeParams {
   const int32_t* k_off;      // RoPE: position of attended row 0 [B]
   const float* k_scale;      // fp8 KV: per-KV-head scales
   const float* v_scale;
+  const float* k_scale_page; // fp8 KV: per-(page, KV head) scales [max_num_pages, H_kv], or
+  const float* v_scale_page; // null; they replace k_scale / v_scale (persistent schedule only)
   void* out;
   float* lse;
   float* part_o;             // split-KV partial outputs [B, T, H_qo, num_chunks, D] (normalised)
@@ -71,7 +73,15 @@ struct AppendParams {
   const float* k_scale;
   const float* v_scale;
   int32_t T, H_kv, D, PS, max_num_pages;
+  const float* k_scale_page;  // fp8 pool: per-(page, KV head) scales [max_num_pages, H_kv], or
+  const float* v_scale_page;  // null (then k_scale / v_scale)
 };
+
+// The scale an fp8 element of (page, KV head h) is stored with: its block's, or its head's.
+__device__ __forceinline__ float append_scale(const AppendParams& p, int kv, size_t page, int h) {
+  const float* tab = kv ? p.v_scale_page : p.k_scale_page;
+  return tab ? tab[page * p.H_kv + h] : (kv ? p.v_scale[h] : p.k_scale[h]);
+}
 
 struct MergeParams {
   void* v;

@@ -130,6 +130,7 @@ struct MfmaCore {
   struct Buf {
     uint4 k[NK];
     VT v[NI];
+    float ks, vs;  // fp8 pools with per-page scales: the item's (page, KV head) K and V scales
   };
 
   int l, n, qg, cv, rg;  // lane coordinates: MFMA layout (n, qg), V layout (cv, rg)
@@ -309,9 +310,11 @@ struct MfmaCore {
   // COLCAP (several query tokens): this lane's column also masks the rows above `cap`, so a
   // column may have no row left in the item, or in the whole job so far (m = -inf).
   template <bool COLCAP = false>
+  // vf: a factor on this item's V rows (an fp8 pool's per-page V scale), applied to P.
   __device__ __forceinline__ void process(const Buf& bf, int lo, int hi, float scale,
                                           unsigned char* tile, int pos0 = 0,
-                                          const float2* s_freq = nullptr, int cap = 15) {
+                                          const float2* s_freq = nullptr, int cap = 15,
+                                          float vf = 1.f) {
     // scores S^T[row][head] on the matrix cores
     f32x4_t acc[RB];
     if constexpr (ROPE) {
@@ -442,7 +445,9 @@ struct MfmaCore {
     // where the QK accumulator left them) is the B operand as bf16; V goes to this wave's LDS tile
     // (rows outside [lo, hi) as zeros: 0 x NaN would poison O) and comes back transposed, 16 dims
     // per read, as the A operand.
-    const uint2 pb = make_uint2(pack_bf16x2(sv[0][0], sv[0][1]), pack_bf16x2(sv[0][2], sv[0][3]));
+    const float pf = FP8 ? vf : 1.f;  // the denominator dl above takes P without it
+    const uint2 pb = make_uint2(pack_bf16x2(sv[0][0] * pf, sv[0][1] * pf),
+                                pack_bf16x2(sv[0][2] * pf, sv[0][3] * pf));
     if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) OT[b] *= alpha;

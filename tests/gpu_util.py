@@ -26,6 +26,10 @@ def upload(w, device="cuda"):
         k_off=torch.from_numpy(w.k_rope_pos_offset).to(device),
         k_scale=None if w.k_scale is None else torch.from_numpy(w.k_scale).to(device),
         v_scale=None if w.v_scale is None else torch.from_numpy(w.v_scale).to(device),
+        k_scale_page=(None if getattr(w, "k_scale_page", None) is None
+                      else torch.from_numpy(w.k_scale_page).to(device)),
+        v_scale_page=(None if getattr(w, "v_scale_page", None) is None
+                      else torch.from_numpy(w.v_scale_page).to(device)),
     )
     return d
 
@@ -38,7 +42,8 @@ def desc_for(w, dev, num_kv_splits=0, max_kv_len=None, sink_logits=None):
                         q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
                         sliding_window=w.sliding_window, max_kv_len=max_kv_len,
                         num_kv_splits=num_kv_splits, k_scale=dev["k_scale"],
-                        v_scale=dev["v_scale"], sink_logits=sink_logits)
+                        v_scale=dev["v_scale"], sink_logits=sink_logits,
+                        k_scale_page=dev.get("k_scale_page"), v_scale_page=dev.get("v_scale_page"))
 
 
 def run_attention(w, dev, num_kv_splits=0, max_kv_len=None, out=None, lse=None, stream=None):

@@ -256,3 +256,23 @@ def test_noalloc_refuses_plans_beyond_its_scratch(L):
     assert noalloc_status(L, desc(num_qo_heads=30)) == 1
     assert noalloc_status(L, desc(), ptrs=False) == 1
     assert noalloc_status(L, desc(head_dim=96)) == 2
+
+
+def test_page_scale_arguments(L):
+    """Per-page fp8 scales: both tables or neither, fp8 pools only (INVALID_ARG); the per-head
+    scales may then be NULL; only the persistent schedule without the fused append takes them
+    (UNSUPPORTED) -- all refused on the host before any launch."""
+    def with_pages(d, k=True, v=True):
+        d.k_scale_page = FAKE.value if k else None
+        d.v_scale_page = FAKE.value if v else None
+        return d
+
+    ok = with_pages(desc(kv_dtype="fp8"))
+    assert pk.workspace_bytes(ok) > 0
+    assert attention_status(L, with_pages(desc(kv_dtype="fp8"), v=False)) == 1
+    assert attention_status(L, with_pages(desc(kv_dtype="bf16"))) == 1
+    big = with_pages(desc(kv_dtype="fp8", batch=2000, max_num_pages=1 << 16))
+    assert attention_status(L, big) == 2
+    P = FAKE
+    assert L.pdecode_append_attention(ctypes.byref(ok), P, P, P, P, P, P, P, None, 0.1, P, P, P,
+                                      1 << 30, None) == 2

@@ -452,6 +452,74 @@ def test_fp8_unit_sigma():
     run_and_check(w, num_kv_splits=5)
 
 
+@pytest.mark.parametrize("D,ps,G,splits,window,rope", [
+    (128, 32, 8, 0, False, 0),   # the fp8 GQA-8 shape
+    (128, 16, 4, 0, False, 0),
+    (64, 16, 2, 3, False, 0),
+    (128, 32, 4, 12, False, 0),  # more chunks than the in-kernel merge takes: the merge kernel
+    (128, 16, 4, 5, True, 0),    # sliding window + sink
+    (128, 32, 8, 0, False, 1),   # rotate-half RoPE
+    (64, 32, 4, 5, False, 2),    # interleaved RoPE, D = 64 (K rotated across lanes)
+    (64, 16, 1, 0, True, 1),
+])
+def test_fp8_page_scales(D, ps, G, splits, window, rope):
+    """fp8 pool with a scale per (page, KV head) in place of the per-head ones: every item takes
+    its block's K scale in the score and its V scale on P; lengths around page boundaries, empty
+    and one-row sequences, every output against the oracle."""
+    lens = [1, ps - 1, ps, ps + 1, 5 * ps + 3, 1700, 0, 2 * ps]
+    w = synth.make_workload(name=f"pgsc_D{D}_ps{ps}_G{G}_s{splits}_w{int(window)}_r{rope}",
+                            B=len(lens), H_qo=2 * G, H_kv=2, D=D, page_size=ps, seq_lens=lens,
+                            q_dtype="bf16", kv_dtype="fp8", seed=1100 + D + ps + G + splits + rope,
+                            max_num_pages=512, page_scales=True, window=300 if window else None,
+                            sink=4 if window else 0, rotary_mode=rope, rope_theta=5e5)
+    run_and_check(w, num_kv_splits=splits)
+
+
+def test_fp8_page_scales_full_size():
+    """The fp8 GQA-8 workload's shape (B=256, 64 q / 8 KV heads, page 32, lognormal lengths) with
+    per-page scales, automatic plan: every output against the oracle."""
+    base = synth.fp8_gqa8()
+    lens = base.seq_lens.astype(np.int64)
+    w = synth.make_workload(name="fp8_gqa8_page_scales", B=base.B, H_qo=64, H_kv=8, D=128,
+                            page_size=32, seq_lens=lens, max_num_pages=65536, kv_dtype="fp8",
+                            seed=1005, page_scales=True)
+    run_and_check(w)
+
+
+@pytest.mark.parametrize("G,T,splits", [(4, 2, 0), (2, 4, 12), (8, 2, 3)])
+def test_fp8_page_scales_multi(G, T, splits):
+    """Several query tokens over an fp8 pool with per-page scales."""
+    w = synth.make_workload(name=f"pgsc_multi_G{G}_T{T}_s{splits}", B=5, H_qo=2 * G, H_kv=2,
+                            D=128, page_size=32, seq_lens=[3000, T - 1, 700, 33, 64],
+                            kv_dtype="fp8", seed=1200 + G + T + splits, max_num_pages=512,
+                            page_scales=True)
+    _multi_case(w, T, seed=121, num_kv_splits=splits)
+
+
+def test_append_page_scales_bitexact():
+    """pdecode_append_kv into an fp8 pool with per-page scales: each row quantised with its slot's
+    page scale, bit-exact against the oracle."""
+    import paged_kv_decode_08_amd as pk
+    H_kv, D, ps, P = 8, 128, 32, 64
+    pool = synth.poisoned_pool(P, H_kv, ps, D, "fp8")
+    k, v, slots = synth.append_inputs(T=40, H_kv=H_kv, D=D, page_size=ps, max_num_pages=P,
+                                      in_dtype="bf16", seed=13, skip_every=5)
+    rng = np.random.default_rng(14)
+    ksp = rng.uniform(0.5 / 448, 2 / 448, (P, H_kv)).astype(np.float32)
+    vsp = rng.uniform(0.5 / 448, 2 / 448, (P, H_kv)).astype(np.float32)
+    tks, tvs = torch.from_numpy(ksp).cuda(), torch.from_numpy(vsp).cuda()
+    desc = pk.make_desc(batch=1, num_qo_heads=H_kv, num_kv_heads=H_kv, head_dim=D, page_size=ps,
+                        max_num_pages=P, q_dtype="bf16", kv_dtype="fp8", k_scale_page=tks,
+                        v_scale_page=tvs)
+    tpool = gu.to_device_storage(pool, "fp8")
+    pk.append_kv(desc, gu.to_device_storage(k, "bf16"), gu.to_device_storage(v, "bf16"),
+                 torch.from_numpy(slots).cuda(), tpool)
+    torch.cuda.synchronize()
+    ref = oracle.append_kv(pages=pool.copy(), new_k=k, new_v=v, slots=slots, H_kv=H_kv, D=D, ps=ps,
+                           in_dtype=1, kv_dtype=2, k_scale_page=ksp, v_scale_page=vsp)
+    assert tpool.cpu().numpy().tobytes() == ref.tobytes()
+
+
 def test_fp8_decode_all_codes():
     """Every finite e4m3fn code, read through decode with one attended row and v_scale = 1: the
     bf16 output equals the code's value exactly (all e4m3fn values are bf16 values)."""
