@@ -35,7 +35,8 @@ def lib():
         f32 = ctypes.c_float
         L.oracle_decode.restype = i32
         L.oracle_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, i32, P,
-                                    i32, i32, f32, f32, P, P, f32, P, P, P, P, i32, P, P, P, i32]
+                                    i32, i32, f32, f32, P, P, f32, P, P, P, P, P, i32, P, P, P,
+                                    i32]
         L.oracle_merge_state.restype = None
         L.oracle_merge_state.argtypes = [i32, i32, i32, P, P, P, P]
         L.oracle_append_kv.restype = i32
@@ -77,10 +78,11 @@ class OracleError(RuntimeError):
 def decode(*, B, H_qo, H_kv, D, ps, max_num_pages, q_dtype, kv_dtype, q, pages, indptr, values,
            length_info, sliding_window=False, rotary_mode=0, rope_scale=1.0, rope_theta=1e4,
            q_rope_position=None, k_rope_pos_offset=None, sm_scale, k_scale=None, v_scale=None,
-           k_scale_page=None, v_scale_page=None, select=None, nthreads=0):
+           k_scale_page=None, v_scale_page=None, q_scale=None, select=None, nthreads=0):
     """Decode attention. q/pages are raw arrays in their storage dtype (fp32, uint16 bf16 bits,
     uint8 fp8 codes). fp8 pools: per-KV-head scales k_scale/v_scale [H_kv], or per (page, KV
-    head) scales k_scale_page/v_scale_page [max_num_pages, H_kv], which replace them.
+    head) scales k_scale_page/v_scale_page [max_num_pages, H_kv], which replace them. fp8 q: a
+    scale per q head q_scale [H_qo] (q = code * scale).
     Returns (out[n, D] fp64, lse[n] fp64) for the selected (b, h_qo) pairs
     (select = int array [n, 2]) or for all pairs in (b, h_qo) order reshaped to [B, H_qo, ...]."""
     indptr = _c(indptr, np.int32)
@@ -94,6 +96,7 @@ def decode(*, B, H_qo, H_kv, D, ps, max_num_pages, q_dtype, kv_dtype, q, pages, 
     vs = _c(v_scale, np.float32)
     ksp = _c(k_scale_page, np.float32)
     vsp = _c(v_scale_page, np.float32)
+    qs = _c(q_scale, np.float32)
     sel = None if select is None else _c(select, np.int32).reshape(-1, 2)
     n = sel.shape[0] if sel is not None else B * H_qo
     out = np.zeros((max(n, 1), D), np.float64)
@@ -106,7 +109,7 @@ def decode(*, B, H_qo, H_kv, D, ps, max_num_pages, q_dtype, kv_dtype, q, pages, 
                              _ptr(length_info), int(bool(sliding_window)), int(rotary_mode),
                              float(rope_scale), float(rope_theta), _ptr(qrp), _ptr(kro),
                              float(sm_scale), _ptr(ks), _ptr(vs), _ptr(ksp), _ptr(vsp),
-                             0 if sel is None else n,
+                             _ptr(qs), 0 if sel is None else n,
                              _ptr(sel), _ptr(out), _ptr(lse), int(nthreads))
     if rc != 0:
         raise OracleError(f"oracle_decode failed with code {rc}")

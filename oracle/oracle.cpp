@@ -173,6 +173,7 @@ struct DecodeArgs {
   const float* v_scale;
   const float* k_scale_page;  // [max_num_pages, H_kv] or null: per (page, KV head) scales
   const float* v_scale_page;
+  const float* q_scale;       // [H_qo], fp8 q only: q = code * q_scale[h_qo]
 };
 
 // Index of element (page, kv, head, off, dim) in the pages[P, 2, H_kv, ps, D] pool.
@@ -209,8 +210,10 @@ int decode_one(const DecodeArgs& a, int b, int h_qo, double* out, double* lse) {
   }
 
   std::vector<double> qv(D), kv(D), vv(D), acc(D, 0.0), scores(L);
+  // fp8 q: a stored value is code * the q head's scale, as for the pool
+  const double qscale = is_fp8(a.q_dtype) ? static_cast<double>(a.q_scale[h_qo]) : 1.0;
   for (int d = 0; d < D; ++d)
-    qv[d] = load_value(a.q, a.q_dtype, (static_cast<size_t>(b) * a.H_qo + h_qo) * D + d);
+    qv[d] = load_value(a.q, a.q_dtype, (static_cast<size_t>(b) * a.H_qo + h_qo) * D + d) * qscale;
   const bool rope = a.rotary_mode == 1 || a.rotary_mode == 2;
   const bool ilv = a.rotary_mode == 2;
   if (rope) rope_rotate(qv.data(), D, a.q_rope_position[b], a.rope_scale, a.rope_theta, ilv);
@@ -293,18 +296,19 @@ int32_t oracle_decode(int32_t B, int32_t H_qo, int32_t H_kv, int32_t D, int32_t 
                       float rope_scale, float rope_theta, const int32_t* q_rope_position,
                       const int32_t* k_rope_pos_offset, float sm_scale, const float* k_scale,
                       const float* v_scale, const float* k_scale_page, const float* v_scale_page,
-                      int32_t n_sel, const int32_t* sel, double* out, double* lse,
-                      int32_t nthreads) {
+                      const float* q_scale, int32_t n_sel, const int32_t* sel, double* out,
+                      double* lse, int32_t nthreads) {
   if (B < 0 || H_kv <= 0 || H_qo <= 0 || H_qo % H_kv != 0 || D <= 0 || D % 2 != 0 || ps <= 0)
     return 4;
   if (elem_bytes(q_dtype) == 0 || elem_bytes(kv_dtype) == 0) return 4;
   if ((k_scale_page == nullptr) != (v_scale_page == nullptr)) return 4;
   if (is_fp8(kv_dtype) && k_scale_page == nullptr && (k_scale == nullptr || v_scale == nullptr))
     return 4;
+  if (is_fp8(q_dtype) && q_scale == nullptr) return 4;
   DecodeArgs a{B, H_qo, H_kv, D, ps, max_num_pages, q_dtype, kv_dtype, q, pages, indptr, values,
                nnz, length_info, sliding_window, rotary_mode, rope_scale, rope_theta,
                q_rope_position, k_rope_pos_offset, sm_scale, k_scale, v_scale, k_scale_page,
-               v_scale_page};
+               v_scale_page, q_scale};
   const int64_t n = n_sel > 0 ? n_sel : static_cast<int64_t>(B) * H_qo;
   std::atomic<int64_t> next{0};
   std::atomic<int32_t> status{0};

@@ -27,6 +27,7 @@ import torch
 # "fp8": OCP e4m3fn codes; "fp8e4m3": IEEE-style e4m3 codes (max 240), drawn within +-240 where
 # both formats give the same code to every value
 DTYPE_CODE = {"f32": 0, "bf16": 1, "fp8": 2, "fp8e4m3": 3}
+Q_PAYLOAD_SIGMA = 112.0  # fp8 q: spread of the codes, a quarter of e4m3fn's range
 STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "fp8e4m3": np.uint8}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "fp8e4m3": 1}
 POISON = {"f32": np.float32(np.nan).view(np.uint32), "bf16": 0x7FC0, "fp8": 0x7F,
@@ -90,6 +91,8 @@ class Workload:
     # fp8 pools with per-(page, KV head) scales [max_num_pages, H_kv] (replace k_scale / v_scale)
     k_scale_page: np.ndarray | None = None
     v_scale_page: np.ndarray | None = None
+    # fp8 q: a scale per q head [H_qo] (q = code * scale)
+    q_scale: np.ndarray | None = None
 
     @property
     def kv_bytes(self) -> int:
@@ -106,7 +109,7 @@ class Workload:
                     rope_theta=self.rope_theta, q_rope_position=self.q_rope_position,
                     k_rope_pos_offset=self.k_rope_pos_offset, sm_scale=self.sm_scale,
                     k_scale=self.k_scale, v_scale=self.v_scale, k_scale_page=self.k_scale_page,
-                    v_scale_page=self.v_scale_page)
+                    v_scale_page=self.v_scale_page, q_scale=self.q_scale)
 
 
 def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_num_pages=None,
@@ -185,7 +188,15 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
         if npages[b] > 0 and last[b] < ps:
             pool[ids[indptr[b + 1] - 1], :, :, last[b]:, :] = poisoned_pool(1, 1, 1, 1, kv_dtype)[0, 0, 0, 0, 0]
     rng_q = _rng(seed, 3)
-    q = cast_f32(rng_q.standard_normal((B, H_qo, D), dtype=np.float32), q_dtype)
+    q_scale = None
+    if q_dtype == "fp8":
+        # codes of N(0, 1) * Q_PAYLOAD_SIGMA, and per-q-head scales ~ U[0.5, 2] / Q_PAYLOAD_SIGMA
+        q = cast_f32(np.clip(rng_q.standard_normal((B, H_qo, D), dtype=np.float32) *
+                             np.float32(Q_PAYLOAD_SIGMA), -448, 448), "fp8")
+        q_scale = _rng(seed, 7).uniform(0.5, 2.0, size=H_qo).astype(np.float32) / np.float32(
+            Q_PAYLOAD_SIGMA)
+    else:
+        q = cast_f32(rng_q.standard_normal((B, H_qo, D), dtype=np.float32), q_dtype)
     if sm_scale is None:
         sm_scale = float(np.float32(1.0 / math.sqrt(D)))
     if q_rope_position is None:
@@ -201,7 +212,7 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
                     q_rope_position=np.asarray(q_rope_position, np.int32),
                     k_rope_pos_offset=np.asarray(k_rope_pos_offset, np.int32),
                     sm_scale=float(sm_scale), k_scale=k_scale, v_scale=v_scale, used_pages=order,
-                    k_scale_page=k_scale_page, v_scale_page=v_scale_page)
+                    k_scale_page=k_scale_page, v_scale_page=v_scale_page, q_scale=q_scale)
 
 
 # The five benchmark workloads. Their sizes follow the decode settings the pages describe
@@ -264,9 +275,13 @@ CONFIGS = {
 
 def multi_query(w, T, seed):
     """q for T query tokens per sequence of workload w: [B, T, H_qo, D] in w.q_dtype storage,
-    N(0, 1) from its own seeded stream."""
+    N(0, 1) from its own seeded stream (fp8 q: codes of N(0, 1) * Q_PAYLOAD_SIGMA, read with the
+    workload's q_scale)."""
     rng = _rng(seed, 6)
-    return cast_f32(rng.standard_normal((w.B, T, w.H_qo, w.D), dtype=np.float32), w.q_dtype)
+    x = rng.standard_normal((w.B, T, w.H_qo, w.D), dtype=np.float32)
+    if w.q_dtype == "fp8":
+        x = np.clip(x * np.float32(Q_PAYLOAD_SIGMA), -448, 448)
+    return cast_f32(x, w.q_dtype)
 
 
 def append_inputs(*, T, H_kv, D, page_size, max_num_pages, in_dtype, seed, skip_every=0,

@@ -930,3 +930,34 @@ def test_append_with_page_scales_matches_library_quantization():
             expect[page, kv, :, s % ps, :] = (torch.from_numpy(np.ascontiguousarray(y))
                                               .to(torch.float8_e4m3fn).view(torch.uint8).numpy())
     assert expect.tobytes() == pool.tobytes()
+
+
+# ---------------------------------------------------------------- fp8 q
+# q stored as e4m3fn codes with a scale per q head: q = code x q_scale[h_qo], read as the pool's
+# codes are.
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_fp8_q_matches_dense_bruteforce(kv_dtype):
+    """fp8 q (codes x per-q-head scales) == textbook attention with the dequantised q."""
+    w = small(kv_dtype=kv_dtype, q_dtype="fp8", seq_lens=[7, 1, 13])
+    out, lse = run_oracle(w)
+    G = w.H_qo // w.H_kv
+    q64 = to_f64(w.q, "fp8") * w.q_scale.astype(np.float64)[None, :, None]
+    for b in range(w.B):
+        for hq in range(w.H_qo):
+            K, V = contiguous_kv(w, b, hq // G)
+            o, l = dense_attention(q64[b, hq], K, V, w.sm_scale)
+            np.testing.assert_allclose(out[b, hq], o, rtol=0, atol=1e-12)
+            assert abs(lse[b, hq] - l) < 1e-12
+
+
+def test_fp8_q_with_power_of_two_scales_is_the_bf16_query():
+    """Scales that are powers of two make every dequantised q element a bf16 value: the fp8-q
+    result then equals the bf16-q result on those values exactly."""
+    w = small(kv_dtype="fp8", q_dtype="fp8", seq_lens=[9, 4, 13])
+    qs = np.float32(2.0) ** np.arange(-8, -8 + w.H_qo, dtype=np.float32)
+    o8, l8 = run_oracle(w, q_scale=qs)
+    qv = to_f64(w.q, "fp8") * qs.astype(np.float64)[None, :, None]
+    qb = synth.cast_f32(qv.astype(np.float32), "bf16")
+    assert np.array_equal(to_f64(qb, "bf16"), qv)  # exact in bf16
+    ob, lb = run_oracle(w, q_dtype=1, q=qb, q_scale=None)
+    assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
