@@ -78,7 +78,8 @@ typedef enum pdecode_dtype {
 /* Problem description shared by pdecode_attention and pdecode_append_kv.
  * Supported set: head_dim in {64, 128}; page_size in {16, 32}; group size
  * num_qo_heads / num_kv_heads in 1..8; (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
- * (BF16, FP8_E4M3FN), (BF16, FP8_E4M3)}. The output dtype equals q_dtype. */
+ * (BF16, FP8_E4M3FN), (BF16, FP8_E4M3), (FP8_E4M3FN, BF16 or either FP8)}. The output dtype
+ * equals q_dtype, except BF16 for an FP8 q. */
 typedef struct pdecode_desc {
   int32_t batch;          /* B >= 0                                                            */
   int32_t num_qo_heads;   /* H_qo > 0, a multiple of num_kv_heads                              */
@@ -118,6 +119,12 @@ typedef struct pdecode_desc {
                              matrix-core schedule (batch <= 1024), not pdecode_append_attention;
                              otherwise UNSUPPORTED.                                             */
   const float *v_scale_page; /* device fp32 [max_num_pages, H_kv] or NULL: V's, as k_scale_page    */
+  const float *q_scale;   /* device fp32 [H_qo]; required iff q_dtype is FP8_E4M3FN: q = code *
+                             q_scale[h_qo] (the pool's reading of a scaled code, applied to q).
+                             fp8 q pairs with a BF16 or FP8 pool, writes a BF16 out, and runs on
+                             the persistent matrix-core schedule (batch <= 1024; attention calls,
+                             single- or multi-token, not pdecode_append_attention); otherwise
+                             UNSUPPORTED. pdecode_append_kv does not take fp8 rows.             */
 } pdecode_desc;
 
 /* Rotary embedding on Q and K inside the kernel; a NULL pointer to this struct means none.

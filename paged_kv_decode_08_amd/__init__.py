@@ -30,7 +30,7 @@ class Desc(ctypes.Structure):
                 ("q_dtype", _c_i32), ("kv_dtype", _c_i32), ("sliding_window", _c_i32),
                 ("max_kv_len", _c_i32), ("num_kv_splits", _c_i32), ("k_scale", _c_ptr),
                 ("v_scale", _c_ptr), ("sink_logits", _c_ptr), ("k_scale_page", _c_ptr),
-                ("v_scale_page", _c_ptr)]
+                ("v_scale_page", _c_ptr), ("q_scale", _c_ptr)]
 
 
 class Rope(ctypes.Structure):
@@ -115,17 +115,18 @@ def dtype_code(dt) -> int:
 def make_desc(*, batch, num_qo_heads, num_kv_heads, head_dim, page_size, max_num_pages,
               q_dtype, kv_dtype, sliding_window=False, max_kv_len=0, num_kv_splits=0,
               k_scale=None, v_scale=None, sink_logits=None, k_scale_page=None,
-              v_scale_page=None) -> Desc:
+              v_scale_page=None, q_scale=None) -> Desc:
     d = Desc(batch, num_qo_heads, num_kv_heads, head_dim, page_size, max_num_pages,
              dtype_code(q_dtype), dtype_code(kv_dtype), int(bool(sliding_window)),
-             int(max_kv_len), int(num_kv_splits), None, None, None, None, None)
+             int(max_kv_len), int(num_kv_splits), None, None, None, None, None, None)
     d.k_scale = _ptr(k_scale)
     d.v_scale = _ptr(v_scale)
     d.sink_logits = _ptr(sink_logits)
     d.k_scale_page = _ptr(k_scale_page)
     d.v_scale_page = _ptr(v_scale_page)
+    d.q_scale = _ptr(q_scale)
     # keep the tensors alive with the struct
-    d._keep = (k_scale, v_scale, sink_logits, k_scale_page, v_scale_page)
+    d._keep = (k_scale, v_scale, sink_logits, k_scale_page, v_scale_page, q_scale)
     return d
 
 

@@ -41,7 +41,8 @@ bool is_fp8(int kv) { return kv == PDECODE_FP8_E4M3FN || kv == PDECODE_FP8_E4M3;
 
 bool supported_pair(int q, int kv) {
   return (q == PDECODE_F32 && kv == PDECODE_F32) || (q == PDECODE_BF16 && kv == PDECODE_BF16) ||
-         (q == PDECODE_BF16 && is_fp8(kv));
+         (q == PDECODE_BF16 && is_fp8(kv)) ||
+         (q == PDECODE_FP8_E4M3FN && (kv == PDECODE_BF16 || is_fp8(kv)));
 }
 
 pdecode_status check_desc(const pdecode_desc* d) {
@@ -60,6 +61,8 @@ pdecode_status check_desc(const pdecode_desc* d) {
   if (is_fp8(d->kv_dtype) && !page_scales && (!d->k_scale || !d->v_scale))
     return PDECODE_ERR_INVALID_ARG;
   if (!supported_pair(d->q_dtype, d->kv_dtype)) return PDECODE_ERR_UNSUPPORTED;
+  // fp8 q: its per-q-head scales, and only then
+  if ((d->q_dtype == PDECODE_FP8_E4M3FN) != (d->q_scale != nullptr)) return PDECODE_ERR_INVALID_ARG;
   return PDECODE_OK;
 }
 
@@ -205,8 +208,8 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   if ((fused || qo_len > 1 || d->sink_logits) && !pl.persistent) return PDECODE_ERR_UNSUPPORTED;
   // the fused append writes e4m3fn codes only, with per-KV-head scales
   if (fused && d->kv_dtype == PDECODE_FP8_E4M3) return PDECODE_ERR_UNSUPPORTED;
-  // per-page fp8 scales: the persistent schedule, attention without the fused append
-  if (d->k_scale_page && (!pl.persistent || fused)) return PDECODE_ERR_UNSUPPORTED;
+  // per-page fp8 scales and fp8 q: the persistent schedule, attention without the fused append
+  if ((d->k_scale_page || d->q_scale) && (!pl.persistent || fused)) return PDECODE_ERR_UNSUPPORTED;
   // interleaved RoPE: the persistent matrix-core kernels only
   if (rotary && rope->rotary_mode == 2 && !pl.persistent)
     return PDECODE_ERR_UNSUPPORTED;
@@ -234,6 +237,7 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   p.v_scale = d->v_scale;
   p.k_scale_page = d->k_scale_page;
   p.v_scale_page = d->v_scale_page;
+  p.q_scale = d->q_scale;
   p.new_k = new_k;
   p.new_v = new_v;
   p.pages_w = fused ? const_cast<void*>(pages) : nullptr;
@@ -376,6 +380,7 @@ pdecode_status pdecode_append_kv(const pdecode_desc* d, const void* new_k, const
   if (st == PDECODE_ERR_UNSUPPORTED && d->q_dtype == PDECODE_F32 && is_fp8(d->kv_dtype))
     st = PDECODE_OK;
   if (st != PDECODE_OK) return st;
+  if (d->q_dtype == PDECODE_FP8_E4M3FN) return PDECODE_ERR_UNSUPPORTED;  // rows come as f32 / bf16
   if (num_tokens < 0) return PDECODE_ERR_INVALID_ARG;
   if (num_tokens == 0) return PDECODE_OK;
   if (!new_k || !new_v || !slot_ids || !pages) return PDECODE_ERR_INVALID_ARG;

@@ -381,6 +381,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   // fused append: the new K and V rows of the current and the next job, in the pool's element type
   __shared__ __attribute__((aligned(16))) uint32_t s_new[FUSED ? 2 : 1][FUSED ? 2 * C::ROW / 4 : 1];
   __shared__ int s_ids[2][kPWaves][64];  // page-table entries of each wave's first 64 items
+  __shared__ float s_qsc[2][16];         // fp8 q: each MFMA column's q-head scale (1 otherwise)
   __shared__ int s_scan[kPWaves];
   __shared__ unsigned long long s_scan64[kPWaves];
   __shared__ int s_ticket;
@@ -611,16 +612,28 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       qoff[i] = ((c / G) * p.H_qo + c % G) * (D / 2) + (wd - c * (D / 2));
     }
   }
+  // fp8 q (p.q_scale set): the same element pairs from 16-bit code pairs, converted exactly to
+  // bf16 pairs; the q head's scale multiplies its column's scores (q_col_scale)
+  const bool q8 = p.q_scale != nullptr;
+  const uint16_t* q8src = static_cast<const uint16_t*>(p.q);
+  auto q_word = [&](size_t i) __attribute__((always_inline)) {
+    return q8 ? fp8x2_to_bf16x2<false>(uint32_t(q8src[i])) : qsrc[i];
+  };
   auto q_words = [&](const Job& J, uint32_t (&qs)[QW]) {
     if constexpr (MT) {
       const size_t base = (size_t(J.b) * T * p.H_qo + size_t(J.h) * G) * (D / 2);
 #pragma unroll
-      for (int i = 0; i < QW; ++i) qs[i] = qsrc[base + qoff[i]];
+      for (int i = 0; i < QW; ++i) qs[i] = q_word(base + qoff[i]);
     } else {
       const size_t base = (size_t(J.b) * p.H_qo + size_t(J.h) * G) * (D / 2);
 #pragma unroll
-      for (int i = 0; i < QW; ++i) qs[i] = qsrc[base + min(tid + i * NT, G * D / 2 - 1)];
+      for (int i = 0; i < QW; ++i) qs[i] = q_word(base + min(tid + i * NT, G * D / 2 - 1));
     }
+  };
+  // per-column score factor of fp8 q: thread c < GC loads column c's q-head scale with J's q
+  // words, and it is staged into s_qsc with them
+  auto q_scale_of = [&](const Job& J) __attribute__((always_inline)) {
+    return q8 && tid < 16 ? p.q_scale[J.h * G + min(tid, GC - 1) % G] : 1.f;
   };
 
   // ---- fused append (p.new_k set): thread t < 2 * D / 8 takes 8 elements of J's new K (t < D / 8)
@@ -687,12 +700,14 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   const int ids0 = load_id(p, J, l);
   uint32_t q0[QW];
   q_words(J, q0);
+  const float qsc0 = q_scale_of(J);
   NewWords nw0;
   if constexpr (FUSED) new_words(J, nw0);
   Job J1 = decode_job<PS, SUB, ROPE>(p, tab, total_jobs, hinv, blockIdx.x + gridDim.x, w, l);
 #pragma unroll
   for (int i = 0; i < QW; ++i) s_q[0][tid + i * NT] = q0[i];
   s_ids[0][w][l] = ids0;
+  if (tid < 16) s_qsc[0][tid] = qsc0;
   if constexpr (FUSED) stage_new(J, nw0, s_new[0]);
   __syncthreads();
 
@@ -702,6 +717,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
     // fp8: the KV head's scales, or 1 with per-page scales (applied per item)
     const bool page_scales = C::FP8 && p.k_scale_page != nullptr;
     float scale = p.score_scale * (C::FP8 && !page_scales ? p.k_scale[J.h] : 1.0f);
+    float qcs = s_qsc[0][core.n];  // this lane's column: its q head's scale (fp8 q), else 1
     float vscale = C::FP8 && !page_scales ? p.v_scale[J.h] : 1.0f;
     core.reset();
     Buf buf0, buf1;
@@ -749,11 +765,12 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         // first one, so window pages shift by the rows the window skips (sink - win_off)
         const int pos0 = J.kro + j * PS + r0 +
                          (J.s_w + kPWaves * si < J.g.n0 ? 0 : J.g.sink - J.g.win_off);
-        // fp8 pool with per-page scales: this item's block scales (the job's are 1)
-        float isc = scale, ivf = 1.f;
+        // fp8 pool with per-page scales: this item's block scales (the job's are 1); fp8 q: this
+        // lane's column scale
+        float isc = scale * qcs, ivf = 1.f;
         if constexpr (C::FP8) {
           if (page_scales) {
-            isc = p.score_scale * cur.ks;
+            isc = p.score_scale * cur.ks * qcs;
             ivf = cur.vs;
           }
         }
@@ -834,6 +851,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         const int ids_n = load_id(p, J1, l);
         uint32_t qs[QW];
         q_words(J1, qs);
+        const float qsc_n = q_scale_of(J1);
         NewWords nw1;
         if constexpr (FUSED) new_words(J1, nw1);
         int ticket_raw = 0;
@@ -854,6 +872,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < QW; ++i) s_q[par ^ 1][tid + i * NT] = qs[i];
         s_ids[par ^ 1][w][l] = ids_n;
+        if (tid < 16) s_qsc[par ^ 1][tid] = qsc_n;
         if constexpr (FUSED) stage_new(J1, nw1, s_new[par ^ 1]);
         if (last && tid == 0) s_ticket = 2 * int(gridDim.x) + ticket_raw;
       }
@@ -962,6 +981,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       J = J1;
       par ^= 1;
       core.load_q(reinterpret_cast<const uint16_t*>(s_q[par]), GC);
+      qcs = s_qsc[par][core.n];
       core.rope_q(J.qpos + tok, s_freq);  // several tokens: token tok sits tok positions later
       if (C::FP8 && !page_scales) {
         scale = p.score_scale * p.k_scale[J.h];

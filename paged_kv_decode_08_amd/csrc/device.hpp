@@ -27,6 +27,8 @@ struct DecodeParams {
   const float* v_scale;
   const float* k_scale_page; // fp8 KV: per-(page, KV head) scales [max_num_pages, H_kv], or
   const float* v_scale_page; // null; they replace k_scale / v_scale (persistent schedule only)
+  const float* q_scale;      // non-null: q holds e4m3fn codes, q = code * q_scale[h_qo]
+                             // (persistent schedule only)
   void* out;
   float* lse;
   float* part_o;             // split-KV partial outputs [B, T, H_qo, num_chunks, D] (normalised)

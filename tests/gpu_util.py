@@ -30,6 +30,8 @@ def upload(w, device="cuda"):
                       else torch.from_numpy(w.k_scale_page).to(device)),
         v_scale_page=(None if getattr(w, "v_scale_page", None) is None
                       else torch.from_numpy(w.v_scale_page).to(device)),
+        q_scale=(None if getattr(w, "q_scale", None) is None
+                 else torch.from_numpy(w.q_scale).to(device)),
     )
     return d
 
@@ -43,14 +45,16 @@ def desc_for(w, dev, num_kv_splits=0, max_kv_len=None, sink_logits=None):
                         sliding_window=w.sliding_window, max_kv_len=max_kv_len,
                         num_kv_splits=num_kv_splits, k_scale=dev["k_scale"],
                         v_scale=dev["v_scale"], sink_logits=sink_logits,
-                        k_scale_page=dev.get("k_scale_page"), v_scale_page=dev.get("v_scale_page"))
+                        k_scale_page=dev.get("k_scale_page"), v_scale_page=dev.get("v_scale_page"),
+                        q_scale=dev.get("q_scale"))
 
 
 def run_attention(w, dev, num_kv_splits=0, max_kv_len=None, out=None, lse=None, stream=None):
     desc = desc_for(w, dev, num_kv_splits, max_kv_len)
     if out is None:
-        out = torch.empty((w.B, w.H_qo, w.D), dtype=TORCH_STORAGE[w.q_dtype], device="cuda")
-        if w.q_dtype == "bf16":
+        odt = "bf16" if w.q_dtype == "fp8" else w.q_dtype  # fp8 q writes a bf16 out
+        out = torch.empty((w.B, w.H_qo, w.D), dtype=TORCH_STORAGE[odt], device="cuda")
+        if odt == "bf16":
             out.view(torch.int16).fill_(0x7FC0)   # NaN: any element not written shows
         else:
             out.fill_(float("nan"))

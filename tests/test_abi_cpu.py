@@ -276,3 +276,23 @@ def test_page_scale_arguments(L):
     P = FAKE
     assert L.pdecode_append_attention(ctypes.byref(ok), P, P, P, P, P, P, P, None, 0.1, P, P, P,
                                       1 << 30, None) == 2
+
+
+def test_fp8_q_arguments(L):
+    """fp8 q: its per-q-head scales are required, and only with it (INVALID_ARG); it pairs with a
+    BF16 or FP8 pool on the persistent schedule, not with the fused append or an fp32 pool, and
+    the append takes no fp8 rows (UNSUPPORTED) -- refused on the host."""
+    def fp8q(d, scale=True):
+        d.q_scale = FAKE.value if scale else None
+        return d
+
+    assert attention_status(L, desc(q_dtype="fp8")) == 1                 # no q_scale
+    assert attention_status(L, fp8q(desc())) == 1                        # q_scale with bf16 q
+    assert attention_status(L, fp8q(desc(q_dtype="fp8", kv_dtype="f32"))) == 2
+    assert attention_status(L, fp8q(desc(q_dtype="fp8", batch=2000, max_num_pages=1 << 16))) == 2
+    ok = fp8q(desc(q_dtype="fp8", kv_dtype="bf16"))
+    assert pk.workspace_bytes(ok) > 0
+    P = FAKE
+    assert L.pdecode_append_attention(ctypes.byref(ok), P, P, P, P, P, P, P, None, 0.1, P, P, P,
+                                      1 << 30, None) == 2
+    assert L.pdecode_append_kv(ctypes.byref(ok), P, P, P, 4, P, None) == 2

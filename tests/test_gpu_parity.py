@@ -520,6 +520,48 @@ def test_append_page_scales_bitexact():
     assert tpool.cpu().numpy().tobytes() == ref.tobytes()
 
 
+@pytest.mark.parametrize("kv,D,ps,G,splits,window,rope,page_scales", [
+    ("bf16", 128, 16, 4, 0, False, 0, False),   # the Llama-3-8B group with an fp8 q
+    ("fp8", 128, 32, 8, 0, False, 0, False),    # the fp8 GQA-8 shape
+    ("fp8", 64, 16, 2, 3, True, 0, False),
+    ("bf16", 128, 32, 1, 12, False, 0, False),  # the merge kernel
+    ("fp8", 128, 16, 4, 5, False, 1, False),    # rotate-half RoPE
+    ("bf16", 64, 32, 8, 0, False, 2, False),    # interleaved RoPE
+    ("fp8", 128, 32, 4, 3, False, 0, True),     # with per-page K/V scales
+    ("fp8e4m3", 128, 16, 2, 0, False, 0, False),
+])
+def test_fp8_q(kv, D, ps, G, splits, window, rope, page_scales):
+    """q as e4m3fn codes with a scale per q head: converted exactly to bf16 in the kernel, the
+    head's scale applied to its column's scores; out is bf16. Every output against the oracle."""
+    lens = [1, ps - 1, ps + 1, 5 * ps + 3, 1700, 0, 2 * ps]
+    w = synth.make_workload(name=f"q8_{kv}_D{D}_ps{ps}_G{G}_s{splits}_w{int(window)}_r{rope}",
+                            B=len(lens), H_qo=2 * G, H_kv=2, D=D, page_size=ps, seq_lens=lens,
+                            q_dtype="fp8", kv_dtype=kv, seed=1300 + D + ps + G + splits + rope,
+                            max_num_pages=512, page_scales=page_scales,
+                            window=300 if window else None, sink=4 if window else 0,
+                            rotary_mode=rope, rope_theta=5e5)
+    run_and_check(w, num_kv_splits=splits)
+
+
+def test_fp8_q_full_size():
+    """The Llama-3-8B workload's shape and lengths with an fp8 q, automatic plan."""
+    base = synth.llama3_8b_bf16()
+    w = synth.make_workload(name="llama_fp8_q", B=32, H_qo=32, H_kv=8, D=128, page_size=16,
+                            seq_lens=base.seq_lens.astype(np.int64), max_num_pages=16384,
+                            q_dtype="fp8", seed=1002)
+    run_and_check(w)
+
+
+@pytest.mark.parametrize("kv,G,T,splits", [("bf16", 4, 2, 0), ("fp8", 2, 4, 12), ("fp8", 8, 2, 3)])
+def test_fp8_q_multi(kv, G, T, splits):
+    """Several query tokens with an fp8 q."""
+    w = synth.make_workload(name=f"q8_multi_{kv}_G{G}_T{T}_s{splits}", B=5, H_qo=2 * G, H_kv=2,
+                            D=128, page_size=16 if kv == "bf16" else 32,
+                            seq_lens=[3000, T - 1, 700, 33, 64], q_dtype="fp8", kv_dtype=kv,
+                            seed=1400 + G + T + splits, max_num_pages=512)
+    _multi_case(w, T, seed=141, num_kv_splits=splits)
+
+
 def test_fp8_decode_all_codes():
     """Every finite e4m3fn code, read through decode with one attended row and v_scale = 1: the
     bf16 output equals the code's value exactly (all e4m3fn values are bf16 values)."""
