@@ -155,6 +155,20 @@ size_t pdecode_workspace_bytes(const pdecode_desc *d);
  * chunks per sequence. Returns PDECODE_OK or an argument error. */
 pdecode_status pdecode_plan(const pdecode_desc *d, int32_t *chunk_pages, int32_t *num_chunks);
 
+/* Inspection of a split plan (debugging; the survey's per-split partial dump): where a call on a
+ * workspace of pdecode_workspace_bytes(_multi)(d[, qo_len]) bytes leaves its split partial states.
+ * Byte offsets into the workspace of part_o [B, qo_len, H_qo, C, D] fp32 (normalised partial
+ * outputs) and part_lse [B, qo_len, H_qo, C] fp32 (base-2 log-sum-exp), C = *num_chunks, and of
+ * the int32 chunk size in page slots that the persistent schedule's automatic plan chose (valid
+ * once the call has run). Chunk c of a split sequence holds the state of the decode over that
+ * chunk's rows alone; rows of sequences that did not split, and chunks past a sequence's count,
+ * hold whatever an earlier call left. All offsets are 0 when the plan has no partial states.
+ * Returns PDECODE_OK or an argument error. Setting PDECODE_DEBUG in the environment makes every
+ * attention call print its plan to stderr. */
+pdecode_status pdecode_workspace_layout(const pdecode_desc *d, int32_t qo_len,
+                                        size_t *part_o_offset, size_t *part_lse_offset,
+                                        size_t *plan_word_offset, int32_t *num_chunks);
+
 /* Decode attention (see the header comment for the computation and layouts).
  * q, pages, page_indptr, page_values, length_info, out, lse: device pointers as above.
  * rope: NULL or a host struct. sm_scale: the score scale (typically 1/sqrt(head_dim)).

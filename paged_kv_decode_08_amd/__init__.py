@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.pdecode_plan.restype = _c_i32
         L.pdecode_plan.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(_c_i32),
                                    ctypes.POINTER(_c_i32)]
+        sz = ctypes.POINTER(ctypes.c_size_t)
+        L.pdecode_workspace_layout.restype = _c_i32
+        L.pdecode_workspace_layout.argtypes = [ctypes.POINTER(Desc), _c_i32, sz, sz, sz,
+                                               ctypes.POINTER(_c_i32)]
         L.pdecode_attention.restype = _c_i32
         L.pdecode_attention.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P,
                                         ctypes.POINTER(Rope), ctypes.c_float, P, P, P,
@@ -158,6 +162,18 @@ def plan(desc: Desc):
     if st:
         raise PdecodeError(st, "pdecode_plan")
     return cp.value, nc.value
+
+
+def workspace_layout(desc: Desc, qo_len: int = 1) -> dict:
+    """pdecode_workspace_layout: byte offsets of the split partial states (part_o, part_lse)
+    and of the automatic plan's chunk-size word in a workspace, and the chunk cap."""
+    o, l, w = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    nc = _c_i32(0)
+    st = lib().pdecode_workspace_layout(ctypes.byref(desc), int(qo_len), ctypes.byref(o),
+                                        ctypes.byref(l), ctypes.byref(w), ctypes.byref(nc))
+    if st:
+        raise PdecodeError(st, "pdecode_workspace_layout")
+    return {"part_o": o.value, "part_lse": l.value, "plan_word": w.value, "num_chunks": nc.value}
 
 
 def alloc_workspace(desc: Desc, device="cuda") -> torch.Tensor | None:

@@ -6,6 +6,8 @@
 
 #include <climits>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 
 #include "api_internal.hpp"
 #include "launch.hpp"
@@ -143,6 +145,13 @@ Plan make_plan(const pdecode_desc* d, int qo_len = 1) {
 
 pdecode_status hip_status(hipError_t e) { return e == hipSuccess ? PDECODE_OK : PDECODE_ERR_HIP; }
 
+// PDECODE_DEBUG set (to anything) in the environment: every attention call prints its plan to
+// stderr. Read once.
+bool debug_enabled() {
+  static const bool on = std::getenv("PDECODE_DEBUG") != nullptr;
+  return on;
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,6 +170,27 @@ const char* pdecode_status_string(pdecode_status s) {
 size_t pdecode_workspace_bytes(const pdecode_desc* d) {
   if (check_desc(d) != PDECODE_OK || check_attention_shape(d) != PDECODE_OK) return 0;
   return make_plan(d).workspace_bytes();
+}
+
+pdecode_status pdecode_workspace_layout(const pdecode_desc* d, int32_t qo_len,
+                                        size_t* part_o_offset, size_t* part_lse_offset,
+                                        size_t* plan_word_offset, int32_t* num_chunks) {
+  pdecode_status st = check_desc(d);
+  if (st != PDECODE_OK) return st;
+  if ((st = check_attention_shape(d)) != PDECODE_OK) return st;
+  if (qo_len < 1 || !part_o_offset || !part_lse_offset || !plan_word_offset || !num_chunks)
+    return PDECODE_ERR_INVALID_ARG;
+  const Plan pl = make_plan(d, qo_len);
+  *num_chunks = pl.num_chunks;
+  if (pl.part_o_bytes == 0) {
+    *part_o_offset = *part_lse_offset = *plan_word_offset = 0;
+    return PDECODE_OK;
+  }
+  *part_o_offset = pl.counter_bytes;
+  *part_lse_offset = pl.counter_bytes + pl.part_o_bytes;
+  *plan_word_offset = pl.counter_bytes + pl.part_o_bytes +
+                      size_t(pl.max_jobs) * qo_len * (d->num_qo_heads / d->num_kv_heads) * 4;
+  return PDECODE_OK;
 }
 
 pdecode_status pdecode_plan(const pdecode_desc* d, int32_t* chunk_pages, int32_t* num_chunks) {
@@ -276,6 +306,15 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   p.chunk_slots = pl.chunk_slots;
   p.num_chunks = pl.num_chunks;
   p.auto_chunk = pl.auto_chunk ? 1 : 0;
+  if (debug_enabled())
+    std::fprintf(stderr,
+                 "pdecode: B=%d H_qo=%d H_kv=%d D=%d page=%d T=%d q=%d kv=%d %s plan: %s chunks of "
+                 "%d slots, at most %d per sequence; workspace %zu bytes%s\n",
+                 d->batch, d->num_qo_heads, d->num_kv_heads, d->head_dim, d->page_size, qo_len,
+                 d->q_dtype, d->kv_dtype, fused ? "fused append," : "",
+                 pl.persistent ? "persistent," : "one workgroup per chunk,",
+                 pl.auto_chunk ? 0 : pl.chunk_slots, pl.num_chunks, pl.workspace_bytes(),
+                 pl.auto_chunk ? " (chunk size chosen on the device; see the plan word)" : "");
   const int cols = p.G * qo_len;  // q columns of the matrix-core B operand
   const int gp = cols <= 1 ? 1 : cols <= 2 ? 2 : cols <= 4 ? 4 : cols <= 8 ? 8 : 16;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -296,3 +296,40 @@ def test_fp8_q_arguments(L):
     assert L.pdecode_append_attention(ctypes.byref(ok), P, P, P, P, P, P, P, None, 0.1, P, P, P,
                                       1 << 30, None) == 2
     assert L.pdecode_append_kv(ctypes.byref(ok), P, P, P, 4, P, None) == 2
+
+
+def test_workspace_layout(L):
+    """pdecode_workspace_layout: partial states after the counters, the plan word after the lse
+    rows, all inside the workspace; zeros without partial states."""
+    d = desc(batch=4)
+    lay = pk.workspace_layout(d)
+    C = lay["num_chunks"]
+    rows = 4 * 32 * C
+    assert lay["part_o"] >= (4 * 8 + 2) * 4 and lay["part_o"] % 256 == 0
+    assert lay["part_lse"] >= lay["part_o"] + rows * 128 * 4
+    assert lay["plan_word"] == lay["part_lse"] + rows * 4
+    assert lay["plan_word"] + 4 <= pk.workspace_bytes(d)
+    lay1 = pk.workspace_layout(desc(num_kv_splits=1))
+    assert lay1["num_chunks"] == 1 and lay1["part_o"] == lay1["part_lse"] == lay1["plan_word"] == 0
+
+
+def test_debug_env_prints_the_plan(tmp_path):
+    """PDECODE_DEBUG in the environment: an attention call prints its plan to stderr (checked in a
+    child process on the CPU, where the launch itself then fails with PDECODE_ERR_HIP)."""
+    import subprocess
+    import sys
+    code = (
+        "import ctypes, sys\n"
+        f"sys.path.insert(0, {os.path.dirname(os.path.dirname(os.path.abspath(__file__)))!r})\n"
+        "import paged_kv_decode_08_amd as pk\n"
+        "L = pk.lib()\n"
+        "d = pk.make_desc(batch=4, num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16,\n"
+        "                 max_num_pages=100, q_dtype='bf16', kv_dtype='bf16', max_kv_len=4096)\n"
+        "P = ctypes.c_void_p(0x1000)\n"
+        "st = L.pdecode_attention(ctypes.byref(d), P, P, P, P, P, None, 0.1, P, P, P, 1 << 30, None)\n"
+        "print('status', st)\n")
+    env = dict(os.environ, PDECODE_DEBUG="1", HIP_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=120)
+    assert "pdecode: B=4 H_qo=32 H_kv=8 D=128 page=16" in r.stderr, r.stderr
+    assert "persistent" in r.stderr

@@ -562,6 +562,81 @@ def test_fp8_q_multi(kv, G, T, splits):
     _multi_case(w, T, seed=141, num_kv_splits=splits)
 
 
+def _persist_chunk_bounds(n, cs, cap, ps):
+    """Page-slot bounds of the chunks the persistent schedule cuts a sequence of n slots into with
+    chunk size cs and at most cap chunks: whole multiples of A = 8 16-row items, the last chunk
+    taking the rest (the kernel's rule, restated)."""
+    A = 8 if ps == 16 else 4
+    if n <= 0:
+        return []
+    nch = min(-(-n // cs), cap)
+    u = n // A
+    if nch > 1 and nch > u:
+        nch = max(u, 1)
+    if nch == 1:
+        return [(0, n)]
+    uq, urem = u // nch, u % nch
+    out = []
+    for c in range(nch):
+        sb = A * (c * uq + min(c, urem))
+        se = n if c == nch - 1 else sb + A * (uq + (1 if c < urem else 0))
+        out.append((sb, se))
+    return out
+
+
+@pytest.mark.parametrize("kv,splits", [("bf16", 0), ("bf16", 5), ("fp8", 0)])
+def test_split_partials_match_oracle_per_chunk(kv, splits):
+    """The split partial states a call leaves in its workspace (pdecode_workspace_layout, the
+    debug view of a split plan): chunk c of every split (sequence, q head) holds the decode over
+    that chunk's rows alone (out normalised, lse base 2), against the oracle run on just those
+    rows. With the automatic plan the chunk size is the one the kernel wrote to the plan word."""
+    import paged_kv_decode_08_amd as pk
+    ps = 16 if kv == "bf16" else 32
+    lens = [3000, 17, 1200, 641, 2500, 90, 4100]
+    w = synth.make_workload(name=f"partials_{kv}_{splits}", B=len(lens), H_qo=8, H_kv=2, D=128,
+                            page_size=ps, seq_lens=lens, kv_dtype=kv, seed=1500 + splits,
+                            max_num_pages=2048)
+    dev = gu.upload(w)
+    desc = gu.desc_for(w, dev, num_kv_splits=splits)
+    ws = pk.alloc_workspace(desc)
+    out = torch.empty((w.B, w.H_qo, w.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H_qo), dtype=torch.float32, device="cuda")
+    pk.attention(desc, dev["q"], dev["pages"], dev["indptr"], dev["values"], dev["length_info"],
+                 out, lse, w.sm_scale, workspace=ws)
+    torch.cuda.synchronize()
+    lay = pk.workspace_layout(desc)
+    cp, _ = pk.plan(desc)
+    C = lay["num_chunks"]
+    wsn = ws.cpu().numpy()
+    cs = cp if cp else int(wsn[lay["plan_word"]:lay["plan_word"] + 4].view(np.int32)[0])
+    assert cs >= 1
+    rows = w.B * w.H_qo * C
+    part_o = wsn[lay["part_o"]:lay["part_o"] + rows * w.D * 4].view(np.float32).reshape(
+        w.B, w.H_qo, C, w.D)
+    part_lse = wsn[lay["part_lse"]:lay["part_lse"] + rows * 4].view(np.float32).reshape(
+        w.B, w.H_qo, C)
+    checked = 0
+    for b in range(w.B):
+        beg, end = int(w.page_indptr[b]), int(w.page_indptr[b + 1])
+        bounds = _persist_chunk_bounds(end - beg, cs, C, ps)
+        if len(bounds) < 2:
+            continue
+        for c, (sb, se) in enumerate(bounds):
+            r1 = min(se * ps, int(lens[b]))
+            kw = w.oracle_kwargs()
+            kw.update(B=1, q=w.q[b:b + 1], indptr=np.array([0, se - sb], np.int32),
+                      values=w.page_values[beg + sb:beg + se].copy(),
+                      length_info=np.array([r1 - (se - 1) * ps], np.int32),
+                      q_rope_position=None, k_rope_pos_offset=None)
+            o_ref, l_ref = oracle.decode(**kw)
+            do, ratio = gu.row_error(w, o_ref[0], part_o[b, :, c].astype(np.float64))
+            dl = float(np.abs(part_lse[b, :, c] - l_ref[0]).max())
+            assert do <= 2e-2 and ratio <= 1.0 and dl <= 1e-3, (b, c, do, ratio, dl)
+            checked += 1
+    print(f"{w.name}: chunk size {cs}, {checked} chunk states checked", flush=True)
+    assert checked >= 8
+
+
 def test_fp8_decode_all_codes():
     """Every finite e4m3fn code, read through decode with one attended row and v_scale = 1: the
     bf16 output equals the code's value exactly (all e4m3fn values are bf16 values)."""
