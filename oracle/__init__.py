@@ -5,7 +5,8 @@ tests, the smoke check and the benchmark's CPU-baseline leg may import this pack
 library never does, and the two share no code.
 
 Every function takes and returns host NumPy arrays. Floating-point results are fp64.
-dtype codes: 0 = fp32, 1 = bf16 (raw uint16 bits), 2 = fp8 e4m3fn (raw uint8 bits).
+dtype codes: 0 = fp32, 1 = bf16 (raw uint16 bits), 2 = fp8 e4m3fn, 3 = IEEE-style e4m3 (max 240),
+4 = fp8 e5m2 (the fp8 codes as raw uint8 bits).
 
 What each function follows is cited in ``oracle.cpp``. Parity against the pages is pinned by the
 ``-m "not gpu"`` tests. The RoPE convention, whose helper body the pages do not show, is pinned
@@ -20,6 +21,7 @@ import numpy as np
 from .build import LIB, build
 
 F32, BF16, FP8 = 0, 1, 2
+FP8_E4M3, FP8_E5M2 = 3, 4
 
 _lib = None
 
@@ -52,6 +54,10 @@ def lib():
         L.oracle_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
         L.oracle_fp8_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_fp8_e4m3_encode.argtypes = [f32]
+        L.oracle_fp8_e5m2_value.restype = ctypes.c_double
+        L.oracle_fp8_e5m2_value.argtypes = [ctypes.c_uint8]
+        L.oracle_fp8_e5m2_encode.restype = ctypes.c_uint8
+        L.oracle_fp8_e5m2_encode.argtypes = [f32]
         L.oracle_bf16_value.restype = ctypes.c_double
         L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
         L.oracle_rope_rotate.restype = None
@@ -276,6 +282,15 @@ def fp8_e4m3_value(code: int) -> float:
 
 def fp8_e4m3_encode(x: float) -> int:
     return int(lib().oracle_fp8_e4m3_encode(x))
+
+
+def fp8_e5m2_value(code: int) -> float:
+    """OCP e5m2 (bias 15, max 57344): value of a code."""
+    return float(lib().oracle_fp8_e5m2_value(code))
+
+
+def fp8_e5m2_encode(x: float) -> int:
+    return int(lib().oracle_fp8_e5m2_encode(x))
 
 
 def bf16_value(bits: int) -> float:

@@ -28,6 +28,9 @@
 //     saturating to +-448. The same docs' default NON_OCP mode takes float8_e4m3 with max 240:
 //     read as the IEEE-style e4m3 (bias 7, exponent 15 = infinity / NaN), encoded the same way
 //     with saturation to +-240.
+//   * fp8 e5m2 pool (the e5m2 entry of the survey's fp8 extras; the pages name no e5m2 format):
+//     read as OCP float8 e5m2 (bias 15, exponent 31 = infinity / NaN, max 1.75 * 2^15 = 57344),
+//     encoded the same way, saturating to +-57344.
 //
 // Readings where the pages are silent (the helper bodies _get_kv_chunk_len, _get_seq_offset and
 // _rope are imported but not shown):
@@ -54,8 +57,9 @@ namespace {
 
 // DT_FP8: OCP e4m3fn (max 448); DT_FP8_E4M3: the IEEE-style e4m3 of the attention_block_tkg
 // page's default NON_OCP dtype mode (max 240: exponent 15 holds infinities and NaN).
-enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_FP8_E4M3 = 3 };
-bool is_fp8(int dt) { return dt == DT_FP8 || dt == DT_FP8_E4M3; }
+// DT_FP8_E5M2: OCP e5m2 (max 57344).
+enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_FP8_E4M3 = 3, DT_FP8_E5M2 = 4 };
+bool is_fp8(int dt) { return dt == DT_FP8 || dt == DT_FP8_E4M3 || dt == DT_FP8_E5M2; }
 
 int elem_bytes(int dt) { return dt == DT_F32 ? 4 : dt == DT_BF16 ? 2 : is_fp8(dt) ? 1 : 0; }
 
@@ -94,10 +98,27 @@ double fp8_e4m3_value(uint8_t c) {
   return s ? -mag : mag;
 }
 
+// OCP e5m2: sign, 5 exponent bits (bias 15), 2 mantissa bits; exponent 0 is subnormal;
+// exponent 31 is infinity (mantissa 0) or NaN; the largest finite value is 1.75 * 2^15 = 57344.
+double fp8_e5m2_value(uint8_t c) {
+  int s = (c >> 7) & 1, e = (c >> 2) & 31, m = c & 3;
+  double mag;
+  if (e == 31) {
+    if (m != 0) return std::nan("");
+    mag = HUGE_VAL;
+  } else if (e == 0) {
+    mag = std::ldexp(m / 4.0, -14);
+  } else {
+    mag = std::ldexp(1.0 + m / 4.0, e - 15);
+  }
+  return s ? -mag : mag;
+}
+
 double load_value(const void* base, int dt, size_t idx) {
   if (dt == DT_F32) return static_cast<const float*>(base)[idx];
   if (dt == DT_BF16) return bf16_value(static_cast<const uint16_t*>(base)[idx]);
   if (dt == DT_FP8_E4M3) return fp8_e4m3_value(static_cast<const uint8_t*>(base)[idx]);
+  if (dt == DT_FP8_E5M2) return fp8_e5m2_value(static_cast<const uint8_t*>(base)[idx]);
   return fp8_value(static_cast<const uint8_t*>(base)[idx]);
 }
 
@@ -131,6 +152,25 @@ uint8_t fp8_e4m3_encode(float x) {
   double best_err = a;
   for (int c = 1; c <= 0x77; ++c) {
     double err = std::fabs(a - fp8_e4m3_value(static_cast<uint8_t>(c)));
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return sign | static_cast<uint8_t>(best);
+}
+
+// Nearest e5m2 code to a float, ties to the even code, saturating to +-57344 (finite codes only).
+// Brute force over the 123 non-negative finite codes.
+uint8_t fp8_e5m2_encode(float x) {
+  if (std::isnan(x)) return 0x7F;
+  uint8_t sign = std::signbit(x) ? 0x80 : 0x00;
+  double a = std::fabs(static_cast<double>(x));
+  if (a >= 57344.0) return sign | 0x7B;
+  int best = 0;
+  double best_err = a;
+  for (int c = 1; c <= 0x7B; ++c) {
+    double err = std::fabs(a - fp8_e5m2_value(static_cast<uint8_t>(c)));
     if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
       best = c;
       best_err = err;
@@ -278,6 +318,8 @@ double oracle_fp8_e4m3fn_value(uint8_t code) { return fp8_value(code); }
 uint8_t oracle_fp8_e4m3fn_encode(float x) { return fp8_encode(x); }
 double oracle_fp8_e4m3_value(uint8_t code) { return fp8_e4m3_value(code); }
 uint8_t oracle_fp8_e4m3_encode(float x) { return fp8_e4m3_encode(x); }
+double oracle_fp8_e5m2_value(uint8_t code) { return fp8_e5m2_value(code); }
+uint8_t oracle_fp8_e5m2_encode(float x) { return fp8_e5m2_encode(x); }
 double oracle_bf16_value(uint16_t bits) { return bf16_value(bits); }
 
 // Applies the RoPE reading to x[D] in place at position pos (exposed for the invariant pins).
@@ -379,7 +421,9 @@ int32_t oracle_append_kv(int32_t T, int32_t H_kv, int32_t D, int32_t ps, int32_t
             const float* tab = kv == 0 ? k_scale_page : v_scale_page;
             float sc = tab ? tab[page * H_kv + h] : (kv == 0 ? k_scale[h] : v_scale[h]);
             static_cast<uint8_t*>(pages)[di] =
-                kv_dtype == DT_FP8 ? fp8_encode(x / sc) : fp8_e4m3_encode(x / sc);
+                kv_dtype == DT_FP8        ? fp8_encode(x / sc)
+                : kv_dtype == DT_FP8_E5M2 ? fp8_e5m2_encode(x / sc)
+                                          : fp8_e4m3_encode(x / sc);
           } else {
             std::memcpy(static_cast<uint8_t*>(pages) + di * kb,
                         static_cast<const uint8_t*>(src) + si * ib, kb);

@@ -25,13 +25,15 @@ import numpy as np
 import torch
 
 # "fp8": OCP e4m3fn codes; "fp8e4m3": IEEE-style e4m3 codes (max 240), drawn within +-240 where
-# both formats give the same code to every value
-DTYPE_CODE = {"f32": 0, "bf16": 1, "fp8": 2, "fp8e4m3": 3}
+# both formats give the same code to every value; "fp8e5m2": OCP e5m2 codes
+DTYPE_CODE = {"f32": 0, "bf16": 1, "fp8": 2, "fp8e4m3": 3, "fp8e5m2": 4}
+FP8_POOLS = ("fp8", "fp8e4m3", "fp8e5m2")
 Q_PAYLOAD_SIGMA = 112.0  # fp8 q: spread of the codes, a quarter of e4m3fn's range
-STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "fp8e4m3": np.uint8}
-ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "fp8e4m3": 1}
+STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "fp8e4m3": np.uint8,
+           "fp8e5m2": np.uint8}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "fp8e4m3": 1, "fp8e5m2": 1}
 POISON = {"f32": np.float32(np.nan).view(np.uint32), "bf16": 0x7FC0, "fp8": 0x7F,
-          "fp8e4m3": 0x7F}
+          "fp8e4m3": 0x7F, "fp8e5m2": 0x7F}
 
 
 def _rng(seed: int, stream: int) -> np.random.Generator:
@@ -50,6 +52,8 @@ def cast_f32(x: np.ndarray, dtype: str) -> np.ndarray:
         return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     if dtype == "fp8e4m3":  # within +-240 the e4m3fn code is the e4m3 code
         return torch.clamp(t, -240.0, 240.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    if dtype == "fp8e5m2":
+        return torch.clamp(t, -57344.0, 57344.0).to(torch.float8_e5m2).view(torch.uint8).numpy()
     raise ValueError(dtype)
 
 
@@ -155,13 +159,13 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
     pool = poisoned_pool(max_num_pages, H_kv, ps, D, kv_dtype)
     order = np.sort(ids)
     k_scale = v_scale = None
-    if kv_dtype in ("fp8", "fp8e4m3"):
+    if kv_dtype in FP8_POOLS:
         rng_sc = _rng(seed, 4)
         k_scale = rng_sc.uniform(*scale_range, size=H_kv).astype(np.float32)
         v_scale = rng_sc.uniform(*scale_range, size=H_kv).astype(np.float32)
     k_scale_page = v_scale_page = None
     if page_scales:
-        assert kv_dtype in ("fp8", "fp8e4m3"), "per-page scales are for fp8 pools"
+        assert kv_dtype in FP8_POOLS, "per-page scales are for fp8 pools"
         rng_ps = _rng(seed, 5)
         k_scale_page = rng_ps.uniform(*scale_range, size=(max_num_pages, H_kv)).astype(np.float32)
         v_scale_page = rng_ps.uniform(*scale_range, size=(max_num_pages, H_kv)).astype(np.float32)
@@ -170,7 +174,7 @@ def make_workload(*, name="custom", B, H_qo, H_kv, D, page_size, seq_lens, max_n
     def fill(i):
         blk = order[i * CH:(i + 1) * CH]
         x = _rng(seed, 1000 + i).standard_normal((blk.size, 2, H_kv, ps, D), dtype=np.float32)
-        if kv_dtype in ("fp8", "fp8e4m3"):
+        if kv_dtype in FP8_POOLS:
             x *= np.float32(fp8_payload_sigma)
             np.clip(x, -448.0, 448.0, out=x)
         elif kv_sigma != 1.0:

@@ -22,6 +22,8 @@ def to_f64(x, dtype):
         # finite IEEE-style e4m3 codes (exponent below 15) have their e4m3fn values
         assert not np.any(((x & 0x78) == 0x78) & ((x & 0x7F) != 0x7F)), "non-finite e4m3 code"
         return torch.from_numpy(x).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    if dtype == "fp8e5m2":
+        return torch.from_numpy(x).view(torch.float8_e5m2).to(torch.float64).numpy()
     raise ValueError(dtype)
 
 
@@ -32,7 +34,7 @@ def contiguous_kv(w, b, h):
     blk = to_f64(w.pages[pages], w.kv_dtype)  # [np, 2, H_kv, ps, D]
     K = blk[:, 0, h].reshape(-1, w.D)[:total]
     V = blk[:, 1, h].reshape(-1, w.D)[:total]
-    if w.kv_dtype in ("fp8", "fp8e4m3"):
+    if w.kv_dtype in ("fp8", "fp8e4m3", "fp8e5m2"):
         if getattr(w, "k_scale_page", None) is not None:
             # row r of the flattened cache sits on page r // ps of the sequence
             ks = np.repeat(w.k_scale_page[pages, h].astype(np.float64), w.page_size)[:total]

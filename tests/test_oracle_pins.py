@@ -856,6 +856,115 @@ def test_fp8_e4m3_pool_matches_dense_bruteforce():
             assert abs(lse[b, hq] - l) < 1e-12
 
 
+# ---- OCP e5m2 (bias 15, max 57344)
+
+def _golden(name):
+    path = os.path.join(os.path.dirname(__file__), "golden", name)
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if line:
+            code, val = line.split()
+            yield int(code, 16), (float.fromhex(val) if "p" in val else float(val))
+
+
+def test_fp8_e5m2_values_definition_and_library():
+    """The fixture's closed-form values, then every code against torch's float8_e5m2 view."""
+    import torch
+    n = 0
+    for code, want in _golden("fp8_e5m2_values.txt"):
+        got = oracle.fp8_e5m2_value(code)
+        assert (np.isnan(got) and np.isnan(want)) or (got == want and
+                                                    np.signbit(got) == np.signbit(want)), hex(code)
+        n += 1
+    assert n >= 12
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).to(torch.float64).numpy()
+    ours = np.array([oracle.fp8_e5m2_value(c) for c in range(256)])
+    assert ((lib == ours) | (np.isnan(lib) & np.isnan(ours))).all()
+    # table shape: strictly increasing over the 124 non-negative finite codes, 4 codes a binade
+    pos = ours[:0x7C]
+    assert np.all(np.diff(pos) > 0) and np.sum(np.isfinite(ours)) == 248
+    for e in range(1, 31):
+        steps = np.diff(pos[4 * e:4 * e + 4])
+        assert np.all(steps == steps[0])
+
+
+def test_fp8_e5m2_encode_roundtrip_ties_saturation_and_library():
+    """Every finite code round-trips; midpoints go to the even code; torch's nearest-even cast
+    agrees inside the range; from 57344 up (infinity included) the encode saturates; NaN stays
+    NaN."""
+    import torch
+    vals = [oracle.fp8_e5m2_value(c) for c in range(256)]
+    for c in range(256):
+        if np.isfinite(vals[c]):
+            assert oracle.fp8_e5m2_encode(vals[c]) == c, hex(c)
+    for c in range(0, 0x7B):
+        mid = (vals[c] + vals[c + 1]) / 2
+        if np.float32(mid) == mid:
+            assert oracle.fp8_e5m2_encode(mid) == (c if c % 2 == 0 else c + 1), hex(c)
+    rng = np.random.default_rng(15)
+    x = np.concatenate([rng.standard_normal(3000) * 300, rng.standard_normal(1000) * 1e-4,
+                        rng.uniform(-57344, 57344, 1000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    got = np.array([oracle.fp8_e5m2_encode(float(v)) for v in x], np.uint8)
+    assert np.array_equal(got, ref)
+    for big in (57344.0, 60000.0, 61439.0, 1e6, np.inf):
+        assert oracle.fp8_e5m2_encode(big) == 0x7B and oracle.fp8_e5m2_encode(-big) == 0xFB
+    nan = oracle.fp8_e5m2_encode(float("nan"))
+    assert (nan & 0x7C) == 0x7C and (nan & 3) != 0
+
+
+@pytest.mark.parametrize("page_scales", [False, True])
+@pytest.mark.parametrize("window", [None, 5])
+def test_fp8_e5m2_pool_matches_dense_bruteforce(page_scales, window):
+    """Decode over an e5m2 pool (per-KV-head or per-page scales, with and without a window)
+    against the textbook softmax on the flattened cache, decoded through torch's e5m2 view."""
+    w = small(kv_dtype="fp8e5m2", q_dtype="bf16", page_order="shuffled", seq_lens=[7, 1, 13],
+              page_scales=page_scales, window=window, sink=2 if window else 0)
+    out, lse = run_oracle(w)
+    G = w.H_qo // w.H_kv
+    q64 = to_f64(w.q, w.q_dtype)
+    for b in range(w.B):
+        for hq in range(w.H_qo):
+            K, V = contiguous_kv(w, b, hq // G)
+            if window:
+                off, sink = int(w.length_info[1, b]), int(w.length_info[2, b])
+                rows = np.r_[0:sink, off:int(w.seq_lens[b])]
+                K, V = K[rows], V[rows]
+            o, l = dense_attention(q64[b, hq], K, V, w.sm_scale)
+            np.testing.assert_allclose(out[b, hq], o, rtol=0, atol=1e-12)
+            assert abs(lse[b, hq] - l) < 1e-12
+
+
+def test_append_e5m2_matches_library_quantization():
+    """Append into an e5m2 pool: x / scale in fp32, saturated to +-57344, then torch's
+    nearest-even e5m2 cast."""
+    import torch
+    H_kv, D, ps, P = 2, 16, 8, 6
+    pool = synth.poisoned_pool(P, H_kv, ps, D, "fp8e5m2")
+    k, v, slots = synth.append_inputs(T=7, H_kv=H_kv, D=D, page_size=ps, max_num_pages=P,
+                                      in_dtype="bf16", seed=18, skip_every=3)
+    ks = np.array([0.5 / 448, 1e-5], np.float32)  # the second drives values past 57344
+    vs = np.array([1.0 / 448, 0.75 / 448], np.float32)
+    before = pool.copy()
+    oracle.append_kv(pages=pool, new_k=k, new_v=v, slots=slots, H_kv=H_kv, D=D, ps=ps,
+                     in_dtype=1, kv_dtype=4, k_scale=ks, v_scale=vs)
+    kf = to_f64(k, "bf16").astype(np.float32)
+    vf = to_f64(v, "bf16").astype(np.float32)
+    expect = before.copy()
+    saturated = 0
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        for kv, x, sc in ((0, kf, ks), (1, vf, vs)):
+            y = x[t] / sc[:, None]
+            saturated += int((np.abs(y) >= 57344).sum())
+            y = np.clip(y, -57344, 57344)
+            expect[s // ps, kv, :, s % ps, :] = (torch.from_numpy(np.ascontiguousarray(y))
+                                                 .to(torch.float8_e5m2).view(torch.uint8).numpy())
+    assert saturated > 0
+    assert expect.tobytes() == pool.tobytes()
+
+
 # ---------------------------------------------------------------- fp8 pools with per-page scales
 # A scale per (page, KV head) block, in place of one per KV head: a stored value is still code x
 # scale, with the scale of the block that holds the row.
