@@ -67,19 +67,28 @@ typedef enum pdecode_dtype {
   PDECODE_F32 = 0,
   PDECODE_BF16 = 1,
   PDECODE_FP8_E4M3FN = 2,               /* OCP e4m3fn: bias 7, no infinities, max 448            */
-  PDECODE_FP8_E4M3 = 3                  /* IEEE-style e4m3: bias 7, exponent 15 = inf / NaN, max
+  PDECODE_FP8_E4M3 = 3,                 /* IEEE-style e4m3: bias 7, exponent 15 = inf / NaN, max
                                            240 (the AWS attention_block_tkg page's default
                                            NON_OCP float8_e4m3). As a pool: the append writes it
                                            (round to nearest even, saturating to +-240); a pool
                                            read by the decode must hold finite codes, which have
                                            their e4m3fn values. Not with pdecode_append_attention. */
+  PDECODE_FP8_E5M2 = 4                  /* OCP e5m2: bias 15, exponent 31 = inf / NaN, max 57344
+                                           (the e5m2 of the fp8 extras; the pages name no e5m2).
+                                           As a pool only: the append writes it (round to nearest
+                                           even, saturating to +-57344); the decode reads finite
+                                           codes exactly, with per-KV-head or per-page scales, on
+                                           the persistent schedule (batch <= 1024), one query
+                                           token, no RoPE or rotate-half RoPE; not with
+                                           pdecode_append_attention or pdecode_attention_multi. */
 } pdecode_dtype;
 
 /* Problem description shared by pdecode_attention and pdecode_append_kv.
  * Supported set: head_dim in {64, 128}; page_size in {16, 32}; group size
  * num_qo_heads / num_kv_heads in 1..8; (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
- * (BF16, FP8_E4M3FN), (BF16, FP8_E4M3), (FP8_E4M3FN, BF16 or either FP8)}. The output dtype
- * equals q_dtype, except BF16 for an FP8 q. */
+ * (BF16, FP8_E4M3FN), (BF16, FP8_E4M3), (BF16, FP8_E5M2), (FP8_E4M3FN, BF16 or any FP8)}
+ * (FP8_E5M2 pools within the limits given at PDECODE_FP8_E5M2). The output dtype equals
+ * q_dtype, except BF16 for an FP8 q. */
 typedef struct pdecode_desc {
   int32_t batch;          /* B >= 0                                                            */
   int32_t num_qo_heads;   /* H_qo > 0, a multiple of num_kv_heads                              */

@@ -14,11 +14,12 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpdecode.so")
 
-F32, BF16, FP8_E4M3FN, FP8_E4M3 = 0, 1, 2, 3
+F32, BF16, FP8_E4M3FN, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
 STATUS = {0: "PDECODE_OK", 1: "PDECODE_ERR_INVALID_ARG", 2: "PDECODE_ERR_UNSUPPORTED",
           3: "PDECODE_ERR_WORKSPACE_TOO_SMALL", 4: "PDECODE_ERR_HIP"}
-_DTYPE_CODE = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3FN, "fp8e4m3": FP8_E4M3}
-_ELEM_BYTES = {F32: 4, BF16: 2, FP8_E4M3FN: 1, FP8_E4M3: 1}
+_DTYPE_CODE = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3FN, "fp8e4m3": FP8_E4M3,
+               "fp8e5m2": FP8_E5M2}
+_ELEM_BYTES = {F32: 4, BF16: 2, FP8_E4M3FN: 1, FP8_E4M3: 1, FP8_E5M2: 1}
 
 _c_i32 = ctypes.c_int32
 _c_ptr = ctypes.c_void_p

@@ -12,6 +12,7 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["decode_mfma.hip", "decode_fused.hip", "decode_multi.hip", "decode_rope_ilv.hip",
+           "decode_e5m2.hip",
            "decode_valu.hip", "merge.hip", "append.hip", "ceiling.hip", "noalloc.hip", "api.cpp"]
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
 # atomic optimizer off: the job-queue ticket is fetched by one lane and consumed a whole job later;

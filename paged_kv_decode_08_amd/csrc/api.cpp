@@ -39,7 +39,9 @@ struct Plan {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-bool is_fp8(int kv) { return kv == PDECODE_FP8_E4M3FN || kv == PDECODE_FP8_E4M3; }
+bool is_fp8(int kv) {
+  return kv == PDECODE_FP8_E4M3FN || kv == PDECODE_FP8_E4M3 || kv == PDECODE_FP8_E5M2;
+}
 
 bool supported_pair(int q, int kv) {
   return (q == PDECODE_F32 && kv == PDECODE_F32) || (q == PDECODE_BF16 && kv == PDECODE_BF16) ||
@@ -54,7 +56,7 @@ pdecode_status check_desc(const pdecode_desc* d) {
     return PDECODE_ERR_INVALID_ARG;
   if (d->num_qo_heads % d->num_kv_heads != 0) return PDECODE_ERR_INVALID_ARG;
   if (d->sliding_window != 0 && d->sliding_window != 1) return PDECODE_ERR_INVALID_ARG;
-  if (d->q_dtype < 0 || d->q_dtype > 2 || d->kv_dtype < 0 || d->kv_dtype > 3)
+  if (d->q_dtype < 0 || d->q_dtype > 2 || d->kv_dtype < 0 || d->kv_dtype > 4)
     return PDECODE_ERR_INVALID_ARG;
   // fp8 scales: per KV head, or per (page, KV head) (both tables or neither; fp8 pools only)
   const bool page_scales = d->k_scale_page != nullptr || d->v_scale_page != nullptr;
@@ -240,6 +242,10 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   if (fused && d->kv_dtype == PDECODE_FP8_E4M3) return PDECODE_ERR_UNSUPPORTED;
   // per-page fp8 scales and fp8 q: the persistent schedule, attention without the fused append
   if ((d->k_scale_page || d->q_scale) && (!pl.persistent || fused)) return PDECODE_ERR_UNSUPPORTED;
+  // e5m2 pool: the persistent single-token kernels, without the fused append or interleaved RoPE
+  if (d->kv_dtype == PDECODE_FP8_E5M2 &&
+      (!pl.persistent || fused || qo_len > 1 || (rotary && rope->rotary_mode == 2)))
+    return PDECODE_ERR_UNSUPPORTED;
   // interleaved RoPE: the persistent matrix-core kernels only
   if (rotary && rope->rotary_mode == 2 && !pl.persistent)
     return PDECODE_ERR_UNSUPPORTED;
@@ -324,7 +330,7 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   // An IEEE-style e4m3 pool holds finite codes only (a precondition; the append saturates to
   // +-240), and every finite code has its e4m3fn value: the decode kernels read it as e4m3fn.
   const int kv_read = d->kv_dtype == PDECODE_FP8_E4M3 ? PDECODE_FP8_E4M3FN : d->kv_dtype;
-  const bool mfma = kv_read == PDECODE_BF16 || kv_read == PDECODE_FP8_E4M3FN;
+  const bool mfma = kv_read == PDECODE_BF16 || is_fp8(kv_read);
   if (mfma)
     st = hip_status(pdk::launch_decode_mfma(p, kv_read, d->head_dim, d->page_size, gp,
                                             pl.persistent, rotary, grid, s));

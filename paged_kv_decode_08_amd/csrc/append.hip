@@ -1,6 +1,7 @@
 // KV append (vLLM nki_flash_attn page, reshape_and_cache): token t's K and V rows go to
 // pages[slot / page_size, 0|1, h, slot % page_size, :] for every KV head; a negative slot (or one
-// past the pool) is skipped. fp8 pools store x / scale[h] (fp32 division) rounded to e4m3fn.
+// past the pool) is skipped. fp8 pools store x / scale (fp32 division) rounded to the pool's
+// format (e4m3fn, IEEE-style e4m3 or e5m2, nearest even, saturating).
 // Vector form: a thread writes 16 bytes of one destination row (8 bf16, 4 fp32 or 16 fp8
 // elements), threads in (token, K|V, head, vector) order, so the reads of the new rows are
 // contiguous and each destination row is written whole. Rows that are not whole 16-byte vectors,
@@ -21,10 +22,16 @@ __device__ __forceinline__ bool append_slot(const AppendParams& p, int t, size_t
   return true;
 }
 
+// x (already divided by its scale) -> the code of fp8 pool type KVT
+template <int KVT> __device__ __forceinline__ uint8_t encode_fp8(float x) {
+  if constexpr (KVT == kFP8E4M3) return f32_to_fp8_e4m3(x);
+  else if constexpr (KVT == kFP8E5M2) return f32_to_fp8_e5m2(x);
+  else return f32_to_fp8(x);
+}
+
 template <int IT, int KVT>
 __global__ __launch_bounds__(256) void append_vec_kernel(AppendParams p, int vpr, long long total) {
   constexpr int EPV = KVT == kF32 ? 4 : KVT == kBF16 ? 8 : 16;  // elements per 16-byte output
-  constexpr bool E4M3 = KVT == kFP8E4M3;
   const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const int v = static_cast<int>(i % vpr);
@@ -54,7 +61,7 @@ __global__ __launch_bounds__(256) void append_vec_kernel(AppendParams p, int vpr
 #pragma unroll
       for (int q = 0; q < 2; ++q) Kv<kBF16>::unpack(s4[q], x + 8 * q);
     }
-    auto enc = [](float v) { return E4M3 ? f32_to_fp8_e4m3(v) : f32_to_fp8(v); };
+    auto enc = [](float v) { return encode_fp8<KVT>(v); };
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -89,7 +96,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
       const float x = load_q<IT>(in, src);
       const float sc = append_scale(p, kv, page, h);
       const float y = __fdiv_rn(x, sc);
-      static_cast<uint8_t*>(p.pages)[dst] = KVT == kFP8E4M3 ? f32_to_fp8_e4m3(y) : f32_to_fp8(y);
+      static_cast<uint8_t*>(p.pages)[dst] = encode_fp8<KVT>(y);
     }
   }
 }
@@ -119,6 +126,8 @@ hipError_t launch_append(const AppendParams& p, int in_dtype, int kv_dtype, hipS
   if (in_dtype == kF32 && kv_dtype == kFP8) return launch_it<kF32, kFP8>(p, st);
   if (in_dtype == kBF16 && kv_dtype == kFP8E4M3) return launch_it<kBF16, kFP8E4M3>(p, st);
   if (in_dtype == kF32 && kv_dtype == kFP8E4M3) return launch_it<kF32, kFP8E4M3>(p, st);
+  if (in_dtype == kBF16 && kv_dtype == kFP8E5M2) return launch_it<kBF16, kFP8E5M2>(p, st);
+  if (in_dtype == kF32 && kv_dtype == kFP8E5M2) return launch_it<kF32, kFP8E5M2>(p, st);
   return hipErrorInvalidValue;
 }
 

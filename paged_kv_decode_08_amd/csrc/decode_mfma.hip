@@ -275,6 +275,16 @@ static hipError_t launch_chunked(const DecodeParams& p, unsigned grid, hipStream
   return hipGetLastError();
 }
 
+// After a persistent decode: the split merge kernel, where split sequences were left to it.
+template <int D, int PS, int GP>
+static hipError_t merge_splits(const DecodeParams& p, hipStream_t st) {
+  if (p.num_chunks <= 1 || merges_in_kernel<GP>(p.num_chunks, p.T > 1)) return hipSuccess;
+  const unsigned rows = static_cast<unsigned>(p.B) * p.T * p.H_qo;
+  hipLaunchKernelGGL((split_merge_kernel<D, PS>), dim3((rows + kMergeRows - 1) / kMergeRows),
+                     dim3(64 * kMergeRows), 0, st, p);
+  return hipGetLastError();
+}
+
 template <int KVT, int D, int PS, int GP, bool ROPE>
 static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipStream_t st) {
   hipError_t e;
@@ -289,11 +299,39 @@ static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipS
     e = p.new_k != nullptr ? launch_persist_fused<KVT, D, PS, GP, ROPE>(p, max_jobs, st)
                            : launch_persist_k<KVT, D, PS, GP, ROPE, false>(p, max_jobs, st);
   }
-  if (e != hipSuccess || p.num_chunks <= 1 || merges_in_kernel<GP>(p.num_chunks, p.T > 1)) return e;
-  const unsigned rows = static_cast<unsigned>(p.B) * p.T * p.H_qo;
-  hipLaunchKernelGGL((split_merge_kernel<D, PS>), dim3((rows + kMergeRows - 1) / kMergeRows),
-                     dim3(64 * kMergeRows), 0, st, p);
-  return hipGetLastError();
+  return e != hipSuccess ? e : merge_splits<D, PS, GP>(p, st);
+}
+
+// e5m2 pool: the persistent schedule, one query token, no fused append, no RoPE or rotate-half
+// RoPE (the host refuses the rest).
+template <int D, int PS, int GP>
+static hipError_t launch_e5m2_g(const DecodeParams& p, bool rope, long long grid, hipStream_t st) {
+  if (p.T != 1 || p.new_k != nullptr || (rope && p.rotary != 1)) return hipErrorInvalidValue;
+  const hipError_t e = rope ? launch_persist_e5m2<D, PS, GP, true>(p, grid, st)
+                            : launch_persist_e5m2<D, PS, GP, false>(p, grid, st);
+  return e != hipSuccess ? e : merge_splits<D, PS, GP>(p, st);
+}
+
+template <int D, int PS>
+static hipError_t launch_e5m2_shape(const DecodeParams& p, int gp, bool rope, long long grid,
+                                    hipStream_t st) {
+  switch (gp) {
+    case 1: return launch_e5m2_g<D, PS, 1>(p, rope, grid, st);
+    case 2: return launch_e5m2_g<D, PS, 2>(p, rope, grid, st);
+    case 4: return launch_e5m2_g<D, PS, 4>(p, rope, grid, st);
+    case 8: return launch_e5m2_g<D, PS, 8>(p, rope, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_e5m2(const DecodeParams& p, int D, int PS, int gp, bool persistent,
+                              bool rope, long long grid, hipStream_t st) {
+  if (!persistent) return hipErrorInvalidValue;
+  if (D == 64 && PS == 16) return launch_e5m2_shape<64, 16>(p, gp, rope, grid, st);
+  if (D == 64 && PS == 32) return launch_e5m2_shape<64, 32>(p, gp, rope, grid, st);
+  if (D == 128 && PS == 16) return launch_e5m2_shape<128, 16>(p, gp, rope, grid, st);
+  if (D == 128 && PS == 32) return launch_e5m2_shape<128, 32>(p, gp, rope, grid, st);
+  return hipErrorInvalidValue;
 }
 
 // RoPE on the matrix cores: bf16 or fp8 KV, every head dim.
@@ -339,6 +377,7 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int D, int PS
                               bool persistent, bool rope, long long grid, hipStream_t st) {
   if (kv_dtype == kBF16) return launch_kv<kBF16>(p, D, PS, gp, persistent, rope, grid, st);
   if (kv_dtype == kFP8) return launch_kv<kFP8>(p, D, PS, gp, persistent, rope, grid, st);
+  if (kv_dtype == kFP8E5M2) return launch_e5m2(p, D, PS, gp, persistent, rope, grid, st);
   return hipErrorInvalidValue;
 }
 

@@ -1058,4 +1058,9 @@ hipError_t launch_persist_multi(const DecodeParams& p, long long max_jobs, hipSt
 template <int KVT, int D, int PS, int GP>
 hipError_t launch_persist_ilv(const DecodeParams& p, long long max_jobs, hipStream_t st);
 
+// The e5m2-pool instantiations of launch_persist_k (decode_e5m2.hip): one query token, no fused
+// append, without RoPE or with rotate-half RoPE.
+template <int D, int PS, int GP, bool ROPE>
+hipError_t launch_persist_e5m2(const DecodeParams& p, long long max_jobs, hipStream_t st);
+
 }  // namespace pdk

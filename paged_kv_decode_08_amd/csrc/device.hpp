@@ -7,8 +7,9 @@
 namespace pdk {
 
 // kFP8: OCP e4m3fn; kFP8E4M3: the IEEE-style e4m3 (max 240), written only by the append kernel
-// (its finite codes decode as e4m3fn codes do, so the decode kernels read it as kFP8)
-enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kFP8E4M3 = 3 };
+// (its finite codes decode as e4m3fn codes do, so the decode kernels read it as kFP8);
+// kFP8E5M2: OCP e5m2 (bias 15, max 57344), a type of its own in the decode kernels too
+enum Dtype : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kFP8E4M3 = 3, kFP8E5M2 = 4 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kEmptyLse = -5e4f;  // lse of a sequence with no attended rows
@@ -125,12 +126,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Two OCP e4m3fn codes (bytes 0,1 or 2,3 of `w`) -> two floats, with the gfx950 converter.
-template <bool HI>
+// Two OCP e4m3fn codes (E5M2: e5m2 codes) (bytes 0,1 or 2,3 of `w`) -> two floats, with the
+// gfx950 converters (exact: every fp8 value is an fp32 value).
+template <bool HI, bool E5M2 = false>
 __device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
-  auto r = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI);
-  a = r[0];
-  b = r[1];
+  if constexpr (E5M2) {
+    auto r = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), HI);
+    a = r[0];
+    b = r[1];
+  } else {
+    auto r = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI);
+    a = r[0];
+    b = r[1];
+  }
 }
 
 // fp32 -> OCP e4m3fn code, round to nearest even, saturating to +-448 (NaN -> 0x7F). Bit-level,
@@ -157,6 +165,25 @@ __device__ __forceinline__ uint8_t f32_to_fp8(float x) {
 __device__ __forceinline__ uint8_t f32_to_fp8_e4m3(float x) {
   const uint8_t c = f32_to_fp8(x);
   return ((c & 0x78) == 0x78 && (c & 0x7F) != 0x7F) ? static_cast<uint8_t>((c & 0x80) | 0x77) : c;
+}
+
+// fp32 -> OCP e5m2 code (bias 15, 2 mantissa bits), round to nearest even, saturating to +-57344
+// (infinity included; NaN -> 0x7F). Bit-level, so e5m2 subnormals (down to 2^-16) are exact.
+__device__ __forceinline__ uint8_t f32_to_fp8_e5m2(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t u = bits & 0x7fffffffu;
+  if (u > 0x7f800000u) return 0x7f;                   // NaN
+  if (u >= 0x47600000u) return sign | 0x7bu;          // |x| >= 57344 (and inf): saturate
+  if (u >= 0x38800000u) {                             // |x| >= 2^-14: normal e5m2
+    // 2 mantissa bits, RNE; below 57344 the rounding never reaches the infinity code
+    const uint32_t r = (u + 0xfffffu + ((u >> 21) & 1u)) >> 21;
+    return static_cast<uint8_t>(sign | (r - (112u << 2)));      // rebias exponent 127 -> 15
+  }
+  // subnormal: value = m * 2^-16; |x| * 65536 is exact, rintf rounds to nearest even (m = 4 is
+  // the smallest normal, code 0x04)
+  const uint32_t m = static_cast<uint32_t>(rintf(__uint_as_float(u) * 65536.0f));
+  return static_cast<uint8_t>(sign | m);
 }
 
 // A 16-byte vector of KV elements decoded to fp32.

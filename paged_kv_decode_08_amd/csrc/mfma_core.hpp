@@ -1,4 +1,5 @@
-// Per-wave building blocks of the matrix-core decode kernels (bf16 or fp8-e4m3fn KV, bf16 q).
+// Per-wave building blocks of the matrix-core decode kernels (bf16, fp8-e4m3fn or fp8-e5m2 KV,
+// bf16 q).
 //
 // Computation (TVM relax decode-kernels page, _attention_decode): score s = sm_scale * q . k kept in
 // log2 units, online softmax with running max m and denominator d, output O / d and
@@ -78,12 +79,18 @@ __device__ __forceinline__ void wave_lds_fence() {
 template <int KVT> struct VVec;
 template <> struct VVec<kBF16> { using type = uint4; };   // 8 bf16
 template <> struct VVec<kFP8> { using type = uint2; };    // 8 e4m3fn codes
+template <> struct VVec<kFP8E5M2> { using type = uint2; };  // 8 e5m2 codes
 
-// Two packed e4m3fn codes (bytes 0,1 or 2,3 of w) -> two packed bf16 (exact).
-template <bool HI>
+// Two packed e4m3fn codes (E5M2: e5m2 codes) (bytes 0,1 or 2,3 of w) -> two packed bf16 (exact:
+// bf16 has the exponent range and mantissa bits of both formats, subnormals included).
+template <bool HI, bool E5M2 = false>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t,
-                            __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, HI));
+  if constexpr (E5M2)
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(static_cast<int>(w), 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, HI));
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -101,7 +108,8 @@ __device__ __forceinline__ void split_bf16(float x, float y, uint32_t& hi, uint3
 // dims a lane holds per k-step.
 template <int KVT, int D, int PS, int GP, bool ROPE = false, bool ILV = false>
 struct MfmaCore {
-  static constexpr bool FP8 = KVT == kFP8;
+  static constexpr bool E5M2 = KVT == kFP8E5M2;  // fp8 codes are e5m2, else e4m3fn
+  static constexpr bool FP8 = KVT == kFP8 || E5M2;
   static constexpr int EB = FP8 ? 1 : 2;        // bytes per element
   static constexpr int ROW = D * EB;            // bytes per row
   static constexpr int BLOCK = PS * ROW;        // bytes of one (page, K|V, head) block
@@ -173,10 +181,10 @@ struct MfmaCore {
   // The 8 fp8 codes of k-step jj (even: words x, y; odd: z, w) of a 16-code load, in fp32.
   __device__ __forceinline__ static void fp8_kstep(const uint4& raw, int jj, float (&x)[8]) {
     const uint32_t w0 = (jj % 2) ? raw.z : raw.x, w1 = (jj % 2) ? raw.w : raw.y;
-    fp8x2_to_f32<false>(w0, x[0], x[1]);
-    fp8x2_to_f32<true>(w0, x[2], x[3]);
-    fp8x2_to_f32<false>(w1, x[4], x[5]);
-    fp8x2_to_f32<true>(w1, x[6], x[7]);
+    fp8x2_to_f32<false, E5M2>(w0, x[0], x[1]);
+    fp8x2_to_f32<true, E5M2>(w0, x[2], x[3]);
+    fp8x2_to_f32<false, E5M2>(w1, x[4], x[5]);
+    fp8x2_to_f32<true, E5M2>(w1, x[6], x[7]);
   }
 
   // The 8 K elements of k-step jj of this lane's row, in fp32 (fp8 codes convert exactly).
@@ -405,8 +413,8 @@ struct MfmaCore {
           if constexpr (FP8) {
             const uint4 raw = bf.k[rb * KL + jj / 2];
             const uint32_t w0 = (jj % 2) ? raw.z : raw.x, w1 = (jj % 2) ? raw.w : raw.y;
-            a = make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
-                           fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
+            a = make_uint4(fp8x2_to_bf16x2<false, E5M2>(w0), fp8x2_to_bf16x2<true, E5M2>(w0),
+                           fp8x2_to_bf16x2<false, E5M2>(w1), fp8x2_to_bf16x2<true, E5M2>(w1));
           } else {
             a = bf.k[rb * KS + jj];
           }
@@ -459,8 +467,8 @@ struct MfmaCore {
       uint4 x;
       if constexpr (FP8) {
         const uint2 c8 = bf.v[i];
-        x = make_uint4(fp8x2_to_bf16x2<false>(c8.x), fp8x2_to_bf16x2<true>(c8.x),
-                       fp8x2_to_bf16x2<false>(c8.y), fp8x2_to_bf16x2<true>(c8.y));
+        x = make_uint4(fp8x2_to_bf16x2<false, E5M2>(c8.x), fp8x2_to_bf16x2<true, E5M2>(c8.x),
+                       fp8x2_to_bf16x2<false, E5M2>(c8.y), fp8x2_to_bf16x2<true, E5M2>(c8.y));
       } else {
         x = bf.v[i];
       }

@@ -5,7 +5,7 @@ import torch
 import paged_kv_decode_08_amd as pk
 
 TORCH_STORAGE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8,
-                 "fp8e4m3": torch.uint8}
+                 "fp8e4m3": torch.uint8, "fp8e5m2": torch.uint8}
 
 
 def to_device_storage(x: np.ndarray, dtype: str, device="cuda"):
@@ -75,7 +75,8 @@ def to_np64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-3), "fp8": (2e-2, 1e-3), "fp8e4m3": (2e-2, 1e-3)}
+TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-3), "fp8": (2e-2, 1e-3), "fp8e4m3": (2e-2, 1e-3),
+       "fp8e5m2": (2e-2, 1e-3)}
 
 
 def tolerance(w):

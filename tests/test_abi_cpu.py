@@ -223,6 +223,47 @@ def test_fp8_e4m3_pool_checks(L):
              FAKE, 1 << 30, None) == 2
 
 
+def test_fp8_e5m2_pool_checks(L):
+    """The e5m2 pool needs its scales, plans like the other fp8 pools, and is refused before
+    anything is launched outside its kernels: several query tokens, the fused append,
+    interleaved RoPE and batches above the persistent schedule's bound. An unknown dtype code is
+    an argument error."""
+    assert attention_status(L, desc(kv_dtype="fp8e5m2")) == 1
+
+    def scaled(**over):
+        d = desc(kv_dtype="fp8e5m2", **over)
+        d.k_scale = FAKE
+        d.v_scale = FAKE
+        return d
+
+    cp, nc = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    assert L.pdecode_plan(ctypes.byref(scaled()), ctypes.byref(cp), ctypes.byref(nc)) == 0
+    cp8, nc8 = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    d8 = desc(kv_dtype="fp8")
+    d8.k_scale = d8.v_scale = FAKE
+    assert L.pdecode_plan(ctypes.byref(d8), ctypes.byref(cp8), ctypes.byref(nc8)) == 0
+    assert (cp.value, nc.value) == (cp8.value, nc8.value)
+    assert L.pdecode_workspace_bytes(ctypes.byref(scaled())) == \
+        L.pdecode_workspace_bytes(ctypes.byref(d8))
+    ws = dict(workspace=FAKE, ws_bytes=1 << 30)
+    # several query tokens
+    m = L.pdecode_attention_multi
+    assert m(ctypes.byref(scaled()), 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.1, FAKE, FAKE, FAKE,
+             1 << 30, None) == 2
+    # the fused append
+    f = L.pdecode_append_attention
+    assert f(ctypes.byref(scaled()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.1, FAKE,
+             FAKE, FAKE, 1 << 30, None) == 2
+    # interleaved RoPE
+    rope = pk.Rope(2, 1.0, 1e4, FAKE, FAKE)
+    assert attention_status(L, scaled(), rope=rope, **ws) == 2
+    # a batch beyond the persistent schedule
+    assert attention_status(L, scaled(batch=2000), **ws) == 2
+    d = desc()
+    d.kv_dtype = 5
+    assert attention_status(L, d) == 1
+
+
 def test_stream_read_argument_errors(L):
     """The ceiling helper checks its arguments on the host before launching anything."""
     sink = FAKE

@@ -1301,6 +1301,138 @@ def test_append_fp8_e4m3_rounding_exhaustive(in_dtype):
     assert got.tobytes() == ref.tobytes()
 
 
+# ---- OCP e5m2 pool (PDECODE_FP8_E5M2)
+
+@pytest.mark.parametrize("G,ps,splits,D,rot,window,page_scales,qd", [
+    (4, 16, 0, 128, 0, False, False, "bf16"),  # the Llama-3-8B group
+    (8, 32, 0, 128, 0, False, False, "bf16"),  # the GQA-8 group: split sequences merged in-kernel
+    (2, 32, 12, 128, 0, False, False, "bf16"),  # more chunks: the split merge kernel
+    (4, 16, 5, 128, 1, True, False, "bf16"),   # rotate-half RoPE, sliding window + sink
+    (8, 32, 3, 64, 1, False, True, "bf16"),    # D = 64 RoPE across lanes, per-page scales
+    (1, 16, 0, 64, 0, True, True, "fp8"),      # fp8 q
+    (2, 16, 3, 128, 0, False, False, "fp8"),
+])
+def test_fp8_e5m2_pool_decode(G, ps, splits, D, rot, window, page_scales, qd):
+    """Decode over an OCP e5m2 pool (codes converted exactly to bf16 in the kernel) against the
+    oracle: per-KV-head or per-page scales, RoPE, a window, forced splits, an fp8 q; lengths
+    around page boundaries, empty and one-row sequences, every output."""
+    lens = [1, ps - 1, ps + 1, 5 * ps + 3, 1700, 0, 2 * ps, 300]
+    w = synth.make_workload(name=f"e5m2_G{G}_ps{ps}_s{splits}_D{D}_r{rot}_w{int(window)}"
+                                 f"_p{int(page_scales)}_{qd}", B=len(lens), H_qo=2 * G, H_kv=2,
+                            D=D, page_size=ps, seq_lens=lens, q_dtype=qd, kv_dtype="fp8e5m2",
+                            seed=1400 + G + ps + D + rot + splits, max_num_pages=512,
+                            page_scales=page_scales, window=300 if window else None,
+                            sink=4 if window else 0, rotary_mode=rot, rope_theta=5e5)
+    run_and_check(w, num_kv_splits=splits)
+
+
+def test_fp8_e5m2_pool_full_size():
+    """The fp8 GQA-8 workload's shape and lengths (B=256, 64 q / 8 KV heads, page 32) over an e5m2
+    pool, automatic plan: every output against the oracle."""
+    base = synth.fp8_gqa8()
+    w = synth.make_workload(name="fp8_gqa8_e5m2", B=base.B, H_qo=64, H_kv=8, D=128,
+                            page_size=32, seq_lens=base.seq_lens.astype(np.int64),
+                            max_num_pages=65536, kv_dtype="fp8e5m2", seed=1006)
+    run_and_check(w)
+
+
+def test_fp8_e5m2_decode_all_codes():
+    """Every finite e5m2 code, read through decode with one attended row and v_scale = 1: the bf16
+    output equals the code's value exactly (every e5m2 value, subnormals included, is a bf16
+    value)."""
+    codes = np.array([c for c in range(256) if (c & 0x7C) != 0x7C], np.uint8)
+    assert codes.size == 248
+    D, ps = 128, 16
+    B = (codes.size + D - 1) // D
+    w = synth.make_workload(name="e5m2_codes", B=B, H_qo=1, H_kv=1, D=D, page_size=ps,
+                            seq_lens=[1] * B, q_dtype="bf16", kv_dtype="fp8e5m2", seed=6,
+                            max_num_pages=B)
+    vals = np.zeros(B * D, np.uint8)
+    vals[:codes.size] = codes
+    w.k_scale[:] = 1.0
+    w.v_scale[:] = 1.0
+    for b in range(B):
+        page = w.page_values[w.page_indptr[b]]
+        w.pages[page, 1, 0, 0, :] = vals[b * D:(b + 1) * D]
+    dev = gu.upload(w)
+    out, lse = gu.run_attention(w, dev)
+    torch.cuda.synchronize()
+    got = gu.to_np64(out).reshape(-1)[:codes.size]
+    expect = np.array([oracle.fp8_e5m2_value(int(c)) for c in codes])
+    assert np.array_equal(got, expect)
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_append_fp8_e5m2_rounding_exhaustive(in_dtype):
+    """Every finite e5m2 value, the midpoints between neighbours (ties to even), values at and
+    beyond 57344 (saturation, infinity included) and tiny values around the subnormal steps,
+    quantised by the GPU append into an e5m2 pool, match the oracle's encoder bit for bit."""
+    import ctypes
+    import paged_kv_decode_08_amd as pk
+    table = np.array([oracle.fp8_e5m2_value(c) for c in range(0x7C)])
+    mids = (table[:-1] + table[1:]) / 2
+    xs = np.concatenate([table, mids, -table, -mids,
+                         [57344.0, 61439.0, 61440.0, 65536.0, 1e6, -1e6, np.inf, -np.inf,
+                          2.0 ** -17, 3 * 2.0 ** -17, 2.0 ** -18, 1e-7, -2e-5]]).astype(np.float32)
+    D, ps = 64, 16
+    T = (xs.size + D - 1) // D
+    x = np.zeros(T * D, np.float32)
+    x[:xs.size] = xs
+    x = synth.cast_f32(x.reshape(T, 1, D), in_dtype)
+    ks = np.array([1.0], np.float32)
+    P = (T + ps - 1) // ps
+    pool = synth.poisoned_pool(P, 1, ps, D, "fp8e5m2")
+    slots = np.arange(T, dtype=np.int32)
+    desc = pk.make_desc(batch=1, num_qo_heads=1, num_kv_heads=1, head_dim=D, page_size=ps,
+                        max_num_pages=P, q_dtype=in_dtype, kv_dtype="fp8e5m2",
+                        k_scale=torch.from_numpy(ks).cuda(), v_scale=torch.from_numpy(ks).cuda())
+    tpool = torch.from_numpy(pool).cuda()
+    tx = gu.to_device_storage(x, in_dtype)
+    tslots = torch.from_numpy(slots).cuda()
+    st = pk.lib().pdecode_append_kv(ctypes.byref(desc), pk._ptr(tx), pk._ptr(tx), pk._ptr(tslots),
+                                    T, pk._ptr(tpool), pk._stream(None))
+    assert st == 0
+    torch.cuda.synchronize()
+    got = tpool.cpu().numpy()
+    ref = oracle.append_kv(pages=pool.copy(), new_k=x, new_v=x, slots=slots, H_kv=1, D=D, ps=ps,
+                           in_dtype=synth.DTYPE_CODE[in_dtype], kv_dtype=4, k_scale=ks,
+                           v_scale=ks)
+    assert got.tobytes() == ref.tobytes()
+
+
+@pytest.mark.parametrize("D,page_scales", [(128, False), (36, False), (128, True)])
+def test_append_fp8_e5m2_bitexact(D, page_scales):
+    """pdecode_append_kv into an e5m2 pool, bit-exact against the oracle: the 16-byte vector form
+    (D = 128), the element form (D = 36), per-KV-head or per-page scales, skipped slots."""
+    import paged_kv_decode_08_amd as pk
+    H_kv, ps, P = 8, 32, 64
+    pool = synth.poisoned_pool(P, H_kv, ps, D, "fp8e5m2")
+    k, v, slots = synth.append_inputs(T=40, H_kv=H_kv, D=D, page_size=ps, max_num_pages=P,
+                                      in_dtype="bf16", seed=15, skip_every=5)
+    rng = np.random.default_rng(16)
+    kw = {}
+    ref_kw = {}
+    if page_scales:
+        ksp = rng.uniform(0.5 / 448, 2 / 448, (P, H_kv)).astype(np.float32)
+        vsp = rng.uniform(0.5 / 448, 2 / 448, (P, H_kv)).astype(np.float32)
+        kw = dict(k_scale_page=torch.from_numpy(ksp).cuda(), v_scale_page=torch.from_numpy(vsp).cuda())
+        ref_kw = dict(k_scale_page=ksp, v_scale_page=vsp)
+    else:
+        ks = rng.uniform(0.5 / 448, 2 / 448, H_kv).astype(np.float32)
+        vs = rng.uniform(0.5 / 448, 2 / 448, H_kv).astype(np.float32)
+        kw = dict(k_scale=torch.from_numpy(ks).cuda(), v_scale=torch.from_numpy(vs).cuda())
+        ref_kw = dict(k_scale=ks, v_scale=vs)
+    desc = pk.make_desc(batch=1, num_qo_heads=H_kv, num_kv_heads=H_kv, head_dim=D, page_size=ps,
+                        max_num_pages=P, q_dtype="bf16", kv_dtype="fp8e5m2", **kw)
+    tpool = gu.to_device_storage(pool, "fp8e5m2")
+    pk.append_kv(desc, gu.to_device_storage(k, "bf16"), gu.to_device_storage(v, "bf16"),
+                 torch.from_numpy(slots).cuda(), tpool)
+    torch.cuda.synchronize()
+    ref = oracle.append_kv(pages=pool.copy(), new_k=k, new_v=v, slots=slots, H_kv=H_kv, D=D, ps=ps,
+                           in_dtype=1, kv_dtype=4, **ref_kw)
+    assert tpool.cpu().numpy().tobytes() == ref.tobytes()
+
+
 def test_append_attention_fp8_rope_window():
     """Fused append into an fp8 pool with RoPE and a window: the substituted row holds the encoded
     codes, which are converted and rotated like every other K row."""
