@@ -789,12 +789,15 @@ void decode_mfma_persist_kernel(DecodeParams p) {
     // arbitration whatever its remaining work: on the Llama-3-8B shape the first workgroup
     // dispatched to each CU drew 16.1 GB/s and the second, which shares the CU with it, 10.4 GB/s,
     // and the second ones' first jobs became the tail of the call. Measured 0.5-1.5 us faster per
-    // call on that shape, 2-3 us on the fp8 GQA-8 one and 8 us on RoPE + window.
+    // call on that shape, 2-3 us on the fp8 GQA-8 one and 8 us on RoPE + window. The levels
+    // start at 24, 12 and 6 items left: against 12, 8 and 4, 3.5 us faster on RoPE + window and
+    // 0.2-0.4 us on the Llama-3-8B, GQA-8 bf16 and long-context shapes (fp8 GQA-8 unchanged);
+    // counting the next job's items too was slower on the Llama-3-8B and GQA-8 bf16 shapes.
     auto set_prio = [&](int k) __attribute__((always_inline)) {
       const int rem = J.nitems - k;
-      if (rem > 12) __builtin_amdgcn_s_setprio(3);
-      else if (rem > 8) __builtin_amdgcn_s_setprio(2);
-      else if (rem > 4) __builtin_amdgcn_s_setprio(1);
+      if (rem > 24) __builtin_amdgcn_s_setprio(3);
+      else if (rem > 12) __builtin_amdgcn_s_setprio(2);
+      else if (rem > 6) __builtin_amdgcn_s_setprio(1);
       else __builtin_amdgcn_s_setprio(0);
     };
     // process_item, then retires `cur`: only the loads just issued stay in flight.
