@@ -65,6 +65,13 @@ def parse():
                     help="instead of the decode, print the streaming-read ceiling sweep (every "
                          "launch shape of pdecode_bench_stream_read over a 2 GiB buffer, and a "
                          "plain read of the workload's KV bytes per step) and exit")
+    ap.add_argument("--timeline", action="store_true",
+                    help="instead of the timed run, load the timeline build of the library "
+                         "(python -m paged_kv_decode_08_amd.build --timeline), run --warmup "
+                         "calls of --workload, then 3 runs of 8 back-to-back calls, and print "
+                         "each run's last call: per-workgroup entry, job table, first K/V issue, "
+                         "jobs and exit times, the KV rate over the call (from each job's slots "
+                         "and duration) and the split merge kernel's times")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the decode, run a plain 512 MiB device-to-device copy "
                          "(the reference point for the HBM byte counters) and exit")
@@ -389,6 +396,139 @@ def step_bench(workload, steps, warmup, nsets):
                       "kv_bytes_per_step": base.kv_bytes, "data": "synthetic", **res}), flush=True)
 
 
+def _timeline_summary(marks, item_bytes):
+    """One call's marks ([4096, 64] uint64: time << 24 | tag << 20 | value; time in 10 ns ticks of
+    s_memrealtime) -> text lines and a dict of the key times (us from the first workgroup entry)."""
+    import numpy as np
+    dec = marks[:2048]
+    used = np.nonzero(dec[:, 0])[0]
+    t = (dec[used] >> np.uint64(24)).astype(np.float64) * 0.01
+    tag = ((dec[used] >> np.uint64(20)) & np.uint64(0xF)).astype(int)
+    val = (dec[used] & np.uint64(0xFFFFF)).astype(int)
+    valid = dec[used] != 0
+    t0 = t[:, 0].min()
+    t = t - t0
+    nwg = len(used)
+
+    def first(i, k):
+        sel = valid[i] & (tag[i] == k)
+        return t[i][sel][0] if sel.any() else np.nan
+
+    entry = t[:, 0]
+    table = np.array([first(i, 2) for i in range(nwg)])
+    issue = np.array([first(i, 3) for i in range(nwg)])
+    exits = np.array([first(i, 6) for i in range(nwg)])
+    pct = lambda x: [round(float(v), 2) for v in np.nanpercentile(x, [0, 10, 50, 90, 100])]
+    jobs = []
+    for i in range(nwg):
+        st = t[i][valid[i] & (tag[i] == 4)]
+        en = t[i][valid[i] & (tag[i] == 5)]
+        nw = val[i][valid[i] & (tag[i] == 4)]
+        for k in range(min(len(st), len(en))):
+            jobs.append((st[k], en[k], nw[k]))
+    jobs = np.array(jobs)
+    nj = np.bincount(np.array([int((valid[i] & (tag[i] == 4)).sum()) for i in range(nwg)]))
+    T = int(np.nanmax(exits)) + 2
+    rate = np.zeros(T)
+    active = np.zeros(T)
+    for s_, e_, nw_ in jobs:  # a job's bytes spread evenly over its duration
+        b = nw_ * 4 * item_bytes
+        for u in range(int(s_), int(e_) + 1):
+            lo, hi = max(s_, u), min(e_, u + 1)
+            if hi > lo:
+                rate[u] += b * (hi - lo) / (e_ - s_)
+                active[u] += hi - lo
+    lines = [f"  workgroups {nwg}; jobs per workgroup: " +
+             ", ".join(f"{k}: {int(c)}" for k, c in enumerate(nj) if c),
+             "  percentiles p0 p10 p50 p90 p100, us from the first workgroup's entry:",
+             f"  entry           {pct(entry)}",
+             f"  job table built {pct(table)}",
+             f"  first K/V issue {pct(issue)}",
+             f"  exit            {pct(exits)}",
+             "  us: KV GB/s (job averages) / workgroups in a job"]
+    cells = [f"{u:3d}: {rate[u] / 1e3:5.0f}/{active[u]:4.0f}" for u in range(T)]
+    lines += ["   " + "  ".join(cells[k:k + 6]) for k in range(0, len(cells), 6)]
+    res = {"entry_p100": pct(entry)[4], "table_p50": pct(table)[2], "first_issue_p50": pct(issue)[2],
+           "first_issue_p90": pct(issue)[3], "exit_p10": pct(exits)[1], "exit_p50": pct(exits)[2],
+           "exit_p100": pct(exits)[4], "peak_GBps": round(float(rate.max()) / 1e3, 0)}
+    mk = marks[2048:]
+    mu = np.nonzero(mk[:, 0])[0]
+    if len(mu):
+        ms = (mk[mu, 0] >> np.uint64(24)).astype(np.float64) * 0.01 - t0
+        ends = mk[mu, 1]
+        me = (ends[ends != 0] >> np.uint64(24)).astype(np.float64) * 0.01 - t0
+        lines.append(f"  split merge kernel: {len(mu)} workgroups, start {pct(ms)}, end {pct(me)}")
+        res.update(merge_start_p0=round(float(ms.min()), 2), merge_end_p100=round(float(me.max()), 2))
+    return lines, res
+
+
+def timeline(args):
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_08_amd as pk
+    from paged_kv_decode_08_amd import build as pbuild
+    import synth
+    from tests import gpu_util as gu
+
+    if not os.path.exists(pbuild.LIB_TIMELINE):
+        sys.exit("bench.py --timeline: build the timeline library first: "
+                 "python -m paged_kv_decode_08_amd.build --timeline")
+    pk.LIB_PATH = pbuild.LIB_TIMELINE
+    pk._lib = None
+    L = pk.lib()
+    L.pdk_timeline_read.argtypes = [ctypes.c_void_p]
+    torch.cuda.set_device(0)
+    make = synth.CONFIGS[args.workload]
+    base = make()
+    nsets = args.sets if base.kv_bytes < 512e6 else 1
+    lens = base.seq_lens.astype(np.int64)
+    sets = [base] + [make(seed=1002 + 100 * i, lens=lens) for i in range(1, nsets)]
+    devs = [gu.upload(w) for w in sets]
+    desc = gu.desc_for(base, devs[0], num_kv_splits=args.splits,
+                       max_kv_len=0 if args.no_hint else None)
+    ws = pk.alloc_workspace(desc)
+    out = torch.empty((base.B, base.H_qo, base.D), dtype=gu.TORCH_STORAGE[base.q_dtype],
+                      device="cuda")
+    lse = torch.empty((base.B, base.H_qo), dtype=torch.float32, device="cuda")
+    ropes = [None] * len(devs)
+    if base.rotary_mode:
+        ropes = [pk.make_rope(rotary_mode=base.rotary_mode, rope_scale=base.rope_scale,
+                              rope_theta=base.rope_theta, q_rope_position=d["q_pos"],
+                              k_rope_pos_offset=d["k_off"]) for d in devs]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        d = devs[i % len(devs)]
+        pk.attention(desc, d["q"], d["pages"], d["indptr"], d["values"], d["length_info"], out,
+                     lse, base.sm_scale, rope=ropes[i % len(devs)], workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # one item: 16 rows of K and of V of one KV head
+    item_bytes = 2 * 16 * base.D * synth.ELEM_BYTES[base.kv_dtype]
+    marks = np.zeros((4096, 64), np.uint64)
+    runs = []
+    print(f"timeline of {args.workload}: plan {pk.plan(desc)}, the last of 8 back-to-back calls",
+          flush=True)
+    for r in range(3):
+        L.pdk_timeline_clear()
+        torch.cuda.synchronize()
+        for i in range(8):
+            step(i + r)
+        torch.cuda.synchronize()
+        if L.pdk_timeline_read(marks.ctypes.data_as(ctypes.c_void_p)) != 0:
+            sys.exit("bench.py --timeline: reading the marks failed")
+        lines, res = _timeline_summary(marks, item_bytes)
+        print(f"run {r}:")
+        print("\n".join(lines), flush=True)
+        runs.append(res)
+    print(json.dumps({"timeline": args.workload, "runs": runs}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -398,6 +538,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(max(args.steps, 1))
+        return
+    if args.timeline:
+        timeline(args)
         return
     if args.ceiling:
         import synth

@@ -8,6 +8,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpdecode.so")
+# the same library with the call-timeline marks compiled in (bench.py --timeline)
+LIB_TIMELINE = os.path.join(HERE, "libpdecode_timeline.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -50,4 +52,8 @@ def build(verbose: bool = False, extra=(), out=LIB, build_dir=BUILD) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--timeline" in sys.argv[1:]:
+        print(build(verbose=True, extra=["-DPDECODE_TIMELINE"], out=LIB_TIMELINE,
+                    build_dir=os.path.join(BUILD, "timeline")))
+    else:
+        print(build(verbose=True))

@@ -193,6 +193,8 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
   constexpr int CB = NB * CPW;  // chunks per batch
   static_assert(64 % CB == 0 || CB % 64 == 0, "batches and lse words line up");
   const int lane = threadIdx.x & 63;
+  PDK_MARK_DECL;
+  PDK_MARK(2048 + blockIdx.x, 7, 0);
   const int row = blockIdx.x * kMergeRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= p.B * p.T * p.H_qo) return;  // rows [B, T, H_qo]
   const int b = row / (p.T * p.H_qo);
@@ -263,6 +265,7 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
     *reinterpret_cast<uint2*>(dst) = packed;
   }
   if (lane == 0) p.lse[row] = none ? kEmptyLse : Mf + log2f(ws);
+  PDK_MARK(2048 + blockIdx.x, 8, 0);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -382,3 +385,16 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int D, int PS
 }
 
 }  // namespace pdk
+
+#ifdef PDECODE_TIMELINE
+// Timeline build only: copy the marks out / clear them (synchronous; host buffer of
+// kTimelineRows x kTimelineMarks uint64).
+extern "C" int pdk_timeline_read(void* host) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(pdk::g_timeline), sizeof(pdk::g_timeline)) ==
+                 hipSuccess ? 0 : 1;
+}
+extern "C" int pdk_timeline_clear() {
+  static unsigned long long zero[pdk::kTimelineRows][pdk::kTimelineMarks];
+  return hipMemcpyToSymbol(HIP_SYMBOL(pdk::g_timeline), zero, sizeof(zero)) == hipSuccess ? 0 : 1;
+}
+#endif

@@ -14,6 +14,30 @@
 namespace pdk {
 
 constexpr int kPWaves = 4;              // wavefronts per workgroup of the persistent schedule
+
+// Call timeline, compiled in only with -DPDECODE_TIMELINE (the separate library that
+// `python -m paged_kv_decode_08_amd.build --timeline` builds; `bench.py --timeline` reads it).
+// Thread 0 of a workgroup stores (s_memrealtime, tag, value) into row blockIdx.x of a static
+// device array at fixed points: 1 entry, 2 job table built, 3 first K/V loads issued, 4 job start
+// (value: wave 0's slots in the job), 5 job end (value: 1 if the workgroup merged a split sequence
+// there), 6 exit; the split merge kernel's workgroups use rows 2048 + blockIdx.x (7 start, 8 end).
+// Each translation unit has its own array; the reader (decode_mfma.hip) sees the plain persistent
+// instantiations and the split merge kernel. Marks past the array's bounds are dropped.
+constexpr int kTimelineRows = 4096, kTimelineMarks = 64;
+#ifdef PDECODE_TIMELINE
+static __device__ unsigned long long g_timeline[kTimelineRows][kTimelineMarks];
+__device__ __forceinline__ void timeline_mark(int row, int& k, int tag, int val) {
+  if (threadIdx.x == 0 && row < kTimelineRows && k < kTimelineMarks)
+    g_timeline[row][k] = ((__builtin_amdgcn_s_memrealtime() & 0xFFFFFFFFFFull) << 24) |
+                         (uint64_t(tag) << 20) | uint64_t(val & 0xfffff);
+  ++k;
+}
+#define PDK_MARK_DECL int pdk_mark_k = 0
+#define PDK_MARK(row, tag, val) timeline_mark(row, pdk_mark_k, tag, val)
+#else
+#define PDK_MARK_DECL static_cast<void>(0)
+#define PDK_MARK(row, tag, val) static_cast<void>(0)
+#endif
 constexpr int kPersistMaxBatch = 1024;  // sequences the persistent schedule's LDS table holds
 constexpr int kPersistMaxGrid = 1024;   // workgroups of the persistent schedule, at most
 
@@ -389,6 +413,8 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   __shared__ float2 s_freq[ROPE ? D / 2 : 1];  // RoPE: frequencies (rope_freq) of dims i, i + D/2
 
   const int tid = threadIdx.x;
+  PDK_MARK_DECL;
+  PDK_MARK(blockIdx.x, 1, 0);
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (wave-uniform)
   const int l = tid & 63;
   const int B = p.B;
@@ -581,6 +607,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
     }
   }
   const int total_jobs = tab.pre[B];
+  PDK_MARK(blockIdx.x, 2, total_jobs);
   const uint32_t hinv = div_reciprocal(uint32_t(max(p.H_kv, 2)));
 
   // ---- sequences without attended rows: out = 0, lse = -5e4 (fused append: a sequence with pages
@@ -724,6 +751,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
     {
       const int page0 = clamp_page(p, uni(s_ids[0][w][0]));
       core.issue(buf0, block_of(page0, J.h), kv_stride);
+      PDK_MARK(blockIdx.x, 3, 0);
       if constexpr (C::FP8) {
         if (page_scales) {
           buf0.ks = p.k_scale_page[size_t(page0) * p.H_kv + J.h];
@@ -845,6 +873,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
     // job's second item before the job-end merge, keeping two items in flight through it, measured
     // 1-2 us slower per call on the Llama-3-8B, long-context and RoPE + window shapes.)
     for (;;) {
+      PDK_MARK(blockIdx.x, 4, J.nw);
       int arrival = 0;  // this wave's arrival for the previous job's split sequence
       // ---- items 0 and 1, with the loads for the next job (its page ids and q words, staged into
       // LDS once item 1 is computed). The ticket of the job after the next one is taken in the
@@ -949,6 +978,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         }
       }
       __syncthreads();  // s_m / s_d / s_o / s_ticket are free again
+      PDK_MARK(blockIdx.x, 5, merge_prev);
       if constexpr (!MT) {  // several tokens never merge in the kernel (merges_in_kernel)
         if (merge_prev) {
           merge_split<D, GP, NT, MT>(p, pb, ph, pnch);
@@ -996,6 +1026,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
 
+  PDK_MARK(blockIdx.x, 6, 0);
   // ---- the last workgroup out puts the queue back to zero for the next call
   if (tid == 0 && atomicAdd(queue + 1, 1) == int(gridDim.x) - 1) {
     __hip_atomic_store(queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
