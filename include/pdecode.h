@@ -227,9 +227,12 @@ pdecode_status pdecode_attention_noalloc(const pdecode_desc *d, const void *q, c
  * pdecode_workspace_bytes_multi(d, qo_len), with the same reuse rules. With RoPE (either
  * rotary_mode), token t's query sits at position q_rope_position[b] + t; the keys are placed as in
  * pdecode_attention.
- * qo_len == 1 is pdecode_attention. Supported for qo_len > 1: no sliding window,
- * (num_qo_heads / num_kv_heads) * qo_len <= 16, and the persistent
- * matrix-core schedule (BF16 or FP8 pool, batch <= 1024); otherwise UNSUPPORTED. Errors: as pdecode_attention, and INVALID_ARG for qo_len < 1. */
+ * qo_len == 1 is pdecode_attention. Supported for qo_len > 1: no sliding window, the persistent
+ * matrix-core schedule (BF16, FP8_E4M3FN or FP8_E4M3 pool, batch <= 1024) and
+ * batch * qo_len * num_qo_heads <= INT_MAX; otherwise UNSUPPORTED. The kernel takes 16 q columns
+ * (G = num_qo_heads / num_kv_heads per token): more than 16 / G tokens run as consecutive launches
+ * of 16 / G tokens each on the stream, each reading the KV cache once. Errors: as
+ * pdecode_attention, and INVALID_ARG for qo_len < 1. */
 size_t pdecode_workspace_bytes_multi(const pdecode_desc *d, int32_t qo_len);
 pdecode_status pdecode_attention_multi(const pdecode_desc *d, int32_t qo_len, const void *q,
                                        const void *pages, const int32_t *page_indptr,

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdio>
@@ -303,6 +304,8 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   p.H_kv = d->num_kv_heads;
   p.G = d->num_qo_heads / d->num_kv_heads;
   p.T = qo_len;
+  p.T_all = qo_len;
+  p.tok0 = 0;
   p.max_num_pages = d->max_num_pages;
   p.sliding = d->sliding_window;
   p.rotary = rotary ? rope->rotary_mode : 0;
@@ -321,8 +324,6 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
                  pl.persistent ? "persistent," : "one workgroup per chunk,",
                  pl.auto_chunk ? 0 : pl.chunk_slots, pl.num_chunks, pl.workspace_bytes(),
                  pl.auto_chunk ? " (chunk size chosen on the device; see the plan word)" : "");
-  const int cols = p.G * qo_len;  // q columns of the matrix-core B operand
-  const int gp = cols <= 1 ? 1 : cols <= 2 ? 2 : cols <= 4 ? 4 : cols <= 8 ? 8 : 16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // bf16 / fp8 KV: q.K on the matrix cores (4-wave workgroups, persistent over a job queue up to
   // kPersistMaxBatch sequences, else one per chunk), RoPE included; fp32 KV: the vector-ALU kernel
@@ -331,12 +332,24 @@ pdecode_status attention_impl(const pdecode_desc* d, const void* new_k, const vo
   // +-240), and every finite code has its e4m3fn value: the decode kernels read it as e4m3fn.
   const int kv_read = d->kv_dtype == PDECODE_FP8_E4M3 ? PDECODE_FP8_E4M3FN : d->kv_dtype;
   const bool mfma = kv_read == PDECODE_BF16 || is_fp8(kv_read);
-  if (mfma)
-    st = hip_status(pdk::launch_decode_mfma(p, kv_read, d->head_dim, d->page_size, gp,
-                                            pl.persistent, rotary, grid, s));
-  else
-    st = hip_status(pdk::launch_decode_valu(p, kv_read, d->head_dim, d->page_size, gp,
-                                            static_cast<unsigned>(grid), s));
+  // Several tokens: the matrix-core B operand holds 16 q columns, G per token, so a call of more
+  // than 16 / G tokens runs as launches of 16 / G tokens each (the last takes the rest), one
+  // after the other on the stream; each reads the KV cache once and writes its tokens' rows (its
+  // split partial states are rows of the same [B, qo_len, H_qo, C, D] layout).
+  const int per = qo_len > 1 ? std::max(1, 16 / p.G) : 1;
+  for (int t0 = 0; t0 < qo_len; t0 += per) {
+    p.tok0 = t0;
+    p.T = std::min(per, qo_len - t0);
+    const int cols = p.G * p.T;  // q columns of the matrix-core B operand
+    const int gp = cols <= 1 ? 1 : cols <= 2 ? 2 : cols <= 4 ? 4 : cols <= 8 ? 8 : 16;
+    if (mfma)
+      st = hip_status(pdk::launch_decode_mfma(p, kv_read, d->head_dim, d->page_size, gp,
+                                              pl.persistent, rotary, grid, s));
+    else
+      st = hip_status(pdk::launch_decode_valu(p, kv_read, d->head_dim, d->page_size, gp,
+                                              static_cast<unsigned>(grid), s));
+    if (st != PDECODE_OK) break;
+  }
   return st;
 }
 
@@ -385,7 +398,7 @@ pdecode_status pdecode_attention_multi(const pdecode_desc* d, int32_t qo_len, co
     return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
                           rope, sm_scale, out, lse, workspace, workspace_bytes, stream);
   if (d->sliding_window) return PDECODE_ERR_UNSUPPORTED;
-  if (int64_t(qo_len) * (d->num_qo_heads / d->num_kv_heads) > 16) return PDECODE_ERR_UNSUPPORTED;
+  if (int64_t(d->batch) * qo_len * d->num_qo_heads > INT_MAX) return PDECODE_ERR_UNSUPPORTED;
   return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
                         rope, sm_scale, out, lse, workspace, workspace_bytes, stream, qo_len);
 }

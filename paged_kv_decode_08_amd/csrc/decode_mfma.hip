@@ -195,9 +195,11 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
   const int lane = threadIdx.x & 63;
   PDK_MARK_DECL;
   PDK_MARK(2048 + blockIdx.x, 7, 0);
-  const int row = blockIdx.x * kMergeRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (row >= p.B * p.T * p.H_qo) return;  // rows [B, T, H_qo]
-  const int b = row / (p.T * p.H_qo);
+  // this launch's rows [B, T, H_qo], i.e. rows (b T_all + tok0 + t) H_qo + q head of the call
+  const int lrow = blockIdx.x * kMergeRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (lrow >= p.B * p.T * p.H_qo) return;
+  const int b = lrow / (p.T * p.H_qo);
+  const int row = (b * p.T_all + p.tok0) * p.H_qo + (lrow - b * p.T * p.H_qo);
   const int nc = p.num_chunks;
   const float* lse_c = p.part_lse + size_t(row) * nc;
   const float* o_c = p.part_o + size_t(row) * nc * D;
@@ -281,7 +283,7 @@ static hipError_t launch_chunked(const DecodeParams& p, unsigned grid, hipStream
 // After a persistent decode: the split merge kernel, where split sequences were left to it.
 template <int D, int PS, int GP>
 static hipError_t merge_splits(const DecodeParams& p, hipStream_t st) {
-  if (p.num_chunks <= 1 || merges_in_kernel<GP>(p.num_chunks, p.T > 1)) return hipSuccess;
+  if (p.num_chunks <= 1 || merges_in_kernel<GP>(p.num_chunks, p.T_all > 1)) return hipSuccess;
   const unsigned rows = static_cast<unsigned>(p.B) * p.T * p.H_qo;
   hipLaunchKernelGGL((split_merge_kernel<D, PS>), dim3((rows + kMergeRows - 1) / kMergeRows),
                      dim3(64 * kMergeRows), 0, st, p);
@@ -292,9 +294,9 @@ template <int KVT, int D, int PS, int GP, bool ROPE>
 static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipStream_t st) {
   hipError_t e;
   if constexpr (GP == 16) {  // 16 q columns: several query tokens only
-    if (p.T <= 1) return hipErrorInvalidValue;
+    if (p.T_all <= 1) return hipErrorInvalidValue;
     e = launch_persist_multi<KVT, D, PS, GP, ROPE>(p, max_jobs, st);
-  } else if (p.T > 1) {
+  } else if (p.T_all > 1) {  // several tokens, also a launch of one of them
     e = launch_persist_multi<KVT, D, PS, GP, ROPE>(p, max_jobs, st);  // either RoPE layout
   } else if (ROPE && p.rotary == 2) {
     e = launch_persist_ilv<KVT, D, PS, GP>(p, max_jobs, st);  // interleaved RoPE, plain or fused
@@ -309,7 +311,7 @@ static hipError_t launch_persist(const DecodeParams& p, long long max_jobs, hipS
 // RoPE (the host refuses the rest).
 template <int D, int PS, int GP>
 static hipError_t launch_e5m2_g(const DecodeParams& p, bool rope, long long grid, hipStream_t st) {
-  if (p.T != 1 || p.new_k != nullptr || (rope && p.rotary != 1)) return hipErrorInvalidValue;
+  if (p.T_all != 1 || p.new_k != nullptr || (rope && p.rotary != 1)) return hipErrorInvalidValue;
   const hipError_t e = rope ? launch_persist_e5m2<D, PS, GP, true>(p, grid, st)
                             : launch_persist_e5m2<D, PS, GP, false>(p, grid, st);
   return e != hipSuccess ? e : merge_splits<D, PS, GP>(p, st);

@@ -305,12 +305,13 @@ constexpr bool merges_in_kernel(int num_chunks, bool several_tokens) {
   return GP <= 8 && !several_tokens && num_chunks <= kInMergeChunks;
 }
 
-// Output row of q column c of (sequence b, KV head h): columns are token-major (token c / G, q
-// head h G + c % G); with one token, c is the q head's index in the group.
+// Output row of q column c of (sequence b, KV head h): columns are token-major (the launch's
+// token c / G, i.e. the call's token tok0 + c / G; q head h G + c % G); with one token, c is the
+// q head's index in the group.
 template <bool MT>
 __device__ __forceinline__ size_t out_row(const DecodeParams& p, int b, int h, int c) {
   if constexpr (MT)
-    return (size_t(b) * p.T + c / p.G) * p.H_qo + size_t(h) * p.G + c % p.G;
+    return (size_t(b) * p.T_all + p.tok0 + c / p.G) * p.H_qo + size_t(h) * p.G + c % p.G;
   else
     return size_t(b) * p.H_qo + size_t(h) * p.G + c;
 }
@@ -321,8 +322,8 @@ __device__ __forceinline__ size_t out_row(const DecodeParams& p, int b, int h, i
 // out = sum_c w_c O_c / sum_c w_c, lse = M + log2(sum_c w_c). Thread t produces 4 dims of one q
 // column and loads the chunks present, 8 at a time, before using any (one memory round trip per
 // 8 chunks; the state is rescaled as the running maximum grows). All threads take part.
-// MT: several query tokens (p.T): G T columns, and a column whose token sees no row of the
-// sequence (all chunk lse -inf) gives out = 0, lse = -5e4.
+// MT: several query tokens (p.T in the launch): G T columns, and a column whose token sees no
+// row of the sequence (all chunk lse -inf) gives out = 0, lse = -5e4.
 template <int D, int GP, int NT, bool MT = false>
 __device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
   constexpr int V = D / 4;
@@ -423,7 +424,11 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   const int GC = G * T;  // q columns of the MFMA B operand
   C core;
   core.init_lane(l);
-  const int tok = MT ? core.n / G : 0;  // query token of this lane's MFMA column
+  const int tok = MT ? core.n / G : 0;  // query token of this lane's MFMA column (in the launch)
+  // several tokens: that token's RoPE offset from the call's first token, and the rows it cannot
+  // see at the end of the sequence (those of the call's later tokens)
+  const int qtok = MT ? p.tok0 + tok : 0;
+  const int tlate = MT ? p.T_all - p.tok0 - tok : 1;
   if constexpr (ROPE) {
     if (tid < D / 2) {
       float fhi, flo;
@@ -614,9 +619,11 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   // still gets its new row, written by append_last_row)
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
     if (tab.njobs[b] != 0) continue;
+    // this launch's tokens of sequence b: rows (b T_all + tok0 + t) H_qo + q head, t < T
+    const size_t r0 = (size_t(b) * (MT ? p.T_all : 1) + (MT ? p.tok0 : 0)) * p.H_qo;
     for (int idx = tid; idx < T * p.H_qo * D; idx += NT)
-      store_out<kBF16>(p.out, size_t(b) * T * p.H_qo * D + idx, 0.f);
-    for (int hq = tid; hq < T * p.H_qo; hq += NT) p.lse[size_t(b) * T * p.H_qo + hq] = kEmptyLse;
+      store_out<kBF16>(p.out, r0 * D + idx, 0.f);
+    for (int hq = tid; hq < T * p.H_qo; hq += NT) p.lse[r0 + hq] = kEmptyLse;
     if constexpr (FUSED) append_last_row<KVT, D, PS, NT>(p, b);
   }
 
@@ -648,7 +655,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   };
   auto q_words = [&](const Job& J, uint32_t (&qs)[QW]) {
     if constexpr (MT) {
-      const size_t base = (size_t(J.b) * T * p.H_qo + size_t(J.h) * G) * (D / 2);
+      const size_t base = ((size_t(J.b) * p.T_all + p.tok0) * p.H_qo + size_t(J.h) * G) * (D / 2);
 #pragma unroll
       for (int i = 0; i < QW; ++i) qs[i] = q_word(base + qoff[i]);
     } else {
@@ -740,7 +747,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
 
   if (J.valid) {
     core.load_q(reinterpret_cast<const uint16_t*>(s_q[0]), GC);
-    core.rope_q(J.qpos + tok, s_freq);  // several tokens: token tok sits tok positions later
+    core.rope_q(J.qpos + qtok, s_freq);  // several tokens: the call's token t sits t positions later
     // fp8: the KV head's scales, or 1 with per-page scales (applied per item)
     const bool page_scales = C::FP8 && p.k_scale_page != nullptr;
     float scale = p.score_scale * (C::FP8 && !page_scales ? p.k_scale[J.h] : 1.0f);
@@ -803,8 +810,9 @@ void decode_mfma_persist_kernel(DecodeParams p) {
           }
         }
         if constexpr (MT) {
-          // this lane's column (token n / G) sees positions <= total - T + n / G
-          const int cap = J.g.total - T + tok - (j * PS + r0);
+          // this lane's column (the call's token tok0 + n / G) sees positions
+          // <= total - T_all + tok0 + n / G
+          const int cap = J.g.total - tlate - (j * PS + r0);
           if (lo < hi)
             core.template process<true>(cur, lo, hi, isc, s_tile[w], pos0, s_freq, cap, ivf);
         } else {
@@ -1015,7 +1023,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       par ^= 1;
       core.load_q(reinterpret_cast<const uint16_t*>(s_q[par]), GC);
       qcs = s_qsc[par][core.n];
-      core.rope_q(J.qpos + tok, s_freq);  // several tokens: token tok sits tok positions later
+      core.rope_q(J.qpos + qtok, s_freq);  // several tokens: the call's token t sits t positions later
       if (C::FP8 && !page_scales) {
         scale = p.score_scale * p.k_scale[J.h];
         vscale = p.v_scale[J.h];

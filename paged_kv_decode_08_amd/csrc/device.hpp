@@ -45,8 +45,12 @@ struct DecodeParams {
   void* pages_w;             // fused append: the pool (the same memory as pages)
   const float* sink;         // learned sink logit per q head [H_qo] (natural-log units), or null
   int32_t B, H_qo, H_kv, G;
-  int32_t T;                 // query tokens per sequence (1: single-token decode); q, out and
-                             // lse are [B, T, H_qo, ...], token t sees positions <= total - T + t
+  int32_t T;                 // query tokens per sequence in this launch (1: single-token decode)
+  int32_t T_all, tok0;       // query tokens of the call, and this launch's first one: q, out and
+                             // lse are [B, T_all, H_qo, ...]; the launch's token t is the call's
+                             // token tok0 + t, which sees positions <= total - T_all + tok0 + t
+                             // (a call of more than 16 q columns per KV head runs as launches of
+                             // at most 16); single token: T = T_all = 1, tok0 = 0
   int32_t max_num_pages;     // page ids are clamped into the pool before any KV address is formed
   int32_t sliding, rotary;
   float rope_scale, rope_theta;

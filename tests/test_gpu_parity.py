@@ -958,6 +958,38 @@ def _multi_case(w, T, seed, num_kv_splits=0):
     return qd, desc, dev, out, lse, ws
 
 
+@pytest.mark.parametrize("kv,G,T,D,ps,splits,rot", [
+    ("bf16", 8, 4, 128, 16, 0, 0),   # GQA-8 with 4 tokens: 2 launches of 16 columns
+    ("fp8", 8, 3, 128, 32, 0, 0),    # 2 launches: 2 tokens, then 1 (the 8-column kernel)
+    ("bf16", 4, 8, 128, 16, 0, 0),   # the Llama-3-8B group with 8 tokens: 2 launches
+    ("bf16", 1, 40, 64, 16, 0, 0),   # one head, 40 tokens: launches of 16, 16 and 8
+    ("fp8", 2, 9, 128, 32, 12, 1),   # launches of 8 and 1 tokens, forced splits, rotate-half RoPE
+    ("bf16", 4, 5, 64, 32, 3, 2),    # launches of 4 and 1 tokens, interleaved RoPE
+    ("fp8e4m3", 8, 6, 128, 16, 0, 0),
+])
+def test_attention_multi_token_groups(kv, G, T, D, ps, splits, rot):
+    """More than 16 q columns per KV head (G x T > 16): the call runs the 16-column kernel once per
+    group of 16 / G tokens, each group with its own causal caps, RoPE positions and output rows.
+    Every output against the oracle; sequences shorter than T and an empty one included."""
+    lens = [1, T - 1, T, ps + 1, 3 * ps - 1, 700, 0, 2 * ps + T, 1500]
+    w = synth.make_workload(name=f"multi_grp_{kv}_G{G}_T{T}_D{D}_ps{ps}_s{splits}_r{rot}",
+                            B=len(lens), H_qo=2 * G, H_kv=2, D=D, page_size=ps, seq_lens=lens,
+                            q_dtype="bf16", kv_dtype=kv, seed=1500 + G + T + D + ps + rot,
+                            max_num_pages=512, rotary_mode=rot, rope_theta=5e5)
+    _multi_case(w, T, seed=151 + T, num_kv_splits=splits)
+
+
+def test_attention_multi_token_groups_full_size():
+    """The fp8 GQA-8 workload's shape (B=256, 64 q / 8 KV heads, page 32, lognormal lengths) with
+    4 query tokens per sequence (32 columns per KV head: two launches), automatic plan: every
+    output against the oracle."""
+    base = synth.fp8_gqa8()
+    w = synth.make_workload(name="fp8_gqa8_T4", B=base.B, H_qo=64, H_kv=8, D=128, page_size=32,
+                            seq_lens=base.seq_lens.astype(np.int64), max_num_pages=65536,
+                            kv_dtype="fp8", seed=1007)
+    _multi_case(w, 4, seed=157)
+
+
 @pytest.mark.parametrize("kv,G,T,D,ps", [("bf16", 4, 2, 128, 16), ("bf16", 1, 8, 64, 32),
                                          ("bf16", 2, 3, 128, 16), ("fp8", 2, 4, 128, 32),
                                          ("fp8", 1, 2, 64, 16), ("bf16", 8, 1, 128, 16),
