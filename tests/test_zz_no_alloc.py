@@ -80,3 +80,11 @@ def test_noalloc_other_paths():
                                seq_lens=[5000, 40, 900, 3, 4200, 16], seed=83, max_num_pages=1024,
                                window=1024, sink=4, rotary_mode=1, rope_theta=500000.0))
     _check(synth.tiny_fp32())
+
+
+def test_noalloc_e5m2_page_scales_fp8_q():
+    """An e5m2 pool with per-(page, KV head) scales and an fp8 q through the no-alloc entry point
+    (the automatic plan with split sequences), bit-identical to the workspace entry point."""
+    _check(synth.make_workload(name="noalloc_e5m2", B=12, H_qo=32, H_kv=8, D=128, page_size=16,
+                               seq_lens=np.arange(12) * 331 + 7, kv_dtype="fp8e5m2", q_dtype="fp8",
+                               page_scales=True, seed=84, max_num_pages=2048))
