@@ -178,17 +178,25 @@ def decode_multi(*, qo_len, q, select=None, **kw):
     tokens: the last qo_len positions of each sequence are the new tokens, and token t attends
     positions 0 .. total - qo_len + t, i.e. it is the TVM page's single-token decode over that
     prefix of the sequence (its first ceil(len / ps) pages, the last one holding len - (np - 1) ps
-    rows). An empty prefix gives the empty convention. No window. With RoPE (rotary_mode 1,
-    rotate-half, or 2, interleaved), token t's query is at position q_rope_position[b] + t (the
-    new tokens are consecutive) and the keys keep the sequence's k_rope_pos_offset[b]. Returns
-    (out [B, T, H_qo, D], lse [B, T, H_qo]), or, for select = int array [n, 3] of (b, t, h_qo),
+    rows). An empty prefix gives the empty convention. With a sliding window (length_info [3, B])
+    the call's window applies to all its tokens (reading: one window start and sink per
+    sequence, as length_info gives them): token t's prefix of n rows keeps the sink rows below n
+    and the window rows from the window start up to n, i.e. the decode over that prefix with
+    window start min(win_off, n) and sink min(sink, n); the keys' RoPE positions are the
+    sequence's compacted row indices, as for one token. With RoPE (rotary_mode 1, rotate-half, or
+    2, interleaved), token t's query is at position q_rope_position[b] + t (the new tokens are
+    consecutive) and the keys keep the sequence's k_rope_pos_offset[b]. Returns (out
+    [B, T, H_qo, D], lse [B, T, H_qo]), or, for select = int array [n, 3] of (b, t, h_qo),
     (out [n, D], lse [n])."""
     B, T, ps = kw["B"], int(qo_len), kw["ps"]
-    assert not kw.get("sliding_window"), "several query tokens: no sliding window"
+    sliding = bool(kw.get("sliding_window"))
     indptr = np.asarray(kw["indptr"], np.int64)
     values = np.asarray(kw["values"], np.int64)
-    last = np.asarray(kw["length_info"], np.int64).reshape(-1)[:B]
-    ip2, val2, last2 = [0], [], []
+    li = np.asarray(kw["length_info"], np.int64).reshape(-1)
+    last = li[:B]
+    win = li[B:2 * B] if sliding else np.zeros(B, np.int64)
+    snk = li[2 * B:3 * B] if sliding else np.zeros(B, np.int64)
+    ip2, val2, last2, win2, snk2 = [0], [], [], [], []
     for b in range(B):
         npg = int(indptr[b + 1] - indptr[b])
         total = (npg - 1) * ps + int(last[b]) if npg else 0
@@ -197,15 +205,19 @@ def decode_multi(*, qo_len, q, select=None, **kw):
             if n <= 0:
                 ip2.append(ip2[-1])
                 last2.append(0)
+                win2.append(0)
+                snk2.append(0)
                 continue
             k = (n + ps - 1) // ps
             val2.extend(values[indptr[b]:indptr[b] + k].tolist())
             ip2.append(ip2[-1] + k)
             last2.append(n - (k - 1) * ps)
+            win2.append(min(int(win[b]), n))
+            snk2.append(min(int(snk[b]), n))
     kw = dict(kw)
+    li2 = np.array(last2 + win2 + snk2 if sliding else last2, np.int32)
     kw.update(B=B * T, indptr=np.array(ip2, np.int32), values=np.array(val2, np.int32),
-              length_info=np.array(last2, np.int32), q=np.ascontiguousarray(q).reshape(
-                  B * T, kw["H_qo"], kw["D"]))
+              length_info=li2, q=np.ascontiguousarray(q).reshape(B * T, kw["H_qo"], kw["D"]))
     if kw.get("rotary_mode", 0) in (1, 2):
         qrp = np.asarray(kw["q_rope_position"], np.int64).reshape(-1)[:B]
         kro = np.asarray(kw["k_rope_pos_offset"], np.int64).reshape(-1)[:B]

@@ -735,6 +735,52 @@ def test_multi_token_rope_matches_dense_causal_bruteforce(kv_dtype, q_dtype, mod
     assert np.abs(out0 - out).max() > 1e-3
 
 
+@pytest.mark.parametrize("rope", [0, 1])
+def test_multi_token_window_matches_dense_causal_bruteforce(rope):
+    """Several tokens with a sliding window and a sink (one window per sequence for all its
+    tokens): token t sees the flattened cache's rows r <= L - T + t with r < sink or r >= win_off;
+    with RoPE the keys sit at k_rope_pos_offset + their compacted index (r below the sink,
+    sink + r - win_off in the window) and token t's query at q_rope_position + t."""
+    T = 4
+    w = small(B=5, kv_dtype="bf16", q_dtype="bf16", page_order="shuffled",
+              seq_lens=[30, 3, 21, 0, 12], window=9, sink=2, rotary_mode=rope, rope_theta=1e4,
+              max_num_pages=24)
+    qm = synth.multi_query(w, T, seed=9)
+    kw = {k: v for k, v in w.oracle_kwargs().items() if k != "q"}
+    qp = np.array([50, 3, 20, 0, 9], np.int32)
+    ko = np.array([5, 0, 11, 0, 2], np.int32)
+    if rope:
+        kw.update(q_rope_position=qp, k_rope_pos_offset=ko)
+    out, lse = oracle.decode_multi(qo_len=T, q=qm, **kw)
+    G = w.H_qo // w.H_kv
+    q64 = to_f64(qm, w.q_dtype)
+    seen_window = seen_sink_only = 0
+    for b in range(w.B):
+        L = int(w.seq_lens[b])
+        off, sink = int(w.length_info[1, b]), int(w.length_info[2, b])
+        for t in range(T):
+            n = L - T + t + 1
+            rows = [r for r in range(max(n, 0)) if r < sink or r >= off]
+            seen_window += any(r >= off for r in rows) and any(r < off for r in range(max(n, 0)))
+            seen_sink_only += bool(rows) and all(r < sink for r in rows) and n > sink
+            for hq in range(w.H_qo):
+                if not rows:
+                    assert np.all(out[b, t, hq] == 0) and lse[b, t, hq] == -5e4
+                    continue
+                K, V = contiguous_kv(w, b, hq // G)
+                K, V = K[rows], V[rows]
+                q = q64[b, t, hq]
+                if rope:
+                    pos = [r if r < sink else sink + r - off for r in rows]
+                    K = np.stack([oracle.rope_rotate(K[i], ko[b] + pos[i], 1.0, 1e4)
+                                  for i in range(len(rows))])
+                    q = oracle.rope_rotate(q, qp[b] + t, 1.0, 1e4)
+                o, l = dense_attention(q, K, V, w.sm_scale)
+                np.testing.assert_allclose(out[b, t, hq], o, rtol=0, atol=1e-12)
+                assert abs(lse[b, t, hq] - l) < 1e-12
+    assert seen_window > 0  # tokens whose prefix crosses the window start
+
+
 def test_multi_token_one_token_is_decode():
     """qo_len = 1 is the single-token decode, bit for bit."""
     w = small(seq_lens=[7, 1, 13])
