@@ -227,7 +227,10 @@ pdecode_status pdecode_attention_noalloc(const pdecode_desc *d, const void *q, c
  * pdecode_workspace_bytes_multi(d, qo_len), with the same reuse rules. With RoPE (either
  * rotary_mode), token t's query sits at position q_rope_position[b] + t; the keys are placed as in
  * pdecode_attention.
- * qo_len == 1 is pdecode_attention. Supported for qo_len > 1: no sliding window, the persistent
+ * With a sliding window (length_info [3, B]) the sequence's window start and sink apply to all
+ * its new tokens: token t attends the sink rows and the window rows at positions up to
+ * total_b - qo_len + t (a reading: the pages define no per-token window).
+ * qo_len == 1 is pdecode_attention. Supported for qo_len > 1: the persistent
  * matrix-core schedule (BF16, FP8_E4M3FN or FP8_E4M3 pool, batch <= 1024) and
  * batch * qo_len * num_qo_heads <= INT_MAX; otherwise UNSUPPORTED. The kernel takes 16 q columns
  * (G = num_qo_heads / num_kv_heads per token): more than 16 / G tokens run as consecutive launches

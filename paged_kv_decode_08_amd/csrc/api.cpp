@@ -397,7 +397,6 @@ pdecode_status pdecode_attention_multi(const pdecode_desc* d, int32_t qo_len, co
   if (qo_len == 1)
     return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
                           rope, sm_scale, out, lse, workspace, workspace_bytes, stream);
-  if (d->sliding_window) return PDECODE_ERR_UNSUPPORTED;
   if (int64_t(d->batch) * qo_len * d->num_qo_heads > INT_MAX) return PDECODE_ERR_UNSUPPORTED;
   return attention_impl(d, nullptr, nullptr, q, pages, page_indptr, page_values, length_info,
                         rope, sm_scale, out, lse, workspace, workspace_bytes, stream, qo_len);

@@ -181,7 +181,7 @@ def test_append_attention_argument_errors(L):
 
 
 def test_attention_multi_argument_errors(L):
-    """pdecode_attention_multi: qo_len < 1, a sliding window, an fp32 pool, a batch beyond the
+    """pdecode_attention_multi: qo_len < 1, an fp32 pool, a batch beyond the
     persistent schedule, more rows than an int holds and an invalid RoPE base are refused before
     anything is launched; the workspace size grows with the tokens. (More than 16 MFMA columns,
     group size x tokens, run as several launches: the GPU tests.)"""
@@ -193,7 +193,6 @@ def test_attention_multi_argument_errors(L):
                  None)
     assert call(desc(), 0) == 1
     assert call(desc(), 2, pk.Rope(1, 1.0, -1.0, FAKE, FAKE)) == 1
-    assert call(desc(sliding_window=True), 2) == 2
     assert call(desc(batch=1024), (1 << 31) // (1024 * 32) + 1) == 2  # rows past INT_MAX
     assert call(desc(num_qo_heads=8, batch=2000), 4) == 2
     assert call(desc(num_qo_heads=8, q_dtype="f32", kv_dtype="f32"), 4) == 2

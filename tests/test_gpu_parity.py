@@ -979,6 +979,26 @@ def test_attention_multi_token_groups(kv, G, T, D, ps, splits, rot):
     _multi_case(w, T, seed=151 + T, num_kv_splits=splits)
 
 
+@pytest.mark.parametrize("kv,G,T,D,ps,splits,rot,win", [
+    ("bf16", 4, 3, 128, 16, 0, 0, 300),
+    ("fp8", 8, 2, 128, 32, 5, 1, 300),     # rotate-half RoPE: keys at their compacted positions
+    ("bf16", 8, 4, 64, 16, 0, 2, 300),     # two launches of 16 columns, interleaved RoPE
+    ("bf16", 2, 5, 128, 32, 12, 0, 300),   # forced splits
+    ("bf16", 4, 4, 128, 16, 0, 1, 2),      # a window of 2 rows: the first tokens see only the sink
+])
+def test_attention_multi_window(kv, G, T, D, ps, splits, rot, win):
+    """Several query tokens with a sliding window and a sink (one window per sequence for all its
+    tokens, each token causal within it): every output against the oracle; prefixes that end
+    before the window start (sink rows only) and empty ones included."""
+    lens = [1, T - 1, 3, ps + 1, 700, 0, 2000, 5 * ps + 3]
+    w = synth.make_workload(name=f"multi_win_{kv}_G{G}_T{T}_D{D}_ps{ps}_s{splits}_r{rot}_w{win}",
+                            B=len(lens), H_qo=2 * G, H_kv=2, D=D, page_size=ps, seq_lens=lens,
+                            q_dtype="bf16", kv_dtype=kv, seed=1600 + G + T + D + rot,
+                            max_num_pages=512, window=win, sink=4, rotary_mode=rot,
+                            rope_theta=5e5)
+    _multi_case(w, T, seed=161 + T, num_kv_splits=splits)
+
+
 def test_attention_multi_token_groups_full_size():
     """The fp8 GQA-8 workload's shape (B=256, 64 q / 8 KV heads, page 32, lognormal lengths) with
     4 query tokens per sequence (32 columns per KV head: two launches), automatic plan: every
