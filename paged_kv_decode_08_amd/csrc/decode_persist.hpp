@@ -382,8 +382,8 @@ __device__ void merge_split(const DecodeParams& p, int b, int h, int nch) {
 }
 
 // FUSED: the call also appends each sequence's new K/V row (p.new_k, p.new_v).
-// MT: several query tokens per sequence (p.T > 1; no window): the G T columns of the
-// MFMA B operand are token-major and each is causally capped.
+// MT: several query tokens per sequence (p.T_all > 1; a sliding window holds for all of them):
+// the G T columns of the MFMA B operand are token-major and each is causally capped.
 // ILV (with ROPE): the interleaved RoPE layout (rotary_mode 2).
 template <int KVT, int D, int PS, int GP, bool ROPE, bool FUSED, bool MT = false, bool ILV = false>
 __global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2)))
