@@ -396,6 +396,21 @@ def step_bench(workload, steps, warmup, nsets):
                       "kv_bytes_per_step": base.kv_bytes, "data": "synthetic", **res}), flush=True)
 
 
+def kernel_desc(kv_dtype, num_chunks):
+    """What one timed pdecode_attention call launches for a plan of at most num_chunks chunks per
+    sequence (the time covers all of it)."""
+    if kv_dtype == "f32":
+        return ("pdecode_attention: the vector-ALU decode kernel, one wave per chunk; the last "
+                "chunk of a split sequence to finish merges it (one launch)")
+    if num_chunks <= 1:
+        return "pdecode_attention: the persistent matrix-core decode kernel (one launch, no splits)"
+    if num_chunks <= 8:
+        return ("pdecode_attention: the persistent matrix-core decode kernel, which merges split "
+                "sequences itself (one launch)")
+    return ("pdecode_attention: the persistent matrix-core decode kernel, then the split merge "
+            "kernel (two launches)")
+
+
 def _timeline_summary(marks, item_bytes):
     """One call's marks ([4096, 64] uint64: time << 24 | tag << 20 | value; time in 10 ns ticks of
     s_memrealtime) -> text lines and a dict of the key times (us from the first workgroup entry)."""
@@ -663,8 +678,7 @@ def main():
                      "traffic": recorded_traffic(args.workload),
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                      "algorithmic_bytes": kv_bytes,
-                     "kernel": ("pdecode_attention: one launch of the persistent decode kernel, "
-                                "which also merges the split sequences"),
+                     "kernel": kernel_desc(base.kv_dtype, nc),
                      "avg_launch_us": round(avg_call_s * 1e6, 3),
                      "ceiling_GBps": ceiling["GBps"] if ceiling else None,
                      "frac_of_ceiling": round(achieved / ceiling["GBps"], 4) if ceiling else None,
