@@ -1242,10 +1242,11 @@ def test_full_size_fused_step():
     assert_close(w, o_ref, l_ref, gu.to_np64(out), gu.to_np64(lse), "full-size fused")
 
 
-@pytest.mark.parametrize("T", [2, 4])
+@pytest.mark.parametrize("T", [2, 4, 6])
 def test_full_size_multi_token_and_sink(T):
-    """pdecode_attention_multi (two tokens, and four: 16 MFMA columns) with learned sinks on the
-    full Llama-3-8B-shaped workload: every (sequence, token, head) output against the oracle."""
+    """pdecode_attention_multi (two tokens, four: 16 MFMA columns, and six: launches of 4 and 2
+    tokens) with learned sinks on the full Llama-3-8B-shaped workload: every (sequence, token,
+    head) output against the oracle."""
     w = synth.CONFIGS["llama3_8b_bf16"]()
     qm = synth.multi_query(w, T, seed=78)
     sinks = np.random.default_rng(79).normal(0.0, 2.0, w.H_qo).astype(np.float32)
