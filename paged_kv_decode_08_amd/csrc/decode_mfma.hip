@@ -220,16 +220,14 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
 
   float mx = lane < nch ? lse_l : -INFINITY;
   for (int c = 64 + lane; c < nch; c += 64) mx = fmaxf(mx, lse_c[c]);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  mx = wave_max_f(mx);
   // several query tokens: a token that sees no row of the sequence has every chunk lse -inf
   const bool none = mx == -INFINITY;
   const float M = none ? 0.f : mx;
   const float w_l = lane < nch ? exp2_fast(lse_l - M) : 0.f;  // weight of chunk `lane`
   float ws = w_l;
   for (int c = 64 + lane; c < nch; c += 64) ws += exp2_fast(lse_c[c] - M);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) ws += __shfl_xor(ws, o, 64);
+  ws = wave_sum_f(ws);
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c0 = 0; c0 < nch; c0 += CB) {

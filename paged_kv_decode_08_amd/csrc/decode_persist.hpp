@@ -129,20 +129,68 @@ __device__ __forceinline__ long long wave_sum64(long long x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
+// Wave reductions and the inclusive scan of the job-table build on the DPP lane network (gfx9
+// row operations: quad permutes, the half-row and row mirrors, row shifts and the row-15 / row-31
+// broadcasts), a few cycles a step instead of an LDS round trip (ds_bpermute) a step; the
+// reductions end with the four rows' values read into scalars, so every lane gets the result.
+// Lanes without a source (or in rows outside the mask) read 0.
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ int dpp0(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_same(int v) {  // every lane has a source here
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 __device__ __forceinline__ float wave_sum_f(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+  int v = __float_as_int(x);
+  v = __float_as_int(__int_as_float(v) + __int_as_float(dpp_same<kDppXor1>(v)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(dpp_same<kDppXor2>(v)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(dpp_same<kDppHalfMirror>(v)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(dpp_same<kDppMirror>(v)));
+  return (__int_as_float(__builtin_amdgcn_readlane(v, 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(v, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(v, 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(v, 48)));
 }
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_same<kDppXor1>(v);
+  v += dpp_same<kDppXor2>(v);
+  v += dpp_same<kDppHalfMirror>(v);
+  v += dpp_same<kDppMirror>(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
-__device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
-  return x;
+__device__ __forceinline__ int wave_max(int v) {
+  v = max(v, dpp_same<kDppXor1>(v));
+  v = max(v, dpp_same<kDppXor2>(v));
+  v = max(v, dpp_same<kDppHalfMirror>(v));
+  v = max(v, dpp_same<kDppMirror>(v));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ float wave_max_f(float x) {
+  int v = __float_as_int(x);
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_same<kDppXor1>(v))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_same<kDppXor2>(v))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_same<kDppHalfMirror>(v))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_same<kDppMirror>(v))));
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(v, 0)),
+                     __int_as_float(__builtin_amdgcn_readlane(v, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(v, 32)),
+                     __int_as_float(__builtin_amdgcn_readlane(v, 48))));
+}
+// Inclusive prefix sum over the wave's 64 lanes: shifts by 1, 2, 4 and 8 within each row of 16,
+// then row 0's and row 2's last lanes into rows 1 and 3, and lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_scan_i(int v) {
+  v += dpp0<0x111>(v);       // row_shr:1
+  v += dpp0<0x112>(v);       // row_shr:2
+  v += dpp0<0x114>(v);       // row_shr:4
+  v += dpp0<0x118>(v);       // row_shr:8
+  v += dpp0<0x142, 0xa>(v);  // row_bcast:15
+  v += dpp0<0x143, 0xc>(v);  // row_bcast:31
+  return v;
 }
 
 // Chunk size in page slots of the automatic plan, chosen from the call's own lengths: N attended
@@ -484,12 +532,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
           if constexpr (ROPE) tab.rpos[rank] = make_int2(p.q_pos[l], p.k_off[l]);
         }
         wave_lds_fence();
-        int x = ok ? tab.rnj[l] : 0;  // jobs of rank l, then the inclusive prefix
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(x, o, 64);
-          if (l >= o) x += y;
-        }
+        const int x = wave_scan_i(ok ? tab.rnj[l] : 0);  // jobs of rank l, inclusive prefix
         if (ok) tab.pre[l + 1] = x;
         if (l == 0) tab.pre[0] = 0;
       }
@@ -557,12 +600,11 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         tab.njobs[b] = nch * p.H_kv;
         cnt += 1ull << (16 * size_class(n, nch, cs));
       }
-      unsigned long long x = cnt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long y = __shfl_up(x, o, 64);
-        if (l >= o) x += y;
-      }
+      // the 16-bit class fields hold at most 4 x 64 sequences of a wave: the two 32-bit halves
+      // scan independently
+      const unsigned long long x =
+          static_cast<unsigned long long>(static_cast<uint32_t>(wave_scan_i(static_cast<int>(cnt & 0xffffffffu)))) |
+          static_cast<unsigned long long>(static_cast<uint32_t>(wave_scan_i(static_cast<int>(cnt >> 32)))) << 32;
       if (l == 63) s_scan64[w] = x;
       __syncthreads();
       unsigned long long off = x - cnt, total = 0;
@@ -596,12 +638,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         run += tab.rnj[r];
         tab.pre[r + 1] = run;
       }
-      int y = run;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int z = __shfl_up(y, o, 64);
-        if (l >= o) y += z;
-      }
+      const int y = wave_scan_i(run);
       if (l == 63) s_scan[w] = y;
       __syncthreads();
       int off2 = y - run;
