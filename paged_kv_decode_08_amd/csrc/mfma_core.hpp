@@ -60,8 +60,22 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const unsigned char* p) {
 
 
 
-__device__ __forceinline__ float xmax(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
+// max / sum of v over lanes l and l ^ 16 (ROWS = 16) or l ^ 32 (ROWS = 32), on the VALU:
+// v_permlane16_swap / v_permlane32_swap with v in both operands return the lane's own value and
+// its partner's (in an order that depends on the lane: the max and the sum do not care).
+template <int ROWS>
+__device__ __forceinline__ float xmax(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p = ROWS == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                            : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+template <int ROWS>
+__device__ __forceinline__ float xsum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p = ROWS == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                            : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 
@@ -434,7 +448,7 @@ struct MfmaCore {
         sv[rb][v] = x;
         tmax = fmaxf(tmax, x);
       }
-    tmax = xmax(xmax(tmax, 16), 32);
+    tmax = xmax<32>(xmax<16>(tmax));
     const float mn = fmaxf(m, tmax);  // finite unless COLCAP: the page has an attended row
     // a column with no row yet keeps m = -inf, O = 0, d = 0 (reference 0: every weight is 0)
     const float mref = COLCAP && mn == -INFINITY ? 0.f : mn;
@@ -485,9 +499,7 @@ struct MfmaCore {
   // Reduces this wave's state over its lanes (d over the row quads, O over the row groups) and
   // writes it to the wave's slots of the workgroup merge buffers.
   __device__ __forceinline__ void to_lds(float* s_m, float* s_d, float (*s_o)[D]) {
-    float d = dl;
-    d += __shfl_xor(d, 16, 64);
-    d += __shfl_xor(d, 32, 64);
+    const float d = xsum<32>(xsum<16>(dl));
     if (qg == 0 && n < GP) {
       s_m[n] = m;
       s_d[n] = d;
