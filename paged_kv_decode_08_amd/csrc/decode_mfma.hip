@@ -244,14 +244,18 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
       }
     }
   }
-  // add the CPW chunk phases (lanes v, v + V, ...)
-#pragma unroll
-  for (int o = V; o < 64; o <<= 1) {
-    acc.x += __shfl_xor(acc.x, o, 64);
-    acc.y += __shfl_xor(acc.y, o, 64);
-    acc.z += __shfl_xor(acc.z, o, 64);
-    acc.w += __shfl_xor(acc.w, o, 64);
+  // add the CPW chunk phases (lanes v, v + V, ...): over l ^ 32, and for V = 16 over l ^ 16 first
+  static_assert(V == 16 || V == 32, "two or four chunk phases");
+  if constexpr (V == 16) {
+    acc.x = xsum<16>(acc.x);
+    acc.y = xsum<16>(acc.y);
+    acc.z = xsum<16>(acc.z);
+    acc.w = xsum<16>(acc.w);
   }
+  acc.x = xsum<32>(acc.x);
+  acc.y = xsum<32>(acc.y);
+  acc.z = xsum<32>(acc.z);
+  acc.w = xsum<32>(acc.w);
   if (nch <= 1) return;  // unsplit (or empty) sequence: the decode kernel wrote its row
   float Mf = M;
   float fo = 1.f;  // learned sink of the row's q head, folded once

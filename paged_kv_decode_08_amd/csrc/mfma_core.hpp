@@ -208,9 +208,15 @@ struct MfmaCore {
   }
 
   // The same words of lane l ^ 32 (the other half of the wave).
-  __device__ __forceinline__ static uint4 other_half(const uint4& v) {
-    return make_uint4(uint32_t(__shfl_xor(int(v.x), 32)), uint32_t(__shfl_xor(int(v.y), 32)),
-                      uint32_t(__shfl_xor(int(v.z), 32)), uint32_t(__shfl_xor(int(v.w), 32)));
+  // (v_permlane32_swap with v in both operands returns (own, partner) in the lower half of the
+  // wave and (partner, own) in the upper half)
+  __device__ __forceinline__ uint4 other_half(const uint4& v) const {
+    const bool lo = l < 32;
+    auto part = [lo](uint32_t x) {
+      const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      return lo ? p[1] : p[0];
+    };
+    return make_uint4(part(v.x), part(v.y), part(v.z), part(v.w));
   }
 
   // XLANE rotate-half at position pos: x holds this lane's 8 dims of k-step j, xp the same
