@@ -11,7 +11,8 @@
 //    16-byte global loads: lane l holds row l % 16; bf16: elements [8 (4j + l/16), +8) for k-step
 //    j; fp8: 16 codes [64 j' + 16 (l/16), +16) converted exactly to bf16 for k-steps 2j', 2j'+1.
 //    The accumulator gives lane l the scores of rows 4 (l/16) + {0..3} for head l % 16.
-//  * softmax: the tile max per head needs two cross-row exchanges; one exp2 per score.
+//  * softmax: the tile max per head needs two cross-row exchanges (v_permlane16/32_swap); one
+//    exp2 per score.
 //  * P.V on the matrix cores too: O^T[dims][heads] += V^T P, one v_mfma_f32_16x16x16_bf16 per 16
 //    dims. P is the B operand as it stands in the score accumulator (lane l: rows 4 (l/16) + {0..3}
 //    of head l % 16), rounded to bf16. V (lane l loads 8 consecutive dims of NI consecutive rows,
