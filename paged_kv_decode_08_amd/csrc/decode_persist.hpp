@@ -40,12 +40,14 @@ __device__ __forceinline__ void timeline_mark(int row, int& k, int tag, int val)
 #endif
 constexpr int kPersistMaxBatch = 1024;  // sequences the persistent schedule's LDS table holds
 constexpr int kPersistMaxGrid = 1024;   // workgroups of the persistent schedule, at most
+// Size classes of the job order, a quarter octave of chunk size each
+constexpr int kSizeClasses = 16;
 
 // ------------------------------------------------------------------------------------------------
 // Persistent workgroups over a job queue.
 
-// Per-sequence table in LDS. Sequences are ranked by the size of their chunks, largest first (four
-// size classes, stable within a class), and jobs are numbered in that order: the queue hands out
+// Per-sequence table in LDS. Sequences are ranked by the size of their chunks, largest first (16
+// size classes a quarter octave wide, stable within a class), and jobs are numbered in that order: the queue hands out
 // long jobs first and ends with short ones, which shortens the tail of the call. Jobs of one
 // sequence are ordered chunk-major, KV head minor. What a job needs is stored by rank, so decoding
 // a job number takes two ballots and one round of LDS reads.
@@ -457,6 +459,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   __shared__ float s_qsc[2][16];         // fp8 q: each MFMA column's q-head scale (1 otherwise)
   __shared__ int s_scan[kPWaves];
   __shared__ unsigned long long s_scan64[kPWaves];
+  __shared__ uint32_t s_cls[kPWaves][kSizeClasses / 2];  // class counts per wave (B > 64)
   __shared__ int s_ticket;
   __shared__ int s_mrg[kPWaves];  // wave w's arrival completed the previous job's split sequence
   __shared__ float2 s_freq[ROPE ? D / 2 : 1];  // RoPE: frequencies (rope_freq) of dims i, i + D/2
@@ -490,10 +493,14 @@ void decode_mfma_persist_kernel(DecodeParams p) {
   const SeqTable tab = seq_table(s_dyn, B);
   {
     constexpr int kUnit = slot_unit<PS>();
-    // size class of a sequence: 0 for chunks above 7/8 of chunk_slots, .. 3 for 5/8 and below
+    // size class of a sequence, on a quarter-octave scale of its chunk size sz against the chunk
+    // target cs: class k holds cs 2^(-(k+1)/4) < sz <= cs 2^(-k/4) (class 0 also everything
+    // larger; the last class everything smaller, and sequences without chunks)
     auto size_class = [&](int n_slots, int nch, int cs) {
-      const int sz = nch > 0 ? (n_slots + nch - 1) / nch : 0;
-      return 8 * sz > 7 * cs ? 0 : 8 * sz > 6 * cs ? 1 : 8 * sz > 5 * cs ? 2 : 3;
+      if (nch <= 0) return kSizeClasses - 1;
+      const float r = float((n_slots + nch - 1) / nch) / float(cs);
+      // the same instructions on the same values in every workgroup: the same class
+      return int(fminf(fmaxf(-4.f * __log2f(r), 0.f), float(kSizeClasses - 1)));
     };
     const int P = int(gridDim.x);
     if (B <= 64) {
@@ -513,11 +520,11 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         if (p.auto_chunk && blockIdx.x == 0 && l == 0 && p.plan_word) *p.plan_word = cs;
         const int nch = persist_chunks<PS>(n, cs, p.num_chunks);
         const int nj = nch * p.H_kv;
-        const int c = ok ? size_class(n, nch, cs) : 4;
+        const int c = ok ? size_class(n, nch, cs) : kSizeClasses;
         int rank = 0;
         unsigned long long same = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kSizeClasses; ++k) {
           const unsigned long long m = __ballot(c == k);
           if (k < c) rank += __popcll(m);
           if (k == c) same = m;
@@ -541,6 +548,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       // Every thread takes `per` consecutive sequences; class counts and the job prefix are
       // scanned over the workgroup.
       const int per = (B + NT - 1) / NT;
+      static_assert(kPersistMaxBatch <= 8 * NT, "a thread's classes fit 4 bits each in an int");
       const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
       // Sums over the workgroup (every thread calls them alike; s_scan64 is free again after).
       auto block_sum = [&](long long x) {
@@ -593,40 +601,59 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         });
         if (blockIdx.x == 0 && tid == 0 && p.plan_word) *p.plan_word = cs;  // for split_merge_kernel
       }
-      unsigned long long cnt = 0;  // this thread's sequences per class, 16 bits each
+      // this thread's sequences per class, 16 bits each, two classes per 32-bit word
+      constexpr int kWords = kSizeClasses / 2;
+      int cls_list = 0;  // classes of this thread's sequences, 4 bits each (computed once)
+      uint32_t cnt[kWords];
+#pragma unroll
+      for (int i = 0; i < kWords; ++i) cnt[i] = 0;
       for (int b = b0; b < b1; ++b) {
         const int n = tab.njobs[b];
         const int nch = persist_chunks<PS>(n, cs, p.num_chunks);
         tab.njobs[b] = nch * p.H_kv;
-        cnt += 1ull << (16 * size_class(n, nch, cs));
+        const int c = size_class(n, nch, cs);
+        cls_list |= c << (4 * (b - b0));
+#pragma unroll
+        for (int i = 0; i < kWords; ++i) cnt[i] += c / 2 == i ? 1u << (16 * (c & 1)) : 0u;
       }
-      // the 16-bit class fields hold at most 4 x 64 sequences of a wave: the two 32-bit halves
-      // scan independently
-      const unsigned long long x =
-          static_cast<unsigned long long>(static_cast<uint32_t>(wave_scan_i(static_cast<int>(cnt & 0xffffffffu)))) |
-          static_cast<unsigned long long>(static_cast<uint32_t>(wave_scan_i(static_cast<int>(cnt >> 32)))) << 32;
-      if (l == 63) s_scan64[w] = x;
+      // the 16-bit class fields hold at most 4 x 64 sequences of a wave and 1024 of the
+      // workgroup: the words scan independently
+      uint32_t off[kWords], total[kWords];
+#pragma unroll
+      for (int i = 0; i < kWords; ++i) {
+        const uint32_t x = static_cast<uint32_t>(wave_scan_i(static_cast<int>(cnt[i])));
+        if (l == 63) s_cls[w][i] = x;
+        off[i] = x - cnt[i];
+        total[i] = 0;
+      }
       __syncthreads();
-      unsigned long long off = x - cnt, total = 0;
 #pragma unroll
       for (int ww = 0; ww < kPWaves; ++ww) {
-        if (ww < w) off += s_scan64[ww];
-        total += s_scan64[ww];
-      }
-      int cls_start[4];
-      int acc = 0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        cls_start[c] = acc + int((off >> (16 * c)) & 0xffff);
-        acc += int((total >> (16 * c)) & 0xffff);
+        for (int i = 0; i < kWords; ++i) {
+          if (ww < w) off[i] += s_cls[ww][i];
+          total[i] += s_cls[ww][i];
+        }
       }
+      // class c's field of a packed word array (selects, no indexed registers)
+      auto field = [](const uint32_t (&a)[kWords], int c) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int i = 0; i < kWords; ++i) v = i == c / 2 ? a[i] : v;
+        return int((v >> (16 * (c & 1))) & 0xffffu);
+      };
       for (int b = b0; b < b1; ++b) {
         const int4 gg = tab.geo[b];
         const int sk = tab.sink[b];
         const int n0 = (sk + PS - 1) / PS;
         const int n_slots = gg.y > 0 ? n0 + (gg.w < gg.z ? gg.y - gg.w / PS : 0) : 0;
         const int nch = tab.njobs[b] / p.H_kv;
-        const int rank = cls_start[size_class(n_slots, nch, cs)]++;
+        const int c = (cls_list >> (4 * (b - b0))) & 15;
+        // sequences of lower classes, then those of class c in lower threads and before b here
+        int rank = field(off, c);
+#pragma unroll
+        for (int k = 0; k < kSizeClasses; ++k) rank += k < c ? field(total, k) : 0;
+        for (int i = 0; i < b - b0; ++i) rank += ((cls_list >> (4 * i)) & 15) == c ? 1 : 0;
         tab.rgeo[rank] = gg;
         tab.rsb[rank] = make_int4(sk, b, nch, nch > 0 ? n_slots / kUnit / nch : 0);
         tab.rnj[rank] = tab.njobs[b];
