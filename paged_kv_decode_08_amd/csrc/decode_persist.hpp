@@ -642,6 +642,12 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         for (int i = 0; i < kWords; ++i) v = i == c / 2 ? a[i] : v;
         return int((v >> (16 * (c & 1))) & 0xffffu);
       };
+      // first rank of each class (the same in every thread), computed once
+      int base[kSizeClasses];
+      base[0] = 0;
+#pragma unroll
+      for (int k = 1; k < kSizeClasses; ++k)
+        base[k] = base[k - 1] + int((total[(k - 1) / 2] >> (16 * ((k - 1) & 1))) & 0xffffu);
       for (int b = b0; b < b1; ++b) {
         const int4 gg = tab.geo[b];
         const int sk = tab.sink[b];
@@ -652,7 +658,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         // sequences of lower classes, then those of class c in lower threads and before b here
         int rank = field(off, c);
 #pragma unroll
-        for (int k = 0; k < kSizeClasses; ++k) rank += k < c ? field(total, k) : 0;
+        for (int k = 1; k < kSizeClasses; ++k) rank += k == c ? base[k] : 0;
         for (int i = 0; i < b - b0; ++i) rank += ((cls_list >> (4 * i)) & 15) == c ? 1 : 0;
         tab.rgeo[rank] = gg;
         tab.rsb[rank] = make_int4(sk, b, nch, nch > 0 ? n_slots / kUnit / nch : 0);
