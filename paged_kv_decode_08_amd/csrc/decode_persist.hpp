@@ -201,16 +201,26 @@ __device__ __forceinline__ int wave_scan_i(int v) {
 // sequence (the partial states have room for that many). jobs(c) is the call's job count with
 // chunks of c slots (non-increasing in c); every thread that calls this calls it with the same
 // values.
-// * One job per workgroup, if no job is then above 5/4 of the mean work of a workgroup (few
-//   sequences of similar length: long contexts, sliding windows); measured 7 us (6 %) faster than
-//   two per workgroup on the long-context shape.
+// * One job per workgroup, if no job is then above one_job (one_job_bound) times the mean work of
+//   a workgroup (few sequences of similar length: long contexts, sliding windows; with split
+//   sequences merged in the kernel also mixed lengths); measured 7 us (6 %) faster than two per
+//   workgroup on the long-context shape.
 // * Otherwise about max(2 P, 2 pairs) chunks of the longest sequence's size over the
 //   (sequence, KV head) pairs: what the host plans from a tight length hint, whose chunk size was
 //   tuned on the Llama-3-8B shape (64 slots there; 61 and 44 slots measured 2.4 and 2.8 us
 //   slower). With more pairs than workgroups this halves the longest sequence.
+// A plan of one job per workgroup is taken when no job is above this many times the mean work of
+// a workgroup (the workgroups that finish early leave the chip to the larger jobs, which then
+// stream faster). Where split sequences are merged in the kernel, a second round of jobs also
+// carries the first round's merges, and one round pays off at larger jobs. Measured at the
+// Llama-3-8B lengths: 8 q heads merged in the kernel, one job per workgroup (97-slot chunks, the
+// largest job 1.4x the mean) 60.0 against 62.7 us for two rounds of 64-slot chunks; merged by the
+// split merge kernel, 4 q heads (109-slot chunks, 1.44x) 64.1 against 60.6 us, and 2 or 4 query
+// tokens 65.2 and 68.2 against 61.8 and 66.4 us.
+constexpr float one_job_bound(bool merges_in_kernel) { return merges_in_kernel ? 1.5f : 1.25f; }
 template <typename Jobs>
 __device__ int auto_chunk_slots(float N, int n_seq, int n_max, int H, int P, int min_chunk,
-                                int max_chunks, Jobs jobs) {
+                                int max_chunks, float one_job, Jobs jobs) {
   // Every workgroup runs this in its prologue, so it decides from single-precision estimates
   // (the same on every workgroup) and counts jobs at most twice: 64-bit divisions and a search
   // here measured 2.3 us per call on the Llama-3-8B shape.
@@ -220,18 +230,20 @@ __device__ int auto_chunk_slots(float N, int n_seq, int n_max, int H, int P, int
   const float NH = N * float(H);
   const float pairs = float(n_seq) * float(H);
   if (pairs <= float(P)) {
-    const float lim = 1.25f * NH / float(P);  // the largest job a balanced one-per-workgroup plan has
-    // about the smallest chunk giving P jobs, a sequence's last chunk taken as half full; whole
-    // sequences (n_max) give pairs <= P jobs
+    const float lim = one_job * NH / float(P);  // the largest job a one-per-workgroup plan may have
+    // about the smallest chunk giving P jobs, a sequence's last chunk taken as half full, grown by
+    // the excess until the plan has at most P jobs; whole sequences (n_max) give pairs <= P jobs
     int c = max(min_chunk, up(NH / (float(P) - 0.5f * pairs)));
-    if (c < n_max && float(c) <= lim) {
+    bool fits = false;
+    for (int it = 0; it < 4 && c < n_max && float(c) <= lim; ++it) {
       const long long J = jobs(c);
-      if (J > P) {  // grow by the excess once
-        c = up(float(c) * float(J) / float(P));
-        if (c < n_max && jobs(c) > P) c = n_max;
+      if (J <= P) {
+        fits = true;
+        break;
       }
+      c = max(c + 1, up(float(c) * float(J) / float(P)));
     }
-    c = min(c, n_max);
+    if (!fits) c = n_max;
     if (float(c) <= lim) return c;
   }
   const float target = fmaxf(2.f * float(P), 2.f * pairs);
@@ -503,6 +515,7 @@ void decode_mfma_persist_kernel(DecodeParams p) {
       return int(fminf(fmaxf(-4.f * __log2f(r), 0.f), float(kSizeClasses - 1)));
     };
     const int P = int(gridDim.x);
+    const float one_job = one_job_bound(merges_in_kernel<GP>(p.num_chunks, MT));
     if (B <= 64) {
       // One wave, lane b for sequence b: the rank counts the sequences of lower classes (ballots)
       // and those of the same class before b (mbcnt); the job prefix is a wave scan.
@@ -513,8 +526,10 @@ void decode_mfma_persist_kernel(DecodeParams p) {
         int cs = p.chunk_slots;
         if (p.auto_chunk)
           cs = auto_chunk_slots(wave_sum_f(float(n)), __popcll(__ballot(n > 0)), wave_max(n), p.H_kv, P,
-                                p.chunk_slots, p.num_chunks, [&](int cc) {
-                                  return p.H_kv * wave_sum64(persist_chunks<PS>(n, cc, p.num_chunks));
+                                p.chunk_slots, p.num_chunks, one_job, [&](int cc) {
+                                  // at most 64 x num_chunks: a 32-bit DPP sum
+                                  return static_cast<long long>(p.H_kv) *
+                                         wave_sum_i(persist_chunks<PS>(n, cc, p.num_chunks));
                                 });
         // the split merge kernel reads the chunk size after the job counters
         if (p.auto_chunk && blockIdx.x == 0 && l == 0 && p.plan_word) *p.plan_word = cs;
@@ -594,7 +609,8 @@ void decode_mfma_persist_kernel(DecodeParams p) {
           bmax = max(bmax, s_scan[ww]);
         }
         __syncthreads();  // s_scan64 is free again (block_sum below)
-        cs = auto_chunk_slots(tot, nseq, bmax, p.H_kv, P, p.chunk_slots, p.num_chunks, [&](int cc) {
+        cs = auto_chunk_slots(tot, nseq, bmax, p.H_kv, P, p.chunk_slots, p.num_chunks, one_job,
+                              [&](int cc) {
           long long x = 0;
           for (int b = b0; b < b1; ++b) x += persist_chunks<PS>(tab.njobs[b], cc, p.num_chunks);
           return p.H_kv * block_sum(x);
