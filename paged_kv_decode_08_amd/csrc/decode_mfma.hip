@@ -204,14 +204,14 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
   const float* lse_c = p.part_lse + size_t(row) * nc;
   const float* o_c = p.part_o + size_t(row) * nc * D;
   const int v = lane % V, ph = lane / V;
+  // the first batch is loaded before the row's chunk count is known (indexes clamped into the
+  // plan's slots); later ones once it is, clamped to the row's own chunks (no stale rows read),
+  // two batches of 2 NB loads per lane in flight
   float4 x[NB];
-  auto load_batch = [&](int c0) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
-      x[i] = *reinterpret_cast<const float4*>(o_c + size_t(min(c0 + i * CPW + ph, nc - 1)) * D + 4 * v);
-  };
+  for (int i = 0; i < NB; ++i)
+    x[i] = *reinterpret_cast<const float4*>(o_c + size_t(min(i * CPW + ph, nc - 1)) * D + 4 * v);
   const float lse_l = lse_c[min(lane, nc - 1)];
-  load_batch(0);
   // automatic plan: the chunk size the decode kernel chose (its workgroup 0 stored it after the
   // partial lse); loaded with the rest, used only once everything has arrived
   const int cs = p.auto_chunk ? *p.plan_word : p.chunk_slots;
@@ -229,19 +229,38 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
   for (int c = 64 + lane; c < nch; c += 64) ws += exp2_fast(lse_c[c] - M);
   ws = wave_sum_f(ws);
 
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < nch; c0 += CB) {
-    if (c0 > 0) load_batch(c0);
+  constexpr int NB2 = 2 * NB;      // float4 loads per lane in a later batch
+  constexpr int CB2 = NB2 * CPW;   // chunks per later batch
+  float4 y[NB2], z[NB2];
+  auto load_later = [&](float4 (&buf)[NB2], int c0) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
+    for (int i = 0; i < NB2; ++i)
+      buf[i] = *reinterpret_cast<const float4*>(o_c + size_t(min(c0 + i * CPW + ph, nch - 1)) * D + 4 * v);
+  };
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto accumulate = [&](const auto& buf, int c0) __attribute__((always_inline)) {
+    constexpr int nb = sizeof(buf) / sizeof(float4);
+#pragma unroll
+    for (int i = 0; i < nb; ++i) {
       const int c = c0 + i * CPW + ph;
       const float wc = c < 64 ? __shfl(w_l, c & 63, 64) : exp2_fast(lse_c[min(c, nc - 1)] - M);
       if (c < nch) {  // select, not a product: a stale partial past nch may hold any bits
-        acc.x = fmaf(wc, x[i].x, acc.x);
-        acc.y = fmaf(wc, x[i].y, acc.y);
-        acc.z = fmaf(wc, x[i].z, acc.z);
-        acc.w = fmaf(wc, x[i].w, acc.w);
+        acc.x = fmaf(wc, buf[i].x, acc.x);
+        acc.y = fmaf(wc, buf[i].y, acc.y);
+        acc.z = fmaf(wc, buf[i].z, acc.z);
+        acc.w = fmaf(wc, buf[i].w, acc.w);
       }
+    }
+  };
+  if (CB < nch) load_later(y, CB);
+  if (CB + CB2 < nch) load_later(z, CB + CB2);
+  accumulate(x, 0);
+  for (int c0 = CB; c0 < nch; c0 += 2 * CB2) {
+    accumulate(y, c0);
+    if (c0 + 2 * CB2 < nch) load_later(y, c0 + 2 * CB2);
+    if (c0 + CB2 < nch) {
+      accumulate(z, c0 + CB2);
+      if (c0 + 3 * CB2 < nch) load_later(z, c0 + 3 * CB2);
     }
   }
   // add the CPW chunk phases (lanes v, v + V, ...): over l ^ 32, and for V = 16 over l ^ 16 first
