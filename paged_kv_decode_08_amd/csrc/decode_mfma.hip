@@ -206,7 +206,7 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
   const int v = lane % V, ph = lane / V;
   // the first batch is loaded before the row's chunk count is known (indexes clamped into the
   // plan's slots); later ones once it is, clamped to the row's own chunks (no stale rows read),
-  // two batches of 2 NB loads per lane in flight
+  // two batches in flight
   float4 x[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(64 * kMergeRows) void split_merge_kernel(DecodePara
   for (int c = 64 + lane; c < nch; c += 64) ws += exp2_fast(lse_c[c] - M);
   ws = wave_sum_f(ws);
 
-  constexpr int NB2 = 2 * NB;      // float4 loads per lane in a later batch
+  constexpr int NB2 = NB;          // float4 loads per lane in a later batch
   constexpr int CB2 = NB2 * CPW;   // chunks per later batch
   float4 y[NB2], z[NB2];
   auto load_later = [&](float4 (&buf)[NB2], int c0) {
