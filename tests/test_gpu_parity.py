@@ -405,11 +405,12 @@ def test_append_then_decode():
 
 # ------------------------------------------------------------------ full-size workloads, every output
 @pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b_bf16", "long_ctx_bf16", "rope_swa_bf16",
-                                  "fp8_gqa8"])
+                                  "fp8_gqa8", "gqa8_bf16"])
 def test_full_size_config(name):
-    """The five workloads at full size in the benchmark's launch configuration (automatic split
-    plan): every output against the oracle, with the stated bounds and the per-row relative one;
-    every output finite."""
+    """The five workloads, and the bf16 GQA-8 layer at the Llama-3-8B lengths (one job per
+    workgroup, split sequences merged in the kernel), at full size in the benchmark's launch
+    configuration (automatic split plan): every output against the oracle, with the stated bounds
+    and the per-row relative one; every output finite."""
     w = synth.CONFIGS[name]()
     print(f"{name}: B={w.B} kv_bytes={w.kv_bytes}", flush=True)
     dev = gu.upload(w)
