@@ -90,10 +90,16 @@ KERNEL_SOURCES = ["paged_kv_decode_08_amd/csrc/decode_mfma.hip",
 
 
 def kernel_source_hash():
+    """sha256 of the kernel sources with comments and blank lines removed (no string literal in
+    them holds a comment marker), so that an edit of comments alone keeps the recorded counters."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

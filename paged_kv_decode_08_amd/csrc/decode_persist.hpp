@@ -47,8 +47,9 @@ constexpr int kSizeClasses = 16;
 // Persistent workgroups over a job queue.
 
 // Per-sequence table in LDS. Sequences are ranked by the size of their chunks, largest first (16
-// size classes a quarter octave wide, stable within a class), and jobs are numbered in that order: the queue hands out
-// long jobs first and ends with short ones, which shortens the tail of the call. Jobs of one
+// size classes a quarter octave wide, stable within a class), and jobs are numbered in that
+// order: the queue hands out long jobs first and ends with short ones, which shortens the tail of
+// the call. Jobs of one
 // sequence are ordered chunk-major, KV head minor. What a job needs is stored by rank, so decoding
 // a job number takes two ballots and one round of LDS reads.
 struct SeqTable {
@@ -195,6 +196,16 @@ __device__ __forceinline__ int wave_scan_i(int v) {
   return v;
 }
 
+// A plan of one job per workgroup is taken when no job is above this many times the mean work of
+// a workgroup (the workgroups that finish early leave the chip to the larger jobs, which then
+// stream faster). Where split sequences are merged in the kernel, a second round of jobs also
+// carries the first round's merges, and one round pays off at larger jobs. Measured at the
+// Llama-3-8B lengths: 8 q heads merged in the kernel, one job per workgroup (97-slot chunks, the
+// largest job 1.4x the mean) 60.0 against 62.7 us for two rounds of 64-slot chunks; merged by the
+// split merge kernel, 4 q heads (109-slot chunks, 1.44x) 64.1 against 60.6 us, and 2 or 4 query
+// tokens 65.2 and 68.2 against 61.8 and 66.4 us.
+constexpr float one_job_bound(bool merges_in_kernel) { return merges_in_kernel ? 1.5f : 1.25f; }
+
 // Chunk size in page slots of the automatic plan, chosen from the call's own lengths: N attended
 // slots over the n_seq sequences that have any, at most n_max in one; H KV heads (a job is one
 // chunk of one KV head); P workgroups; at least min_chunk slots and at most max_chunks chunks per
@@ -209,21 +220,12 @@ __device__ __forceinline__ int wave_scan_i(int v) {
 //   (sequence, KV head) pairs: what the host plans from a tight length hint, whose chunk size was
 //   tuned on the Llama-3-8B shape (64 slots there; 61 and 44 slots measured 2.4 and 2.8 us
 //   slower). With more pairs than workgroups this halves the longest sequence.
-// A plan of one job per workgroup is taken when no job is above this many times the mean work of
-// a workgroup (the workgroups that finish early leave the chip to the larger jobs, which then
-// stream faster). Where split sequences are merged in the kernel, a second round of jobs also
-// carries the first round's merges, and one round pays off at larger jobs. Measured at the
-// Llama-3-8B lengths: 8 q heads merged in the kernel, one job per workgroup (97-slot chunks, the
-// largest job 1.4x the mean) 60.0 against 62.7 us for two rounds of 64-slot chunks; merged by the
-// split merge kernel, 4 q heads (109-slot chunks, 1.44x) 64.1 against 60.6 us, and 2 or 4 query
-// tokens 65.2 and 68.2 against 61.8 and 66.4 us.
-constexpr float one_job_bound(bool merges_in_kernel) { return merges_in_kernel ? 1.5f : 1.25f; }
 template <typename Jobs>
 __device__ int auto_chunk_slots(float N, int n_seq, int n_max, int H, int P, int min_chunk,
                                 int max_chunks, float one_job, Jobs jobs) {
   // Every workgroup runs this in its prologue, so it decides from single-precision estimates
-  // (the same on every workgroup) and counts jobs at most twice: 64-bit divisions and a search
-  // here measured 2.3 us per call on the Llama-3-8B shape.
+  // (the same on every workgroup) and counts jobs at most four times: 64-bit divisions and a
+  // search here measured 2.3 us per call on the Llama-3-8B shape.
   if (n_max <= 0) return max(min_chunk, 1);
   min_chunk = max(min_chunk, (n_max + max_chunks - 1) / max_chunks);
   auto up = [](float x) { return int(fminf(ceilf(x), 1073741824.f)); };
