@@ -206,6 +206,12 @@ __device__ __forceinline__ int wave_scan_i(int v) {
 // tokens 65.2 and 68.2 against 61.8 and 66.4 us.
 constexpr float one_job_bound(bool merges_in_kernel) { return merges_in_kernel ? 1.5f : 1.25f; }
 
+// With more (sequence, KV head) pairs than workgroups, sequences stay whole when the longest is at
+// most this many times the mean work of a workgroup. Measured: fp8 GQA-8 shape (2048 pairs) 200.4
+// against 210.3 us with the longest sequence halved; 1024 and 512 sequences of 64-1023 rows (8
+// KV heads) 403.5 and 191.1 against 466.4 and 222.4 us.
+constexpr float kWholeSeqBound = 1.0f;
+
 // Chunk size in page slots of the automatic plan, chosen from the call's own lengths: N attended
 // slots over the n_seq sequences that have any, at most n_max in one; H KV heads (a job is one
 // chunk of one KV head); P workgroups; at least min_chunk slots and at most max_chunks chunks per
@@ -219,7 +225,8 @@ constexpr float one_job_bound(bool merges_in_kernel) { return merges_in_kernel ?
 // * Otherwise about max(2 P, 2 pairs) chunks of the longest sequence's size over the
 //   (sequence, KV head) pairs: what the host plans from a tight length hint, whose chunk size was
 //   tuned on the Llama-3-8B shape (64 slots there; 61 and 44 slots measured 2.4 and 2.8 us
-//   slower). With more pairs than workgroups this halves the longest sequence.
+//   slower). With more pairs than workgroups: whole sequences if none is above kWholeSeqBound
+//   times the mean work of a workgroup, else the longest sequence halved.
 template <typename Jobs>
 __device__ int auto_chunk_slots(float N, int n_seq, int n_max, int H, int P, int min_chunk,
                                 int max_chunks, float one_job, Jobs jobs) {
@@ -248,6 +255,9 @@ __device__ int auto_chunk_slots(float N, int n_seq, int n_max, int H, int P, int
     if (!fits) c = n_max;
     if (float(c) <= lim) return c;
   }
+  // more pairs than workgroups: whole sequences while the longest is no more than the mean work
+  // of a workgroup (the queue, largest first, then balances them); else halve the longest
+  if (pairs > float(P) && float(n_max) <= kWholeSeqBound * NH / float(P)) return max(min_chunk, n_max);
   const float target = fmaxf(2.f * float(P), 2.f * pairs);
   return max(min_chunk, up(pairs * float(n_max) / target));
 }
