@@ -106,9 +106,11 @@ typedef struct pdecode_desc {
                              the bound is still computed exactly.                               */
   int32_t num_kv_splits;  /* 0 = automatic: for bf16 / fp8 KV and batch <= 1024 the chunk size is
                              chosen on the device at each call from the lengths (about one or two
-                             jobs per resident workgroup); 1 = never split a sequence; n > 1 =
-                             split each sequence's pages into at most n chunks merged by
-                             log-sum-exp                                                        */
+                             jobs per resident workgroup where sequences must be split to fill
+                             the chip; whole sequences where (sequence, KV head) pairs outnumber
+                             the resident workgroups and none exceeds a workgroup's share);
+                             1 = never split a sequence; n > 1 = split each sequence's pages
+                             into at most n chunks merged by log-sum-exp                        */
   const float *k_scale;   /* device fp32 [H_kv]; required iff kv_dtype is an FP8: K = code * scale */
   const float *v_scale;   /* device fp32 [H_kv]; required iff kv_dtype is an FP8: V = code * scale */
   const float *sink_logits; /* device fp32 [H_qo] or NULL: learned attention sink per q head (the
